@@ -162,6 +162,10 @@ void or_q8k_pack(const float* x, int64_t T, int64_t K, int8_t* qs, float* d, int
             for (int i = 0; i < QK; ++i) {
                 float v = xb[i] * iscale; /* one fp32 multiply */
                 float r = nearbyintf(v);  /* default mode: round half to even */
+                /* When 127/amax overflows to inf (amax below ~3.7e-37) a zero
+                   value gives 0*inf = NaN: its code is 0; nonzero values
+                   saturate to +-127 through the clamp below. */
+                if (r != r) r = 0.0f;
                 if (r > 127.0f) r = 127.0f;
                 if (r < -127.0f) r = -127.0f;
                 qb[i] = (int8_t)r;
