@@ -1,0 +1,155 @@
+/*
+ * q8k.h -- C ABI of libq8k: GGUF K-quant weights (Q4_K, Q6_K) times
+ * activations packed on the GPU into q8_K blocks, on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operations follow "Language models on the device: the cajeta-llm
+ * kernels" (cajeta.dev/xpu/kernels-llm/):
+ *   - section 1: weights arrive in GGUF K-quant blocks (256 values, per
+ *     sub-block scales); activations are quantised on the device to q8_K
+ *     (256 values a block, one scale, eight sub-block sums); an integer dot
+ *     product does the arithmetic and the per-sub-block scales and mins are
+ *     applied in an epilogue; at bind, Q6_K blocks may be split into a scale
+ *     prefix and 208-byte bodies so kernels read them with aligned 16-byte
+ *     loads;
+ *   - section 2.1: decode mat-vec, one wavefront owns one output row;
+ *   - section 2.2: batched decode, one pass over a weight row serves several
+ *     activation columns;
+ *   - section 2.3: prefill, a tiled matrix-core GEMM with a scale epilogue;
+ *   - section 2.4: mixture of experts, a decode mat-vec that visits each
+ *     token's selected experts and sums their weighted outputs;
+ *   - section 3.2 (and SKaiNET's "Kernel SPI and the selection algorithm",
+ *     decline reasons): the input width must be a multiple of 256.
+ *
+ * Conventions for every entry point
+ *   - Buffers are device pointers owned by the caller; the library never
+ *     allocates, never synchronises and keeps no state besides the calling
+ *     thread's last-error text.  Buffers must stay alive until the work
+ *     enqueued on `stream` has finished.
+ *   - `stream` is a hipStream_t (NULL = the default stream).
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     refusal returns a non-zero q8k_status, enqueues nothing, leaves every
+ *     output untouched and sets q8k_last_error() to a message naming the
+ *     rule and the values.  Refusals are never replaced by a fallback.
+ *   - Q8K_OK means the kernels were enqueued and will overwrite every element
+ *     of the outputs (nothing is accumulated into what the caller passed).
+ *   - Sizes: K (the reduction width) must be a positive multiple of 256.
+ *     Zero rows / tokens are accepted and enqueue nothing.
+ *   - Alignment: weights, packed activations, fp32 inputs and workspaces must
+ *     be 16-byte aligned; fp32 outputs, ids and router weights 4-byte aligned.
+ *   - Device-side values are not inspected (that would need a sync): x must be
+ *     finite; an expert id outside [0, E) selects nothing.
+ */
+#ifndef Q8K_H
+#define Q8K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q8K_OK = 0,
+    Q8K_ERR_NULL = 1,      /* a required pointer is NULL                        */
+    Q8K_ERR_SHAPE = 2,     /* K not a positive multiple of 256, negative size,  */
+                           /* or a size beyond the supported maximum            */
+    Q8K_ERR_ALIGN = 3,     /* a pointer is not aligned as required              */
+    Q8K_ERR_QTYPE = 4,     /* weight format not served by this entry point      */
+    Q8K_ERR_ARG = 5,       /* topk / ncols / E / token count out of range       */
+    Q8K_ERR_WORKSPACE = 6, /* workspace smaller than the size helper reports    */
+    Q8K_ERR_LAUNCH = 7     /* the HIP runtime refused the launch                */
+} q8k_status;
+
+typedef enum {
+    Q8K_Q4_K = 1,        /* GGUF Q4_K: 144-byte blocks, row-major block order   */
+    Q8K_Q6_K_RELAID = 2, /* Q6_K after q8k_bind_q6k: fp16 prefix + 208-B bodies */
+    Q8K_Q6_K_GGUF = 3    /* raw GGUF Q6_K (210-byte blocks): bind input only    */
+} q8k_qtype;
+
+#define Q8K_QK 256         /* values per K-quant super-block / q8_K block       */
+#define Q8K_COLS_MAX 8     /* most activation columns qmatvec_batched serves    */
+#define Q8K_MOE_MAX_TOKENS 256 /* most tokens qmatvec_moe serves per call       */
+
+/* ---------------------------------------------------------------- sizing --
+ * q8_K activation buffer for T tokens of K values: three sections, each
+ * starting on a 256-byte boundary:
+ *   qs    int8  [T][K]          at offset 0
+ *   d     fp32  [T][K/256]      at *off_d      (block scale, amax/127)
+ *   bsums int16 [T][K/32]       at *off_bsums  (sum of the 32 codes of each of
+ *                                               the block's eight sub-blocks)
+ * Returns the total size in bytes (0 if K is not a positive multiple of 256
+ * or T < 0).  off_d / off_bsums may be NULL. */
+size_t q8k_act_bytes(int64_t T, int64_t K);
+size_t q8k_act_layout(int64_t T, int64_t K, size_t* off_d, size_t* off_bsums);
+
+/* Bytes of a rows x K weight in the given layout (0 on a bad shape):
+ *   Q8K_Q4_K         rows*K/256 blocks of 144 B;
+ *   Q8K_Q6_K_GGUF    rows*K/256 blocks of 210 B;
+ *   Q8K_Q6_K_RELAID  fp16 d prefix [rows*K/256] padded to 256 B, then
+ *                    rows*K/256 bodies of 208 B (ql[128] | qh[64] | scales[16]);
+ *                    block (r, b) is entry r*K/256 + b of both arrays. */
+size_t q8k_weight_bytes(int qtype, int64_t rows, int64_t K);
+
+/* ------------------------------------------------------------ operations --
+ * q8k_pack: quantise x (fp32 [T][K], row-major) into the q8_K buffer xq.
+ * Per 256-value block: amax = max |x|; d = amax/127 (0 for an all-zero
+ * block); qs = round-half-even(x * (127/amax)) clamped to [-127, 127], all in
+ * fp32 (correctly rounded division, single multiply); bsums = int16 sums of
+ * the eight 32-value groups of qs. */
+int q8k_pack(const float* x, int64_t T, int64_t K, void* xq, void* stream);
+
+/* q8k_bind_q6k: bind-time relayout of a raw GGUF Q6_K weight (rows x K) into
+ * the Q8K_Q6_K_RELAID layout (scale prefix + 208-byte bodies).  Byte moves
+ * only.  w_gguf may be 2-byte aligned; w_relaid must be 16-byte aligned and
+ * q8k_weight_bytes(Q8K_Q6_K_RELAID, rows, K) long. */
+int q8k_bind_q6k(const void* w_gguf, int64_t rows, int64_t K, void* w_relaid, void* stream);
+
+/* qmatvec: decode mat-vec for one packed token.
+ *   y[r] = sum_b d8_b * (d_rb * sum_j sc_rbj * S_rbj - dmin_rb * sum_j m_rbj * bsums_bj)   (Q4_K)
+ *   y[r] = sum_b d8_b * d_rb * sum_s sc_rbs * S_rbs                                        (Q6_K)
+ * with S the exact int32 sub-block sums of quant x code (Q6_K quants minus 32).
+ * qtype: Q8K_Q4_K or Q8K_Q6_K_RELAID.  xq: q8_K buffer of one token (T = 1).
+ * y: fp32 [rows]. */
+int qmatvec(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, float* y, void* stream);
+
+/* qmatvec_batched: the same for ncols packed tokens (1 <= ncols <=
+ * Q8K_COLS_MAX), each weight row read once for all columns.
+ * xq: q8_K buffer of T = ncols tokens.  y: fp32 [ncols][rows]. */
+int qmatvec_batched(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int64_t ncols, float* y,
+                    void* stream);
+
+/* qmatvec_moe: expert-indexed decode.  w holds E experts, each a rows x K
+ * weight in the given layout, expert e's blocks following expert e-1's.
+ * xq: q8_K buffer of T tokens (0 <= T <= Q8K_MOE_MAX_TOKENS); ids int32
+ * [T][topk]; rw fp32 [T][topk]; 1 <= topk <= E.
+ *   y[t][r] = sum_k rw[t][k] * (W_{ids[t][k]} x_t)[r]
+ * Each expert row that at least one token selected is read once for all of
+ * its tokens; an expert nobody selected is not read.  y: fp32 [T][rows]. */
+int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq, int64_t T,
+                const int32_t* ids, const float* rw, int32_t topk, float* y, void* stream);
+
+/* qmatmul_prefill: y[m][n] = qmatvec's formula for every token m < M and
+ * weight row n < rows, computed as a tiled int8 matrix-core GEMM.
+ * qtype: Q8K_Q4_K.  xq: q8_K buffer of M tokens.  y: fp32 [M][rows].
+ * ws / ws_bytes: caller-owned workspace of at least
+ * qmatmul_prefill_workspace_bytes(...) bytes (may be NULL when that is 0). */
+size_t qmatmul_prefill_workspace_bytes(int qtype, int64_t rows, int64_t K, int64_t M);
+int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int64_t M, float* y, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* Test support: the exact int32 sub-block sums of every weight row against
+ * one packed token, computed by the same device code as qmatvec.
+ * S: int32 [rows][K/32] for Q8K_Q4_K, [rows][K/16] for Q8K_Q6_K_RELAID. */
+int q8k_debug_subblock_sums(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int32_t* S,
+                            void* stream);
+
+/* ---------------------------------------------------------------- errors -- */
+const char* q8k_status_str(int status);
+const char* q8k_last_error(void); /* calling thread's last refusal message */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q8K_H */

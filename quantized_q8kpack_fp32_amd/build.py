@@ -1,0 +1,83 @@
+"""Build libq8k.so in-tree for gfx950 with hipcc.
+
+Every source is compiled for gfx950 only, with packed FP32 instructions
+disabled, and the kernel resource report of each translation unit is checked:
+a kernel that uses scratch (spills) fails the build, since a spilling kernel is
+not a tuned kernel (the build gate idea of "One kernel, any device", section
+2.2).  Usage: ``python -m quantized_q8kpack_fp32_amd.build`` (or via
+``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import re
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+OUT = os.path.join(HERE, "libq8k.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+SOURCES = ["api.cpp", "pack.hip", "matvec.hip", "moe.hip", "prefill.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-Rpass-analysis=kernel-resource-usage",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+_SCRATCH = re.compile(r"remark: .*?:\d+:\d+: Function Name: (\S+)")
+_SCRATCH_SIZE = re.compile(r"ScratchSize \[bytes/lane\]: (\d+)")
+
+
+def _compile(src: str) -> tuple[str, str]:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    return obj, r.stderr
+
+
+def _check_scratch(log: str, src: str) -> list[str]:
+    """Return 'kernel: N bytes' for every kernel in the report that uses scratch."""
+    bad = []
+    name = None
+    for line in log.splitlines():
+        m = _SCRATCH.search(line)
+        if m:
+            name = m.group(1)
+            continue
+        m = _SCRATCH_SIZE.search(line)
+        if m and name is not None and int(m.group(1)) > 0:
+            bad.append(f"{src}: {name}: {m.group(1)} bytes/lane of scratch")
+    return bad
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    problems = []
+    for src, (_, log) in zip(SOURCES, results):
+        problems += _check_scratch(log, src)
+        if verbose:
+            sys.stderr.write(log)
+    if problems:
+        raise RuntimeError("kernels using scratch (spills):\n  " + "\n  ".join(problems))
+    tmp = OUT + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

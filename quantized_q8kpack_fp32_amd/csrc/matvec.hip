@@ -1,0 +1,201 @@
+// Decode mat-vecs for Q4_K and relaid Q6_K weights against q8_K activations.
+//
+// "Language models on the device: the cajeta-llm kernels", section 2.1: one
+// wavefront owns one output row; consecutive lanes read consecutive bytes of
+// the row's blocks as whole words, dot them with the matching q8_K codes using
+// the integer dot product, fold the sub-block scales, and a wave reduction
+// finishes the row.  Section 2.2: the batched form reads each weight row once
+// for up to Q8K_COLS_MAX activation columns.
+//
+// Lane map (gfx950 wave64): lane l serves block b = 8k + (l >> 3) of the row
+// (k = 0, 1, ...) and its 16-byte quant chunk ci = l & 7, so each 64-lane
+// load instruction covers the quant bytes of eight consecutive blocks.
+#include "kquant.h"
+#include "q8k_launch.h"
+
+namespace q8k {
+
+template <int NC>
+__global__ __launch_bounds__(256) void matvec_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
+                                                         const int8_t* __restrict__ qs, const float* __restrict__ d8,
+                                                         const int16_t* __restrict__ bs, int64_t K,
+                                                         float* __restrict__ y) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;  // uniform per wave
+    const int ci = lane & 7, c = ci >> 1, half = ci & 1;
+    const uint8_t* wr = w + row * (int64_t)nb * Q4K_BLOCK;
+    float acc[NC];
+#pragma unroll
+    for (int t = 0; t < NC; ++t) acc[t] = 0.0f;
+    for (int b = lane >> 3; b < nb; b += 8) {
+        const uint8_t* blk = wr + (int64_t)b * Q4K_BLOCK;
+        const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
+        const uint4 qv = *reinterpret_cast<const uint4*>(blk + 16 + 16 * ci);
+        int sc0, sc1, m0, m1;
+        q4k_scales(hdr, c, sc0, sc1, m0, m1);
+        const float dd = half_bits_to_float(hdr.x & 0xffffu);
+        const float dm = half_bits_to_float(hdr.x >> 16);
+        uint32_t lo[4], hi[4];
+        q4k_unpack(qv, lo, hi);
+#pragma unroll
+        for (int t = 0; t < NC; ++t) {
+            const int8_t* a = qs + t * K + (int64_t)b * QK + 64 * c + 16 * half;
+            const int4 alo = *reinterpret_cast<const int4*>(a);
+            const int4 ahi = *reinterpret_cast<const int4*>(a + 32);
+            const uint32_t bb = *reinterpret_cast<const uint32_t*>(bs + ((int64_t)t * nb + b) * 8 + 2 * c);
+            int S0, S1;
+            q4k_chunk_sums(lo, hi, alo, ahi, S0, S1);
+            const int isum = sc0 * S0 + sc1 * S1;
+            // the min term uses whole sub-block sums: counted once per chunk pair
+            const int msum = half ? 0 : m0 * (int)(int16_t)(bb & 0xffffu) + m1 * (int)(int16_t)(bb >> 16);
+            acc[t] += d8[(int64_t)t * nb + b] * (dd * (float)isum - dm * (float)msum);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+        const float v = wave_sum(acc[t]);
+        if (lane == 0) y[(int64_t)t * rows + row] = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void sums_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
+                                                       const int8_t* __restrict__ qs, int32_t* __restrict__ S) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const int ci = lane & 7, c = ci >> 1, half = ci & 1;
+    const uint8_t* wr = w + row * (int64_t)nb * Q4K_BLOCK;
+    for (int b = lane >> 3; b < nb; b += 8) {
+        const uint4 qv = *reinterpret_cast<const uint4*>(wr + (int64_t)b * Q4K_BLOCK + 16 + 16 * ci);
+        const int8_t* a = qs + (int64_t)b * QK + 64 * c + 16 * half;
+        uint32_t lo[4], hi[4];
+        q4k_unpack(qv, lo, hi);
+        int S0, S1;
+        q4k_chunk_sums(lo, hi, *reinterpret_cast<const int4*>(a), *reinterpret_cast<const int4*>(a + 32), S0, S1);
+        // the two halves of each sub-block sit in lanes ci and ci^1
+        S0 += __shfl_xor(S0, 1, WAVE);
+        S1 += __shfl_xor(S1, 1, WAVE);
+        if (!half) {
+            S[(row * nb + b) * 8 + 2 * c] = S0;
+            S[(row * nb + b) * 8 + 2 * c + 1] = S1;
+        }
+    }
+}
+
+template <int NC>
+__global__ __launch_bounds__(256) void matvec_q6k_kernel(const uint16_t* __restrict__ prefix,
+                                                         const uint8_t* __restrict__ bodies, int64_t rows, int nb,
+                                                         const int8_t* __restrict__ qs, const float* __restrict__ d8,
+                                                         int64_t K, float* __restrict__ y) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const int ci = lane & 7, h = ci >> 2, tt = (ci >> 1) & 1, lh = ci & 1;
+    const int s0 = 8 * h + 2 * tt + lh;
+    const int aoff = 128 * h + 32 * tt + 16 * lh;
+    float acc[NC];
+#pragma unroll
+    for (int t = 0; t < NC; ++t) acc[t] = 0.0f;
+    for (int b = lane >> 3; b < nb; b += 8) {
+        const int64_t ib = row * nb + b;
+        const uint8_t* body = bodies + ib * Q6K_BODY;
+        const uint4 qlv = *reinterpret_cast<const uint4*>(body + 16 * ci);
+        const uint4 qhv = *reinterpret_cast<const uint4*>(body + 128 + 16 * (2 * h + lh));
+        const uint4 scv = *reinterpret_cast<const uint4*>(body + 192);
+        const int sc0 = (int)(int8_t)byte_of(scv, s0);
+        const int sc1 = (int)(int8_t)byte_of(scv, s0 + 4);
+        const float dd = half_bits_to_float(prefix[ib]);
+        uint32_t lo[4], hi[4];
+        q6k_unpack(qlv, qhv, tt, lo, hi);
+#pragma unroll
+        for (int t = 0; t < NC; ++t) {
+            const int8_t* a = qs + t * K + (int64_t)b * QK + aoff;
+            const int S0 = q6k_sum16(lo, *reinterpret_cast<const int4*>(a));
+            const int S1 = q6k_sum16(hi, *reinterpret_cast<const int4*>(a + 64));
+            acc[t] += d8[(int64_t)t * nb + b] * dd * (float)(sc0 * S0 + sc1 * S1);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+        const float v = wave_sum(acc[t]);
+        if (lane == 0) y[(int64_t)t * rows + row] = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void sums_q6k_kernel(const uint8_t* __restrict__ bodies, int64_t rows, int nb,
+                                                       const int8_t* __restrict__ qs, int32_t* __restrict__ S) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const int ci = lane & 7, h = ci >> 2, tt = (ci >> 1) & 1, lh = ci & 1;
+    const int s0 = 8 * h + 2 * tt + lh;
+    const int aoff = 128 * h + 32 * tt + 16 * lh;
+    for (int b = lane >> 3; b < nb; b += 8) {
+        const int64_t ib = row * nb + b;
+        const uint8_t* body = bodies + ib * Q6K_BODY;
+        uint32_t lo[4], hi[4];
+        q6k_unpack(*reinterpret_cast<const uint4*>(body + 16 * ci),
+                   *reinterpret_cast<const uint4*>(body + 128 + 16 * (2 * h + lh)), tt, lo, hi);
+        const int8_t* a = qs + (int64_t)b * QK + aoff;
+        S[ib * 16 + s0] = q6k_sum16(lo, *reinterpret_cast<const int4*>(a));
+        S[ib * 16 + s0 + 4] = q6k_sum16(hi, *reinterpret_cast<const int4*>(a + 64));
+    }
+}
+
+// ----------------------------------------------------------- launchers ----
+template <int NC>
+static void go_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, float* y, hipStream_t s) {
+    hipLaunchKernelGGL(matvec_q4k_kernel<NC>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb, a.qs, a.d,
+                       a.bs, a.K, y);
+}
+template <int NC>
+static void go_q6k(const uint16_t* p, const uint8_t* bodies, int64_t rows, int nb, Acts a, float* y, hipStream_t s) {
+    hipLaunchKernelGGL(matvec_q6k_kernel<NC>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, bodies, rows, nb,
+                       a.qs, a.d, a.K, y);
+}
+
+hipError_t launch_matvec_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int ncols, float* y, hipStream_t s) {
+    switch (ncols) {
+        case 1: go_q4k<1>(w, rows, nb, a, y, s); break;
+        case 2: go_q4k<2>(w, rows, nb, a, y, s); break;
+        case 3: go_q4k<3>(w, rows, nb, a, y, s); break;
+        case 4: go_q4k<4>(w, rows, nb, a, y, s); break;
+        case 5: go_q4k<5>(w, rows, nb, a, y, s); break;
+        case 6: go_q4k<6>(w, rows, nb, a, y, s); break;
+        case 7: go_q4k<7>(w, rows, nb, a, y, s); break;
+        case 8: go_q4k<8>(w, rows, nb, a, y, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_matvec_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t rows, int nb, Acts a, int ncols,
+                             float* y, hipStream_t s) {
+    switch (ncols) {
+        case 1: go_q6k<1>(prefix, bodies, rows, nb, a, y, s); break;
+        case 2: go_q6k<2>(prefix, bodies, rows, nb, a, y, s); break;
+        case 3: go_q6k<3>(prefix, bodies, rows, nb, a, y, s); break;
+        case 4: go_q6k<4>(prefix, bodies, rows, nb, a, y, s); break;
+        case 5: go_q6k<5>(prefix, bodies, rows, nb, a, y, s); break;
+        case 6: go_q6k<6>(prefix, bodies, rows, nb, a, y, s); break;
+        case 7: go_q6k<7>(prefix, bodies, rows, nb, a, y, s); break;
+        case 8: go_q6k<8>(prefix, bodies, rows, nb, a, y, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sums_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int32_t* S, hipStream_t s) {
+    hipLaunchKernelGGL(sums_q4k_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb, a.qs, S);
+    return hipGetLastError();
+}
+
+hipError_t launch_sums_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t rows, int nb, Acts a, int32_t* S,
+                           hipStream_t s) {
+    (void)prefix;
+    hipLaunchKernelGGL(sums_q6k_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, bodies, rows, nb, a.qs, S);
+    return hipGetLastError();
+}
+
+}  // namespace q8k

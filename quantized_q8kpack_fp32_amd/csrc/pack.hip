@@ -1,0 +1,79 @@
+// q8_K activation packing and the bind-time Q6_K relayout.
+//
+// q8_K: 256 values a block, one scale and eight sub-block sums ("Language
+// models on the device: the cajeta-llm kernels", section 1; the device
+// quantiser is listed among the utility kernels of section 2.6).
+// Q6_K relayout: split each block into a scale prefix and a 208-byte body so
+// that kernels read bodies with aligned 16-byte loads (same page, section 1).
+#include "q8k_device.h"
+#include "q8k_launch.h"
+
+namespace q8k {
+
+// One wavefront per 256-value block; lane l owns values 4l..4l+3 (one 16-byte
+// load), so the eight lanes 8j..8j+7 hold sub-block j.
+__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ x, int64_t nblocks,
+                                                   int8_t* __restrict__ qs, float* __restrict__ d,
+                                                   int16_t* __restrict__ bsums) {
+    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (blk >= nblocks) return;  // uniform per wave
+    const float4 v = *reinterpret_cast<const float4*>(x + blk * QK + lane * 4);
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    amax = wave_max(amax);
+    int q[4] = {0, 0, 0, 0};
+    if (amax != 0.0f) {
+        // IEEE division (hipcc keeps fp32 '/' correctly rounded by default),
+        // then one multiply and round-half-even per value.
+        const float iscale = 127.0f / amax;
+        const float xs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float r = __builtin_rintf(xs[i] * iscale);
+            if (r != r) r = 0.0f;  // 0 * inf when 127/amax overflows
+            r = r > 127.0f ? 127.0f : r;
+            r = r < -127.0f ? -127.0f : r;
+            q[i] = (int)r;
+        }
+    }
+    const uint32_t packed = (uint32_t)(q[0] & 255) | ((uint32_t)(q[1] & 255) << 8) | ((uint32_t)(q[2] & 255) << 16) |
+                            ((uint32_t)(q[3] & 255) << 24);
+    *reinterpret_cast<uint32_t*>(qs + blk * QK + lane * 4) = packed;
+    int s = q[0] + q[1] + q[2] + q[3];
+    s += __shfl_xor(s, 1, WAVE);
+    s += __shfl_xor(s, 2, WAVE);
+    s += __shfl_xor(s, 4, WAVE);
+    if ((lane & 7) == 0) bsums[blk * 8 + (lane >> 3)] = (int16_t)s;
+    if (lane == 0) d[blk] = amax != 0.0f ? amax / 127.0f : 0.0f;
+}
+
+hipError_t launch_pack(const float* x, int64_t nblocks, int8_t* qs, float* d, int16_t* bsums, hipStream_t s) {
+    const int64_t grid = (nblocks + 3) / 4;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nblocks, qs, d, bsums);
+    return hipGetLastError();
+}
+
+// One wavefront per block.  The 210-byte source blocks are only 2-byte
+// aligned: lanes 0..51 each assemble one 32-bit word of the body from two
+// halfwords; lane 52 moves the fp16 scale into the prefix.
+__global__ __launch_bounds__(256) void bind_q6k_kernel(const uint8_t* __restrict__ src, int64_t nblocks,
+                                                       uint16_t* __restrict__ prefix, uint8_t* __restrict__ bodies) {
+    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (blk >= nblocks) return;
+    const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src + blk * Q6K_BLOCK);
+    if (lane < Q6K_BODY / 4) {
+        const uint32_t word = (uint32_t)s16[2 * lane] | ((uint32_t)s16[2 * lane + 1] << 16);
+        reinterpret_cast<uint32_t*>(bodies + blk * Q6K_BODY)[lane] = word;
+    } else if (lane == Q6K_BODY / 4) {
+        prefix[blk] = s16[Q6K_BODY / 2];
+    }
+}
+
+hipError_t launch_bind_q6k(const uint8_t* src, int64_t nblocks, uint16_t* prefix, uint8_t* bodies, hipStream_t s) {
+    const int64_t grid = (nblocks + 3) / 4;
+    hipLaunchKernelGGL(bind_q6k_kernel, dim3((unsigned)grid), dim3(256), 0, s, src, nblocks, prefix, bodies);
+    return hipGetLastError();
+}
+
+}  // namespace q8k

@@ -1,0 +1,54 @@
+// Internal device helpers for the gfx950 kernels (wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q8k {
+
+constexpr int QK = 256;          // values per K-quant super-block and q8_K block
+constexpr int Q4K_BLOCK = 144;   // GGUF Q4_K block bytes
+constexpr int Q6K_BLOCK = 210;   // GGUF Q6_K block bytes
+constexpr int Q6K_BODY = 208;    // Q6_K body after the bind relayout
+constexpr int WAVE = 64;
+
+__host__ __device__ constexpr size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// q8_K activation buffer sections (see include/q8k.h).
+struct ActLayout {
+    size_t off_d, off_bs, total;
+};
+__host__ __device__ inline ActLayout act_layout(int64_t T, int64_t K) {
+    ActLayout l;
+    size_t nb = (size_t)T * (size_t)(K / QK);
+    l.off_d = align256((size_t)T * (size_t)K);
+    l.off_bs = align256(l.off_d + 4 * nb);
+    l.total = align256(l.off_bs + 2 * 8 * nb);
+    return l;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// int8x4 . int8x4 + acc, signed (v_dot4_i32_i8).
+__device__ __forceinline__ int sdot4(int a, int b, int acc) { return __builtin_amdgcn_sdot4(a, b, acc, false); }
+
+// Butterfly sums / max over the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, WAVE);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, WAVE));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t byte_of(uint4 v, int i) {
+    uint32_t w = (i < 4) ? v.x : (i < 8) ? v.y : (i < 12) ? v.z : v.w;
+    return (w >> (8 * (i & 3))) & 0xffu;
+}
+
+}  // namespace q8k

@@ -1,0 +1,121 @@
+"""The C ABI library on the CPU: it loads, exports every symbol declared in
+include/q8k.h, sizes buffers as documented, and refuses bad arguments by name
+before touching the GPU (no kernel is launched here).
+
+Named refusals and the 256-multiple width rule: "One kernel, any device"
+(cajeta.dev/xpu/, section 1, checked launches) and "Language models on the
+device: the cajeta-llm kernels" (section 3.2); SKaiNET's "Kernel SPI and the
+selection algorithm" (decline reasons, block alignment).
+"""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def q():
+    import quantized_q8kpack_fp32_amd as q
+
+    return q
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "q8k.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M))
+
+
+def test_exports_every_declared_symbol(q):
+    declared = header_functions()
+    assert declared == set(q.EXPORTED), declared ^ set(q.EXPORTED)
+    for name in declared:
+        assert hasattr(q.lib, name), name
+
+
+def test_act_layout(q):
+    total, od, ob = q.q8k_act_layout(1, 4096)
+    assert (od, ob, total) == (4096, 4352, 4608)
+    total, od, ob = q.q8k_act_layout(512, 14336)
+    assert od == 512 * 14336 and od % 256 == 0
+    assert ob == od + 4 * 512 * 56 and ob % 256 == 0
+    assert total == ob + 2 * 8 * 512 * 56
+    assert q.q8k_act_bytes(3, 1000) == 0 and q.q8k_act_bytes(-1, 256) == 0
+
+
+def test_weight_bytes(q):
+    assert q.q8k_weight_bytes(q.Q8K_Q4_K, 4096, 4096) == 9437184
+    assert q.q8k_weight_bytes(q.Q8K_Q6_K_GGUF, 32000, 4096) == 107520000
+    nblk = 32000 * 16
+    assert q.q8k_weight_bytes(q.Q8K_Q6_K_RELAID, 32000, 4096) == ((2 * nblk + 255) // 256) * 256 + 208 * nblk
+    assert q.q8k_weight_bytes(9, 1, 256) == 0
+
+
+A16 = 1 << 20  # an aligned fake device address: never dereferenced (refused first)
+
+
+def refused(q, status_name, fn, *args):
+    with pytest.raises(q.Q8KError) as ei:
+        fn(*args)
+    assert ei.value.name == status_name, str(ei.value)
+    return str(ei.value)
+
+
+def test_k_must_be_multiple_of_256(q):
+    msg = refused(q, "Q8K_ERR_SHAPE", q.qmatvec, q.Q8K_Q4_K, A16, 4, 1000, A16, A16, 0)
+    assert "K=1000" in msg and "256" in msg
+    refused(q, "Q8K_ERR_SHAPE", q.q8k_pack, A16, 1, 0, A16, 0)
+    refused(q, "Q8K_ERR_SHAPE", q.q8k_pack, A16, 1, -256, A16, 0)
+    refused(q, "Q8K_ERR_SHAPE", q.qmatmul_prefill, q.Q8K_Q4_K, A16, 8, 300, A16, 4, A16, None, 0, 0)
+    refused(q, "Q8K_ERR_SHAPE", q.qmatvec, q.Q8K_Q4_K, A16, 4, (1 << 24) + 256, A16, A16, 0)
+
+
+def test_negative_sizes(q):
+    refused(q, "Q8K_ERR_SHAPE", q.qmatvec, q.Q8K_Q4_K, A16, -1, 256, A16, A16, 0)
+    refused(q, "Q8K_ERR_SHAPE", q.q8k_pack, A16, -3, 256, A16, 0)
+    refused(q, "Q8K_ERR_SHAPE", q.qmatmul_prefill, q.Q8K_Q4_K, A16, 8, 256, A16, -1, A16, None, 0, 0)
+
+
+def test_null_and_alignment(q):
+    refused(q, "Q8K_ERR_NULL", q.qmatvec, q.Q8K_Q4_K, None, 4, 256, A16, A16, 0)
+    refused(q, "Q8K_ERR_NULL", q.q8k_pack, None, 1, 256, A16, 0)
+    msg = refused(q, "Q8K_ERR_ALIGN", q.qmatvec, q.Q8K_Q4_K, A16 + 4, 4, 256, A16, A16, 0)
+    assert "16-byte" in msg
+    refused(q, "Q8K_ERR_ALIGN", q.qmatvec, q.Q8K_Q4_K, A16, 4, 256, A16 + 8, A16, 0)
+    refused(q, "Q8K_ERR_ALIGN", q.qmatvec, q.Q8K_Q4_K, A16, 4, 256, A16, A16 + 2, 0)
+    refused(q, "Q8K_ERR_ALIGN", q.q8k_bind_q6k, A16 + 1, 4, 256, A16, 0)
+
+
+def test_qtype_refusals(q):
+    msg = refused(q, "Q8K_ERR_QTYPE", q.qmatvec, q.Q8K_Q6_K_GGUF, A16, 4, 256, A16, A16, 0)
+    assert "q8k_bind_q6k" in msg
+    refused(q, "Q8K_ERR_QTYPE", q.qmatvec, 42, A16, 4, 256, A16, A16, 0)
+    refused(q, "Q8K_ERR_QTYPE", q.qmatmul_prefill, q.Q8K_Q6_K_RELAID, A16, 8, 256, A16, 4, A16, None, 0, 0)
+
+
+def test_batched_and_moe_arguments(q):
+    refused(q, "Q8K_ERR_ARG", q.qmatvec_batched, q.Q8K_Q4_K, A16, 4, 256, A16, 0, A16, 0)
+    refused(q, "Q8K_ERR_ARG", q.qmatvec_batched, q.Q8K_Q4_K, A16, 4, 256, A16, q.Q8K_COLS_MAX + 1, A16, 0)
+    refused(q, "Q8K_ERR_ARG", q.qmatvec_moe, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, A16, A16, 0, A16, 0)
+    refused(q, "Q8K_ERR_ARG", q.qmatvec_moe, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, A16, A16, 9, A16, 0)
+    refused(q, "Q8K_ERR_ARG", q.qmatvec_moe, q.Q8K_Q4_K, A16, 0, 4, 256, A16, 16, A16, A16, 1, A16, 0)
+    refused(q, "Q8K_ERR_ARG", q.qmatvec_moe, q.Q8K_Q4_K, A16, 8, 4, 256, A16, q.Q8K_MOE_MAX_TOKENS + 1,
+            A16, A16, 2, A16, 0)
+    refused(q, "Q8K_ERR_NULL", q.qmatvec_moe, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, None, A16, 2, A16, 0)
+
+
+def test_empty_inputs_enqueue_nothing(q):
+    # zero rows / tokens are valid and return before any launch
+    q.qmatvec(q.Q8K_Q4_K, A16, 0, 256, A16, A16, 0)
+    q.q8k_pack(A16, 0, 256, A16, 0)
+    q.qmatvec_moe(q.Q8K_Q4_K, A16, 8, 4, 256, A16, 0, A16, A16, 2, A16, 0)
+    q.qmatmul_prefill(q.Q8K_Q4_K, A16, 8, 256, A16, 0, A16, None, 0, 0)
+    q.q8k_bind_q6k(A16, 0, 256, A16, 0)
+
+
+def test_status_strings(q):
+    assert q.q8k_status_str(0) == "Q8K_OK"
+    assert q.q8k_status_str(7) == "Q8K_ERR_LAUNCH"
+    assert q.q8k_status_str(99) == "Q8K_ERR_UNKNOWN"

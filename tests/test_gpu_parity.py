@@ -1,0 +1,305 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle.
+
+Inputs are seeded and synthetic (synth/), outputs are poisoned with 0xFF before
+every call, integer results (q8_K bytes, int32 sub-block sums, relaid weight
+bytes) must match bit-exactly and fp32 outputs must satisfy
+|err| <= 1e-5 * sum|terms| + 1e-6 against the oracle's fp64 result.
+
+Method: "Language models on the device: the cajeta-llm kernels"
+(cajeta.dev/xpu/kernels-llm/), sections 1 (q8_K, K-quants, Q6_K split), 2.1
+(decode mat-vec), 2.2 (batched), 2.3 (prefill tiles), 2.4 (MoE decode).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import (assert_close, host, pack_on_device, poisoned, poisoned_f32, poisoned_i32, split_act,
+                         to_dev)
+
+pytestmark = pytest.mark.gpu
+
+NTH = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+@pytest.fixture(scope="module")
+def q():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_q8kpack_fp32_amd as q
+
+    oracle.build()
+    return q
+
+
+def q4k(seed, rows, K):
+    return synth.q4k_weights(np.random.default_rng(seed), rows, K)
+
+
+def acts(seed, T, K):
+    return synth.activations(np.random.default_rng(seed + 7919), T, K)
+
+
+# ================================================================== a1 pack
+def special_blocks(K):
+    """Blocks that exercise the quantiser's corners (one per 256 values)."""
+    nb = K // 256
+    g = np.random.default_rng(99)
+    x = g.standard_normal((nb, 256)).astype(np.float32)
+    kinds = [
+        lambda v: v,                                   # N(0,1)
+        lambda v: np.zeros_like(v),                    # all zero -> d = 0
+        lambda v: np.round(v * 40) / 2 + 0.0 * v,     # many exact halves
+        lambda v: v * np.float32(1e-39),               # subnormal inputs
+        lambda v: v * np.float32(1e30),                # huge inputs
+        lambda v: np.where(np.arange(256) == 17, np.float32(-3.0), 0).astype(np.float32),  # one value
+        lambda v: np.full_like(v, 0.5),                # constant block
+        lambda v: v * np.float32(1e-38) / np.abs(v).max(),  # 127/amax overflows
+    ]
+    for b in range(nb):
+        x[b] = kinds[b % len(kinds)](x[b])
+    # exact ties: amax = 127 makes the inverse scale 1
+    if nb > 2:
+        x[2, 0] = 127.0
+    return x.reshape(1, K)
+
+
+@pytest.mark.parametrize("T,K", [(1, 256), (1, 1024), (3, 4096), (17, 512), (16, 4096), (512, 14336)])
+def test_pack_bit_exact(q, T, K):
+    x = acts(T * 31 + K, T, K)
+    xq = pack_on_device(q, x)
+    qs, d, bs = split_act(q, host(xq), T, K)
+    oqs, od, obs = oracle.q8k_pack(x)
+    assert np.array_equal(qs, oqs)
+    assert np.array_equal(d.view(np.uint32), od.view(np.uint32))
+    assert np.array_equal(bs, obs)
+
+
+@pytest.mark.parametrize("K", [2048, 4096])
+def test_pack_special_blocks_bit_exact(q, K):
+    x = special_blocks(K)
+    xq = pack_on_device(q, x)
+    qs, d, bs = split_act(q, host(xq), 1, K)
+    oqs, od, obs = oracle.q8k_pack(x)
+    assert np.array_equal(qs, oqs)
+    assert np.array_equal(d.view(np.uint32), od.view(np.uint32))
+    assert np.array_equal(bs, obs)
+
+
+# ================================================================== a3 Q4_K decode
+@pytest.mark.parametrize("rows,K,seed", [(256, 1024, 0), (4096, 4096, 1), (37, 256, 5), (13, 768, 6),
+                                         (70, 1280, 7), (9, 14336, 8)])
+def test_q4k_subblock_sums_bit_exact(q, rows, K, seed):
+    w = q4k(seed, rows, K)
+    x = acts(seed, 1, K)
+    xq = pack_on_device(q, x)
+    S = poisoned_i32(rows, K // 32)
+    q.q8k_debug_subblock_sums(q.Q8K_Q4_K, to_dev(w), rows, K, xq, S)
+    oqs, _, _ = oracle.q8k_pack(x)
+    assert np.array_equal(host(S), oracle.subblock_sums(oracle.Q4_K, w, rows, K, oqs[0]))
+
+
+@pytest.mark.parametrize("rows,K,seed", [(256, 1024, 0), (4096, 4096, 1), (37, 256, 5), (13, 768, 6),
+                                         (70, 1280, 7), (9, 14336, 8), (1, 256, 9)])
+def test_q4k_matvec(q, rows, K, seed):
+    w = q4k(seed, rows, K)
+    x = acts(seed, 1, K)
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(rows)
+    q.qmatvec(q.Q8K_Q4_K, to_dev(w), rows, K, xq, y)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(oracle.Q4_K, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(y), want[0], A[0], f"q4k {rows}x{K}")
+
+
+def test_q4k_matvec_extreme_scales(q):
+    """Subnormal fp16 dmin, zero d, the largest fp16 scales and zero blocks."""
+    rows, K = 64, 1024
+    w = q4k(21, rows, K).reshape(-1, 144).copy()
+    f16 = lambda v: np.array([v], np.float16).view(np.uint8)
+    w[0::4, 0:2] = f16(0.0)
+    w[1::4, 2:4] = f16(3e-7)          # subnormal fp16
+    w[2::4, 0:2] = f16(60000.0)
+    w[3::4, 2:4] = f16(60000.0)
+    w = w.reshape(-1)
+    x = special_blocks(K)
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(rows)
+    q.qmatvec(q.Q8K_Q4_K, to_dev(w), rows, K, xq, y)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(oracle.Q4_K, w, rows, K, oqs, od, obs)
+    assert_close(host(y), want[0], A[0], "q4k extreme")
+
+
+# ================================================================== a2 bind + a4 Q6_K decode
+def q6k_bound(q, seed, rows, K):
+    w = synth.q6k_weights(np.random.default_rng(seed), rows, K)
+    wr = poisoned(q.q8k_weight_bytes(q.Q8K_Q6_K_RELAID, rows, K))
+    q.q8k_bind_q6k(to_dev(w), rows, K, wr)
+    return w, wr
+
+
+@pytest.mark.parametrize("rows,K", [(3, 256), (32000, 4096), (5, 768)])
+def test_q6k_bind_bit_exact(q, rows, K):
+    w, wr = q6k_bound(q, 2, rows, K)
+    nblk = rows * K // 256
+    got = host(wr)
+    prefix, bodies = oracle.q6k_relayout(w, nblk)
+    pad = ((2 * nblk + 255) // 256) * 256
+    assert np.array_equal(got[: 2 * nblk].view(np.uint16), prefix)
+    assert np.array_equal(got[pad: pad + 208 * nblk], bodies)
+
+
+@pytest.mark.parametrize("rows,K,seed", [(32000, 4096, 2), (37, 256, 11), (100, 1280, 12), (7, 14336, 13)])
+def test_q6k_subblock_sums_bit_exact(q, rows, K, seed):
+    w, wr = q6k_bound(q, seed, rows, K)
+    x = acts(seed, 1, K)
+    xq = pack_on_device(q, x)
+    S = poisoned_i32(rows, K // 16)
+    q.q8k_debug_subblock_sums(q.Q8K_Q6_K_RELAID, wr, rows, K, xq, S)
+    oqs, _, _ = oracle.q8k_pack(x)
+    assert np.array_equal(host(S), oracle.subblock_sums(oracle.Q6_K, w, rows, K, oqs[0]))
+
+
+@pytest.mark.parametrize("rows,K,seed", [(32000, 4096, 2), (37, 256, 11), (100, 1280, 12), (7, 14336, 13)])
+def test_q6k_matvec(q, rows, K, seed):
+    w, wr = q6k_bound(q, seed, rows, K)
+    x = acts(seed, 1, K)
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(rows)
+    q.qmatvec(q.Q8K_Q6_K_RELAID, wr, rows, K, xq, y)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(oracle.Q6_K, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(y), want[0], A[0], f"q6k {rows}x{K}")
+
+
+# ================================================================== a5 batched
+@pytest.mark.parametrize("ncols", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_batched(q, ncols, fmt):
+    rows, K = (4096, 4096) if fmt == "q4k" else (1000, 4096)
+    if fmt == "q4k":
+        w = q4k(1, rows, K)
+        wd, qt, ot = to_dev(w), q.Q8K_Q4_K, oracle.Q4_K
+    else:
+        w, wd = q6k_bound(q, 2, rows, K)
+        qt, ot = q.Q8K_Q6_K_RELAID, oracle.Q6_K
+    x = acts(40 + ncols, ncols, K)
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(ncols, rows)
+    q.qmatvec_batched(qt, wd, rows, K, xq, ncols, y)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(ot, w, rows, K, oqs, od, obs, nthreads=NTH)
+    got = host(y)
+    assert_close(got, want, A, f"batched {fmt} ncols={ncols}")
+    # each column is the single-column mat-vec of that token, bit for bit
+    for c in range(ncols):
+        xq1 = pack_on_device(q, x[c:c + 1])
+        y1 = poisoned_f32(rows)
+        q.qmatvec(qt, wd, rows, K, xq1, y1)
+        assert np.array_equal(host(y1).view(np.uint32), got[c].view(np.uint32)), f"column {c}"
+
+
+# ================================================================== a6 MoE decode
+def moe_case(q, fmt, E, rows, K, T, topk, seed, ids=None):
+    g = np.random.default_rng(seed)
+    if fmt == "q4k":
+        w = synth.q4k_weights(g, E * rows, K)
+        wd, qt, ot = to_dev(w), q.Q8K_Q4_K, oracle.Q4_K
+    else:
+        w = synth.q6k_weights(g, E * rows, K)
+        wd = poisoned(q.q8k_weight_bytes(q.Q8K_Q6_K_RELAID, E * rows, K))
+        q.q8k_bind_q6k(to_dev(w), E * rows, K, wd)
+        qt, ot = q.Q8K_Q6_K_RELAID, oracle.Q6_K
+    x = synth.activations(g, T, K)
+    r_ids, rw = synth.moe_routing(g, T, E, topk)
+    if ids is None:
+        ids = r_ids
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(T, rows)
+    q.qmatvec_moe(qt, wd, E, rows, K, xq, T, to_dev(ids.astype(np.int32)), to_dev(rw), topk, y)
+    oqs, od, obs = oracle.q8k_pack(x)
+    return host(y), w, ot, oqs, od, obs, ids, rw
+
+
+@pytest.mark.parametrize("fmt,E,rows,K,T,topk,seed", [
+    ("q4k", 8, 14336, 4096, 16, 2, 3),     # the MoE decode layer shape
+    ("q4k", 4, 100, 512, 5, 3, 31),
+    ("q4k", 8, 37, 1280, 1, 2, 32),
+    ("q4k", 16, 64, 256, 200, 4, 33),      # many tokens: several token slots per lane
+    ("q6k", 8, 300, 1024, 16, 2, 34),
+])
+def test_moe(q, fmt, E, rows, K, T, topk, seed):
+    got, w, ot, oqs, od, obs, ids, rw = moe_case(q, fmt, E, rows, K, T, topk, seed)
+    want, A = oracle.moe(ot, w, E, rows, K, oqs, od, obs, ids, rw, nthreads=NTH)
+    assert_close(got, want, A, f"moe {fmt} E={E} rows={rows} T={T}")
+
+
+def test_moe_crowded_expert_and_bad_ids(q):
+    """20 tokens all choose experts 0 and 1 (more pairs than one group holds);
+    an id outside [0, E) selects nothing."""
+    E, rows, K, T, topk = 4, 50, 512, 20, 2
+    ids = np.tile(np.array([[0, 1]], np.int32), (T, 1))
+    ids[3, 1] = 7      # out of range: dropped
+    ids[5, 0] = -1     # out of range: dropped
+    got, w, ot, oqs, od, obs, ids, rw = moe_case(q, "q4k", E, rows, K, T, topk, 77, ids=ids)
+    ok = (ids >= 0) & (ids < E)
+    want, A = oracle.moe(ot, w, E, rows, K, oqs, od, obs, np.where(ok, ids, 0), np.where(ok, rw, 0).astype(np.float32))
+    assert_close(got, want, A, "moe crowded")
+
+
+# ================================================================== a7 prefill
+@pytest.mark.parametrize("M,rows,K,seed", [(1, 64, 256, 41), (17, 100, 512, 42), (64, 64, 256, 43),
+                                           (127, 256, 1024, 44), (200, 130, 768, 45), (65, 4096, 256, 46)])
+def test_prefill_full(q, M, rows, K, seed):
+    w = q4k(seed, rows, K)
+    x = acts(seed, M, K)
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(M, rows)
+    ws_bytes = q.qmatmul_prefill_workspace_bytes(q.Q8K_Q4_K, rows, K, M)
+    ws = poisoned(ws_bytes) if ws_bytes else None
+    q.qmatmul_prefill(q.Q8K_Q4_K, to_dev(w), rows, K, xq, M, y, ws, ws_bytes)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(oracle.Q4_K, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(y), want, A, f"prefill M={M} N={rows} K={K}")
+
+
+def test_prefill_down_projection_sampled(q):
+    """The 512-token x 4096-row x 14336 prefill: every output is finite and a
+    sample of whole token rows and whole weight-row columns matches the oracle."""
+    M, rows, K = 512, 4096, 14336
+    w = q4k(4, rows, K)
+    x = acts(4, M, K)
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(M, rows)
+    ws_bytes = q.qmatmul_prefill_workspace_bytes(q.Q8K_Q4_K, rows, K, M)
+    ws = poisoned(ws_bytes) if ws_bytes else None
+    q.qmatmul_prefill(q.Q8K_Q4_K, to_dev(w), rows, K, xq, M, y, ws, ws_bytes)
+    got = host(y)
+    assert np.isfinite(got).all()
+    oqs, od, obs = oracle.q8k_pack(x)
+    g = np.random.default_rng(123)
+    toks = np.sort(g.choice(M, 6, replace=False))
+    toks[0] = 0
+    toks[-1] = M - 1
+    want, A = oracle.matvec(oracle.Q4_K, w, rows, K, oqs[toks], od[toks], obs[toks], nthreads=NTH)
+    assert_close(got[toks], want, A, "prefill token rows")
+    sel = np.sort(g.choice(rows, 24, replace=False))
+    sel[-1] = rows - 1
+    wsel = w.reshape(rows, -1)[sel].reshape(-1)
+    want, A = oracle.matvec(oracle.Q4_K, wsel, len(sel), K, oqs, od, obs, nthreads=NTH)
+    assert_close(got[:, sel], want, A, "prefill weight columns")
+
+
+# ================================================================== empty inputs
+def test_empty_calls_leave_outputs_untouched(q):
+    y = poisoned_f32(8)
+    w = to_dev(q4k(0, 8, 256))
+    xq = pack_on_device(q, acts(0, 1, 256))
+    q.qmatvec(q.Q8K_Q4_K, w, 0, 256, xq, y)
+    q.qmatmul_prefill(q.Q8K_Q4_K, w, 8, 256, xq, 0, y, None, 0)
+    assert np.isnan(host(y)).all()
