@@ -1,0 +1,445 @@
+#!/usr/bin/env python3
+"""Benchmark of the q8_K-packed K-quant path on one MI355X.
+
+Headline (one JSON line on stdout): the 4096x4096 Q4_K decode step -- pack one
+fp32 token into q8_K on the device, then the Q4_K mat-vec -- as algorithmic
+HBM GB/s.  The other workloads of the path (Q6_K output-head decode, MoE
+decode, 512-token prefill GEMM, batched decode, the q8_K pack of a prefill
+batch) are measured in the same run and reported under "workloads".
+
+Protocol (measurement discipline of "One kernel, any device", section 5, and
+the five interleaved rounds / medians of its section 4.2):
+  * inputs are resident in HBM before timing starts;
+  * weights are rotated through R distinct copies whose total is at least 2x
+    the 256 MB Infinity Cache, so every weight read comes from HBM;
+  * W untimed warmup steps, then exactly K timed steps between two
+    device synchronisations;
+  * each launch of the dominant kernel inside the timed region is bracketed
+    by HIP events on the stream it runs on; their mean is the per-launch
+    duration used for the roofline;
+  * a workload's numbers are reported together with its parity verdict
+    against the CPU oracle, computed in the same run.
+
+The CPU baseline is the oracle as it stands (plain C, not tuned), timed on
+this host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q4_K decode mat-vec HBM GB/s (% of peak); prefill int8 TOPS (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+MALL_BYTES = 256 << 20         # Infinity Cache
+TOL_REL, TOL_ABS = 1e-5, 1e-6
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "matvec_q4k": ["quantized_q8kpack_fp32_amd/csrc/matvec.hip", "quantized_q8kpack_fp32_amd/csrc/kquant.h"],
+    "matvec_q6k": ["quantized_q8kpack_fp32_amd/csrc/matvec.hip", "quantized_q8kpack_fp32_amd/csrc/kquant.h"],
+    "moe": ["quantized_q8kpack_fp32_amd/csrc/moe.hip", "quantized_q8kpack_fp32_amd/csrc/kquant.h"],
+    "prefill_q4k": ["quantized_q8kpack_fp32_amd/csrc/prefill.hip"],
+    "pack": ["quantized_q8kpack_fp32_amd/csrc/pack.hip"],
+}
+
+
+def traffic_record(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    the kernel's source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec or rec.get("source_sha") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- helpers
+class Timer:
+    """HIP-event brackets around launches on torch's current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def mean_us(self):
+        if not self.pairs:
+            return None
+        return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+
+
+def close(got, want, A):
+    got = np.asarray(got, np.float64)
+    return bool(np.isfinite(got).all() and (np.abs(got - want) <= TOL_REL * A + TOL_ABS).all())
+
+
+def rotations(nbytes: int, minimum: int = 2) -> int:
+    return max(minimum, -(-2 * MALL_BYTES // max(nbytes, 1)))
+
+
+# ---------------------------------------------------------------- workloads
+class Decode:
+    """One token through q8k_pack + qmatvec (Q4_K or relaid Q6_K)."""
+
+    def __init__(self, q, torch, fmt, rows, K, seed, R=None):
+        import synth
+
+        self.q, self.torch, self.fmt, self.rows, self.K = q, torch, fmt, rows, K
+        g = np.random.default_rng(seed)
+        dev = torch.device("cuda")
+        if fmt == "q4k":
+            self.w_host = synth.q4k_weights(g, rows, K)
+            w0 = torch.from_numpy(self.w_host).to(dev)
+            self.qt = q.Q8K_Q4_K
+        else:
+            self.w_host = synth.q6k_weights(g, rows, K)
+            wg = torch.from_numpy(self.w_host).to(dev)
+            w0 = torch.empty(q.q8k_weight_bytes(q.Q8K_Q6_K_RELAID, rows, K), dtype=torch.uint8, device=dev)
+            q.q8k_bind_q6k(wg, rows, K, w0)
+            del wg
+            self.qt = q.Q8K_Q6_K_RELAID
+        self.wbytes_alg = rows * (K // 256) * (144 if fmt == "q4k" else 210)
+        self.R = R or rotations(w0.numel())
+        self.ws = [w0] + [w0.clone() for _ in range(self.R - 1)]
+        self.x_host = synth.activations(g, 1, K)
+        self.x = torch.from_numpy(self.x_host).to(dev)
+        self.xq = torch.empty(q.q8k_act_bytes(1, K), dtype=torch.uint8, device=dev)
+        self.y = torch.empty(rows, dtype=torch.float32, device=dev)
+        nb = K // 256
+        # algorithmic bytes: weight once, q8_K codes+scales (+ sums for Q4_K) once, output once
+        self.mv_bytes = self.wbytes_alg + K + 4 * nb + (16 * nb if fmt == "q4k" else 0) + 4 * rows
+        self.pack_bytes = 4 * K + K + 4 * nb + 16 * nb
+        self.step_bytes = self.mv_bytes + self.pack_bytes
+
+    def step(self, i, timer=None):
+        self.q.q8k_pack(self.x, 1, self.K, self.xq)
+        e = timer.start() if timer else None
+        self.q.qmatvec(self.qt, self.ws[i % self.R], self.rows, self.K, self.xq, self.y)
+        if timer:
+            timer.stop(e)
+
+    def parity(self):
+        import oracle
+
+        self.step(0)
+        got = self.y.cpu().numpy()
+        qs, d, bs = oracle.q8k_pack(self.x_host)
+        want, A = oracle.matvec(oracle.Q4_K if self.fmt == "q4k" else oracle.Q6_K, self.w_host, self.rows,
+                                self.K, qs, d, bs, nthreads=ncores())
+        return close(got, want[0], A[0])
+
+
+class Batched(Decode):
+    def __init__(self, q, torch, fmt, rows, K, seed, ncols):
+        super().__init__(q, torch, fmt, rows, K, seed)
+        import synth
+
+        self.ncols = ncols
+        g = np.random.default_rng(seed + 1)
+        self.x_host = synth.activations(g, ncols, K)
+        dev = torch.device("cuda")
+        self.x = torch.from_numpy(self.x_host).to(dev)
+        self.xq = torch.empty(q.q8k_act_bytes(ncols, K), dtype=torch.uint8, device=dev)
+        self.y = torch.empty(ncols * rows, dtype=torch.float32, device=dev)
+        nb = K // 256
+        self.mv_bytes = self.wbytes_alg + ncols * (K + 4 * nb + 16 * nb + 4 * rows)
+
+    def step(self, i, timer=None):
+        self.q.q8k_pack(self.x, self.ncols, self.K, self.xq)
+        e = timer.start() if timer else None
+        self.q.qmatvec_batched(self.qt, self.ws[i % self.R], self.rows, self.K, self.xq, self.ncols, self.y)
+        if timer:
+            timer.stop(e)
+
+    def parity(self):
+        import oracle
+
+        self.step(0)
+        got = self.y.cpu().numpy().reshape(self.ncols, self.rows)
+        qs, d, bs = oracle.q8k_pack(self.x_host)
+        want, A = oracle.matvec(oracle.Q4_K if self.fmt == "q4k" else oracle.Q6_K, self.w_host, self.rows,
+                                self.K, qs, d, bs, nthreads=ncores())
+        return close(got, want, A)
+
+
+class MoE:
+    """16 tokens, top-2 of 8 Q4_K experts of 14336 x 4096: pack + qmatvec_moe."""
+
+    def __init__(self, q, torch, E=8, rows=14336, K=4096, T=16, topk=2, seed=3):
+        import synth
+
+        self.q, self.torch, self.E, self.rows, self.K, self.T, self.topk = q, torch, E, rows, K, T, topk
+        g = np.random.default_rng(seed)
+        dev = torch.device("cuda")
+        self.w_host = synth.q4k_weights(g, E * rows, K)
+        w0 = torch.from_numpy(self.w_host).to(dev)
+        self.R = rotations(w0.numel())
+        self.ws = [w0] + [w0.clone() for _ in range(self.R - 1)]
+        self.x_host = synth.activations(g, T, K)
+        self.ids_host, self.rw_host = synth.moe_routing(g, T, E, topk)
+        self.x = torch.from_numpy(self.x_host).to(dev)
+        self.ids = torch.from_numpy(self.ids_host).to(dev)
+        self.rw = torch.from_numpy(self.rw_host).to(dev)
+        self.xq = torch.empty(q.q8k_act_bytes(T, K), dtype=torch.uint8, device=dev)
+        self.y = torch.empty(T * rows, dtype=torch.float32, device=dev)
+        nb = K // 256
+        hit = len(set(self.ids_host.ravel().tolist()))
+        self.experts_hit = hit
+        self.mv_bytes = hit * rows * nb * 144 + T * (K + 20 * nb) + 8 * T * topk + 4 * T * rows
+        self.pack_bytes = T * (4 * K + K + 20 * nb)
+        self.step_bytes = self.mv_bytes + self.pack_bytes
+
+    def step(self, i, timer=None):
+        self.q.q8k_pack(self.x, self.T, self.K, self.xq)
+        e = timer.start() if timer else None
+        self.q.qmatvec_moe(self.q.Q8K_Q4_K, self.ws[i % self.R], self.E, self.rows, self.K, self.xq, self.T,
+                           self.ids, self.rw, self.topk, self.y)
+        if timer:
+            timer.stop(e)
+
+    def parity(self):
+        import oracle
+
+        self.step(0)
+        got = self.y.cpu().numpy().reshape(self.T, self.rows)
+        qs, d, bs = oracle.q8k_pack(self.x_host)
+        want, A = oracle.moe(oracle.Q4_K, self.w_host, self.E, self.rows, self.K, qs, d, bs, self.ids_host,
+                             self.rw_host, nthreads=ncores())
+        return close(got, want, A)
+
+
+class Prefill:
+    """512 tokens through q8k_pack + qmatmul_prefill against a 4096 x 14336 Q4_K weight."""
+
+    def __init__(self, q, torch, rows=4096, K=14336, M=512, seed=4):
+        import synth
+
+        self.q, self.torch, self.rows, self.K, self.M = q, torch, rows, K, M
+        g = np.random.default_rng(seed)
+        dev = torch.device("cuda")
+        self.w_host = synth.q4k_weights(g, rows, K)
+        w0 = torch.from_numpy(self.w_host).to(dev)
+        self.R = rotations(w0.numel())
+        self.ws = [w0] + [w0.clone() for _ in range(self.R - 1)]
+        self.x_host = synth.activations(g, M, K)
+        self.x = torch.from_numpy(self.x_host).to(dev)
+        self.xq = torch.empty(q.q8k_act_bytes(M, K), dtype=torch.uint8, device=dev)
+        self.y = torch.empty(M * rows, dtype=torch.float32, device=dev)
+        self.ws_bytes = q.qmatmul_prefill_workspace_bytes(q.Q8K_Q4_K, rows, K, M)
+        self.wsp = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev) if self.ws_bytes else None
+        self.ops = 2 * M * rows * K
+        nb = K // 256
+        self.pack_bytes = M * (4 * K + K + 20 * nb)
+
+    def step(self, i, timer=None):
+        self.q.q8k_pack(self.x, self.M, self.K, self.xq)
+        e = timer.start() if timer else None
+        self.q.qmatmul_prefill(self.q.Q8K_Q4_K, self.ws[i % self.R], self.rows, self.K, self.xq, self.M, self.y,
+                               self.wsp, self.ws_bytes)
+        if timer:
+            timer.stop(e)
+
+    def parity(self):
+        import oracle
+
+        self.step(0)
+        got = self.y.cpu().numpy().reshape(self.M, self.rows)
+        qs, d, bs = oracle.q8k_pack(self.x_host)
+        toks = np.array([0, 1, 255, 256, self.M - 1])
+        want, A = oracle.matvec(oracle.Q4_K, self.w_host, self.rows, self.K, qs[toks], d[toks], bs[toks],
+                                nthreads=ncores())
+        return bool(np.isfinite(got).all()) and close(got[toks], want, A)
+
+
+def ncores() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def run_timed(torch, wl, steps, warmup):
+    for i in range(warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        wl.step(i, timer)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) / steps, timer.mean_us()
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(budget_s: float):
+    """The oracle's pack + Q4_K mat-vec of the 4096x4096 decode step, repeated
+    for about budget_s seconds on this host's cores."""
+    import oracle
+    import synth
+
+    oracle.build()
+    g = np.random.default_rng(1)
+    rows, K = 4096, 4096
+    w = synth.q4k_weights(g, rows, K)
+    x = synth.activations(g, 1, K)
+    nth = ncores()
+    nb = K // 256
+    step_bytes = rows * nb * 144 + K + 20 * nb + 4 * rows + 4 * K + K + 20 * nb
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        qs, d, bs = oracle.q8k_pack(x)
+        oracle.matvec(oracle.Q4_K, w, rows, K, qs, d, bs, nthreads=nth)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "sample": f"{n} full decode steps (q8_K pack + 4096x4096 Q4_K mat-vec, fp64 epilogue) "
+                      f"in {n * dt:.1f} s, {dt * 1e3:.2f} ms per step"}
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "multi-GPU sharding is described in the design notes but not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import quantized_q8kpack_fp32_amd as q
+
+    # ---- headline: 4096x4096 Q4_K decode step
+    log("headline: decode_q4k_4096x4096")
+    hd = Decode(q, torch, "q4k", 4096, 4096, seed=1)
+    parity = hd.parity()
+    sec, mv_us = run_timed(torch, hd, args.steps, args.warmup)
+    value = hd.step_bytes / sec / 1e9
+    achieved = hd.mv_bytes / (mv_us * 1e-6) / 1e9
+    tr = traffic_record("matvec_q4k")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "decode_q4k_4096x4096", "rows": 4096, "K": 4096, "tokens": 1,
+                   "weight": "GGUF Q4_K, 144 B per 256 values", "weight_copies_rotated": hd.R,
+                   "step": "q8k_pack + qmatvec", "step_bytes": hd.step_bytes, "parity": "pass" if parity else "FAIL"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
+                     "kernel": "matvec_q4k_kernel<1>", "launch_us": round(mv_us, 3),
+                     "algorithmic_bytes_per_launch": hd.mv_bytes},
+    }
+    del hd
+    torch.cuda.empty_cache()
+
+    # ---- the other workloads of the path
+    if not args.only_headline:
+        wl = {}
+        steps = max(20, min(args.steps, 100))
+
+        def decode_entry(name, d):
+            p = d.parity()
+            s, us = run_timed(torch, d, steps, 5)
+            gbs = d.mv_bytes / (us * 1e-6) / 1e9
+            wl[name] = {"parity": "pass" if p else "FAIL", "kernel_us": round(us, 3), "GB/s": round(gbs, 1),
+                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "step_ms": round(s * 1e3, 4),
+                        "bytes_per_launch": d.mv_bytes, "weight_copies_rotated": d.R}
+
+        log("workload: decode_q6k_32000x4096")
+        decode_entry("decode_q6k_32000x4096", Decode(q, torch, "q6k", 32000, 4096, seed=2))
+        torch.cuda.empty_cache()
+        for nc in (4, 8):
+            log(f"workload: batched_q4k_4096x4096_cols{nc}")
+            decode_entry(f"batched_q4k_4096x4096_cols{nc}", Batched(q, torch, "q4k", 4096, 4096, seed=1, ncols=nc))
+            torch.cuda.empty_cache()
+        log("workload: moe_q4k_8x14336x4096_t16_top2")
+        m = MoE(q, torch)
+        decode_entry("moe_q4k_8x14336x4096_t16_top2", m)
+        wl["moe_q4k_8x14336x4096_t16_top2"]["experts_hit"] = m.experts_hit
+        del m
+        torch.cuda.empty_cache()
+        log("workload: prefill_q4k_4096x14336_m512")
+        p = Prefill(q, torch)
+        ok = p.parity()
+        s, us = run_timed(torch, p, max(10, steps // 4), 3)
+        tops = p.ops / (us * 1e-6) / 1e12
+        wl["prefill_q4k_4096x14336_m512"] = {
+            "parity": "pass" if ok else "FAIL", "kernel_us": round(us, 2), "TOPS": round(tops, 1),
+            "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "step_ms": round(s * 1e3, 4),
+            "ops_per_launch": p.ops, "traffic": traffic_record("prefill_q4k")}
+        # q8_K pack of the 512 x 14336 batch, timed on its own
+        t = Timer(torch)
+        for i in range(20):
+            e = t.start()
+            q.q8k_pack(p.x, p.M, p.K, p.xq)
+            t.stop(e)
+        torch.cuda.synchronize()
+        pus = t.mean_us()
+        wl["pack_512x14336"] = {"kernel_us": round(pus, 2), "GB/s": round(p.pack_bytes / (pus * 1e-6) / 1e9, 1),
+                                "bytes_per_launch": p.pack_bytes}
+        del p
+        out["workloads"] = wl
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

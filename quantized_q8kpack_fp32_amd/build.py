@@ -4,7 +4,7 @@ Every source is compiled for gfx950 only, with packed FP32 instructions
 disabled, and the kernel resource report of each translation unit is checked:
 a kernel that uses scratch (spills) fails the build, since a spilling kernel is
 not a tuned kernel (the build gate idea of "One kernel, any device", section
-2.2).  Usage: ``python -m quantized_q8kpack_fp32_amd.build`` (or via
+2.2).  Usage: ``python quantized_q8kpack_fp32_amd/build.py`` (or via
 ``__graft_entry__.build()``).
 """
 from __future__ import annotations
