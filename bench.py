@@ -12,11 +12,14 @@ the five interleaved rounds / medians of its section 4.2):
   * inputs are resident in HBM before timing starts;
   * weights are rotated through R distinct copies whose total is at least 2x
     the 256 MB Infinity Cache, so every weight read comes from HBM;
-  * W untimed warmup steps, then exactly K timed steps between two
-    device synchronisations;
-  * each launch of the dominant kernel inside the timed region is bracketed
-    by HIP events on the stream it runs on; their mean is the per-launch
-    duration used for the roofline;
+  * W untimed eager warmup steps; then the K steps are captured once into a
+    HIP graph (launch-bound decode loops are replayed as graphs, so host
+    launch overhead does not pace the GPU), the graph is replayed once
+    untimed, and exactly K steps are timed as one replay between two device
+    synchronisations;
+  * the dominant kernel's per-launch duration comes from HIP events on the
+    stream it runs on, bracketing a replayed graph of back-to-back launches
+    of that kernel alone (rotating weight copies);
   * a workload's numbers are reported together with its parity verdict
     against the CPU oracle, computed in the same run.
 
@@ -79,27 +82,28 @@ def traffic_record(kernel: str):
 
 
 # ---------------------------------------------------------------- helpers
-class Timer:
-    """HIP-event brackets around launches on torch's current stream."""
+def graph_of(torch, fn, n):
+    """Capture fn(0..n-1) into one HIP graph on a side stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    return g
 
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
 
-    def start(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-    def stop(self, e0):
-        e1 = self.torch.cuda.Event(enable_timing=True)
-        e1.record()
-        self.pairs.append((e0, e1))
-
-    def mean_us(self):
-        if not self.pairs:
-            return None
-        return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+def replay_us(torch, g, n, reps=1):
+    """Mean per-call time of a graph of n calls, from HIP events on the
+    replay stream (torch's current stream)."""
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / (n * reps)
 
 
 def close(got, want, A):
@@ -145,12 +149,12 @@ class Decode:
         self.pack_bytes = 4 * K + K + 4 * nb + 16 * nb
         self.step_bytes = self.mv_bytes + self.pack_bytes
 
-    def step(self, i, timer=None):
+    def step(self, i):
         self.q.q8k_pack(self.x, 1, self.K, self.xq)
-        e = timer.start() if timer else None
+        self.main(i)
+
+    def main(self, i):
         self.q.qmatvec(self.qt, self.ws[i % self.R], self.rows, self.K, self.xq, self.y)
-        if timer:
-            timer.stop(e)
 
     def parity(self):
         import oracle
@@ -178,12 +182,12 @@ class Batched(Decode):
         nb = K // 256
         self.mv_bytes = self.wbytes_alg + ncols * (K + 4 * nb + 16 * nb + 4 * rows)
 
-    def step(self, i, timer=None):
+    def step(self, i):
         self.q.q8k_pack(self.x, self.ncols, self.K, self.xq)
-        e = timer.start() if timer else None
+        self.main(i)
+
+    def main(self, i):
         self.q.qmatvec_batched(self.qt, self.ws[i % self.R], self.rows, self.K, self.xq, self.ncols, self.y)
-        if timer:
-            timer.stop(e)
 
     def parity(self):
         import oracle
@@ -223,13 +227,13 @@ class MoE:
         self.pack_bytes = T * (4 * K + K + 20 * nb)
         self.step_bytes = self.mv_bytes + self.pack_bytes
 
-    def step(self, i, timer=None):
+    def step(self, i):
         self.q.q8k_pack(self.x, self.T, self.K, self.xq)
-        e = timer.start() if timer else None
+        self.main(i)
+
+    def main(self, i):
         self.q.qmatvec_moe(self.q.Q8K_Q4_K, self.ws[i % self.R], self.E, self.rows, self.K, self.xq, self.T,
                            self.ids, self.rw, self.topk, self.y)
-        if timer:
-            timer.stop(e)
 
     def parity(self):
         import oracle
@@ -265,13 +269,13 @@ class Prefill:
         nb = K // 256
         self.pack_bytes = M * (4 * K + K + 20 * nb)
 
-    def step(self, i, timer=None):
+    def step(self, i):
         self.q.q8k_pack(self.x, self.M, self.K, self.xq)
-        e = timer.start() if timer else None
+        self.main(i)
+
+    def main(self, i):
         self.q.qmatmul_prefill(self.q.Q8K_Q4_K, self.ws[i % self.R], self.rows, self.K, self.xq, self.M, self.y,
                                self.wsp, self.ws_bytes)
-        if timer:
-            timer.stop(e)
 
     def parity(self):
         import oracle
@@ -290,16 +294,23 @@ def ncores() -> int:
 
 
 def run_timed(torch, wl, steps, warmup):
+    """-> (seconds per step over exactly `steps` timed steps, dominant-kernel us per launch)."""
     for i in range(warmup):
         wl.step(i)
     torch.cuda.synchronize()
-    timer = Timer(torch)
+    g = graph_of(torch, wl.step, steps)
+    g.replay()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        wl.step(i, timer)
+    g.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    return (t1 - t0) / steps, timer.mean_us()
+    del g
+    n = wl.R * max(1, -(-64 // wl.R))  # whole rotations, at least 64 launches
+    gk = graph_of(torch, wl.main, n)
+    us = replay_us(torch, gk, n, reps=2)
+    del gk
+    return (t1 - t0) / steps, us
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -377,7 +388,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_q4k_4096x4096", "rows": 4096, "K": 4096, "tokens": 1,
                    "weight": "GGUF Q4_K, 144 B per 256 values", "weight_copies_rotated": hd.R,
-                   "step": "q8k_pack + qmatvec", "step_bytes": hd.step_bytes, "parity": "pass" if parity else "FAIL"},
+                   "step": "q8k_pack + qmatvec", "step_bytes": hd.step_bytes, "timing": "hip graph replay",
+                   "parity": "pass" if parity else "FAIL"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
                      "kernel": "matvec_q4k_kernel<1>", "launch_us": round(mv_us, 3),
@@ -422,13 +434,9 @@ def main():
             "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "step_ms": round(s * 1e3, 4),
             "ops_per_launch": p.ops, "traffic": traffic_record("prefill_q4k")}
         # q8_K pack of the 512 x 14336 batch, timed on its own
-        t = Timer(torch)
-        for i in range(20):
-            e = t.start()
-            q.q8k_pack(p.x, p.M, p.K, p.xq)
-            t.stop(e)
-        torch.cuda.synchronize()
-        pus = t.mean_us()
+        gp = graph_of(torch, lambda i: q.q8k_pack(p.x, p.M, p.K, p.xq), 32)
+        pus = replay_us(torch, gp, 32, reps=2)
+        del gp
         wl["pack_512x14336"] = {"kernel_us": round(pus, 2), "GB/s": round(p.pack_bytes / (pus * 1e-6) / 1e9, 1),
                                 "bytes_per_launch": p.pack_bytes}
         del p

@@ -35,9 +35,9 @@ _SCRATCH = re.compile(r"remark: .*?:\d+:\d+: Function Name: (\S+)")
 _SCRATCH_SIZE = re.compile(r"ScratchSize \[bytes/lane\]: (\d+)")
 
 
-def _compile(src: str) -> tuple[str, str]:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> tuple[str, str]:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -59,10 +59,11 @@ def _check_scratch(log: str, src: str) -> list[str]:
     return bad
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = OUT, build_dir: str = BUILD_DIR, defines=()) -> str:
+    """Compile and link; `defines` override compile-time tile parameters."""
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda s: _compile(s, build_dir, defines), SOURCES))
     problems = []
     for src, (_, log) in zip(SOURCES, results):
         problems += _check_scratch(log, src)
@@ -70,13 +71,13 @@ def build(verbose: bool = False) -> str:
             sys.stderr.write(log)
     if problems:
         raise RuntimeError("kernels using scratch (spills):\n  " + "\n  ".join(problems))
-    tmp = OUT + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -10,12 +10,66 @@
 // Lane map (gfx950 wave64): lane l serves block b = 8k + (l >> 3) of the row
 // (k = 0, 1, ...) and its 16-byte quant chunk ci = l & 7, so each 64-lane
 // load instruction covers the quant bytes of eight consecutive blocks.
+//
+// Latency: a decode mat-vec of a 4096-wide row is only two such 8-block
+// groups per lane, so a wave would otherwise wait for two dependent HBM round
+// trips.  Each trip of the main loop therefore issues every load of U groups
+// (weight chunk, block header, q8_K codes, sums and scales) before any
+// arithmetic.  Lanes whose block index runs past the row load the row's last
+// block and contribute nothing, which keeps the wave convergent.
 #include "kquant.h"
 #include "q8k_launch.h"
 
 namespace q8k {
 
+// ---------------------------------------------------------------- Q4_K ----
 template <int NC>
+struct Q4Chunk {
+    uint4 hdr, qv;
+    int4 alo[NC], ahi[NC];
+    uint32_t bs[NC];
+    float d8[NC];
+};
+
+template <int NC>
+__device__ __forceinline__ void q4k_load(Q4Chunk<NC>& L, const uint8_t* __restrict__ wr, int b, int ci, int aoff,
+                                         int boff, const int8_t* __restrict__ qs, const float* __restrict__ d8,
+                                         const int16_t* __restrict__ bs, int64_t K, int nb) {
+    const uint8_t* blk = wr + (int64_t)b * Q4K_BLOCK;
+    L.hdr = *reinterpret_cast<const uint4*>(blk);
+    L.qv = *reinterpret_cast<const uint4*>(blk + 16 + 16 * ci);
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+        const int8_t* a = qs + t * K + (int64_t)b * QK + aoff;
+        L.alo[t] = *reinterpret_cast<const int4*>(a);
+        L.ahi[t] = *reinterpret_cast<const int4*>(a + 32);
+        L.bs[t] = *reinterpret_cast<const uint32_t*>(bs + ((int64_t)t * nb + b) * 8 + boff);
+        L.d8[t] = d8[(int64_t)t * nb + b];
+    }
+}
+
+template <int NC>
+__device__ __forceinline__ void q4k_accum(const Q4Chunk<NC>& L, int c, int half, bool valid, float (&acc)[NC]) {
+    int sc0, sc1, m0, m1;
+    q4k_scales(L.hdr, c, sc0, sc1, m0, m1);
+    const float dd = half_bits_to_float(L.hdr.x & 0xffffu);
+    const float dm = half_bits_to_float(L.hdr.x >> 16);
+    uint32_t lo[4], hi[4];
+    q4k_unpack(L.qv, lo, hi);
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+        int S0, S1;
+        q4k_chunk_sums(lo, hi, L.alo[t], L.ahi[t], S0, S1);
+        const int isum = sc0 * S0 + sc1 * S1;
+        // the min term uses whole sub-block sums: counted once per chunk pair
+        const int msum =
+            half ? 0 : m0 * (int)(int16_t)(L.bs[t] & 0xffffu) + m1 * (int)(int16_t)(L.bs[t] >> 16);
+        const float v = L.d8[t] * (dd * (float)isum - dm * (float)msum);
+        acc[t] += valid ? v : 0.0f;
+    }
+}
+
+template <int NC, int U>
 __global__ __launch_bounds__(256) void matvec_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
                                                          const int8_t* __restrict__ qs, const float* __restrict__ d8,
                                                          const int16_t* __restrict__ bs, int64_t K,
@@ -24,37 +78,24 @@ __global__ __launch_bounds__(256) void matvec_q4k_kernel(const uint8_t* __restri
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;  // uniform per wave
     const int ci = lane & 7, c = ci >> 1, half = ci & 1;
+    const int aoff = 64 * c + 16 * half, boff = 2 * c;
     const uint8_t* wr = w + row * (int64_t)nb * Q4K_BLOCK;
     float acc[NC];
 #pragma unroll
     for (int t = 0; t < NC; ++t) acc[t] = 0.0f;
-    for (int b = lane >> 3; b < nb; b += 8) {
-        const uint8_t* blk = wr + (int64_t)b * Q4K_BLOCK;
-        const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
-        const uint4 qv = *reinterpret_cast<const uint4*>(blk + 16 + 16 * ci);
-        int sc0, sc1, m0, m1;
-        q4k_scales(hdr, c, sc0, sc1, m0, m1);
-        const float dd = half_bits_to_float(hdr.x & 0xffffu);
-        const float dm = half_bits_to_float(hdr.x >> 16);
-        uint32_t lo[4], hi[4];
-        q4k_unpack(qv, lo, hi);
+    for (int b0 = lane >> 3; b0 - (lane >> 3) < nb; b0 += 8 * U) {
+        Q4Chunk<NC> L[U];
 #pragma unroll
-        for (int t = 0; t < NC; ++t) {
-            const int8_t* a = qs + t * K + (int64_t)b * QK + 64 * c + 16 * half;
-            const int4 alo = *reinterpret_cast<const int4*>(a);
-            const int4 ahi = *reinterpret_cast<const int4*>(a + 32);
-            const uint32_t bb = *reinterpret_cast<const uint32_t*>(bs + ((int64_t)t * nb + b) * 8 + 2 * c);
-            int S0, S1;
-            q4k_chunk_sums(lo, hi, alo, ahi, S0, S1);
-            const int isum = sc0 * S0 + sc1 * S1;
-            // the min term uses whole sub-block sums: counted once per chunk pair
-            const int msum = half ? 0 : m0 * (int)(int16_t)(bb & 0xffffu) + m1 * (int)(int16_t)(bb >> 16);
-            acc[t] += d8[(int64_t)t * nb + b] * (dd * (float)isum - dm * (float)msum);
+        for (int u = 0; u < U; ++u) {
+            const int b = b0 + 8 * u;
+            q4k_load(L[u], wr, b < nb ? b : nb - 1, ci, aoff, boff, qs, d8, bs, K, nb);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) q4k_accum(L[u], c, half, b0 + 8 * u < nb, acc);
     }
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
-        const float v = wave_sum(acc[t]);
+        const float v = wave_sum_dpp(acc[t]);
         if (lane == 0) y[(int64_t)t * rows + row] = v;
     }
 }
@@ -83,7 +124,52 @@ __global__ __launch_bounds__(256) void sums_q4k_kernel(const uint8_t* __restrict
     }
 }
 
+// ---------------------------------------------------------------- Q6_K ----
 template <int NC>
+struct Q6Chunk {
+    uint4 qlv, qhv, scv;
+    uint32_t dbits;
+    int4 alo[NC], ahi[NC];
+    float d8[NC];
+};
+
+template <int NC>
+__device__ __forceinline__ void q6k_load(Q6Chunk<NC>& L, const uint16_t* __restrict__ prefix,
+                                         const uint8_t* __restrict__ bodies, int64_t row, int b, int ci, int qhoff,
+                                         int aoff, const int8_t* __restrict__ qs, const float* __restrict__ d8,
+                                         int64_t K, int nb) {
+    const int64_t ib = row * nb + b;
+    const uint8_t* body = bodies + ib * Q6K_BODY;
+    L.qlv = *reinterpret_cast<const uint4*>(body + 16 * ci);
+    L.qhv = *reinterpret_cast<const uint4*>(body + qhoff);
+    L.scv = *reinterpret_cast<const uint4*>(body + 192);
+    L.dbits = prefix[ib];
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+        const int8_t* a = qs + t * K + (int64_t)b * QK + aoff;
+        L.alo[t] = *reinterpret_cast<const int4*>(a);
+        L.ahi[t] = *reinterpret_cast<const int4*>(a + 64);
+        L.d8[t] = d8[(int64_t)t * nb + b];
+    }
+}
+
+template <int NC>
+__device__ __forceinline__ void q6k_accum(const Q6Chunk<NC>& L, int tt, int s0, bool valid, float (&acc)[NC]) {
+    const int sc0 = (int)(int8_t)byte_of(L.scv, s0);
+    const int sc1 = (int)(int8_t)byte_of(L.scv, s0 + 4);
+    const float dd = half_bits_to_float(L.dbits);
+    uint32_t lo[4], hi[4];
+    q6k_unpack(L.qlv, L.qhv, tt, lo, hi);
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+        const int S0 = q6k_sum16(lo, L.alo[t]);
+        const int S1 = q6k_sum16(hi, L.ahi[t]);
+        const float v = L.d8[t] * dd * (float)(sc0 * S0 + sc1 * S1);
+        acc[t] += valid ? v : 0.0f;
+    }
+}
+
+template <int NC, int U>
 __global__ __launch_bounds__(256) void matvec_q6k_kernel(const uint16_t* __restrict__ prefix,
                                                          const uint8_t* __restrict__ bodies, int64_t rows, int nb,
                                                          const int8_t* __restrict__ qs, const float* __restrict__ d8,
@@ -94,31 +180,23 @@ __global__ __launch_bounds__(256) void matvec_q6k_kernel(const uint16_t* __restr
     const int ci = lane & 7, h = ci >> 2, tt = (ci >> 1) & 1, lh = ci & 1;
     const int s0 = 8 * h + 2 * tt + lh;
     const int aoff = 128 * h + 32 * tt + 16 * lh;
+    const int qhoff = 128 + 16 * (2 * h + lh);
     float acc[NC];
 #pragma unroll
     for (int t = 0; t < NC; ++t) acc[t] = 0.0f;
-    for (int b = lane >> 3; b < nb; b += 8) {
-        const int64_t ib = row * nb + b;
-        const uint8_t* body = bodies + ib * Q6K_BODY;
-        const uint4 qlv = *reinterpret_cast<const uint4*>(body + 16 * ci);
-        const uint4 qhv = *reinterpret_cast<const uint4*>(body + 128 + 16 * (2 * h + lh));
-        const uint4 scv = *reinterpret_cast<const uint4*>(body + 192);
-        const int sc0 = (int)(int8_t)byte_of(scv, s0);
-        const int sc1 = (int)(int8_t)byte_of(scv, s0 + 4);
-        const float dd = half_bits_to_float(prefix[ib]);
-        uint32_t lo[4], hi[4];
-        q6k_unpack(qlv, qhv, tt, lo, hi);
+    for (int b0 = lane >> 3; b0 - (lane >> 3) < nb; b0 += 8 * U) {
+        Q6Chunk<NC> L[U];
 #pragma unroll
-        for (int t = 0; t < NC; ++t) {
-            const int8_t* a = qs + t * K + (int64_t)b * QK + aoff;
-            const int S0 = q6k_sum16(lo, *reinterpret_cast<const int4*>(a));
-            const int S1 = q6k_sum16(hi, *reinterpret_cast<const int4*>(a + 64));
-            acc[t] += d8[(int64_t)t * nb + b] * dd * (float)(sc0 * S0 + sc1 * S1);
+        for (int u = 0; u < U; ++u) {
+            const int b = b0 + 8 * u;
+            q6k_load(L[u], prefix, bodies, row, b < nb ? b : nb - 1, ci, qhoff, aoff, qs, d8, K, nb);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) q6k_accum(L[u], tt, s0, b0 + 8 * u < nb, acc);
     }
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
-        const float v = wave_sum(acc[t]);
+        const float v = wave_sum_dpp(acc[t]);
         if (lane == 0) y[(int64_t)t * rows + row] = v;
     }
 }
@@ -144,15 +222,20 @@ __global__ __launch_bounds__(256) void sums_q6k_kernel(const uint8_t* __restrict
 }
 
 // ----------------------------------------------------------- launchers ----
+// Two 8-block groups per loop trip for up to two columns (covers a 4096-wide
+// row in one trip); one group per trip for more columns, where the activation
+// registers of every column already give enough loads in flight.
 template <int NC>
 static void go_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, float* y, hipStream_t s) {
-    hipLaunchKernelGGL(matvec_q4k_kernel<NC>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb, a.qs, a.d,
-                       a.bs, a.K, y);
+    constexpr int U = NC <= 2 ? 2 : 1;
+    hipLaunchKernelGGL((matvec_q4k_kernel<NC, U>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb,
+                       a.qs, a.d, a.bs, a.K, y);
 }
 template <int NC>
 static void go_q6k(const uint16_t* p, const uint8_t* bodies, int64_t rows, int nb, Acts a, float* y, hipStream_t s) {
-    hipLaunchKernelGGL(matvec_q6k_kernel<NC>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, bodies, rows, nb,
-                       a.qs, a.d, a.K, y);
+    constexpr int U = NC <= 2 ? 2 : 1;
+    hipLaunchKernelGGL((matvec_q6k_kernel<NC, U>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, bodies, rows,
+                       nb, a.qs, a.d, a.K, y);
 }
 
 hipError_t launch_matvec_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int ncols, float* y, hipStream_t s) {

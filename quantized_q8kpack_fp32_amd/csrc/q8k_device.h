@@ -52,3 +52,36 @@ __device__ __forceinline__ uint32_t byte_of(uint4 v, int i) {
 }
 
 }  // namespace q8k
+
+namespace q8k {
+
+// DPP lane shuffles (gfx9 encodings): quad_perm [1,0,3,2] and [2,3,0,1],
+// row_ror:4 and row_ror:8 within each 16-lane row.
+__device__ __forceinline__ float dpp_f(float v, int ctrl_id) {
+    const int x = __builtin_bit_cast(int, v);
+    int r;
+    switch (ctrl_id) {
+        case 0: r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+        case 1: r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+        case 2: r = __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false); break;  // row_ror:4
+        default: r = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false); break; // row_ror:8
+    }
+    return __builtin_bit_cast(float, r);
+}
+
+// Sum over all 64 lanes of a wavefront (all lanes must be active); the total
+// is returned in every lane.  Four DPP steps give each 16-lane row its sum,
+// then the four row sums are read as scalars.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_f(v, 0);
+    v += dpp_f(v, 1);
+    v += dpp_f(v, 2);
+    v += dpp_f(v, 3);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+}  // namespace q8k
