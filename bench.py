@@ -342,6 +342,43 @@ def cpu_baseline(budget_s: float):
                       f"in {n * dt:.1f} s, {dt * 1e3:.2f} ms per step"}
 
 
+# ---------------------------------------------------------------- profiling
+PROFILE_TARGETS = {
+    "decode_q4k": "qmatvec on the 4096x4096 Q4_K decode workload",
+    "decode_q6k": "qmatvec on the 32000x4096 relaid Q6_K workload",
+    "moe": "qmatvec_moe on the 8 x 14336x4096 Q4_K, 16-token top-2 workload",
+    "prefill": "qmatmul_prefill on the 4096x14336 Q4_K, 512-token workload",
+    "pack": "q8k_pack of 512 x 14336 fp32 activations",
+    "copy": "a plain 256 MiB device-to-device copy (torch), the counter calibration reference",
+}
+
+
+def profile_run(q, torch, target, launches):
+    """A few eager launches of one kernel with its inputs already resident, so
+    that one rocprofv3 counter pass sees only that kernel's dispatches."""
+    if target == "copy":
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            dst.copy_(src)
+    else:
+        wl = {"decode_q4k": lambda: Decode(q, torch, "q4k", 4096, 4096, seed=1),
+              "decode_q6k": lambda: Decode(q, torch, "q6k", 32000, 4096, seed=2),
+              "moe": lambda: MoE(q, torch),
+              "prefill": lambda: Prefill(q, torch),
+              "pack": lambda: Prefill(q, torch)}[target]()
+        wl.step(0)
+        torch.cuda.synchronize()
+        for i in range(launches):
+            if target == "pack":
+                q.q8k_pack(wl.x, wl.M, wl.K, wl.xq)
+            else:
+                wl.main(i)
+    torch.cuda.synchronize()
+    print(json.dumps({"profiled": target, "launches": launches, "what": PROFILE_TARGETS[target]}), flush=True)
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -351,6 +388,9 @@ def main():
     ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", choices=sorted(PROFILE_TARGETS), default=None,
+                    help="run only a few launches of one workload's kernel (for rocprofv3 counter passes)")
+    ap.add_argument("--launches", type=int, default=8)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -364,6 +404,10 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     import quantized_q8kpack_fp32_amd as q
+
+    if args.profile:
+        profile_run(q, torch, args.profile, args.launches)
+        return
 
     # ---- headline: 4096x4096 Q4_K decode step
     log("headline: decode_q4k_4096x4096")

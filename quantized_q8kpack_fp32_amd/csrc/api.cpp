@@ -240,7 +240,7 @@ int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const voi
     if (ws_bytes < need)
         return fail(Q8K_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
     if (need > 0) Q8K_TRY(check_ptr(fn, "ws", ws, 16));
-    Q8K_TRY(check_grid(fn, ((rows + 63) / 64) * ((M + 63) / 64)));
+    Q8K_TRY(check_grid(fn, ((rows + 31) / 32) * ((M + 63) / 64)));  // bound for every tile shape
     if (rows == 0 || M == 0) return Q8K_OK;
     const int nb = (int)(K / QK);
     return launched(fn, launch_prefill_q4k(static_cast<const uint8_t*>(w), rows, nb, acts_of(xq, M, K), M, y,
