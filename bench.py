@@ -59,12 +59,13 @@ def source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
+_CS = "quantized_q8kpack_fp32_amd/csrc/"
 KERNEL_SOURCES = {
-    "matvec_q4k": ["quantized_q8kpack_fp32_amd/csrc/matvec.hip", "quantized_q8kpack_fp32_amd/csrc/kquant.h"],
-    "matvec_q6k": ["quantized_q8kpack_fp32_amd/csrc/matvec.hip", "quantized_q8kpack_fp32_amd/csrc/kquant.h"],
-    "moe": ["quantized_q8kpack_fp32_amd/csrc/moe.hip", "quantized_q8kpack_fp32_amd/csrc/kquant.h"],
-    "prefill_q4k": ["quantized_q8kpack_fp32_amd/csrc/prefill.hip"],
-    "pack": ["quantized_q8kpack_fp32_amd/csrc/pack.hip"],
+    "matvec_q4k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
+    "matvec_q6k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
+    "moe": [_CS + "moe.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
+    "prefill_q4k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
+    "pack": [_CS + "pack.hip", _CS + "q8k_device.h"],
 }
 
 
