@@ -26,7 +26,8 @@
 //
 // Work split (producer / consumer waves).  A workgroup of 8 waves owns 128
 // tokens x 64 weight rows.  Waves 4..7 are producers: they keep the global
-// loads two blocks ahead in registers and, per block, build the two weight
+// loads two blocks ahead in registers (coalesced buffer loads, one instruction
+// covering four tokens' 256 code bytes) and, per block, build the two weight
 // planes, the min-term operands and the token codes into one of two LDS
 // buffers.  Waves 0..3 are consumers: each multiplies 64 tokens (two 32-token
 // MFMA tiles) against 32 weight rows from the other buffer and folds the block
@@ -81,16 +82,15 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
 }
 __device__ __forceinline__ float bf16_val(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
 
-// Sub-block scale and min j (0..7) from the 12 packed bytes (hdr.y|z|w).
+// Sub-block scale and min j (0..7) from the 12 packed bytes (hdr.y|z|w),
+// without branches (j differs across the lanes of a wave).
 __device__ __forceinline__ void q4k_scale_min(uint4 hdr, int j, int& sc, int& mn) {
-    if (j < 4) {
-        sc = (int)((hdr.y >> (8 * j)) & 63);
-        mn = (int)((hdr.z >> (8 * j)) & 63);
-    } else {
-        const uint32_t lo = (hdr.w >> (8 * (j - 4))) & 0xffu;
-        sc = (int)((lo & 15) | (((hdr.y >> (8 * (j - 4))) >> 6 & 3) << 4));
-        mn = (int)((lo >> 4) | (((hdr.z >> (8 * (j - 4))) >> 6 & 3) << 4));
-    }
+    const int sh = 8 * (j & 3);
+    const uint32_t yb = (hdr.y >> sh) & 0xffu, zb = (hdr.z >> sh) & 0xffu, wb = (hdr.w >> sh) & 0xffu;
+    const uint32_t sc_lo = yb & 63, mn_lo = zb & 63;
+    const uint32_t sc_hi = (wb & 15) | ((yb >> 6) << 4), mn_hi = (wb >> 4) | ((zb >> 6) << 4);
+    sc = (int)(j < 4 ? sc_lo : sc_hi);
+    mn = (int)(j < 4 ? mn_lo : mn_hi);
 }
 
 // Workgroup barrier for the LDS hand-over only.  __syncthreads() also
@@ -104,47 +104,80 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ------------------------------------------------------------ producers ----
-// Producer thread p (0..255) owns: weight row p/4, quant bytes 32(p&3)..+31
-// (values 64c..64c+63 with c = p&3, i.e. sub-blocks 2c and 2c+1) and that
-// row's header; token p/2, codes 128(p&1)..+127; for p < 128, token p's sums
-// and scale.
+// Global reads go through buffer resources whose range ends at the last row
+// (token) of the problem: a read past it returns zeros and touches no memory,
+// so the tails of the row and token tiles need no clamping and no branches.
+// Lane offsets stay 32-bit: one workgroup's rows span at most
+// 64 * (K / 256) * 144 bytes and its tokens 128 * K bytes, both < 2^31.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_FLAGS = 0x00020000;  // raw untyped buffer, 32-bit dword format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int64_t lim = bytes <= 0 ? 0 : bytes < 0x7fffffff ? bytes : 0x7fffffff;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)lim, RSRC_FLAGS);
+}
+
+// Producer thread p (0..255), wave w = p / 64, lane l = p % 64, owns:
+//  * weight row p/4, quant bytes 32(p&3)..+31 (values 64c..64c+63 with
+//    c = p&3, i.e. sub-blocks 2c and 2c+1) and that row's header;
+//  * 16 bytes of the codes of each of 8 tokens, 16i + 4w + l/16 for
+//    i = 0..7, at byte 16(l&15) of the block: one load instruction of a wave
+//    reads four tokens' 256 contiguous code bytes;
+//  * sub-block sums 4h..4h+3 (h = p&1) and the block scale of token p/2.
 struct PrefillRegs {
     uint4 hdr, q0, q1;
     uint4 x[8];
-    uint4 bsv;
+    uint2 bsv;
     float d8;
 };
 
-__device__ __forceinline__ void producer_load(PrefillRegs& R, const uint8_t* __restrict__ w, int64_t rows, int nb,
-                                              const int8_t* __restrict__ qs, const float* __restrict__ d8,
-                                              const int16_t* __restrict__ bs, int64_t K, int64_t M, int64_t n0,
-                                              int64_t m0, int b, int p) {
-    R.hdr = R.q0 = R.q1 = make_uint4(0, 0, 0, 0);
-    const int64_t n = n0 + (p >> 2);
-    if (b < nb && n < rows) {
-        const uint8_t* blk = w + (n * nb + b) * Q4K_BLOCK;
-        R.hdr = *reinterpret_cast<const uint4*>(blk);
-        R.q0 = *reinterpret_cast<const uint4*>(blk + 16 + 32 * (p & 3));
-        R.q1 = *reinterpret_cast<const uint4*>(blk + 32 + 32 * (p & 3));
-    }
-    const int64_t m = m0 + (p >> 1);
-    if (b < nb && m < M) {
-        const int8_t* src = qs + m * K + (int64_t)b * QK + 128 * (p & 1);
+// Per-workgroup sources (wave-uniform) and per-thread byte offsets.  For
+// block b the resources are rebased to block b (scalar arithmetic), so the
+// range check "offset < records" is exactly "inside the problem".
+struct PrefillSrc {
+    const uint8_t* w;
+    const int8_t* x;
+    const int16_t* bs;
+    const float* d8;
+    int64_t wbytes, xbytes, bsbytes, d8bytes;  // bytes from the tile's first row/token to the end
+    int wo, xo[8], bso, d8o;
+};
+
+__device__ __forceinline__ void producer_src(PrefillSrc& S, const uint8_t* __restrict__ w, int64_t rows, int nb,
+                                             const int8_t* __restrict__ qs, const float* __restrict__ d8,
+                                             const int16_t* __restrict__ bs, int64_t K, int64_t M, int64_t n0,
+                                             int64_t m0, int p) {
+    const int64_t wrow = (int64_t)nb * Q4K_BLOCK;
+    S.w = w + n0 * wrow;
+    S.x = qs + m0 * K;
+    S.bs = bs + m0 * nb * 8;
+    S.d8 = d8 + m0 * nb;
+    S.wbytes = (rows - n0) * wrow;
+    S.xbytes = (M - m0) * K;
+    S.bsbytes = (M - m0) * nb * 16;
+    S.d8bytes = (M - m0) * nb * 4;
+    const int wv = p >> 6, l = p & 63;
+    S.wo = (p >> 2) * (int)wrow;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) R.x[i] = *reinterpret_cast<const uint4*>(src + 16 * i);
-    } else {
+    for (int i = 0; i < 8; ++i) S.xo[i] = (16 * i + 4 * wv + (l >> 4)) * (int)K + 16 * (l & 15);
+    S.bso = (p >> 1) * nb * 16 + 8 * (p & 1);
+    S.d8o = (p >> 1) * nb * 4;
+}
+
+__device__ __forceinline__ void producer_load(PrefillRegs& R, const PrefillSrc& S, int b, int p) {
+    const rsrc_t rw = make_rsrc(S.w + (int64_t)b * Q4K_BLOCK, S.wbytes - (int64_t)b * Q4K_BLOCK);
+    const rsrc_t rx = make_rsrc(S.x + (int64_t)b * QK, S.xbytes - (int64_t)b * QK);
+    const rsrc_t rb = make_rsrc(S.bs + (int64_t)b * 8, S.bsbytes - (int64_t)b * 16);
+    const rsrc_t rd = make_rsrc(S.d8 + b, S.d8bytes - (int64_t)b * 4);
+    const int wq = S.wo + 32 * (p & 3);
+    R.hdr = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, S.wo, 0, 0));
+    R.q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wq + 16, 0, 0));
+    R.q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wq + 32, 0, 0));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) R.x[i] = make_uint4(0, 0, 0, 0);
-    }
-    R.bsv = make_uint4(0, 0, 0, 0);
-    R.d8 = 0.0f;
-    if (p < PF_TM) {
-        const int64_t mt = m0 + p;
-        if (b < nb && mt < M) {
-            R.bsv = *reinterpret_cast<const uint4*>(bs + (mt * nb + b) * 8);
-            R.d8 = d8[mt * nb + b];
-        }
-    }
+    for (int i = 0; i < 8; ++i)
+        R.x[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, S.xo[i], 0, 0));
+    R.bsv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rb, S.bso, 0, 0));
+    R.d8 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, S.d8o, 0, 0));
 }
 
 __device__ __forceinline__ void producer_store(const PrefillRegs& R, PrefillBuf& sm, int p) {
@@ -187,25 +220,26 @@ __device__ __forceinline__ void producer_store(const PrefillRegs& R, PrefillBuf&
     }
     // ---- token codes
     {
-        int8_t* dst = sm.xa + (p >> 1) * PF_LD + 128 * (p & 1);
+        const int wv = p >> 6, l = p & 63;
+        int8_t* dst = sm.xa + (4 * wv + (l >> 4)) * PF_LD + 16 * (l & 15);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(dst + 16 * i) = R.x[i];
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(dst + 16 * i * PF_LD) = R.x[i];
     }
-    // ---- token min-term operand d8 * bsum_j and scale
-    if (p < PF_TM) {
-        const uint32_t bw[4] = {R.bsv.x, R.bsv.y, R.bsv.z, R.bsv.w};
-        uint32_t hb[8], lb[8];
+    // ---- token min-term operand d8 * bsum_j (j = 4h..4h+3) and scale
+    {
+        const int t = p >> 1, h = p & 1;
+        const uint32_t bw[2] = {R.bsv.x, R.bsv.y};
+        uint32_t hb[4], lb[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             const int s = (int)(int16_t)((j & 1) ? (bw[j >> 1] >> 16) : (bw[j >> 1] & 0xffffu));
             const float v = R.d8 * (float)s;
             hb[j] = bf16_bits(v);
             lb[j] = bf16_bits(v - bf16_val(hb[j]));
         }
-        uint4* ajp = reinterpret_cast<uint4*>(&sm.aj[p][0]);
-        ajp[0] = make_uint4(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, hb[4] | hb[5] << 16, hb[6] | hb[7] << 16);
-        ajp[1] = make_uint4(lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, lb[4] | lb[5] << 16, lb[6] | lb[7] << 16);
-        sm.d8[p] = R.d8;
+        *reinterpret_cast<uint2*>(&sm.aj[t][4 * h]) = make_uint2(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16);
+        *reinterpret_cast<uint2*>(&sm.aj[t][8 + 4 * h]) = make_uint2(lb[0] | lb[1] << 16, lb[2] | lb[3] << 16);
+        if (h == 0) sm.d8[t] = R.d8;
     }
 }
 
@@ -289,21 +323,27 @@ __global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restr
         // iteration b - 1 (block 0 before the loop) from registers loaded two
         // iterations earlier; the two register sets alternate.
         const int p = tid - 256;
+        PrefillSrc S;
+        producer_src(S, w, rows, nb, qs, d8, bs, K, M, n0, m0, p);
         PrefillRegs RA, RB;
-        producer_load(RA, w, rows, nb, qs, d8, bs, K, M, n0, m0, 0, p);
-        producer_load(RB, w, rows, nb, qs, d8, bs, K, M, n0, m0, 1, p);
+        // The loads are unconditional: past the last block the resources
+        // have no records, so the reads return zeros without touching memory.
+        // Branch-free loads keep the compiler's wait counts exact, so that a
+        // store waits only for its own register set, two blocks old.
+        producer_load(RA, S, 0, p);
+        producer_load(RB, S, 1, p);
         producer_store(RA, sm.buf[0], p);
-        producer_load(RA, w, rows, nb, qs, d8, bs, K, M, n0, m0, 2, p);
+        producer_load(RA, S, 2, p);
         lds_barrier();
         for (int b = 0; b < nb; b += 2) {
             // after block b is consumed: build block b+1 (RB), refill RB with b+3
             if (b + 1 < nb) producer_store(RB, sm.buf[1], p);
-            producer_load(RB, w, rows, nb, qs, d8, bs, K, M, n0, m0, b + 3, p);
+            producer_load(RB, S, b + 3, p);
             lds_barrier();
             if (b + 1 >= nb) break;
             // after block b+1 is consumed: build block b+2 (RA), refill RA with b+4
             if (b + 2 < nb) producer_store(RA, sm.buf[0], p);
-            producer_load(RA, w, rows, nb, qs, d8, bs, K, M, n0, m0, b + 4, p);
+            producer_load(RA, S, b + 4, p);
             lds_barrier();
         }
     } else {
