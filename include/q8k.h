@@ -71,6 +71,7 @@ typedef enum {
 #define Q8K_QK 256         /* values per K-quant super-block / q8_K block       */
 #define Q8K_COLS_MAX 8     /* most activation columns qmatvec_batched serves    */
 #define Q8K_MOE_MAX_TOKENS 256 /* most tokens qmatvec_moe serves per call       */
+#define Q8K_MOE_MAX_TOPK 64    /* most experts per token qmatvec_moe serves     */
 
 /* ---------------------------------------------------------------- sizing --
  * q8_K activation buffer for T tokens of K values: three sections, each
@@ -123,7 +124,7 @@ int qmatvec_batched(int qtype, const void* w, int64_t rows, int64_t K, const voi
 /* qmatvec_moe: expert-indexed decode.  w holds E experts, each a rows x K
  * weight in the given layout, expert e's blocks following expert e-1's.
  * xq: q8_K buffer of T tokens (0 <= T <= Q8K_MOE_MAX_TOKENS); ids int32
- * [T][topk]; rw fp32 [T][topk]; 1 <= topk <= E.
+ * [T][topk]; rw fp32 [T][topk]; 1 <= topk <= min(E, Q8K_MOE_MAX_TOPK).
  *   y[t][r] = sum_k rw[t][k] * (W_{ids[t][k]} x_t)[r]
  * Each expert row that at least one token selected is read once for all of
  * its tokens; an expert nobody selected is not read.  y: fp32 [T][rows]. */

@@ -31,7 +31,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
-_SCRATCH = re.compile(r"remark: .*?:\d+:\d+: Function Name: (\S+)")
+_SCRATCH = re.compile(r"remark: Function Name: (\S+)")
 _SCRATCH_SIZE = re.compile(r"ScratchSize \[bytes/lane\]: (\d+)")
 
 

@@ -199,8 +199,9 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
         return fail(Q8K_ERR_SHAPE, "%s: E*rows=%lld exceeds %lld", fn, (long long)(E * rows), (long long)MAX_ROWS);
     if (T < 0 || T > Q8K_MOE_MAX_TOKENS)
         return fail(Q8K_ERR_ARG, "%s: T=%lld must be in [0, %d]", fn, (long long)T, Q8K_MOE_MAX_TOKENS);
-    if (topk < 1 || topk > E)
-        return fail(Q8K_ERR_ARG, "%s: topk=%d must be in [1, E=%lld]", fn, topk, (long long)E);
+    if (topk < 1 || topk > E || topk > Q8K_MOE_MAX_TOPK)
+        return fail(Q8K_ERR_ARG, "%s: topk=%d must be in [1, min(E=%lld, %d)]", fn, topk, (long long)E,
+                    Q8K_MOE_MAX_TOPK);
     Q8K_TRY(check_weight(fn, qtype, w, true));
     Q8K_TRY(check_ptr(fn, "xq", xq, 16));
     Q8K_TRY(check_ptr(fn, "ids", ids, 4));

@@ -109,14 +109,6 @@ __device__ __forceinline__ void lds_barrier() {
 // so the tails of the row and token tiles need no clamping and no branches.
 // Lane offsets stay 32-bit: one workgroup's rows span at most
 // 64 * (K / 256) * 144 bytes and its tokens 128 * K bytes, both < 2^31.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int RSRC_FLAGS = 0x00020000;  // raw untyped buffer, 32-bit dword format
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    const int64_t lim = bytes <= 0 ? 0 : bytes < 0x7fffffff ? bytes : 0x7fffffff;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)lim, RSRC_FLAGS);
-}
-
 // Producer thread p (0..255), wave w = p / 64, lane l = p % 64, owns:
 //  * weight row p/4, quant bytes 32(p&3)..+31 (values 64c..64c+63 with
 //    c = p&3, i.e. sub-blocks 2c and 2c+1) and that row's header;
@@ -170,14 +162,14 @@ __device__ __forceinline__ void producer_load(PrefillRegs& R, const PrefillSrc& 
     const rsrc_t rb = make_rsrc(S.bs + (int64_t)b * 8, S.bsbytes - (int64_t)b * 16);
     const rsrc_t rd = make_rsrc(S.d8 + b, S.d8bytes - (int64_t)b * 4);
     const int wq = S.wo + 32 * (p & 3);
-    R.hdr = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, S.wo, 0, 0));
-    R.q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wq + 16, 0, 0));
-    R.q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wq + 32, 0, 0));
+    R.hdr = load16(rw, S.wo);
+    R.q0 = load16(rw, wq + 16);
+    R.q1 = load16(rw, wq + 32);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        R.x[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, S.xo[i], 0, 0));
-    R.bsv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rb, S.bso, 0, 0));
-    R.d8 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, S.d8o, 0, 0));
+        R.x[i] = load16(rx, S.xo[i]);
+    R.bsv = load8(rb, S.bso);
+    R.d8 = __builtin_bit_cast(float, load4(rd, S.d8o));
 }
 
 __device__ __forceinline__ void producer_store(const PrefillRegs& R, PrefillBuf& sm, int p) {

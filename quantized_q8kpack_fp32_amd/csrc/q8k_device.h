@@ -31,6 +31,25 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
+// Raw buffer resource over [base, base + bytes): a read at a byte offset at
+// or past `bytes` returns zeros and touches no memory.  The record count is a
+// 32-bit field, so ranges are capped at 2^31 - 1 bytes; callers keep their
+// offsets below that.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int64_t lim = bytes <= 0 ? 0 : bytes < 0x7fffffff ? bytes : 0x7fffffff;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)lim,
+                                             0x00020000 /* raw, untyped dwords */);
+}
+__device__ __forceinline__ uint4 load16(rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 load8(rsrc_t r, int off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t load4(rsrc_t r, int off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+__device__ __forceinline__ uint32_t load2(rsrc_t r, int off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
+
 // int8x4 . int8x4 + acc, signed (v_dot4_i32_i8).
 __device__ __forceinline__ int sdot4(int a, int b, int acc) { return __builtin_amdgcn_sdot4(a, b, acc, false); }
 

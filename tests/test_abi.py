@@ -103,6 +103,8 @@ def test_batched_and_moe_arguments(q):
     refused(q, "Q8K_ERR_ARG", q.qmatvec_moe, q.Q8K_Q4_K, A16, 0, 4, 256, A16, 16, A16, A16, 1, A16, 0)
     refused(q, "Q8K_ERR_ARG", q.qmatvec_moe, q.Q8K_Q4_K, A16, 8, 4, 256, A16, q.Q8K_MOE_MAX_TOKENS + 1,
             A16, A16, 2, A16, 0)
+    refused(q, "Q8K_ERR_ARG", q.qmatvec_moe, q.Q8K_Q4_K, A16, 128, 4, 256, A16, 2, A16, A16,
+            q.Q8K_MOE_MAX_TOPK + 1, A16, 0)
     refused(q, "Q8K_ERR_NULL", q.qmatvec_moe, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, None, A16, 2, A16, 0)
 
 
