@@ -22,6 +22,11 @@
 
 namespace q8k {
 
+// Up to this many columns a wave keeps two 8-block groups (U = 2) in flight.
+#ifndef Q8K_MV_U2_MAXNC
+#define Q8K_MV_U2_MAXNC 4
+#endif
+
 // ---------------------------------------------------------------- Q4_K ----
 template <int NC>
 struct Q4Chunk {
@@ -125,79 +130,139 @@ __global__ __launch_bounds__(256) void sums_q4k_kernel(const uint8_t* __restrict
 }
 
 // ---------------------------------------------------------------- Q6_K ----
-template <int NC>
-struct Q6Chunk {
-    uint4 qlv, qhv, scv;
+// Lane map: lane l serves block b = 16k + (l >> 2) and the pair (h, lh) =
+// ((l >> 1) & 1, l & 1): the two ql chunks 4h + lh and 4h + 2 + lh (tt = 0
+// and 1), their shared qh chunk 2h + lh and the 8 scale bytes 8h..8h+7.  Four
+// lanes cover a block, so a 64-lane pass spans 16 blocks (a 4096-wide row),
+// every qh byte is read once and the scales need one 8-byte load per lane.
+struct Q6W {  // one pass of one row
+    uint4 ql0, ql1, qhv;
+    uint2 scv;
     uint32_t dbits;
-    int4 alo[NC], ahi[NC];
+};
+template <int NC>
+struct Q6A {  // one pass of the activation columns
+    int4 a[NC][4];  // codes of tt = 0 (low, high nibbles), tt = 1 (low, high)
     float d8[NC];
 };
 
-template <int NC>
-__device__ __forceinline__ void q6k_load(Q6Chunk<NC>& L, const uint16_t* __restrict__ prefix,
-                                         const uint8_t* __restrict__ bodies, int64_t row, int b, int ci, int qhoff,
-                                         int aoff, const int8_t* __restrict__ qs, const float* __restrict__ d8,
-                                         int64_t K, int nb) {
+__device__ __forceinline__ void q6k_load_w(Q6W& W, const uint16_t* __restrict__ prefix,
+                                           const uint8_t* __restrict__ bodies, int64_t row, int b, int h, int lh,
+                                           int nb) {
     const int64_t ib = row * nb + b;
     const uint8_t* body = bodies + ib * Q6K_BODY;
-    L.qlv = *reinterpret_cast<const uint4*>(body + 16 * ci);
-    L.qhv = *reinterpret_cast<const uint4*>(body + qhoff);
-    L.scv = *reinterpret_cast<const uint4*>(body + 192);
-    L.dbits = prefix[ib];
+    W.ql0 = *reinterpret_cast<const uint4*>(body + 16 * (4 * h + lh));
+    W.ql1 = *reinterpret_cast<const uint4*>(body + 16 * (4 * h + 2 + lh));
+    W.qhv = *reinterpret_cast<const uint4*>(body + 128 + 16 * (2 * h + lh));
+    W.scv = *reinterpret_cast<const uint2*>(body + 192 + 8 * h);
+    W.dbits = prefix[ib];
+}
+
+template <int NC>
+__device__ __forceinline__ void q6k_load_a(Q6A<NC>& A, int b, int h, int lh, const int8_t* __restrict__ qs,
+                                           const float* __restrict__ d8, int64_t K, int nb) {
+    const int aoff = 128 * h + 16 * lh;
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
         const int8_t* a = qs + t * K + (int64_t)b * QK + aoff;
-        L.alo[t] = *reinterpret_cast<const int4*>(a);
-        L.ahi[t] = *reinterpret_cast<const int4*>(a + 64);
-        L.d8[t] = d8[(int64_t)t * nb + b];
+        A.a[t][0] = *reinterpret_cast<const int4*>(a);       // tt = 0, low nibbles
+        A.a[t][1] = *reinterpret_cast<const int4*>(a + 64);  // tt = 0, high nibbles
+        A.a[t][2] = *reinterpret_cast<const int4*>(a + 32);  // tt = 1, low nibbles
+        A.a[t][3] = *reinterpret_cast<const int4*>(a + 96);  // tt = 1, high nibbles
+        A.d8[t] = d8[(int64_t)t * nb + b];
     }
 }
 
 template <int NC>
-__device__ __forceinline__ void q6k_accum(const Q6Chunk<NC>& L, int tt, int s0, bool valid, float (&acc)[NC]) {
-    const int sc0 = (int)(int8_t)byte_of(L.scv, s0);
-    const int sc1 = (int)(int8_t)byte_of(L.scv, s0 + 4);
-    const float dd = half_bits_to_float(L.dbits);
-    uint32_t lo[4], hi[4];
-    q6k_unpack(L.qlv, L.qhv, tt, lo, hi);
+__device__ __forceinline__ void q6k_accum(const Q6W& W, const Q6A<NC>& A, int lh, bool valid, float (&acc)[NC]) {
+    // scale bytes (relative to 8h): sub-blocks 8h + 2tt + lh and +4
+    const uint32_t sw0 = W.scv.x >> (8 * lh), sw1 = W.scv.y >> (8 * lh);
+    const int sc00 = (int)(int8_t)(sw0 & 0xffu), sc01 = (int)(int8_t)(sw1 & 0xffu);                  // tt = 0
+    const int sc10 = (int)(int8_t)((sw0 >> 16) & 0xffu), sc11 = (int)(int8_t)((sw1 >> 16) & 0xffu);  // tt = 1
+    const float dd = half_bits_to_float(W.dbits);
+    uint32_t lo0[4], hi0[4], lo1[4], hi1[4];
+    q6k_unpack(W.ql0, W.qhv, 0, lo0, hi0);
+    q6k_unpack(W.ql1, W.qhv, 1, lo1, hi1);
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
-        const int S0 = q6k_sum16(lo, L.alo[t]);
-        const int S1 = q6k_sum16(hi, L.ahi[t]);
-        const float v = L.d8[t] * dd * (float)(sc0 * S0 + sc1 * S1);
+        const int I = sc00 * q6k_sum16(lo0, A.a[t][0]) + sc01 * q6k_sum16(hi0, A.a[t][1]) +
+                      sc10 * q6k_sum16(lo1, A.a[t][2]) + sc11 * q6k_sum16(hi1, A.a[t][3]);
+        const float v = A.d8[t] * dd * (float)I;
         acc[t] += valid ? v : 0.0f;
     }
 }
 
-template <int NC, int U>
-__global__ __launch_bounds__(256) void matvec_q6k_kernel(const uint16_t* __restrict__ prefix,
-                                                         const uint8_t* __restrict__ bodies, int64_t rows, int nb,
-                                                         const int8_t* __restrict__ qs, const float* __restrict__ d8,
-                                                         int64_t K, float* __restrict__ y) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (row >= rows) return;
-    const int ci = lane & 7, h = ci >> 2, tt = (ci >> 1) & 1, lh = ci & 1;
-    const int s0 = 8 * h + 2 * tt + lh;
-    const int aoff = 128 * h + 32 * tt + 16 * lh;
-    const int qhoff = 128 + 16 * (2 * h + lh);
-    float acc[NC];
-#pragma unroll
-    for (int t = 0; t < NC; ++t) acc[t] = 0.0f;
-    for (int b0 = lane >> 3; b0 - (lane >> 3) < nb; b0 += 8 * U) {
-        Q6Chunk<NC> L[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int b = b0 + 8 * u;
-            q6k_load(L[u], prefix, bodies, row, b < nb ? b : nb - 1, ci, qhoff, aoff, qs, d8, K, nb);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) q6k_accum(L[u], tt, s0, b0 + 8 * u < nb, acc);
-    }
+template <int NC>
+__device__ __forceinline__ void q6k_store(const float (&acc)[NC], int lane, int64_t rows, int64_t row,
+                                          float* __restrict__ y) {
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
         const float v = wave_sum_dpp(acc[t]);
         if (lane == 0) y[(int64_t)t * rows + row] = v;
+    }
+}
+
+// One wave walks rows row0, row0 + stride, ... (stride = all waves of the
+// grid).  When a row fits one pass (K <= 4096) the activation codes are loaded
+// once per wave and the weights of the wave's next Q6_DEPTH - 1 rows are
+// issued before the current row is reduced, so Q6_DEPTH rows are in flight;
+// a prefetch past the last row re-reads the wave's current row (cache-hot)
+// and is not used.
+#ifndef Q8K_Q6_DEPTH
+#define Q8K_Q6_DEPTH 2
+#endif
+constexpr int Q6_DEPTH = Q8K_Q6_DEPTH;
+template <int NC>
+__global__ __launch_bounds__(256) void matvec_q6k_kernel(const uint16_t* __restrict__ prefix,
+                                                         const uint8_t* __restrict__ bodies, int64_t rows, int nb,
+                                                         const int8_t* __restrict__ qs, const float* __restrict__ d8,
+                                                         int64_t K, float* __restrict__ y) {
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;  // uniform per wave
+    const int h = (lane >> 1) & 1, lh = lane & 1;
+    const int bl = lane >> 2;
+    if (nb <= 16) {
+        const bool valid = bl < nb;
+        const int b = valid ? bl : nb - 1;
+        Q6A<NC> A;
+        q6k_load_a(A, b, h, lh, qs, d8, K, nb);
+        Q6W W[Q6_DEPTH];
+#pragma unroll
+        for (int i = 0; i < Q6_DEPTH - 1; ++i) {
+            const int64_t r = row + i * stride;
+            q6k_load_w(W[i], prefix, bodies, r < rows ? r : row, b, h, lh, nb);
+        }
+        for (;;) {
+#pragma unroll
+            for (int i = 0; i < Q6_DEPTH; ++i) {
+                const int64_t cur = row + i * stride;
+                const int64_t pre = cur + (Q6_DEPTH - 1) * stride;
+                q6k_load_w(W[(i + Q6_DEPTH - 1) % Q6_DEPTH], prefix, bodies, pre < rows ? pre : cur, b, h, lh, nb);
+                float acc[NC];
+#pragma unroll
+                for (int t = 0; t < NC; ++t) acc[t] = 0.0f;
+                q6k_accum(W[i], A, lh, valid, acc);
+                q6k_store(acc, lane, rows, cur, y);
+                if (cur + stride >= rows) return;
+            }
+            row += Q6_DEPTH * stride;
+        }
+    }
+    for (; row < rows; row += stride) {
+        float acc[NC];
+#pragma unroll
+        for (int t = 0; t < NC; ++t) acc[t] = 0.0f;
+        for (int b0 = bl; b0 - bl < nb; b0 += 16) {
+            const int b = b0 < nb ? b0 : nb - 1;
+            Q6W W;
+            Q6A<NC> A;
+            q6k_load_w(W, prefix, bodies, row, b, h, lh, nb);
+            q6k_load_a(A, b, h, lh, qs, d8, K, nb);
+            q6k_accum(W, A, lh, b0 < nb, acc);
+        }
+        q6k_store(acc, lane, rows, row, y);
     }
 }
 
@@ -222,20 +287,24 @@ __global__ __launch_bounds__(256) void sums_q6k_kernel(const uint8_t* __restrict
 }
 
 // ----------------------------------------------------------- launchers ----
-// Two 8-block groups per loop trip for up to two columns (covers a 4096-wide
-// row in one trip); one group per trip for more columns, where the activation
-// registers of every column already give enough loads in flight.
+// Q4_K: two 8-block groups per loop trip for up to Q8K_MV_U2_MAXNC columns
+// (a 4096-wide row in one trip); one group per trip for more columns, where
+// the activation registers of every column already give enough loads in
+// flight.  Q6_K: one 16-block pass per trip.
 template <int NC>
 static void go_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, float* y, hipStream_t s) {
-    constexpr int U = NC <= 2 ? 2 : 1;
+    constexpr int U = NC <= Q8K_MV_U2_MAXNC ? 2 : 1;
     hipLaunchKernelGGL((matvec_q4k_kernel<NC, U>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb,
                        a.qs, a.d, a.bs, a.K, y);
 }
+#ifndef Q8K_Q6_GRID
+#define Q8K_Q6_GRID 512
+#endif
 template <int NC>
 static void go_q6k(const uint16_t* p, const uint8_t* bodies, int64_t rows, int nb, Acts a, float* y, hipStream_t s) {
-    constexpr int U = NC <= 2 ? 2 : 1;
-    hipLaunchKernelGGL((matvec_q6k_kernel<NC, U>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, bodies, rows,
-                       nb, a.qs, a.d, a.K, y);
+    const int64_t wgs = (rows + 3) / 4;
+    const unsigned grid = (unsigned)(wgs < Q8K_Q6_GRID ? wgs : Q8K_Q6_GRID);
+    hipLaunchKernelGGL((matvec_q6k_kernel<NC>), dim3(grid), dim3(256), 0, s, p, bodies, rows, nb, a.qs, a.d, a.K, y);
 }
 
 hipError_t launch_matvec_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int ncols, float* y, hipStream_t s) {
