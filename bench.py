@@ -448,16 +448,18 @@ def main():
         wl = {}
         steps = max(20, min(args.steps, 100))
 
-        def decode_entry(name, d):
+        def decode_entry(name, d, kernel=None):
             p = d.parity()
             s, us = run_timed(torch, d, steps, 5)
             gbs = d.mv_bytes / (us * 1e-6) / 1e9
             wl[name] = {"parity": "pass" if p else "FAIL", "kernel_us": round(us, 3), "GB/s": round(gbs, 1),
                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "step_ms": round(s * 1e3, 4),
                         "bytes_per_launch": d.mv_bytes, "weight_copies_rotated": d.R}
+            if kernel:
+                wl[name]["traffic"] = traffic_record(kernel)
 
         log("workload: decode_q6k_32000x4096")
-        decode_entry("decode_q6k_32000x4096", Decode(q, torch, "q6k", 32000, 4096, seed=2))
+        decode_entry("decode_q6k_32000x4096", Decode(q, torch, "q6k", 32000, 4096, seed=2), "matvec_q6k")
         torch.cuda.empty_cache()
         for nc in (4, 8):
             log(f"workload: batched_q4k_4096x4096_cols{nc}")
@@ -465,7 +467,7 @@ def main():
             torch.cuda.empty_cache()
         log("workload: moe_q4k_8x14336x4096_t16_top2")
         m = MoE(q, torch)
-        decode_entry("moe_q4k_8x14336x4096_t16_top2", m)
+        decode_entry("moe_q4k_8x14336x4096_t16_top2", m, "moe")
         wl["moe_q4k_8x14336x4096_t16_top2"]["experts_hit"] = m.experts_hit
         del m
         torch.cuda.empty_cache()
