@@ -437,7 +437,7 @@ def main():
                    "parity": "pass" if parity else "FAIL"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
-                     "kernel": "matvec_q4k_kernel<1>", "launch_us": round(mv_us, 3),
+                     "kernel": "matvec_q4k_kernel<1, 2>", "launch_us": round(mv_us, 3),
                      "algorithmic_bytes_per_launch": hd.mv_bytes},
     }
     del hd
