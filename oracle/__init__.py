@@ -26,8 +26,10 @@ _lib = None
 QK = 256
 Q4_K = 1
 Q6_K = 2
+Q5_K = 3
 Q4K_BLOCK_BYTES = 144
 Q6K_BLOCK_BYTES = 210
+Q5K_BLOCK_BYTES = 176
 
 
 def build(force: bool = False) -> str:
@@ -55,6 +57,9 @@ def _load():
     lib.or_f16_to_f32.argtypes = [ctypes.c_uint16]
     lib.or_q4k_fields.argtypes = [P, P, P, P, P, P]
     lib.or_q6k_fields.argtypes = [P, P, P, P]
+    lib.or_q5k_fields.argtypes = [P, P, P, P, P, P]
+    lib.or_dequant_q5k.argtypes = [P, I64, I64, P]
+    lib.or_subblock_sums_q5k.argtypes = [P, I64, I64, P, P]
     lib.or_dequant_q4k.argtypes = [P, I64, I64, P]
     lib.or_dequant_q6k.argtypes = [P, I64, I64, P]
     lib.or_q8k_pack.argtypes = [P, I64, I64, P, P, P]
@@ -106,6 +111,19 @@ def q4k_fields(block: np.ndarray):
     return float(d[0]), float(dmin[0]), sc, mn, q
 
 
+def q5k_fields(block: np.ndarray):
+    """Decode one 176-byte Q5_K block -> (d, dmin, sc[8], m[8], q[256] in 0..31)."""
+    block = _c(block, np.uint8)
+    assert block.size == Q5K_BLOCK_BYTES
+    d = np.zeros(1, np.float32)
+    dmin = np.zeros(1, np.float32)
+    sc = np.zeros(8, np.uint8)
+    mn = np.zeros(8, np.uint8)
+    q = np.zeros(QK, np.uint8)
+    _load().or_q5k_fields(_p(block), _p(d), _p(dmin), _p(sc), _p(mn), _p(q))
+    return float(d[0]), float(dmin[0]), sc, mn, q
+
+
 def q6k_fields(block: np.ndarray):
     """Decode one 210-byte Q6_K block -> (d, sc[16] int8, q[256] in 0..63)."""
     block = _c(block, np.uint8)
@@ -122,6 +140,8 @@ def dequant(qtype: int, w: np.ndarray, rows: int, K: int) -> np.ndarray:
     out = np.empty((rows, K), np.float64)
     if qtype == Q4_K:
         _load().or_dequant_q4k(_p(w), rows, K, _p(out))
+    elif qtype == Q5_K:
+        _load().or_dequant_q5k(_p(w), rows, K, _p(out))
     else:
         _load().or_dequant_q6k(_p(w), rows, K, _p(out))
     return out
@@ -147,6 +167,9 @@ def subblock_sums(qtype: int, w: np.ndarray, rows: int, K: int, qs_row: np.ndarr
     if qtype == Q4_K:
         S = np.empty((rows, K // 32), np.int32)
         _load().or_subblock_sums_q4k(_p(w), rows, K, _p(qs_row), _p(S))
+    elif qtype == Q5_K:
+        S = np.empty((rows, K // 32), np.int32)
+        _load().or_subblock_sums_q5k(_p(w), rows, K, _p(qs_row), _p(S))
     else:
         S = np.empty((rows, K // 16), np.int32)
         _load().or_subblock_sums_q6k(_p(w), rows, K, _p(qs_row), _p(S))

@@ -17,8 +17,9 @@
  *
  * Readings taken where the pages are silent (each one is listed with its
  * reason in the design notes of the repository):
- *  - Q4_K and Q6_K byte layouts are the public GGUF block definitions (the
- *    pages name the formats but print no layout).
+ *  - Q4_K, Q5_K and Q6_K byte layouts are the public GGUF block definitions
+ *    (the pages name the formats but print no layout; for Q5_K they say only
+ *    that it is Q4_K with a fifth-bit plane that supplies bit 4 of each value).
  *  - q8_K: d = amax/127 (positive), qs = round-half-even(x * (127/amax))
  *    clamped to [-127,127], computed in fp32 (a floating-point decision that
  *    produces integers is taken in the kernel's precision); an all-zero block
@@ -94,6 +95,25 @@ void or_q4k_fields(const uint8_t* blk, float* d, float* dmin, uint8_t sc[8], uin
 }
 
 /* ------------------------------------------------------------------------ */
+/* O2b. Q5_K block (176 bytes): fp16 d @0, fp16 dmin @2, the 12 scale/min    */
+/* bytes @4 packed as in Q4_K, qh[32] @16, 128 bytes of low nibbles @48.     */
+/* Value l (0..31) of sub-block j is the nibble Q4_K would give it plus 16   */
+/* times bit j of qh[l], so q is in 0..31.                                    */
+/* ------------------------------------------------------------------------ */
+void or_q5k_fields(const uint8_t* blk, float* d, float* dmin, uint8_t sc[8], uint8_t mn[8],
+                   uint8_t q[QK]) {
+    /* d, dmin and the scale bytes sit where Q4_K has them; Q4_K's decode of
+       a block whose quant bytes are ours gives the four low bits */
+    uint8_t tmp[144];
+    memcpy(tmp, blk, 16);
+    memcpy(tmp + 16, blk + 48, 128);
+    or_q4k_fields(tmp, d, dmin, sc, mn, q);
+    const uint8_t* qh = blk + 16;
+    for (int j = 0; j < 8; ++j)
+        for (int l = 0; l < 32; ++l) q[32 * j + l] = (uint8_t)(q[32 * j + l] | (((qh[l] >> j) & 1) << 4));
+}
+
+/* ------------------------------------------------------------------------ */
 /* O3. Q6_K block (210 bytes): ql[128] @0 (low 4 bits), qh[64] @128 (high 2  */
 /* bits), int8 scales[16] @192, fp16 d @208.  Quant q in 0..63, value q-32.  */
 /* ------------------------------------------------------------------------ */
@@ -119,6 +139,18 @@ void or_dequant_q4k(const uint8_t* w, int64_t rows, int64_t K, double* out) {
             float d, dmin;
             uint8_t sc[8], mn[8], q[QK];
             or_q4k_fields(w + (r * nb + b) * 144, &d, &dmin, sc, mn, q);
+            for (int v = 0; v < QK; ++v)
+                out[r * K + b * QK + v] = (double)d * sc[v / 32] * q[v] - (double)dmin * mn[v / 32];
+        }
+}
+
+void or_dequant_q5k(const uint8_t* w, int64_t rows, int64_t K, double* out) {
+    int64_t nb = K / QK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            float d, dmin;
+            uint8_t sc[8], mn[8], q[QK];
+            or_q5k_fields(w + (r * nb + b) * 176, &d, &dmin, sc, mn, q);
             for (int v = 0; v < QK; ++v)
                 out[r * K + b * QK + v] = (double)d * sc[v / 32] * q[v] - (double)dmin * mn[v / 32];
         }
@@ -200,6 +232,22 @@ void or_subblock_sums_q4k(const uint8_t* w, int64_t rows, int64_t K, const int8_
         }
 }
 
+/* Q5_K: as Q4_K, over the 5-bit quants. */
+void or_subblock_sums_q5k(const uint8_t* w, int64_t rows, int64_t K, const int8_t* qs, int32_t* S) {
+    int64_t nb = K / QK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            float d, dmin;
+            uint8_t sc[8], mn[8], q[QK];
+            or_q5k_fields(w + (r * nb + b) * 176, &d, &dmin, sc, mn, q);
+            for (int j = 0; j < 8; ++j) {
+                int32_t s = 0;
+                for (int i = 0; i < 32; ++i) s += (int32_t)q[32 * j + i] * qs[b * QK + 32 * j + i];
+                S[r * nb * 8 + b * 8 + j] = s;
+            }
+        }
+}
+
 void or_subblock_sums_q6k(const uint8_t* w, int64_t rows, int64_t K, const int8_t* qs, int32_t* S) {
     int64_t nb = K / QK;
     for (int64_t r = 0; r < rows; ++r)
@@ -221,13 +269,18 @@ void or_subblock_sums_q6k(const uint8_t* w, int64_t rows, int64_t K, const int8_
 /* token (qs, d8, bsums of that token).  fp64 epilogue over exact integers;  */
 /* *A receives the sum of |terms| at sub-block granularity.                  */
 /* ------------------------------------------------------------------------ */
+/* Q4_K and Q5_K share the epilogue: y = sum_b d8 (d sum_j sc_j S_j - dmin
+   sum_j m_j bsum_j); `five` selects the 176-byte Q5_K block. */
 static double dot_q4k_row(const uint8_t* wr, int64_t nb, const int8_t* qs, const float* d8,
-                          const int16_t* bsums, double* A) {
+                          const int16_t* bsums, double* A, int five) {
     double y = 0.0, a = 0.0;
     for (int64_t b = 0; b < nb; ++b) {
         float d, dmin;
         uint8_t sc[8], mn[8], q[QK];
-        or_q4k_fields(wr + b * 144, &d, &dmin, sc, mn, q);
+        if (five)
+            or_q5k_fields(wr + b * 176, &d, &dmin, sc, mn, q);
+        else
+            or_q4k_fields(wr + b * 144, &d, &dmin, sc, mn, q);
         int64_t isum = 0, msum = 0;
         for (int j = 0; j < 8; ++j) {
             int64_t S = 0;
@@ -266,10 +319,13 @@ static double dot_q6k_row(const uint8_t* wr, int64_t nb, const int8_t* qs, const
 
 /* ------------------------------------------------------------------------ */
 /* O7. Mat-vec over T packed tokens: y[t][r], A[t][r].  qtype 1 = Q4_K       */
-/* (144-byte GGUF blocks), 2 = Q6_K (210-byte GGUF blocks).  Rows are split  */
+/* (144-byte GGUF blocks), 2 = Q6_K (210-byte GGUF blocks), 3 = Q5_K         */
+/* (176-byte GGUF blocks).  Rows are split                                   */
 /* across `nthreads` pthreads (each output is computed by one thread, so the */
 /* result does not depend on the thread count).                              */
 /* ------------------------------------------------------------------------ */
+int64_t or_block_bytes(int qtype) { return qtype == 1 ? 144 : qtype == 2 ? 210 : qtype == 3 ? 176 : 0; }
+
 typedef struct {
     int qtype;
     const uint8_t* w;
@@ -285,13 +341,14 @@ typedef struct {
 static void* mv_worker(void* p) {
     mv_job* j = (mv_job*)p;
     int64_t nb = j->K / QK;
-    int64_t bb = j->qtype == 1 ? 144 : 210;
+    int64_t bb = or_block_bytes(j->qtype);
     for (int64_t t = 0; t < j->T; ++t)
         for (int64_t r = j->r0; r < j->r1; ++r) {
             const uint8_t* wr = j->w + r * nb * bb;
             double a;
-            double y = j->qtype == 1 ? dot_q4k_row(wr, nb, j->qs + t * j->K, j->d8 + t * nb, j->bsums + t * nb * 8, &a)
-                                     : dot_q6k_row(wr, nb, j->qs + t * j->K, j->d8 + t * nb, &a);
+            double y = j->qtype == 2 ? dot_q6k_row(wr, nb, j->qs + t * j->K, j->d8 + t * nb, &a)
+                                     : dot_q4k_row(wr, nb, j->qs + t * j->K, j->d8 + t * nb, j->bsums + t * nb * 8,
+                                                   &a, j->qtype == 3);
             j->y[t * j->rows + r] = y;
             if (j->A) j->A[t * j->rows + r] = a;
         }
@@ -300,7 +357,7 @@ static void* mv_worker(void* p) {
 
 int or_matvec(int qtype, const uint8_t* w, int64_t rows, int64_t K, const int8_t* qs, const float* d8,
               const int16_t* bsums, int64_t T, double* y, double* A, int nthreads) {
-    if ((qtype != 1 && qtype != 2) || rows < 0 || T < 0 || K % QK) return -1;
+    if (or_block_bytes(qtype) == 0 || rows < 0 || T < 0 || K % QK) return -1;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     if ((int64_t)nthreads > rows) nthreads = rows > 0 ? (int)rows : 1;
@@ -326,9 +383,9 @@ int or_matvec(int qtype, const uint8_t* w, int64_t rows, int64_t K, const int8_t
 int or_moe(int qtype, const uint8_t* w, int64_t E, int64_t rows, int64_t K, const int8_t* qs, const float* d8,
            const int16_t* bsums, int64_t T, const int32_t* ids, const float* rw, int64_t topk, double* y, double* A,
            int nthreads) {
-    if ((qtype != 1 && qtype != 2) || K % QK || E < 1 || topk < 1) return -1;
+    if (or_block_bytes(qtype) == 0 || K % QK || E < 1 || topk < 1) return -1;
     int64_t nb = K / QK;
-    int64_t bb = qtype == 1 ? 144 : 210;
+    int64_t bb = or_block_bytes(qtype);
     double* ye = (double*)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1));
     double* ae = (double*)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1));
     if (!ye || !ae) {

@@ -12,6 +12,10 @@ Why raw random bytes give the documented field distributions:
   hold 256 nibbles, one-to-one, so uniform bytes give quants uniform on 0..15.
   Only the two fp16 fields (d at byte 0, dmin at byte 2) are drawn as reals and
   rounded to fp16 (numpy's float16 cast rounds to nearest even).
+* Q5_K (176-byte GGUF block): the same d, dmin and 12 scale/min bytes as
+  Q4_K, then 32 bytes whose 256 bits are the fifth bits of the 256 values
+  one-to-one, then 128 bytes of low nibbles: uniform bytes give quants uniform
+  on 0..31.
 * Q6_K (210-byte GGUF block): ql (128 bytes) and qh (64 bytes) hold 256 4-bit
   and 256 2-bit fields one-to-one, so uniform bytes give 6-bit quants uniform on
   0..63; the 16 int8 scales are uniform bytes, i.e. uniform on -128..127; d
@@ -27,6 +31,7 @@ import numpy as np
 
 QK = 256
 Q4K_BLOCK_BYTES = 144
+Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
 
 
@@ -44,6 +49,19 @@ def q4k_weights(g: np.random.Generator, rows: int, K: int,
     assert K % QK == 0
     nblk = rows * (K // QK)
     blk = g.integers(0, 256, size=(nblk, Q4K_BLOCK_BYTES), dtype=np.uint8)
+    d = _f16_bits(g.uniform(*d_range, size=nblk))
+    dmin = _f16_bits(g.uniform(*dmin_range, size=nblk))
+    blk[:, 0:2] = d.view(np.uint8).reshape(nblk, 2)
+    blk[:, 2:4] = dmin.view(np.uint8).reshape(nblk, 2)
+    return blk.reshape(-1)
+
+
+def q5k_weights(g: np.random.Generator, rows: int, K: int,
+                d_range=(5e-4, 5e-3), dmin_range=(0.0, 1e-2)) -> np.ndarray:
+    """rows x K weight as GGUF Q5_K blocks, flat uint8 [rows * K/256 * 176]."""
+    assert K % QK == 0
+    nblk = rows * (K // QK)
+    blk = g.integers(0, 256, size=(nblk, Q5K_BLOCK_BYTES), dtype=np.uint8)
     d = _f16_bits(g.uniform(*d_range, size=nblk))
     dmin = _f16_bits(g.uniform(*dmin_range, size=nblk))
     blk[:, 0:2] = d.view(np.uint8).reshape(nblk, 2)

@@ -3,7 +3,7 @@
 The oracle only reads blocks (bytes -> fields); these writers go the other way
 and are written separately from it, so a round trip through both catches a
 wrong shift, mask or index on either side.  Layouts are the public GGUF Q4_K
-(144 bytes) and Q6_K (210 bytes) definitions.
+(144 bytes), Q5_K (176 bytes) and Q6_K (210 bytes) definitions.
 """
 from __future__ import annotations
 
@@ -38,6 +38,24 @@ def pack_q4k_block(d: float, dmin: float, sc, mn, q) -> np.ndarray:
         for l in range(32):
             qs[32 * c + l] = q[64 * c + l] | (q[64 * c + 32 + l] << 4)
     out[16:144] = qs.astype(np.uint8)
+    return out
+
+
+def pack_q5k_block(d: float, dmin: float, sc, mn, q) -> np.ndarray:
+    """Q5_K: d, dmin and the 12 scale/min bytes as in Q4_K, then qh[32] (bit j
+    of qh[l] is bit 4 of value l of sub-block j), then the low nibbles packed
+    as Q4_K packs its quants."""
+    q = np.asarray(q, np.int64)
+    assert q.shape == (256,) and q.min() >= 0 and q.max() < 32
+    q4 = pack_q4k_block(d, dmin, sc, mn, q & 15)
+    qh = np.zeros(32, np.int64)
+    for j in range(8):
+        for l in range(32):
+            qh[l] |= ((q[32 * j + l] >> 4) & 1) << j
+    out = np.zeros(176, np.uint8)
+    out[0:16] = q4[0:16]
+    out[16:48] = qh.astype(np.uint8)
+    out[48:176] = q4[16:144]
     return out
 
 

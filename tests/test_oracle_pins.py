@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import synth
-from gguf_pack import pack_q4k_block, pack_q6k_block
+from gguf_pack import pack_q4k_block, pack_q5k_block, pack_q6k_block
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -56,6 +56,78 @@ def test_q6k_roundtrip_random_fields(orc, seed):
     assert np.array_equal(sc2.astype(np.int64), sc) and np.array_equal(q2, q)
 
 
+@pytest.mark.parametrize("seed", range(20))
+def test_q5k_roundtrip_random_fields(orc, seed):
+    g = np.random.default_rng(3000 + seed)
+    sc = g.integers(0, 64, 8)
+    mn = g.integers(0, 64, 8)
+    q = g.integers(0, 32, 256)
+    d = float(np.float16(g.uniform(5e-4, 5e-3)))
+    dmin = float(np.float16(g.uniform(0, 1e-2)))
+    blk = pack_q5k_block(d, dmin, sc, mn, q)
+    d2, dmin2, sc2, mn2, q2 = orc.q5k_fields(blk)
+    assert d2 == np.float32(d) and dmin2 == np.float32(dmin)
+    assert np.array_equal(sc2, sc) and np.array_equal(mn2, mn) and np.array_equal(q2, q)
+
+
+def test_q5k_fifth_bit_positions(orc):
+    """Bit j of qh[l] (byte 16 + l) is bit 4 of value l of sub-block j, i.e. of value 32j + l."""
+    for j in range(8):
+        for l in (0, 13, 31):
+            blk = np.zeros(176, np.uint8)
+            blk[16 + l] = 1 << j
+            _, _, _, _, q = orc.q5k_fields(blk)
+            want = np.zeros(256, np.uint8)
+            want[32 * j + l] = 16
+            assert np.array_equal(q, want)
+
+
+def test_q5k_without_fifth_bits_equals_q4k(orc):
+    """qh = 0 leaves the Q4_K block with the same d, dmin, scales and nibbles:
+    the oracle's Q4_K result (pinned above) must come out bit for bit."""
+    g = np.random.default_rng(21)
+    rows, K, T = 6, 768, 3
+    nb = K // 256
+    w4 = synth.q4k_weights(g, rows, K).reshape(rows * nb, 144)
+    w5 = np.zeros((rows * nb, 176), np.uint8)
+    w5[:, 0:16] = w4[:, 0:16]
+    w5[:, 48:176] = w4[:, 16:144]
+    qs, d8, bs = orc.q8k_pack(synth.activations(g, T, K))
+    y4, a4 = orc.matvec(orc.Q4_K, w4.reshape(-1), rows, K, qs, d8, bs)
+    y5, a5 = orc.matvec(orc.Q5_K, w5.reshape(-1), rows, K, qs, d8, bs)
+    assert np.array_equal(y4, y5) and np.array_equal(a4, a5)
+
+
+def test_q5k_all_fifth_bits_closed_form(orc):
+    """Setting every fifth bit adds 16 to every quant, so the result grows by
+    sum_b d8_b * d_b * sum_j sc_j * 16 * bsum_bj (fields read back by the packer's
+    inverse, not by the oracle)."""
+    g = np.random.default_rng(22)
+    K = 512
+    nb = K // 256
+    flds = []
+    blocks0, blocks1 = [], []
+    for b in range(nb):
+        sc = g.integers(0, 64, 8)
+        mn = g.integers(0, 64, 8)
+        q = g.integers(0, 16, 256)
+        d = float(np.float16(g.uniform(5e-4, 5e-3)))
+        dmin = float(np.float16(g.uniform(0, 1e-2)))
+        flds.append((d, sc))
+        blocks0.append(pack_q5k_block(d, dmin, sc, mn, q))
+        blocks1.append(pack_q5k_block(d, dmin, sc, mn, q + 16))
+    w0 = np.concatenate(blocks0)
+    w1 = np.concatenate(blocks1)
+    qs, d8, bs = orc.q8k_pack(synth.activations(g, 1, K))
+    y0, A0 = orc.matvec(orc.Q5_K, w0, 1, K, qs, d8, bs)
+    y1, A1 = orc.matvec(orc.Q5_K, w1, 1, K, qs, d8, bs)
+    want = 0.0
+    for b in range(nb):
+        d, sc = flds[b]
+        want += float(d8[0, b]) * d * float(np.dot(sc.astype(np.int64) * 16, bs[0, 8 * b:8 * b + 8].astype(np.int64)))
+    assert abs((y1[0, 0] - y0[0, 0]) - want) <= 1e-12 * (A0[0, 0] + A1[0, 0])
+
+
 def test_q4k_single_byte_positions(orc):
     """Byte 32c+l of the quants carries value 64c+l (low nibble) and 64c+32+l (high)."""
     for c in range(4):
@@ -76,6 +148,9 @@ def test_hand_blocks_golden(orc):
         if cs["fmt"] == "q4k":
             blk = pack_q4k_block(cs["d"], cs["dmin"], cs["sc"], cs["m"], [cs["q_all"]] * 256)
             w = orc.dequant(orc.Q4_K, blk, 1, 256)
+        elif cs["fmt"] == "q5k":
+            blk = pack_q5k_block(cs["d"], cs["dmin"], cs["sc"], cs["m"], [cs["q_all"]] * 256)
+            w = orc.dequant(orc.Q5_K, blk, 1, 256)
         else:
             blk = pack_q6k_block(cs["d"], cs["sc"], [cs["q_all"]] * 256)
             w = orc.dequant(orc.Q6_K, blk, 1, 256)
@@ -151,34 +226,38 @@ def test_q6k_subblock_sums_closed_form(orc):
     assert np.array_equal(S[0], want) and np.array_equal(S[1], want)
 
 
-@pytest.mark.parametrize("qtype", [1, 2])
+_GEN = {1: synth.q4k_weights, 2: synth.q6k_weights, 3: synth.q5k_weights}
+_BB = {1: 144, 2: 210, 3: 176}
+
+
+@pytest.mark.parametrize("qtype", [1, 2, 3])
 def test_subblock_sums_brute_force(orc, qtype):
     """Integer sums against numpy products of the decoded quants."""
     g = np.random.default_rng(11 + qtype)
     rows, K = 5, 768
-    w = synth.q4k_weights(g, rows, K) if qtype == 1 else synth.q6k_weights(g, rows, K)
+    w = _GEN[qtype](g, rows, K)
     qs = g.integers(-127, 128, K).astype(np.int8)
     S = orc.subblock_sums(qtype, w, rows, K, qs)
-    bb = 144 if qtype == 1 else 210
+    bb = _BB[qtype]
+    fields = {1: orc.q4k_fields, 2: orc.q6k_fields, 3: orc.q5k_fields}[qtype]
     for r in range(rows):
         qv = []
         for b in range(K // 256):
             blk = w[(r * (K // 256) + b) * bb:(r * (K // 256) + b + 1) * bb]
-            f = orc.q4k_fields(blk) if qtype == 1 else orc.q6k_fields(blk)
-            qv.append(f[-1].astype(np.int64) - (0 if qtype == 1 else 32))
+            qv.append(fields(blk)[-1].astype(np.int64) - (32 if qtype == 2 else 0))
         qv = np.concatenate(qv)
-        gs = 32 if qtype == 1 else 16
+        gs = 16 if qtype == 2 else 32
         assert np.array_equal(S[r], (qv * qs).reshape(-1, gs).sum(1))
 
 
 # --------------------------------------------------------------------------- epilogue
-@pytest.mark.parametrize("qtype", [1, 2])
+@pytest.mark.parametrize("qtype", [1, 2, 3])
 @pytest.mark.parametrize("seed", range(8))
 def test_matvec_equals_dequant_then_dot(orc, qtype, seed):
     """Integer-structured result = fp64 dequantise-then-dot (brute force)."""
     g = np.random.default_rng(100 * qtype + seed)
     rows, K, T = 7, 256 * (1 + seed % 4), 2
-    w = synth.q4k_weights(g, rows, K) if qtype == 1 else synth.q6k_weights(g, rows, K)
+    w = _GEN[qtype](g, rows, K)
     x = synth.activations(g, T, K)
     qs, d8, bs = orc.q8k_pack(x)
     y, A = orc.matvec(qtype, w, rows, K, qs, d8, bs)
@@ -245,19 +324,20 @@ def test_threads_do_not_change_results(orc):
     assert np.array_equal(y1, y4) and np.array_equal(a1, a4)
 
 
-def test_moe_equals_weighted_single_calls(orc):
+@pytest.mark.parametrize("qtype", [1, 3])
+def test_moe_equals_weighted_single_calls(orc, qtype):
     g = np.random.default_rng(12)
     E, rows, K, T, topk = 4, 9, 512, 6, 2
-    w = synth.q4k_weights(g, E * rows, K)
+    w = _GEN[qtype](g, E * rows, K)
     qs, d8, bs = orc.q8k_pack(synth.activations(g, T, K))
     ids, rw = synth.moe_routing(g, T, E, topk)
-    y, A = orc.moe(orc.Q4_K, w, E, rows, K, qs, d8, bs, ids, rw)
-    per = rows * (K // 256) * 144
+    y, A = orc.moe(qtype, w, E, rows, K, qs, d8, bs, ids, rw)
+    per = rows * (K // 256) * _BB[qtype]
     for t in range(T):
         acc = np.zeros(rows)
         for k in range(topk):
             e = ids[t, k]
-            ye, _ = orc.matvec(orc.Q4_K, w[e * per:(e + 1) * per], rows, K, qs[t:t + 1], d8[t:t + 1], bs[t:t + 1])
+            ye, _ = orc.matvec(qtype, w[e * per:(e + 1) * per], rows, K, qs[t:t + 1], d8[t:t + 1], bs[t:t + 1])
             acc = acc + float(rw[t, k]) * ye[0]
         assert np.array_equal(y[t], acc)
 
