@@ -1,5 +1,5 @@
 /*
- * q8k.h -- C ABI of libq8k: GGUF K-quant weights (Q4_K, Q6_K) times
+ * q8k.h -- C ABI of libq8k: GGUF K-quant weights (Q4_K, Q5_K, Q6_K) times
  * activations packed on the GPU into q8_K blocks, on AMD Instinct MI355X
  * (gfx950).
  *
@@ -16,6 +16,9 @@
  *   - section 2.2: batched decode, one pass over a weight row serves several
  *     activation columns;
  *   - section 2.3: prefill, a tiled matrix-core GEMM with a scale epilogue;
+ *     a Q5_K member is the Q4_K one with the fifth-bit plane OR-ed into bit
+ *     four of each staged value (here: the Q5_K mat-vec, batched and MoE
+ *     forms; the Q5_K prefill is not built and is refused);
  *   - section 2.4: mixture of experts, a decode mat-vec that visits each
  *     token's selected experts and sums their weighted outputs;
  *   - section 3.2 (and SKaiNET's "Kernel SPI and the selection algorithm",
@@ -65,7 +68,8 @@ typedef enum {
 typedef enum {
     Q8K_Q4_K = 1,        /* GGUF Q4_K: 144-byte blocks, row-major block order   */
     Q8K_Q6_K_RELAID = 2, /* Q6_K after q8k_bind_q6k: fp16 prefix + 208-B bodies */
-    Q8K_Q6_K_GGUF = 3    /* raw GGUF Q6_K (210-byte blocks): bind input only    */
+    Q8K_Q6_K_GGUF = 3,   /* raw GGUF Q6_K (210-byte blocks): bind input only    */
+    Q8K_Q5_K = 4         /* GGUF Q5_K: 176-byte blocks, row-major block order   */
 } q8k_qtype;
 
 #define Q8K_QK 256         /* values per K-quant super-block / q8_K block       */
@@ -87,6 +91,7 @@ size_t q8k_act_layout(int64_t T, int64_t K, size_t* off_d, size_t* off_bsums);
 
 /* Bytes of a rows x K weight in the given layout (0 on a bad shape):
  *   Q8K_Q4_K         rows*K/256 blocks of 144 B;
+ *   Q8K_Q5_K         rows*K/256 blocks of 176 B;
  *   Q8K_Q6_K_GGUF    rows*K/256 blocks of 210 B;
  *   Q8K_Q6_K_RELAID  fp16 d prefix [rows*K/256] padded to 256 B, then
  *                    rows*K/256 bodies of 208 B (ql[128] | qh[64] | scales[16]);
@@ -108,10 +113,11 @@ int q8k_pack(const float* x, int64_t T, int64_t K, void* xq, void* stream);
 int q8k_bind_q6k(const void* w_gguf, int64_t rows, int64_t K, void* w_relaid, void* stream);
 
 /* qmatvec: decode mat-vec for one packed token.
- *   y[r] = sum_b d8_b * (d_rb * sum_j sc_rbj * S_rbj - dmin_rb * sum_j m_rbj * bsums_bj)   (Q4_K)
+ *   y[r] = sum_b d8_b * (d_rb * sum_j sc_rbj * S_rbj - dmin_rb * sum_j m_rbj * bsums_bj)   (Q4_K, Q5_K)
  *   y[r] = sum_b d8_b * d_rb * sum_s sc_rbs * S_rbs                                        (Q6_K)
- * with S the exact int32 sub-block sums of quant x code (Q6_K quants minus 32).
- * qtype: Q8K_Q4_K or Q8K_Q6_K_RELAID.  xq: q8_K buffer of one token (T = 1).
+ * with S the exact int32 sub-block sums of quant x code (Q6_K quants minus 32;
+ * Q5_K quants 0..31 with the fifth bit from the block's qh plane).
+ * qtype: Q8K_Q4_K, Q8K_Q5_K or Q8K_Q6_K_RELAID.  xq: q8_K buffer of one token (T = 1).
  * y: fp32 [rows]. */
 int qmatvec(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, float* y, void* stream);
 
@@ -133,7 +139,9 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
 
 /* qmatmul_prefill: y[m][n] = qmatvec's formula for every token m < M and
  * weight row n < rows, computed as a tiled int8 matrix-core GEMM.
- * qtype: Q8K_Q4_K.  xq: q8_K buffer of M tokens.  y: fp32 [M][rows].
+ * qtype: Q8K_Q4_K (Q8K_Q5_K and Q8K_Q6_K_RELAID are refused with
+ * Q8K_ERR_QTYPE: no prefill tile is built for them).  xq: q8_K buffer of M
+ * tokens.  y: fp32 [M][rows].
  * ws / ws_bytes: caller-owned workspace of at least
  * qmatmul_prefill_workspace_bytes(...) bytes (may be NULL when that is 0). */
 size_t qmatmul_prefill_workspace_bytes(int qtype, int64_t rows, int64_t K, int64_t M);
@@ -142,7 +150,8 @@ int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const voi
 
 /* Test support: the exact int32 sub-block sums of every weight row against
  * one packed token, computed by the same device code as qmatvec.
- * S: int32 [rows][K/32] for Q8K_Q4_K, [rows][K/16] for Q8K_Q6_K_RELAID. */
+ * S: int32 [rows][K/32] for Q8K_Q4_K and Q8K_Q5_K, [rows][K/16] for
+ * Q8K_Q6_K_RELAID. */
 int q8k_debug_subblock_sums(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int32_t* S,
                             void* stream);
 

@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = [
-    "Q8K_Q4_K", "Q8K_Q6_K_RELAID", "Q8K_Q6_K_GGUF", "Q8K_COLS_MAX", "Q8K_MOE_MAX_TOKENS", "Q8K_MOE_MAX_TOPK", "Q8KError",
+    "Q8K_Q4_K", "Q8K_Q5_K", "Q8K_Q6_K_RELAID", "Q8K_Q6_K_GGUF", "Q8K_COLS_MAX", "Q8K_MOE_MAX_TOKENS", "Q8K_MOE_MAX_TOPK", "Q8KError",
     "lib", "LIB_PATH", "q8k_act_bytes", "q8k_act_layout", "q8k_weight_bytes", "q8k_pack", "q8k_bind_q6k",
     "qmatvec", "qmatvec_batched", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
     "q8k_debug_subblock_sums", "q8k_status_str", "q8k_last_error", "EXPORTED",
@@ -24,6 +24,7 @@ __all__ = [
 Q8K_Q4_K = 1
 Q8K_Q6_K_RELAID = 2
 Q8K_Q6_K_GGUF = 3
+Q8K_Q5_K = 4
 Q8K_COLS_MAX = 8
 Q8K_MOE_MAX_TOKENS = 256
 Q8K_MOE_MAX_TOPK = 64

@@ -95,12 +95,18 @@ int launched(const char* fn, hipError_t e) {
         if (_st != Q8K_OK) return _st; \
     } while (0)
 
-int check_weight(const char* fn, int qtype, const void* w, bool allow_q6) {
-    if (qtype == Q8K_Q4_K || (allow_q6 && qtype == Q8K_Q6_K_RELAID)) return check_ptr(fn, "w", w, 16);
+// `decode`: the mat-vec family (Q4_K, Q5_K, relaid Q6_K); otherwise the
+// prefill tile (Q4_K only).
+int check_weight(const char* fn, int qtype, const void* w, bool decode) {
+    if (qtype == Q8K_Q4_K || (decode && (qtype == Q8K_Q5_K || qtype == Q8K_Q6_K_RELAID)))
+        return check_ptr(fn, "w", w, 16);
     if (qtype == Q8K_Q6_K_GGUF)
         return fail(Q8K_ERR_QTYPE, "%s: raw GGUF Q6_K must be bound first (q8k_bind_q6k -> Q8K_Q6_K_RELAID)", fn);
+    if (!decode && (qtype == Q8K_Q5_K || qtype == Q8K_Q6_K_RELAID))
+        return fail(Q8K_ERR_QTYPE, "%s: no %s prefill tile is built (qmatvec_batched serves up to %d tokens)", fn,
+                    qtype == Q8K_Q5_K ? "Q5_K" : "Q6_K", Q8K_COLS_MAX);
     return fail(Q8K_ERR_QTYPE, "%s: qtype=%d not served here (use %s)", fn, qtype,
-                allow_q6 ? "Q8K_Q4_K=1 or Q8K_Q6_K_RELAID=2" : "Q8K_Q4_K=1");
+                decode ? "Q8K_Q4_K=1, Q8K_Q6_K_RELAID=2 or Q8K_Q5_K=4" : "Q8K_Q4_K=1");
 }
 
 }  // namespace
@@ -122,6 +128,7 @@ size_t q8k_weight_bytes(int qtype, int64_t rows, int64_t K) {
     const size_t nblk = (size_t)rows * (size_t)(K / QK);
     switch (qtype) {
         case Q8K_Q4_K: return nblk * Q4K_BLOCK;
+        case Q8K_Q5_K: return nblk * Q5K_BLOCK;
         case Q8K_Q6_K_GGUF: return nblk * Q6K_BLOCK;
         case Q8K_Q6_K_RELAID: return align256(2 * nblk) + nblk * Q6K_BODY;
         default: return 0;
@@ -170,6 +177,8 @@ static int matvec_common(const char* fn, int qtype, const void* w, int64_t rows,
     hipError_t e;
     if (qtype == Q8K_Q4_K) {
         e = launch_matvec_q4k(static_cast<const uint8_t*>(w), rows, nb, a, (int)ncols, y, (hipStream_t)stream);
+    } else if (qtype == Q8K_Q5_K) {
+        e = launch_matvec_q5k(static_cast<const uint8_t*>(w), rows, nb, a, (int)ncols, y, (hipStream_t)stream);
     } else {
         const Q6View v = q6_view(w, rows * nb);
         e = launch_matvec_q6k(v.prefix, v.bodies, rows, nb, a, (int)ncols, y, (hipStream_t)stream);
@@ -213,6 +222,8 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
     hipError_t e;
     if (qtype == Q8K_Q4_K) {
         e = launch_moe_q4k(static_cast<const uint8_t*>(w), E, rows, nb, a, T, ids, rw, topk, y, (hipStream_t)stream);
+    } else if (qtype == Q8K_Q5_K) {
+        e = launch_moe_q5k(static_cast<const uint8_t*>(w), E, rows, nb, a, T, ids, rw, topk, y, (hipStream_t)stream);
     } else {
         const Q6View v = q6_view(w, E * rows * nb);
         e = launch_moe_q6k(v.prefix, v.bodies, E, rows, nb, a, T, ids, rw, topk, y, (hipStream_t)stream);
@@ -262,6 +273,8 @@ int q8k_debug_subblock_sums(int qtype, const void* w, int64_t rows, int64_t K, c
     hipError_t e;
     if (qtype == Q8K_Q4_K) {
         e = launch_sums_q4k(static_cast<const uint8_t*>(w), rows, nb, a, S, (hipStream_t)stream);
+    } else if (qtype == Q8K_Q5_K) {
+        e = launch_sums_q5k(static_cast<const uint8_t*>(w), rows, nb, a, S, (hipStream_t)stream);
     } else {
         const Q6View v = q6_view(w, rows * nb);
         e = launch_sums_q6k(v.prefix, v.bodies, rows, nb, a, S, (hipStream_t)stream);

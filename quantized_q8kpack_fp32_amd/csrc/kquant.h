@@ -58,6 +58,22 @@ __device__ __forceinline__ void q4k_unpack(uint4 qv, uint32_t lo[4], uint32_t hi
     hi[3] = (qv.w >> 4) & 0x0F0F0F0Fu;
 }
 
+// Q5_K: the same fields and quant packing as Q4_K (quants at byte 48), plus
+// qh[32] at byte 16: bit j of qh[l] is bit 4 of value l of sub-block j.  For
+// the chunk of quant bytes 32c + 16h .. +15 (qh bytes 16h .. +15), bit 2c of
+// each qh byte goes to bit 4 of the low-nibble value and bit 2c + 1 to bit 4
+// of the high-nibble value: one rotate and one masked OR per word, so the
+// 5-bit quants (0..31) stay byte-wise for sdot4.
+__device__ __forceinline__ void q5k_fifth_bits(uint4 qhv, int c, uint32_t lo[4], uint32_t hi[4]) {
+    const uint32_t h[4] = {qhv.x, qhv.y, qhv.z, qhv.w};
+    const int rl = (2 * c + 28) & 31, rh = (2 * c + 29) & 31;  // rotate right by 2c - 4 and 2c - 3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo[i] |= __builtin_rotateright32(h[i], rl) & 0x10101010u;
+        hi[i] |= __builtin_rotateright32(h[i], rh) & 0x10101010u;
+    }
+}
+
 // ---------------------------------------------------------------- Q6_K ----
 // Relaid Q6_K: fp16 d in the prefix, body = ql[128] | qh[64] | int8 scales[16].
 // Value v = 128h + 32t + l: low 4 bits in ql[64h + 32(t&1) + l] (nibble t>>1),

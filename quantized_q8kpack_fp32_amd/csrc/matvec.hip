@@ -1,4 +1,5 @@
-// Decode mat-vecs for Q4_K and relaid Q6_K weights against q8_K activations.
+// Decode mat-vecs for Q4_K, Q5_K and relaid Q6_K weights against q8_K
+// activations.
 //
 // "Language models on the device: the cajeta-llm kernels", section 2.1: one
 // wavefront owns one output row; consecutive lanes read consecutive bytes of
@@ -27,22 +28,29 @@ namespace q8k {
 #define Q8K_MV_U2_MAXNC 4
 #endif
 
-// ---------------------------------------------------------------- Q4_K ----
-template <int NC>
+// ---------------------------------------------------------- Q4_K, Q5_K ----
+// Q5_K ("Language models on the device", section 2.3: the Q4_K member with
+// the fifth-bit plane OR-ed into bit four) runs the Q4_K code with a 176-byte
+// block, quants at byte 48 and each chunk's 16 qh bytes loaded beside it.
+template <bool Q5>
+constexpr int kblock() { return Q5 ? Q5K_BLOCK : Q4K_BLOCK; }
+
+template <int NC, bool Q5>
 struct Q4Chunk {
-    uint4 hdr, qv;
+    uint4 hdr, qv, qh;
     int4 alo[NC], ahi[NC];
     uint32_t bs[NC];
     float d8[NC];
 };
 
-template <int NC>
-__device__ __forceinline__ void q4k_load(Q4Chunk<NC>& L, const uint8_t* __restrict__ wr, int b, int ci, int aoff,
+template <int NC, bool Q5>
+__device__ __forceinline__ void q4k_load(Q4Chunk<NC, Q5>& L, const uint8_t* __restrict__ wr, int b, int ci, int aoff,
                                          int boff, const int8_t* __restrict__ qs, const float* __restrict__ d8,
                                          const int16_t* __restrict__ bs, int64_t K, int nb) {
-    const uint8_t* blk = wr + (int64_t)b * Q4K_BLOCK;
+    const uint8_t* blk = wr + (int64_t)b * kblock<Q5>();
     L.hdr = *reinterpret_cast<const uint4*>(blk);
-    L.qv = *reinterpret_cast<const uint4*>(blk + 16 + 16 * ci);
+    L.qv = *reinterpret_cast<const uint4*>(blk + (Q5 ? 48 : 16) + 16 * ci);
+    if (Q5) L.qh = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (ci & 1));
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
         const int8_t* a = qs + t * K + (int64_t)b * QK + aoff;
@@ -53,14 +61,15 @@ __device__ __forceinline__ void q4k_load(Q4Chunk<NC>& L, const uint8_t* __restri
     }
 }
 
-template <int NC>
-__device__ __forceinline__ void q4k_accum(const Q4Chunk<NC>& L, int c, int half, bool valid, float (&acc)[NC]) {
+template <int NC, bool Q5>
+__device__ __forceinline__ void q4k_accum(const Q4Chunk<NC, Q5>& L, int c, int half, bool valid, float (&acc)[NC]) {
     int sc0, sc1, m0, m1;
     q4k_scales(L.hdr, c, sc0, sc1, m0, m1);
     const float dd = half_bits_to_float(L.hdr.x & 0xffffu);
     const float dm = half_bits_to_float(L.hdr.x >> 16);
     uint32_t lo[4], hi[4];
     q4k_unpack(L.qv, lo, hi);
+    if (Q5) q5k_fifth_bits(L.qh, c, lo, hi);
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
         int S0, S1;
@@ -74,7 +83,7 @@ __device__ __forceinline__ void q4k_accum(const Q4Chunk<NC>& L, int c, int half,
     }
 }
 
-template <int NC, int U>
+template <int NC, int U, bool Q5>
 __global__ __launch_bounds__(256) void matvec_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
                                                          const int8_t* __restrict__ qs, const float* __restrict__ d8,
                                                          const int16_t* __restrict__ bs, int64_t K,
@@ -84,12 +93,12 @@ __global__ __launch_bounds__(256) void matvec_q4k_kernel(const uint8_t* __restri
     if (row >= rows) return;  // uniform per wave
     const int ci = lane & 7, c = ci >> 1, half = ci & 1;
     const int aoff = 64 * c + 16 * half, boff = 2 * c;
-    const uint8_t* wr = w + row * (int64_t)nb * Q4K_BLOCK;
+    const uint8_t* wr = w + row * (int64_t)nb * kblock<Q5>();
     float acc[NC];
 #pragma unroll
     for (int t = 0; t < NC; ++t) acc[t] = 0.0f;
     for (int b0 = lane >> 3; b0 - (lane >> 3) < nb; b0 += 8 * U) {
-        Q4Chunk<NC> L[U];
+        Q4Chunk<NC, Q5> L[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int b = b0 + 8 * u;
@@ -105,18 +114,21 @@ __global__ __launch_bounds__(256) void matvec_q4k_kernel(const uint8_t* __restri
     }
 }
 
+template <bool Q5>
 __global__ __launch_bounds__(256) void sums_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
                                                        const int8_t* __restrict__ qs, int32_t* __restrict__ S) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
     const int ci = lane & 7, c = ci >> 1, half = ci & 1;
-    const uint8_t* wr = w + row * (int64_t)nb * Q4K_BLOCK;
+    const uint8_t* wr = w + row * (int64_t)nb * kblock<Q5>();
     for (int b = lane >> 3; b < nb; b += 8) {
-        const uint4 qv = *reinterpret_cast<const uint4*>(wr + (int64_t)b * Q4K_BLOCK + 16 + 16 * ci);
+        const uint8_t* blk = wr + (int64_t)b * kblock<Q5>();
+        const uint4 qv = *reinterpret_cast<const uint4*>(blk + (Q5 ? 48 : 16) + 16 * ci);
         const int8_t* a = qs + (int64_t)b * QK + 64 * c + 16 * half;
         uint32_t lo[4], hi[4];
         q4k_unpack(qv, lo, hi);
+        if (Q5) q5k_fifth_bits(*reinterpret_cast<const uint4*>(blk + 16 + 16 * half), c, lo, hi);
         int S0, S1;
         q4k_chunk_sums(lo, hi, *reinterpret_cast<const int4*>(a), *reinterpret_cast<const int4*>(a + 32), S0, S1);
         // the two halves of each sub-block sit in lanes ci and ci^1
@@ -291,10 +303,10 @@ __global__ __launch_bounds__(256) void sums_q6k_kernel(const uint8_t* __restrict
 // (a 4096-wide row in one trip); one group per trip for more columns, where
 // the activation registers of every column already give enough loads in
 // flight.  Q6_K: one 16-block pass per trip.
-template <int NC>
+template <int NC, bool Q5>
 static void go_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, float* y, hipStream_t s) {
     constexpr int U = NC <= Q8K_MV_U2_MAXNC ? 2 : 1;
-    hipLaunchKernelGGL((matvec_q4k_kernel<NC, U>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb,
+    hipLaunchKernelGGL((matvec_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb,
                        a.qs, a.d, a.bs, a.K, y);
 }
 #ifndef Q8K_Q6_GRID
@@ -307,19 +319,29 @@ static void go_q6k(const uint16_t* p, const uint8_t* bodies, int64_t rows, int n
     hipLaunchKernelGGL((matvec_q6k_kernel<NC>), dim3(grid), dim3(256), 0, s, p, bodies, rows, nb, a.qs, a.d, a.K, y);
 }
 
-hipError_t launch_matvec_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int ncols, float* y, hipStream_t s) {
+template <bool Q5>
+static hipError_t launch_q4k_family(const uint8_t* w, int64_t rows, int nb, Acts a, int ncols, float* y,
+                                    hipStream_t s) {
     switch (ncols) {
-        case 1: go_q4k<1>(w, rows, nb, a, y, s); break;
-        case 2: go_q4k<2>(w, rows, nb, a, y, s); break;
-        case 3: go_q4k<3>(w, rows, nb, a, y, s); break;
-        case 4: go_q4k<4>(w, rows, nb, a, y, s); break;
-        case 5: go_q4k<5>(w, rows, nb, a, y, s); break;
-        case 6: go_q4k<6>(w, rows, nb, a, y, s); break;
-        case 7: go_q4k<7>(w, rows, nb, a, y, s); break;
-        case 8: go_q4k<8>(w, rows, nb, a, y, s); break;
+        case 1: go_q4k<1, Q5>(w, rows, nb, a, y, s); break;
+        case 2: go_q4k<2, Q5>(w, rows, nb, a, y, s); break;
+        case 3: go_q4k<3, Q5>(w, rows, nb, a, y, s); break;
+        case 4: go_q4k<4, Q5>(w, rows, nb, a, y, s); break;
+        case 5: go_q4k<5, Q5>(w, rows, nb, a, y, s); break;
+        case 6: go_q4k<6, Q5>(w, rows, nb, a, y, s); break;
+        case 7: go_q4k<7, Q5>(w, rows, nb, a, y, s); break;
+        case 8: go_q4k<8, Q5>(w, rows, nb, a, y, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_matvec_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int ncols, float* y, hipStream_t s) {
+    return launch_q4k_family<false>(w, rows, nb, a, ncols, y, s);
+}
+
+hipError_t launch_matvec_q5k(const uint8_t* w, int64_t rows, int nb, Acts a, int ncols, float* y, hipStream_t s) {
+    return launch_q4k_family<true>(w, rows, nb, a, ncols, y, s);
 }
 
 hipError_t launch_matvec_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t rows, int nb, Acts a, int ncols,
@@ -339,7 +361,14 @@ hipError_t launch_matvec_q6k(const uint16_t* prefix, const uint8_t* bodies, int6
 }
 
 hipError_t launch_sums_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int32_t* S, hipStream_t s) {
-    hipLaunchKernelGGL(sums_q4k_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb, a.qs, S);
+    hipLaunchKernelGGL(sums_q4k_kernel<false>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb, a.qs,
+                       S);
+    return hipGetLastError();
+}
+
+hipError_t launch_sums_q5k(const uint8_t* w, int64_t rows, int nb, Acts a, int32_t* S, hipStream_t s) {
+    hipLaunchKernelGGL(sums_q4k_kernel<true>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb, a.qs,
+                       S);
     return hipGetLastError();
 }
 

@@ -6,11 +6,12 @@
 // experts' outputs are summed as they are produced; weights are read through
 // the index of which expert each token chose (section intro).
 //
-// Q4_K (moe_rows_q4k_kernel): one lane per weight row.  A workgroup owns 64
+// Q4_K and Q5_K (moe_rows_q4k_kernel<Q5>): one lane per weight row.  A workgroup owns 64
 // consecutive rows of every expert; its MQ_WAVES waves take the experts
 // w, w + MQ_WAVES, ... .  For expert e a wave collects the (token, slot) pairs
 // that chose e with a ballot over ids and takes them MQ_G at a time.  Per
-// block it loads the 64 rows' 144-byte blocks with coalesced reads, passes
+// block it loads the 64 rows' 144-byte (Q5_K: 176-byte) blocks with coalesced
+// reads, passes
 // them through its own LDS region so that lane r holds row r's block, and
 // reads the group's q8_K codes from LDS as wave-uniform operands: one code
 // read serves 64 rows, and a lane's sub-block sums, the scale/min fold and the
@@ -40,43 +41,57 @@ constexpr int MQ_ROWS = 64;                            // rows per workgroup, on
 #endif
 constexpr int MQ_G = Q8K_MOE_ROW_GROUP;                // tokens per group
 constexpr int MQ_SLOT = 128;                           // (token, slot) pairs per slab
-constexpr int MQ_PIECES = MQ_ROWS * Q4K_BLOCK / 16;    // 16-byte pieces of one block of 64 rows
-static_assert(MQ_PIECES == 9 * 64, "nine pieces per lane");
+// Block format: 16-byte pieces per row block (9 for Q4_K, 11 for Q5_K); the
+// header is piece 0, Q5_K's qh pieces 1 and 2, the quants start at piece
+// 1 (Q4_K) or 3 (Q5_K).
+template <bool Q5>
+struct MqFmt {
+    static constexpr int BLK = Q5 ? Q5K_BLOCK : Q4K_BLOCK;
+    static constexpr int PR = BLK / 16;
+    static constexpr int QO = Q5 ? 3 : 1;
+};
+static_assert(MqFmt<false>::PR * 16 == Q4K_BLOCK && MqFmt<true>::PR * 16 == Q5K_BLOCK, "whole pieces");
 static_assert(MQ_SLOT >= Q8K_MOE_MAX_TOPK, "a slab holds at least one token's pairs");
 
+template <bool Q5>
 struct MqWave {
-    uint4 w[MQ_PIECES];   // one block of the 64 rows, row-major (row r at 9r)
-    uint4 x[MQ_G * 16];   // the group's codes of that block, token g at 16g
-    uint4 bs[MQ_G];       // their eight int16 sub-block sums
-    float d8[MQ_G];       // their block scales
+    uint4 w[MQ_ROWS * MqFmt<Q5>::PR];  // one block of the 64 rows, row-major (row r at PR r)
+    uint4 x[MQ_G * 16];                // the group's codes of that block, token g at 16g
+    uint4 bs[MQ_G];                    // their eight int16 sub-block sums
+    float d8[MQ_G];                    // their block scales
 };
+template <bool Q5>
 struct MqSmem {
-    MqWave wave[MQ_WAVES];
+    MqWave<Q5> wave[MQ_WAVES];
     float slot[MQ_SLOT * MQ_ROWS];  // dot of (pair, row), pair-major
 };
+static_assert(sizeof(MqSmem<true>) <= 160 * 1024, "LDS of one workgroup");
 
 // One block's worth of loads of a wave: piece 64i + lane of the 64 rows'
 // block, 16 code bytes (token lane / 16, piece lane % 16), and the sums and
 // scale of token lane % 4.
+template <bool Q5>
 struct MqStage {
-    uint4 w[9];
+    uint4 w[MqFmt<Q5>::PR];
     uint4 x[MQ_G / 4], bs;
     float d8;
 };
 static_assert(MQ_G == 4 || MQ_G == 8, "groups of 4 or 8 tokens");
 
+template <bool Q5>
 struct MqSrc {
-    rsrc_t wr;            // the 64 rows of expert e; reads past the last row give zeros
-    int woff[9];          // byte offset of piece 64i + lane inside block 0
-    const int8_t* x;      // codes of token tok[lane / 16], piece lane % 16, block 0
-    const int8_t* x2;     // the same for token tok[lane / 16 + 4] (groups of 8)
-    const int16_t* bs;    // sums of token tok[lane % 4], block 0
-    const float* d8;      // scale of token tok[lane % 4], block 0
+    rsrc_t wr;                  // the 64 rows of expert e; reads past the last row give zeros
+    int woff[MqFmt<Q5>::PR];    // byte offset of piece 64i + lane inside block 0
+    const int8_t* x;            // codes of token tok[lane / 16], piece lane % 16, block 0
+    const int8_t* x2;           // the same for token tok[lane / 16 + 4] (groups of 8)
+    const int16_t* bs;          // sums of token tok[lane % 4], block 0
+    const float* d8;            // scale of token tok[lane % 4], block 0
 };
 
-__device__ __forceinline__ void mq_load(MqStage& S, const MqSrc& R, int b, int nb) {
+template <bool Q5>
+__device__ __forceinline__ void mq_load(MqStage<Q5>& S, const MqSrc<Q5>& R, int b, int nb) {
 #pragma unroll
-    for (int i = 0; i < 9; ++i) S.w[i] = load16(R.wr, R.woff[i] + b * Q4K_BLOCK);
+    for (int i = 0; i < MqFmt<Q5>::PR; ++i) S.w[i] = load16(R.wr, R.woff[i] + b * MqFmt<Q5>::BLK);
     const int bc = b < nb ? b : nb - 1;  // steps past the end reload the last block (unused)
     S.x[0] = *reinterpret_cast<const uint4*>(R.x + (int64_t)bc * QK);
     if (MQ_G == 8) S.x[MQ_G / 4 - 1] = *reinterpret_cast<const uint4*>(R.x2 + (int64_t)bc * QK);
@@ -88,10 +103,11 @@ __device__ __forceinline__ void mq_load(MqStage& S, const MqSrc& R, int b, int n
 // one wave's LDS instructions in order, but the compiler reasons per thread:
 // it may forward a lane's earlier read past other lanes' writes, or hoist the
 // writes above earlier reads.  The memory clobbers forbid both.
-__device__ __forceinline__ void mq_store(const MqStage& S, MqWave& L, int lane) {
+template <bool Q5>
+__device__ __forceinline__ void mq_store(const MqStage<Q5>& S, MqWave<Q5>& L, int lane) {
     asm volatile("" ::: "memory");  // the previous block's reads come first
 #pragma unroll
-    for (int i = 0; i < 9; ++i) L.w[64 * i + lane] = S.w[i];
+    for (int i = 0; i < MqFmt<Q5>::PR; ++i) L.w[64 * i + lane] = S.w[i];
     L.x[lane] = S.x[0];
     if (MQ_G == 8) L.x[64 + lane] = S.x[MQ_G / 4 - 1];
     if (lane < MQ_G) {
@@ -116,50 +132,65 @@ __device__ __forceinline__ void mq_scale_min(uint4 hdr, int& sc, int& mn) {
     }
 }
 
-// sum over 32 values of sub-block (c, h) of row `lane` times token g's codes
-template <int c, int h>
-__device__ __forceinline__ int mq_sub(const uint4 q0, const uint4 q1, const MqWave& L, int g) {
+// sum over 32 values of sub-block (c, h) of row `lane` times token g's codes;
+// Q5_K ORs bit j = 2c + h of each qh byte into bit 4 of the value (a rotate
+// right by j - 4 puts it there in every byte of a word)
+template <int c, int h, bool Q5>
+__device__ __forceinline__ int mq_sub(const uint4 q0, const uint4 q1, const uint4 qh0, const uint4 qh1,
+                                      const MqWave<Q5>& L, int g) {
     constexpr int j = 2 * c + h;
+    constexpr int rot = (j + 28) & 31;
     const uint4 c0 = L.x[16 * g + 2 * j], c1 = L.x[16 * g + 2 * j + 1];
-    const uint32_t m = 0x0F0F0F0Fu;
-    int s = sdot4((int)((h ? q0.x >> 4 : q0.x) & m), (int)c0.x, 0);
-    s = sdot4((int)((h ? q0.y >> 4 : q0.y) & m), (int)c0.y, s);
-    s = sdot4((int)((h ? q0.z >> 4 : q0.z) & m), (int)c0.z, s);
-    s = sdot4((int)((h ? q0.w >> 4 : q0.w) & m), (int)c0.w, s);
-    s = sdot4((int)((h ? q1.x >> 4 : q1.x) & m), (int)c1.x, s);
-    s = sdot4((int)((h ? q1.y >> 4 : q1.y) & m), (int)c1.y, s);
-    s = sdot4((int)((h ? q1.z >> 4 : q1.z) & m), (int)c1.z, s);
-    s = sdot4((int)((h ? q1.w >> 4 : q1.w) & m), (int)c1.w, s);
+    auto val = [](uint32_t q, uint32_t qh) {
+        uint32_t v = (h ? q >> 4 : q) & 0x0F0F0F0Fu;
+        if (Q5) v |= __builtin_rotateright32(qh, rot) & 0x10101010u;
+        return (int)v;
+    };
+    int s = sdot4(val(q0.x, qh0.x), (int)c0.x, 0);
+    s = sdot4(val(q0.y, qh0.y), (int)c0.y, s);
+    s = sdot4(val(q0.z, qh0.z), (int)c0.z, s);
+    s = sdot4(val(q0.w, qh0.w), (int)c0.w, s);
+    s = sdot4(val(q1.x, qh1.x), (int)c1.x, s);
+    s = sdot4(val(q1.y, qh1.y), (int)c1.y, s);
+    s = sdot4(val(q1.z, qh1.z), (int)c1.z, s);
+    s = sdot4(val(q1.w, qh1.w), (int)c1.w, s);
     return s;
 }
 
-template <int c>
-__device__ __forceinline__ void mq_pair(const MqWave& L, int lane, uint4 hdr, int ng, int (&I)[MQ_G]) {
+template <int c, bool Q5>
+__device__ __forceinline__ void mq_pair(const MqWave<Q5>& L, int lane, uint4 hdr, int ng, int (&I)[MQ_G]) {
     // quant bytes 32c..32c+31: low nibbles are sub-block 2c, high 2c+1
-    const uint4 q0 = L.w[9 * lane + 1 + 2 * c], q1 = L.w[9 * lane + 2 + 2 * c];
+    constexpr int PR = MqFmt<Q5>::PR, QO = MqFmt<Q5>::QO;
+    const uint4 q0 = L.w[PR * lane + QO + 2 * c], q1 = L.w[PR * lane + QO + 1 + 2 * c];
+    uint4 qh0 = q0, qh1 = q1;  // unused for Q4_K
+    if (Q5) {
+        qh0 = L.w[PR * lane + 1];
+        qh1 = L.w[PR * lane + 2];
+    }
     int sc0, mn0, sc1, mn1;
     mq_scale_min<2 * c>(hdr, sc0, mn0);
     mq_scale_min<2 * c + 1>(hdr, sc1, mn1);
 #pragma unroll
     for (int g = 0; g < MQ_G; ++g) {
         if (g < ng) {  // wave-uniform
-            I[g] += sc0 * mq_sub<c, 0>(q0, q1, L, g);
-            I[g] += sc1 * mq_sub<c, 1>(q0, q1, L, g);
+            I[g] += sc0 * mq_sub<c, 0, Q5>(q0, q1, qh0, qh1, L, g);
+            I[g] += sc1 * mq_sub<c, 1, Q5>(q0, q1, qh0, qh1, L, g);
         }
     }
 }
 
 // Block b of row `lane` against the group's tokens: for each token g,
 //   acc[g] += d8_g * (d * sum_j sc_j S_gj - dmin * sum_j m_j bsum_gj).
-__device__ __forceinline__ void mq_compute(const MqWave& L, int lane, int ng, float (&acc)[MQ_G]) {
-    const uint4 hdr = L.w[9 * lane];
+template <bool Q5>
+__device__ __forceinline__ void mq_compute(const MqWave<Q5>& L, int lane, int ng, float (&acc)[MQ_G]) {
+    const uint4 hdr = L.w[MqFmt<Q5>::PR * lane];
     int I[MQ_G];
 #pragma unroll
     for (int g = 0; g < MQ_G; ++g) I[g] = 0;
-    mq_pair<0>(L, lane, hdr, ng, I);
-    mq_pair<1>(L, lane, hdr, ng, I);
-    mq_pair<2>(L, lane, hdr, ng, I);
-    mq_pair<3>(L, lane, hdr, ng, I);
+    mq_pair<0, Q5>(L, lane, hdr, ng, I);
+    mq_pair<1, Q5>(L, lane, hdr, ng, I);
+    mq_pair<2, Q5>(L, lane, hdr, ng, I);
+    mq_pair<3, Q5>(L, lane, hdr, ng, I);
     const float d = half_bits_to_float(hdr.x & 0xffffu);
     const float dmin = half_bits_to_float(hdr.x >> 16);
     // mins packed as int16 pairs (m0|m1, m2|m3, ...) against the sums' pairs
@@ -189,22 +220,24 @@ __device__ __forceinline__ void mq_compute(const MqWave& L, int lane, int ng, fl
     }
 }
 
+template <bool Q5>
 __global__ __launch_bounds__(64 * MQ_WAVES) void moe_rows_q4k_kernel(
     const uint8_t* __restrict__ w, int64_t E, int64_t rows, int nb, const int8_t* __restrict__ qs,
     const float* __restrict__ d8, const int16_t* __restrict__ bs, int64_t K, int64_t T,
     const int32_t* __restrict__ ids, const float* __restrict__ rw, int topk, float* __restrict__ y) {
-    __shared__ MqSmem sm;
+    constexpr int PR = MqFmt<Q5>::PR;
+    __shared__ MqSmem<Q5> sm;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, so e and rsrc are scalar
     const int lane = threadIdx.x & 63;
     const int64_t r0 = (int64_t)blockIdx.x * MQ_ROWS;
-    const int64_t wrow = (int64_t)nb * Q4K_BLOCK;
+    const int64_t wrow = (int64_t)nb * MqFmt<Q5>::BLK;
     const int64_t live = rows - r0 < MQ_ROWS ? rows - r0 : MQ_ROWS;  // rows of this workgroup
-    MqWave& L = sm.wave[wv];
-    int woff[9];
+    MqWave<Q5>& L = sm.wave[wv];
+    int woff[PR];
 #pragma unroll
-    for (int i = 0; i < 9; ++i) {
-        const int piece = 64 * i + lane;  // row piece / 9, 16-byte piece piece % 9 of the block
-        woff[i] = (piece / 9) * (int)wrow + 16 * (piece % 9);
+    for (int i = 0; i < PR; ++i) {
+        const int piece = 64 * i + lane;  // row piece / PR, 16-byte piece piece % PR of the block
+        woff[i] = (piece / PR) * (int)wrow + 16 * (piece % PR);
     }
     const int64_t ts = MQ_SLOT / topk > 0 ? MQ_SLOT / topk : 1;  // tokens per slab
     for (int64_t t0 = 0; t0 < T; t0 += ts) {
@@ -231,10 +264,10 @@ __global__ __launch_bounds__(64 * MQ_WAVES) void moe_rows_q4k_kernel(
                             tok[g] = tok[0];
                         }
                     }
-                    MqSrc R;
+                    MqSrc<Q5> R;
                     R.wr = make_rsrc(w + (e * rows + r0) * wrow, live * wrow);
 #pragma unroll
-                    for (int i = 0; i < 9; ++i) R.woff[i] = woff[i];
+                    for (int i = 0; i < PR; ++i) R.woff[i] = woff[i];
                     {
                         // codes: piece lane % 16 of token lane / 16 (and of token
                         // lane / 16 + 4 for the second half of a group of 8);
@@ -255,7 +288,7 @@ __global__ __launch_bounds__(64 * MQ_WAVES) void moe_rows_q4k_kernel(
 #pragma unroll
                     for (int g = 0; g < MQ_G; ++g) acc[g] = 0.0f;
                     // ---- blocks, two in flight: A holds even, B odd blocks
-                    MqStage A, B;
+                    MqStage<Q5> A, B;
                     mq_load(A, R, 0, nb);
                     mq_load(B, R, 1, nb);
                     for (int b = 0; b < nb; b += 2) {
@@ -469,8 +502,16 @@ __global__ __launch_bounds__(256) void moe_chunk_kernel(const uint8_t* __restric
 hipError_t launch_moe_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T, const int32_t* ids,
                           const float* rw, int topk, float* y, hipStream_t s) {
     const unsigned grid = (unsigned)((rows + MQ_ROWS - 1) / MQ_ROWS);
-    hipLaunchKernelGGL(moe_rows_q4k_kernel, dim3(grid), dim3(64 * MQ_WAVES), 0, s, w, E, rows, nb, a.qs, a.d, a.bs,
-                       a.K, T, ids, rw, topk, y);
+    hipLaunchKernelGGL(moe_rows_q4k_kernel<false>, dim3(grid), dim3(64 * MQ_WAVES), 0, s, w, E, rows, nb, a.qs, a.d,
+                       a.bs, a.K, T, ids, rw, topk, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_q5k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T, const int32_t* ids,
+                          const float* rw, int topk, float* y, hipStream_t s) {
+    const unsigned grid = (unsigned)((rows + MQ_ROWS - 1) / MQ_ROWS);
+    hipLaunchKernelGGL(moe_rows_q4k_kernel<true>, dim3(grid), dim3(64 * MQ_WAVES), 0, s, w, E, rows, nb, a.qs, a.d,
+                       a.bs, a.K, T, ids, rw, topk, y);
     return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@ namespace q8k {
 
 constexpr int QK = 256;          // values per K-quant super-block and q8_K block
 constexpr int Q4K_BLOCK = 144;   // GGUF Q4_K block bytes
+constexpr int Q5K_BLOCK = 176;   // GGUF Q5_K block bytes
 constexpr int Q6K_BLOCK = 210;   // GGUF Q6_K block bytes
 constexpr int Q6K_BODY = 208;    // Q6_K body after the bind relayout
 constexpr int WAVE = 64;

@@ -48,6 +48,7 @@ def test_act_layout(q):
 def test_weight_bytes(q):
     assert q.q8k_weight_bytes(q.Q8K_Q4_K, 4096, 4096) == 9437184
     assert q.q8k_weight_bytes(q.Q8K_Q6_K_GGUF, 32000, 4096) == 107520000
+    assert q.q8k_weight_bytes(q.Q8K_Q5_K, 4096, 4096) == 4096 * 16 * 176
     nblk = 32000 * 16
     assert q.q8k_weight_bytes(q.Q8K_Q6_K_RELAID, 32000, 4096) == ((2 * nblk + 255) // 256) * 256 + 208 * nblk
     assert q.q8k_weight_bytes(9, 1, 256) == 0
@@ -93,6 +94,8 @@ def test_qtype_refusals(q):
     assert "q8k_bind_q6k" in msg
     refused(q, "Q8K_ERR_QTYPE", q.qmatvec, 42, A16, 4, 256, A16, A16, 0)
     refused(q, "Q8K_ERR_QTYPE", q.qmatmul_prefill, q.Q8K_Q6_K_RELAID, A16, 8, 256, A16, 4, A16, None, 0, 0)
+    msg = refused(q, "Q8K_ERR_QTYPE", q.qmatmul_prefill, q.Q8K_Q5_K, A16, 8, 256, A16, 4, A16, None, 0, 0)
+    assert "Q5_K" in msg
 
 
 def test_batched_and_moe_arguments(q):

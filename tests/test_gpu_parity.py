@@ -135,6 +135,72 @@ def test_q4k_matvec_extreme_scales(q):
     assert_close(host(y), want[0], A[0], "q4k extreme")
 
 
+# ================================================================== Q5_K decode (NEXT row)
+def q5k(seed, rows, K):
+    return synth.q5k_weights(np.random.default_rng(seed), rows, K)
+
+
+@pytest.mark.parametrize("rows,K,seed", [(256, 1024, 50), (4096, 4096, 51), (37, 256, 52), (13, 768, 53),
+                                         (9, 14336, 54)])
+def test_q5k_subblock_sums_bit_exact(q, rows, K, seed):
+    w = q5k(seed, rows, K)
+    x = acts(seed, 1, K)
+    xq = pack_on_device(q, x)
+    S = poisoned_i32(rows, K // 32)
+    q.q8k_debug_subblock_sums(q.Q8K_Q5_K, to_dev(w), rows, K, xq, S)
+    oqs, _, _ = oracle.q8k_pack(x)
+    assert np.array_equal(host(S), oracle.subblock_sums(oracle.Q5_K, w, rows, K, oqs[0]))
+
+
+@pytest.mark.parametrize("rows,K,seed", [(256, 1024, 50), (4096, 4096, 51), (37, 256, 52), (13, 768, 53),
+                                         (70, 1280, 55), (9, 14336, 54), (1, 256, 56)])
+def test_q5k_matvec(q, rows, K, seed):
+    w = q5k(seed, rows, K)
+    x = acts(seed, 1, K)
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(rows)
+    q.qmatvec(q.Q8K_Q5_K, to_dev(w), rows, K, xq, y)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(oracle.Q5_K, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(y), want[0], A[0], f"q5k {rows}x{K}")
+
+
+def test_q5k_matvec_extreme_scales(q):
+    """Subnormal fp16 dmin, zero d, the largest fp16 scales and zero blocks."""
+    rows, K = 64, 1024
+    w = q5k(57, rows, K).reshape(-1, 176).copy()
+    f16 = lambda v: np.array([v], np.float16).view(np.uint8)
+    w[0::4, 0:2] = f16(0.0)
+    w[1::4, 2:4] = f16(3e-7)          # subnormal fp16
+    w[2::4, 0:2] = f16(60000.0)
+    w[3::4, 2:4] = f16(60000.0)
+    w = w.reshape(-1)
+    x = special_blocks(K)
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(rows)
+    q.qmatvec(q.Q8K_Q5_K, to_dev(w), rows, K, xq, y)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(oracle.Q5_K, w, rows, K, oqs, od, obs)
+    assert_close(host(y), want[0], A[0], "q5k extreme")
+
+
+def test_q5k_without_fifth_bits_matches_q4k_kernel(q):
+    """A Q5_K weight with every qh byte zero runs the same integer sums and
+    epilogue as the Q4_K kernel on the same fields: bit-identical outputs."""
+    rows, K = 512, 2048
+    nb = K // 256
+    w4 = q4k(58, rows, K).reshape(rows * nb, 144)
+    w5 = np.zeros((rows * nb, 176), np.uint8)
+    w5[:, 0:16] = w4[:, 0:16]
+    w5[:, 48:176] = w4[:, 16:144]
+    xq = pack_on_device(q, acts(58, 1, K))
+    y4 = poisoned_f32(rows)
+    y5 = poisoned_f32(rows)
+    q.qmatvec(q.Q8K_Q4_K, to_dev(w4.reshape(-1)), rows, K, xq, y4)
+    q.qmatvec(q.Q8K_Q5_K, to_dev(w5.reshape(-1)), rows, K, xq, y5)
+    assert np.array_equal(host(y4).view(np.uint32), host(y5).view(np.uint32))
+
+
 # ================================================================== a2 bind + a4 Q6_K decode
 def q6k_bound(q, seed, rows, K):
     w = synth.q6k_weights(np.random.default_rng(seed), rows, K)
@@ -179,12 +245,15 @@ def test_q6k_matvec(q, rows, K, seed):
 
 # ================================================================== a5 batched
 @pytest.mark.parametrize("ncols", [1, 2, 3, 4, 5, 8])
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 def test_batched(q, ncols, fmt):
-    rows, K = (4096, 4096) if fmt == "q4k" else (1000, 4096)
+    rows, K = (4096, 4096) if fmt != "q6k" else (1000, 4096)
     if fmt == "q4k":
         w = q4k(1, rows, K)
         wd, qt, ot = to_dev(w), q.Q8K_Q4_K, oracle.Q4_K
+    elif fmt == "q5k":
+        w = q5k(59, rows, K)
+        wd, qt, ot = to_dev(w), q.Q8K_Q5_K, oracle.Q5_K
     else:
         w, wd = q6k_bound(q, 2, rows, K)
         qt, ot = q.Q8K_Q6_K_RELAID, oracle.Q6_K
@@ -210,6 +279,9 @@ def moe_case(q, fmt, E, rows, K, T, topk, seed, ids=None):
     if fmt == "q4k":
         w = synth.q4k_weights(g, E * rows, K)
         wd, qt, ot = to_dev(w), q.Q8K_Q4_K, oracle.Q4_K
+    elif fmt == "q5k":
+        w = synth.q5k_weights(g, E * rows, K)
+        wd, qt, ot = to_dev(w), q.Q8K_Q5_K, oracle.Q5_K
     else:
         w = synth.q6k_weights(g, E * rows, K)
         wd = poisoned(q.q8k_weight_bytes(q.Q8K_Q6_K_RELAID, E * rows, K))
@@ -232,6 +304,9 @@ def moe_case(q, fmt, E, rows, K, T, topk, seed, ids=None):
     ("q4k", 8, 37, 1280, 1, 2, 32),
     ("q4k", 16, 64, 256, 200, 4, 33),      # many tokens: several token slots per lane
     ("q6k", 8, 300, 1024, 16, 2, 34),
+    ("q5k", 8, 14336, 4096, 16, 2, 35),    # the MoE decode layer shape in Q5_K
+    ("q5k", 4, 100, 512, 5, 3, 36),
+    ("q5k", 16, 64, 256, 200, 4, 37),
 ])
 def test_moe(q, fmt, E, rows, K, T, topk, seed):
     got, w, ot, oqs, od, obs, ids, rw = moe_case(q, fmt, E, rows, K, T, topk, seed)
