@@ -64,6 +64,8 @@ KERNEL_SOURCES = {
     "matvec_q4k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
     "matvec_q6k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
     "moe": [_CS + "moe.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
+    "matvec_q5k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
+    "moe_q5k": [_CS + "moe.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
     "prefill_q4k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
     "pack": [_CS + "pack.hip", _CS + "q8k_device.h"],
 }
@@ -117,8 +119,15 @@ def rotations(nbytes: int, minimum: int = 2) -> int:
 
 
 # ---------------------------------------------------------------- workloads
+_BLOCK_BYTES = {"q4k": 144, "q5k": 176, "q6k": 210}
+
+
+def _oracle_qtype(oracle, fmt):
+    return {"q4k": oracle.Q4_K, "q5k": oracle.Q5_K, "q6k": oracle.Q6_K}[fmt]
+
+
 class Decode:
-    """One token through q8k_pack + qmatvec (Q4_K or relaid Q6_K)."""
+    """One token through q8k_pack + qmatvec (Q4_K, Q5_K or relaid Q6_K)."""
 
     def __init__(self, q, torch, fmt, rows, K, seed, R=None):
         import synth
@@ -126,10 +135,10 @@ class Decode:
         self.q, self.torch, self.fmt, self.rows, self.K = q, torch, fmt, rows, K
         g = np.random.default_rng(seed)
         dev = torch.device("cuda")
-        if fmt == "q4k":
-            self.w_host = synth.q4k_weights(g, rows, K)
+        if fmt in ("q4k", "q5k"):
+            self.w_host = (synth.q4k_weights if fmt == "q4k" else synth.q5k_weights)(g, rows, K)
             w0 = torch.from_numpy(self.w_host).to(dev)
-            self.qt = q.Q8K_Q4_K
+            self.qt = q.Q8K_Q4_K if fmt == "q4k" else q.Q8K_Q5_K
         else:
             self.w_host = synth.q6k_weights(g, rows, K)
             wg = torch.from_numpy(self.w_host).to(dev)
@@ -137,7 +146,7 @@ class Decode:
             q.q8k_bind_q6k(wg, rows, K, w0)
             del wg
             self.qt = q.Q8K_Q6_K_RELAID
-        self.wbytes_alg = rows * (K // 256) * (144 if fmt == "q4k" else 210)
+        self.wbytes_alg = rows * (K // 256) * _BLOCK_BYTES[fmt]
         self.R = R or rotations(w0.numel())
         self.ws = [w0] + [w0.clone() for _ in range(self.R - 1)]
         self.x_host = synth.activations(g, 1, K)
@@ -145,8 +154,8 @@ class Decode:
         self.xq = torch.empty(q.q8k_act_bytes(1, K), dtype=torch.uint8, device=dev)
         self.y = torch.empty(rows, dtype=torch.float32, device=dev)
         nb = K // 256
-        # algorithmic bytes: weight once, q8_K codes+scales (+ sums for Q4_K) once, output once
-        self.mv_bytes = self.wbytes_alg + K + 4 * nb + (16 * nb if fmt == "q4k" else 0) + 4 * rows
+        # algorithmic bytes: weight once, q8_K codes+scales (+ sums for Q4_K/Q5_K) once, output once
+        self.mv_bytes = self.wbytes_alg + K + 4 * nb + (16 * nb if fmt != "q6k" else 0) + 4 * rows
         self.pack_bytes = 4 * K + K + 4 * nb + 16 * nb
         self.step_bytes = self.mv_bytes + self.pack_bytes
 
@@ -163,8 +172,8 @@ class Decode:
         self.step(0)
         got = self.y.cpu().numpy()
         qs, d, bs = oracle.q8k_pack(self.x_host)
-        want, A = oracle.matvec(oracle.Q4_K if self.fmt == "q4k" else oracle.Q6_K, self.w_host, self.rows,
-                                self.K, qs, d, bs, nthreads=ncores())
+        want, A = oracle.matvec(_oracle_qtype(oracle, self.fmt), self.w_host, self.rows, self.K, qs, d, bs,
+                                nthreads=ncores())
         return close(got, want[0], A[0])
 
 
@@ -196,21 +205,23 @@ class Batched(Decode):
         self.step(0)
         got = self.y.cpu().numpy().reshape(self.ncols, self.rows)
         qs, d, bs = oracle.q8k_pack(self.x_host)
-        want, A = oracle.matvec(oracle.Q4_K if self.fmt == "q4k" else oracle.Q6_K, self.w_host, self.rows,
-                                self.K, qs, d, bs, nthreads=ncores())
+        want, A = oracle.matvec(_oracle_qtype(oracle, self.fmt), self.w_host, self.rows, self.K, qs, d, bs,
+                                nthreads=ncores())
         return close(got, want, A)
 
 
 class MoE:
-    """16 tokens, top-2 of 8 Q4_K experts of 14336 x 4096: pack + qmatvec_moe."""
+    """16 tokens, top-2 of 8 Q4_K (or Q5_K) experts of 14336 x 4096: pack + qmatvec_moe."""
 
-    def __init__(self, q, torch, E=8, rows=14336, K=4096, T=16, topk=2, seed=3):
+    def __init__(self, q, torch, E=8, rows=14336, K=4096, T=16, topk=2, seed=3, fmt="q4k"):
         import synth
 
         self.q, self.torch, self.E, self.rows, self.K, self.T, self.topk = q, torch, E, rows, K, T, topk
+        self.fmt = fmt
+        self.qt = q.Q8K_Q4_K if fmt == "q4k" else q.Q8K_Q5_K
         g = np.random.default_rng(seed)
         dev = torch.device("cuda")
-        self.w_host = synth.q4k_weights(g, E * rows, K)
+        self.w_host = (synth.q4k_weights if fmt == "q4k" else synth.q5k_weights)(g, E * rows, K)
         w0 = torch.from_numpy(self.w_host).to(dev)
         self.R = rotations(w0.numel())
         self.ws = [w0] + [w0.clone() for _ in range(self.R - 1)]
@@ -224,7 +235,7 @@ class MoE:
         nb = K // 256
         hit = len(set(self.ids_host.ravel().tolist()))
         self.experts_hit = hit
-        self.mv_bytes = hit * rows * nb * 144 + T * (K + 20 * nb) + 8 * T * topk + 4 * T * rows
+        self.mv_bytes = hit * rows * nb * _BLOCK_BYTES[fmt] + T * (K + 20 * nb) + 8 * T * topk + 4 * T * rows
         self.pack_bytes = T * (4 * K + K + 20 * nb)
         self.step_bytes = self.mv_bytes + self.pack_bytes
 
@@ -233,7 +244,7 @@ class MoE:
         self.main(i)
 
     def main(self, i):
-        self.q.qmatvec_moe(self.q.Q8K_Q4_K, self.ws[i % self.R], self.E, self.rows, self.K, self.xq, self.T,
+        self.q.qmatvec_moe(self.qt, self.ws[i % self.R], self.E, self.rows, self.K, self.xq, self.T,
                            self.ids, self.rw, self.topk, self.y)
 
     def parity(self):
@@ -242,8 +253,8 @@ class MoE:
         self.step(0)
         got = self.y.cpu().numpy().reshape(self.T, self.rows)
         qs, d, bs = oracle.q8k_pack(self.x_host)
-        want, A = oracle.moe(oracle.Q4_K, self.w_host, self.E, self.rows, self.K, qs, d, bs, self.ids_host,
-                             self.rw_host, nthreads=ncores())
+        want, A = oracle.moe(_oracle_qtype(oracle, self.fmt), self.w_host, self.E, self.rows, self.K, qs, d, bs,
+                             self.ids_host, self.rw_host, nthreads=ncores())
         return close(got, want, A)
 
 
@@ -348,6 +359,8 @@ PROFILE_TARGETS = {
     "decode_q4k": "qmatvec on the 4096x4096 Q4_K decode workload",
     "decode_q6k": "qmatvec on the 32000x4096 relaid Q6_K workload",
     "moe": "qmatvec_moe on the 8 x 14336x4096 Q4_K, 16-token top-2 workload",
+    "decode_q5k": "qmatvec on the 4096x4096 Q5_K decode workload",
+    "moe_q5k": "qmatvec_moe on the 8 x 14336x4096 Q5_K, 16-token top-2 workload",
     "prefill": "qmatmul_prefill on the 4096x14336 Q4_K, 512-token workload",
     "pack": "q8k_pack of 512 x 14336 fp32 activations",
     "copy": "a plain 256 MiB device-to-device copy (torch), the counter calibration reference",
@@ -367,6 +380,8 @@ def profile_run(q, torch, target, launches):
         wl = {"decode_q4k": lambda: Decode(q, torch, "q4k", 4096, 4096, seed=1),
               "decode_q6k": lambda: Decode(q, torch, "q6k", 32000, 4096, seed=2),
               "moe": lambda: MoE(q, torch),
+              "decode_q5k": lambda: Decode(q, torch, "q5k", 4096, 4096, seed=5),
+              "moe_q5k": lambda: MoE(q, torch, seed=6, fmt="q5k"),
               "prefill": lambda: Prefill(q, torch),
               "pack": lambda: Prefill(q, torch)}[target]()
         wl.step(0)
@@ -437,7 +452,7 @@ def main():
                    "parity": "pass" if parity else "FAIL"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
-                     "kernel": "matvec_q4k_kernel<1, 2>", "launch_us": round(mv_us, 3),
+                     "kernel": "matvec_q4k_kernel<1, 2, false>", "launch_us": round(mv_us, 3),
                      "algorithmic_bytes_per_launch": hd.mv_bytes},
     }
     del hd
@@ -469,6 +484,16 @@ def main():
         m = MoE(q, torch)
         decode_entry("moe_q4k_8x14336x4096_t16_top2", m, "moe")
         wl["moe_q4k_8x14336x4096_t16_top2"]["experts_hit"] = m.experts_hit
+        del m
+        torch.cuda.empty_cache()
+        # Q5_K: the Q4_K decode shape and the MoE layer shape with 176-byte blocks
+        log("workload: decode_q5k_4096x4096")
+        decode_entry("decode_q5k_4096x4096", Decode(q, torch, "q5k", 4096, 4096, seed=5), "matvec_q5k")
+        torch.cuda.empty_cache()
+        log("workload: moe_q5k_8x14336x4096_t16_top2")
+        m = MoE(q, torch, seed=6, fmt="q5k")
+        decode_entry("moe_q5k_8x14336x4096_t16_top2", m, "moe_q5k")
+        wl["moe_q5k_8x14336x4096_t16_top2"]["experts_hit"] = m.experts_hit
         del m
         torch.cuda.empty_cache()
         log("workload: prefill_q4k_4096x14336_m512")
