@@ -20,7 +20,8 @@
  *     four of each staged value (here: the Q5_K mat-vec, batched and MoE
  *     forms; the Q5_K prefill is not built and is refused);
  *   - section 2.4: mixture of experts, a decode mat-vec that visits each
- *     token's selected experts and sums their weighted outputs;
+ *     token's selected experts and sums their weighted outputs, and the
+ *     prefill form that runs the prefill tile per expert chunk;
  *   - section 3.2 (and SKaiNET's "Kernel SPI and the selection algorithm",
  *     decline reasons): the input width must be a multiple of 256.
  *
@@ -147,6 +148,21 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
 size_t qmatmul_prefill_workspace_bytes(int qtype, int64_t rows, int64_t K, int64_t M);
 int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int64_t M, float* y, void* ws,
                     size_t ws_bytes, void* stream);
+
+/* qmatmul_prefill_moe: the prefill of a mixture-of-experts layer ("Language
+ * models on the device", section 2.4: each expert's (token, slot) pairs are
+ * grouped into chunks and the prefill tile runs per expert and chunk).
+ * Same weights, tokens, ids, router weights and result as qmatvec_moe,
+ *   y[t][r] = sum_k rw[t][k] * (W_{ids[t][k]} x_t)[r],
+ * for T tokens (0 <= T, T * K < 2^30) instead of at most 256.
+ * qtype: Q8K_Q4_K.  1 <= topk <= min(E, Q8K_MOE_MAX_TOPK).  An id outside
+ * [0, E) selects nothing.  ws / ws_bytes: caller-owned workspace of at least
+ * qmatmul_prefill_moe_workspace_bytes(...) bytes (the fp32 result of every
+ * (token, slot) pair), not overlapping y.  y: fp32 [T][rows]. */
+size_t qmatmul_prefill_moe_workspace_bytes(int qtype, int64_t E, int64_t rows, int64_t K, int64_t T, int32_t topk);
+int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq, int64_t T,
+                        const int32_t* ids, const float* rw, int32_t topk, float* y, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* Test support: the exact int32 sub-block sums of every weight row against
  * one packed token, computed by the same device code as qmatvec.

@@ -18,6 +18,7 @@ __all__ = [
     "Q8K_Q4_K", "Q8K_Q5_K", "Q8K_Q6_K_RELAID", "Q8K_Q6_K_GGUF", "Q8K_COLS_MAX", "Q8K_MOE_MAX_TOKENS", "Q8K_MOE_MAX_TOPK", "Q8KError",
     "lib", "LIB_PATH", "q8k_act_bytes", "q8k_act_layout", "q8k_weight_bytes", "q8k_pack", "q8k_bind_q6k",
     "qmatvec", "qmatvec_batched", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
+    "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe",
     "q8k_debug_subblock_sums", "q8k_status_str", "q8k_last_error", "EXPORTED",
 ]
 
@@ -35,6 +36,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq8k.so")
 EXPORTED = (
     "q8k_act_bytes", "q8k_act_layout", "q8k_weight_bytes", "q8k_pack", "q8k_bind_q6k", "qmatvec",
     "qmatvec_batched", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
+    "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe",
     "q8k_debug_subblock_sums", "q8k_status_str", "q8k_last_error",
 )
 
@@ -70,6 +72,10 @@ lib.qmatmul_prefill_workspace_bytes.restype = _SZ
 lib.qmatmul_prefill_workspace_bytes.argtypes = [_INT, _I64, _I64, _I64]
 lib.qmatmul_prefill.restype = _INT
 lib.qmatmul_prefill.argtypes = [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]
+lib.qmatmul_prefill_moe_workspace_bytes.restype = _SZ
+lib.qmatmul_prefill_moe_workspace_bytes.argtypes = [_INT, _I64, _I64, _I64, _I64, ctypes.c_int32]
+lib.qmatmul_prefill_moe.restype = _INT
+lib.qmatmul_prefill_moe.argtypes = [_INT, _P, _I64, _I64, _I64, _P, _I64, _P, _P, ctypes.c_int32, _P, _P, _SZ, _P]
 lib.q8k_debug_subblock_sums.restype = _INT
 lib.q8k_debug_subblock_sums.argtypes = [_INT, _P, _I64, _I64, _P, _P, _P]
 lib.q8k_status_str.restype = ctypes.c_char_p
@@ -163,6 +169,16 @@ def qmatmul_prefill(qtype: int, w, rows: int, K: int, xq, M: int, y, ws=None, ws
                     stream=None) -> None:
     _check(lib.qmatmul_prefill(qtype, _ptr(w), rows, K, _ptr(xq), M, _ptr(y), _ptr(ws), ws_bytes,
                                _stream(stream)))
+
+
+def qmatmul_prefill_moe_workspace_bytes(qtype: int, E: int, rows: int, K: int, T: int, topk: int) -> int:
+    return int(lib.qmatmul_prefill_moe_workspace_bytes(qtype, E, rows, K, T, topk))
+
+
+def qmatmul_prefill_moe(qtype: int, w, E: int, rows: int, K: int, xq, T: int, ids, rw, topk: int, y, ws=None,
+                        ws_bytes: int = 0, stream=None) -> None:
+    _check(lib.qmatmul_prefill_moe(qtype, _ptr(w), E, rows, K, _ptr(xq), T, _ptr(ids), _ptr(rw), topk, _ptr(y),
+                                   _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def q8k_debug_subblock_sums(qtype: int, w, rows: int, K: int, xq, S, stream=None) -> None:

@@ -259,6 +259,45 @@ int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const voi
                                            (hipStream_t)stream));
 }
 
+size_t qmatmul_prefill_moe_workspace_bytes(int qtype, int64_t E, int64_t rows, int64_t K, int64_t T, int32_t topk) {
+    if (qtype != Q8K_Q4_K || E < 1 || rows < 0 || K <= 0 || K % QK != 0 || T < 0 || topk < 1) return 0;
+    return (size_t)T * (size_t)topk * (size_t)rows * sizeof(float);
+}
+
+int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq, int64_t T,
+                        const int32_t* ids, const float* rw, int32_t topk, float* y, void* ws, size_t ws_bytes,
+                        void* stream) {
+    const char* fn = "qmatmul_prefill_moe";
+    Q8K_TRY(check_k(fn, K));
+    Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
+    if (E < 1 || E > MAX_EXPERTS)
+        return fail(Q8K_ERR_ARG, "%s: E=%lld must be in [1, %lld]", fn, (long long)E, (long long)MAX_EXPERTS);
+    if (E * rows > MAX_ROWS)
+        return fail(Q8K_ERR_SHAPE, "%s: E*rows=%lld exceeds %lld", fn, (long long)(E * rows), (long long)MAX_ROWS);
+    Q8K_TRY(check_count(fn, "T", T, MAX_TOKENS));
+    if (T * K >= ((int64_t)1 << 30))
+        return fail(Q8K_ERR_SHAPE, "%s: T*K=%lld must be below 2^30 (32-bit gather offsets)", fn,
+                    (long long)(T * K));
+    if (topk < 1 || topk > E || topk > Q8K_MOE_MAX_TOPK)
+        return fail(Q8K_ERR_ARG, "%s: topk=%d must be in [1, min(E=%lld, %d)]", fn, topk, (long long)E,
+                    Q8K_MOE_MAX_TOPK);
+    Q8K_TRY(check_weight(fn, qtype, w, false));
+    Q8K_TRY(check_ptr(fn, "xq", xq, 16));
+    Q8K_TRY(check_ptr(fn, "ids", ids, 4));
+    Q8K_TRY(check_ptr(fn, "rw", rw, 4));
+    Q8K_TRY(check_ptr(fn, "y", y, 4));
+    const size_t need = qmatmul_prefill_moe_workspace_bytes(qtype, E, rows, K, T, topk);
+    if (ws_bytes < need)
+        return fail(Q8K_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+    if (need > 0) Q8K_TRY(check_ptr(fn, "ws", ws, 16));
+    Q8K_TRY(check_grid(fn, E * ((rows + 63) / 64)));
+    Q8K_TRY(check_grid(fn, (T * rows + 255) / 256));
+    if (rows == 0 || T == 0) return Q8K_OK;
+    const int nb = (int)(K / QK);
+    return launched(fn, launch_prefill_moe_q4k(static_cast<const uint8_t*>(w), E, rows, nb, acts_of(xq, T, K), T, ids,
+                                               rw, topk, y, static_cast<float*>(ws), (hipStream_t)stream));
+}
+
 int q8k_debug_subblock_sums(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int32_t* S,
                             void* stream) {
     const char* fn = "q8k_debug_subblock_sums";

@@ -156,6 +156,36 @@ __device__ __forceinline__ void producer_src(PrefillSrc& S, const uint8_t* __res
     S.d8o = (p >> 1) * nb * 4;
 }
 
+// Mixture-of-experts form: the tile's 128 token rows are the tokens tok[0..127]
+// (gathered from anywhere in the q8_K buffer of T tokens; tok < 0 marks an
+// empty row).  An empty row's offsets point past every record, so its reads
+// return zeros.  Offsets stay 32-bit: T * K < 2^30 is checked by the caller.
+constexpr int PF_NONE = 0x7ffffff0;
+__device__ __forceinline__ void producer_src_gather(PrefillSrc& S, const uint8_t* __restrict__ w, int64_t rows,
+                                                    int nb, const int8_t* __restrict__ qs,
+                                                    const float* __restrict__ d8, const int16_t* __restrict__ bs,
+                                                    int64_t K, int64_t T, int64_t n0, const int* tok, int p) {
+    const int64_t wrow = (int64_t)nb * Q4K_BLOCK;
+    S.w = w + n0 * wrow;
+    S.x = qs;
+    S.bs = bs;
+    S.d8 = d8;
+    S.wbytes = (rows - n0) * wrow;
+    S.xbytes = T * K;
+    S.bsbytes = T * nb * 16;
+    S.d8bytes = T * nb * 4;
+    const int wv = p >> 6, l = p & 63;
+    S.wo = (p >> 2) * (int)wrow;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = tok[16 * i + 4 * wv + (l >> 4)];
+        S.xo[i] = t >= 0 ? t * (int)K + 16 * (l & 15) : PF_NONE;
+    }
+    const int tb = tok[p >> 1];
+    S.bso = tb >= 0 ? tb * nb * 16 + 8 * (p & 1) : PF_NONE;
+    S.d8o = tb >= 0 ? tb * nb * 4 : PF_NONE;
+}
+
 __device__ __forceinline__ void producer_load(PrefillRegs& R, const PrefillSrc& S, int b, int p) {
     const rsrc_t rw = make_rsrc(S.w + (int64_t)b * Q4K_BLOCK, S.wbytes - (int64_t)b * Q4K_BLOCK);
     const rsrc_t rx = make_rsrc(S.x + (int64_t)b * QK, S.xbytes - (int64_t)b * QK);
@@ -298,16 +328,13 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf& sm, int lane, i
     }
 }
 
-__global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
-                                                          const int8_t* __restrict__ qs, const float* __restrict__ d8,
-                                                          const int16_t* __restrict__ bs, int64_t K, int64_t M,
-                                                          float* __restrict__ y) {
-    __shared__ __attribute__((aligned(16))) PrefillSmem sm;
+// One 128-token x 64-row tile over all nb blocks.  The producers' sources are
+// in S (built by the caller); consumer output row m of the tile goes to
+// y[orow(m) * rows + n] when ok(m).
+template <class ORow, class OK>
+__device__ __forceinline__ void prefill_tile(PrefillSmem& sm, const PrefillSrc& S, int nb, int64_t rows, int64_t n0,
+                                             float* __restrict__ y, ORow orow, OK ok) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
-    const int64_t n0 = ((int64_t)blockIdx.x % ntn) * PF_TN;
-    const int64_t m0 = ((int64_t)blockIdx.x / ntn) * PF_TM;
-
     // Both roles run the same number of barriers: one before the first
     // block and one after each block (checked for every block count).
     if (wv >= 4) {
@@ -315,8 +342,6 @@ __global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restr
         // iteration b - 1 (block 0 before the loop) from registers loaded two
         // iterations earlier; the two register sets alternate.
         const int p = tid - 256;
-        PrefillSrc S;
-        producer_src(S, w, rows, nb, qs, d8, bs, K, M, n0, m0, p);
         PrefillRegs RA, RB;
         // The loads are unconditional: past the last block the resources
         // have no records, so the reads return zeros without touching memory.
@@ -356,11 +381,144 @@ __global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restr
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + tg0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m < M && n < rows) y[m * rows + n] = accf[i][r] - accj[i][r];
+                const int m = tg0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (ok(m) && n < rows) y[orow(m) * rows + n] = accf[i][r] - accj[i][r];
             }
         }
     }
+}
+
+__global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
+                                                          const int8_t* __restrict__ qs, const float* __restrict__ d8,
+                                                          const int16_t* __restrict__ bs, int64_t K, int64_t M,
+                                                          float* __restrict__ y) {
+    __shared__ __attribute__((aligned(16))) PrefillSmem sm;
+    const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
+    const int64_t n0 = ((int64_t)blockIdx.x % ntn) * PF_TN;
+    const int64_t m0 = ((int64_t)blockIdx.x / ntn) * PF_TM;
+    PrefillSrc S;
+    if (threadIdx.x >= 256) producer_src(S, w, rows, nb, qs, d8, bs, K, M, n0, m0, (int)threadIdx.x - 256);
+    prefill_tile(
+        sm, S, nb, rows, n0, y, [&](int m) { return m0 + m; }, [&](int m) { return m0 + m < M; });
+}
+
+// ----------------------------------------------------- mixture of experts ----
+// "Language models on the device", section 2.4: the prefill of an MoE layer
+// groups each expert's (token, slot) pairs into chunks and runs the prefill
+// tile per (expert, chunk), with a ragged last chunk.  Here workgroup
+// (e, row tile) walks the pairs in ascending order, collects the next 128
+// that chose expert e (a block-wide compaction of ids == e) and runs the
+// tile on them; pair p's dot products go to row p of the per-pair output
+// `out` [T * topk][rows].  A second kernel adds each token's pairs in slot
+// order: y[t][r] = sum_k rw[t][k] * out[t * topk + k][r], skipping ids
+// outside [0, E) (no workgroup writes those rows).
+struct MoeLists {
+    int tok[PF_TM];   // token of each tile row, -1 past the chunk's end
+    int pair[PF_TM];  // pair index of each tile row
+    int wcount[8];    // per-wave match counts of one 512-pair slab
+    int count, pos;   // pairs collected, next pair to examine
+};
+
+// Collect the next up-to-128 pairs p >= L.pos with ids[p] == e, in ascending
+// order.  Block-wide and barrier-synchronised; returns the count (uniform).
+__device__ __forceinline__ int moe_collect(MoeLists& L, const int32_t* __restrict__ ids, int64_t P, int64_t e,
+                                           int topk) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (tid == 0) L.count = 0;
+    __syncthreads();
+    for (;;) {
+        const int count = L.count;
+        const int64_t pos = L.pos;
+        if (count >= PF_TM || pos >= P) break;  // uniform: read after a barrier
+        const int64_t p = pos + tid;
+        const bool m = p < P && ids[p] == (int32_t)e;
+        const uint64_t ball = __ballot(m);
+        const int below = __builtin_popcountll(ball & ((1ull << lane) - 1ull));
+        if (lane == 0) L.wcount[wv] = __builtin_popcountll(ball);
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = L.wcount[i];
+            before += i < wv ? c : 0;
+            total += c;
+        }
+        const int idx = count + before + below;
+        if (m && idx < PF_TM) {
+            L.tok[idx] = (int)(p / topk);
+            L.pair[idx] = (int)p;
+        }
+        __syncthreads();  // every thread has read count, pos and wcount
+        if (count + total <= PF_TM) {
+            if (tid == 0) {
+                L.count = count + total;
+                L.pos = pos + 512;
+            }
+        } else if (m && idx == PF_TM) {
+            // the first pair that did not fit: the next chunk starts there
+            L.count = PF_TM;
+            L.pos = p;
+        }
+        __syncthreads();
+    }
+    const int count = L.count;
+    for (int i = count + (int)threadIdx.x; i < PF_TM; i += 512) L.tok[i] = -1;
+    __syncthreads();
+    return count;
+}
+
+__global__ __launch_bounds__(512) void prefill_moe_q4k_kernel(const uint8_t* __restrict__ w, int64_t E, int64_t rows,
+                                                              int nb, const int8_t* __restrict__ qs,
+                                                              const float* __restrict__ d8,
+                                                              const int16_t* __restrict__ bs, int64_t K, int64_t T,
+                                                              const int32_t* __restrict__ ids, int topk,
+                                                              float* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) PrefillSmem sm;
+    __shared__ MoeLists L;
+    const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
+    const int64_t e = (int64_t)blockIdx.x / ntn;
+    const int64_t n0 = ((int64_t)blockIdx.x % ntn) * PF_TN;
+    const uint8_t* we = w + e * rows * (int64_t)nb * Q4K_BLOCK;
+    const int64_t P = T * topk;
+    if (threadIdx.x == 0) L.pos = 0;
+    for (;;) {
+        const int count = moe_collect(L, ids, P, e, topk);
+        if (count == 0) break;  // uniform
+        PrefillSrc S;
+        if (threadIdx.x >= 256)
+            producer_src_gather(S, we, rows, nb, qs, d8, bs, K, T, n0, L.tok, (int)threadIdx.x - 256);
+        prefill_tile(
+            sm, S, nb, rows, n0, out, [&](int m) { return (int64_t)L.pair[m]; }, [&](int m) { return m < count; });
+        __syncthreads();  // the lists are rebuilt next
+    }
+}
+
+// y[t][r] = sum_k rw[t][k] * out[t * topk + k][r] over ids in [0, E), k ascending.
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ out, int64_t rows, int64_t T,
+                                                          const int32_t* __restrict__ ids,
+                                                          const float* __restrict__ rw, int topk, int64_t E,
+                                                          float* __restrict__ y) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= T * rows) return;
+    const int64_t t = i / rows, r = i % rows;
+    float s = 0.0f;
+    for (int k = 0; k < topk; ++k) {
+        const int64_t pp = t * topk + k;
+        const int32_t id = ids[pp];
+        if (id >= 0 && id < E) s += rw[pp] * out[pp * rows + r];
+    }
+    y[i] = s;
+}
+
+hipError_t launch_prefill_moe_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
+                                  const int32_t* ids, const float* rw, int topk, float* y, float* ws, hipStream_t s) {
+    const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
+    hipLaunchKernelGGL(prefill_moe_q4k_kernel, dim3((unsigned)(E * ntn)), dim3(512), 0, s, w, E, rows, nb, a.qs, a.d,
+                       a.bs, a.K, T, ids, topk, ws);
+    const int64_t n = T * rows;
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws, rows, T, ids, rw,
+                       topk, E, y);
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y, hipStream_t s) {

@@ -33,5 +33,7 @@ hipError_t launch_moe_q5k(const uint8_t* w, int64_t E, int64_t rows, int nb, Act
 hipError_t launch_moe_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t E, int64_t rows, int nb, Acts a,
                           int64_t T, const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s);
 hipError_t launch_prefill_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y, hipStream_t s);
+hipError_t launch_prefill_moe_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
+                                  const int32_t* ids, const float* rw, int topk, float* y, float* ws, hipStream_t s);
 
 }  // namespace q8k

@@ -111,12 +111,32 @@ def test_batched_and_moe_arguments(q):
     refused(q, "Q8K_ERR_NULL", q.qmatvec_moe, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, None, A16, 2, A16, 0)
 
 
+def test_prefill_moe_arguments(q):
+    f = q.qmatmul_prefill_moe
+    # E, topk, qtype, T*K, workspace
+    refused(q, "Q8K_ERR_ARG", f, q.Q8K_Q4_K, A16, 0, 4, 256, A16, 16, A16, A16, 1, A16, A16, 1 << 20, 0)
+    refused(q, "Q8K_ERR_ARG", f, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, A16, A16, 9, A16, A16, 1 << 20, 0)
+    refused(q, "Q8K_ERR_ARG", f, q.Q8K_Q4_K, A16, 128, 4, 256, A16, 2, A16, A16, q.Q8K_MOE_MAX_TOPK + 1, A16,
+            A16, 1 << 20, 0)
+    msg = refused(q, "Q8K_ERR_QTYPE", f, q.Q8K_Q5_K, A16, 8, 4, 256, A16, 16, A16, A16, 2, A16, A16, 1 << 20, 0)
+    assert "Q5_K" in msg
+    msg = refused(q, "Q8K_ERR_SHAPE", f, q.Q8K_Q4_K, A16, 8, 4, 16384, A16, 1 << 16, A16, A16, 2, A16, A16,
+                  1 << 40, 0)
+    assert "2^30" in msg
+    need = q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, 8, 4, 256, 16, 2)
+    assert need == 16 * 2 * 4 * 4
+    refused(q, "Q8K_ERR_WORKSPACE", f, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, A16, A16, 2, A16, A16, need - 1, 0)
+    refused(q, "Q8K_ERR_NULL", f, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, None, A16, 2, A16, A16, need, 0)
+    assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q6_K_RELAID, 8, 4, 256, 16, 2) == 0
+
+
 def test_empty_inputs_enqueue_nothing(q):
     # zero rows / tokens are valid and return before any launch
     q.qmatvec(q.Q8K_Q4_K, A16, 0, 256, A16, A16, 0)
     q.q8k_pack(A16, 0, 256, A16, 0)
     q.qmatvec_moe(q.Q8K_Q4_K, A16, 8, 4, 256, A16, 0, A16, A16, 2, A16, 0)
     q.qmatmul_prefill(q.Q8K_Q4_K, A16, 8, 256, A16, 0, A16, None, 0, 0)
+    q.qmatmul_prefill_moe(q.Q8K_Q4_K, A16, 8, 4, 256, A16, 0, A16, A16, 2, A16, None, 0, 0)
     q.q8k_bind_q6k(A16, 0, 256, A16, 0)
 
 

@@ -327,6 +327,67 @@ def test_moe_crowded_expert_and_bad_ids(q):
     assert_close(got, want, A, "moe crowded")
 
 
+# ================================================================== MoE prefill (NEXT row)
+def moe_prefill_case(q, E, rows, K, T, topk, seed, ids=None):
+    g = np.random.default_rng(seed)
+    w = synth.q4k_weights(g, E * rows, K)
+    x = synth.activations(g, T, K)
+    r_ids, rw = synth.moe_routing(g, T, E, topk)
+    if ids is None:
+        ids = r_ids
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(T, rows)
+    wsb = q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, E, rows, K, T, topk)
+    ws = poisoned(wsb)
+    q.qmatmul_prefill_moe(q.Q8K_Q4_K, to_dev(w), E, rows, K, xq, T, to_dev(ids.astype(np.int32)), to_dev(rw), topk,
+                          y, ws, wsb)
+    oqs, od, obs = oracle.q8k_pack(x)
+    return host(y), w, oqs, od, obs, ids, rw
+
+
+@pytest.mark.parametrize("E,rows,K,T,topk,seed", [
+    (8, 512, 4096, 512, 2, 60),     # ~128 pairs per expert: one or two chunks each
+    (4, 130, 768, 37, 3, 61),       # ragged row tile, a few pairs per expert
+    (16, 64, 256, 200, 4, 62),      # many experts
+    (2, 96, 512, 1, 1, 63),         # one token
+])
+def test_prefill_moe(q, E, rows, K, T, topk, seed):
+    got, w, oqs, od, obs, ids, rw = moe_prefill_case(q, E, rows, K, T, topk, seed)
+    want, A = oracle.moe(oracle.Q4_K, w, E, rows, K, oqs, od, obs, ids, rw, nthreads=NTH)
+    assert_close(got, want, A, f"moe prefill E={E} rows={rows} T={T}")
+
+
+def test_prefill_moe_crowded_expert_and_bad_ids(q):
+    """300 tokens all choose expert 0 first (three chunks, the last ragged);
+    ids outside [0, E) select nothing."""
+    E, rows, K, T, topk = 4, 100, 512, 300, 2
+    g = np.random.default_rng(64)
+    ids = np.stack([np.zeros(T, np.int32), g.integers(1, E, T).astype(np.int32)], axis=1)
+    ids[7, 1] = 9
+    ids[11, 0] = -2
+    got, w, oqs, od, obs, ids, rw = moe_prefill_case(q, E, rows, K, T, topk, 64, ids=ids)
+    ok = (ids >= 0) & (ids < E)
+    want, A = oracle.moe(oracle.Q4_K, w, E, rows, K, oqs, od, obs, np.where(ok, ids, 0),
+                         np.where(ok, rw, 0).astype(np.float32), nthreads=NTH)
+    assert_close(got, want, A, "moe prefill crowded")
+
+
+def test_prefill_moe_rows_equal_decode_moe(q):
+    """The prefill form and the decode form compute the same y (within the
+    tolerance: their fp32 sums run in different orders)."""
+    E, rows, K, T, topk = 8, 256, 1024, 16, 2
+    got, w, oqs, od, obs, ids, rw = moe_prefill_case(q, E, rows, K, T, topk, 65)
+    g = np.random.default_rng(65)  # the same draws as moe_prefill_case
+    _ = synth.q4k_weights(g, E * rows, K)
+    x = synth.activations(g, T, K)
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(T, rows)
+    q.qmatvec_moe(q.Q8K_Q4_K, to_dev(w), E, rows, K, xq, T, to_dev(ids.astype(np.int32)), to_dev(rw), topk, y)
+    want, A = oracle.moe(oracle.Q4_K, w, E, rows, K, oqs, od, obs, ids, rw)
+    assert_close(host(y), want, A, "decode moe")
+    assert_close(got, want, A, "prefill moe")
+
+
 # ================================================================== a7 prefill
 @pytest.mark.parametrize("M,rows,K,seed", [(1, 64, 256, 41), (17, 100, 512, 42), (64, 64, 256, 43),
                                            (127, 256, 1024, 44), (200, 130, 768, 45), (65, 4096, 256, 46)])
