@@ -67,6 +67,7 @@ KERNEL_SOURCES = {
     "matvec_q5k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
     "moe_q5k": [_CS + "moe.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
     "prefill_q4k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
+    "moe_prefill_q4k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
     "pack": [_CS + "pack.hip", _CS + "q8k_device.h"],
 }
 
@@ -301,6 +302,54 @@ class Prefill:
         return bool(np.isfinite(got).all()) and close(got[toks], want, A)
 
 
+class MoEPrefill:
+    """512 tokens, top-2 of 8 Q4_K experts of 14336 x 4096: pack + qmatmul_prefill_moe."""
+
+    def __init__(self, q, torch, E=8, rows=14336, K=4096, T=512, topk=2, seed=7):
+        import synth
+
+        self.q, self.torch, self.E, self.rows, self.K, self.T, self.topk = q, torch, E, rows, K, T, topk
+        g = np.random.default_rng(seed)
+        dev = torch.device("cuda")
+        self.w_host = synth.q4k_weights(g, E * rows, K)
+        w0 = torch.from_numpy(self.w_host).to(dev)
+        self.R = rotations(w0.numel())
+        self.ws = [w0] + [w0.clone() for _ in range(self.R - 1)]
+        self.x_host = synth.activations(g, T, K)
+        self.ids_host, self.rw_host = synth.moe_routing(g, T, E, topk)
+        self.x = torch.from_numpy(self.x_host).to(dev)
+        self.ids = torch.from_numpy(self.ids_host).to(dev)
+        self.rw = torch.from_numpy(self.rw_host).to(dev)
+        self.xq = torch.empty(q.q8k_act_bytes(T, K), dtype=torch.uint8, device=dev)
+        self.y = torch.empty(T * rows, dtype=torch.float32, device=dev)
+        self.ws_bytes = q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, E, rows, K, T, topk)
+        self.wsp = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        # useful int8 operations: every (token, slot) pair against its expert's rows
+        self.ops = 2 * T * topk * rows * K
+        nb = K // 256
+        self.pack_bytes = T * (4 * K + K + 20 * nb)
+
+    def step(self, i):
+        self.q.q8k_pack(self.x, self.T, self.K, self.xq)
+        self.main(i)
+
+    def main(self, i):
+        self.q.qmatmul_prefill_moe(self.q.Q8K_Q4_K, self.ws[i % self.R], self.E, self.rows, self.K, self.xq, self.T,
+                                   self.ids, self.rw, self.topk, self.y, self.wsp, self.ws_bytes)
+
+    def parity(self):
+        """Sampled tokens against the oracle's MoE (the same per-token formula)."""
+        import oracle
+
+        self.step(0)
+        got = self.y.cpu().numpy().reshape(self.T, self.rows)
+        qs, d, bs = oracle.q8k_pack(self.x_host)
+        toks = np.array([0, 1, 200, self.T - 1])
+        want, A = oracle.moe(oracle.Q4_K, self.w_host, self.E, self.rows, self.K, qs[toks], d[toks], bs[toks],
+                             self.ids_host[toks], self.rw_host[toks], nthreads=ncores())
+        return bool(np.isfinite(got).all()) and close(got[toks], want, A)
+
+
 def ncores() -> int:
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
@@ -362,6 +411,7 @@ PROFILE_TARGETS = {
     "decode_q5k": "qmatvec on the 4096x4096 Q5_K decode workload",
     "moe_q5k": "qmatvec_moe on the 8 x 14336x4096 Q5_K, 16-token top-2 workload",
     "prefill": "qmatmul_prefill on the 4096x14336 Q4_K, 512-token workload",
+    "moe_prefill": "qmatmul_prefill_moe on the 8 x 14336x4096 Q4_K, 512-token top-2 workload",
     "pack": "q8k_pack of 512 x 14336 fp32 activations",
     "copy": "a plain 256 MiB device-to-device copy (torch), the counter calibration reference",
 }
@@ -383,6 +433,7 @@ def profile_run(q, torch, target, launches):
               "decode_q5k": lambda: Decode(q, torch, "q5k", 4096, 4096, seed=5),
               "moe_q5k": lambda: MoE(q, torch, seed=6, fmt="q5k"),
               "prefill": lambda: Prefill(q, torch),
+              "moe_prefill": lambda: MoEPrefill(q, torch),
               "pack": lambda: Prefill(q, torch)}[target]()
         wl.step(0)
         torch.cuda.synchronize()
@@ -505,6 +556,20 @@ def main():
             "parity": "pass" if ok else "FAIL", "kernel_us": round(us, 2), "TOPS": round(tops, 1),
             "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "step_ms": round(s * 1e3, 4),
             "ops_per_launch": p.ops, "traffic": traffic_record("prefill_q4k")}
+        del p
+        torch.cuda.empty_cache()
+        log("workload: moe_prefill_q4k_8x14336x4096_t512_top2")
+        mp = MoEPrefill(q, torch)
+        ok = mp.parity()
+        s, us = run_timed(torch, mp, max(10, steps // 4), 3)
+        tops = mp.ops / (us * 1e-6) / 1e12
+        wl["moe_prefill_q4k_8x14336x4096_t512_top2"] = {
+            "parity": "pass" if ok else "FAIL", "kernel_us": round(us, 2), "TOPS": round(tops, 1),
+            "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "step_ms": round(s * 1e3, 4),
+            "ops_per_launch": mp.ops, "weight_copies_rotated": mp.R, "traffic": traffic_record("moe_prefill_q4k")}
+        del mp
+        torch.cuda.empty_cache()
+        p = Prefill(q, torch)
         # q8_K pack of the 512 x 14336 batch, timed on its own
         gp = graph_of(torch, lambda i: q.q8k_pack(p.x, p.M, p.K, p.xq), 32)
         pus = replay_us(torch, gp, 32, reps=2)
