@@ -68,6 +68,8 @@ KERNEL_SOURCES = {
     "moe_q5k": [_CS + "moe.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
     "prefill_q4k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
     "moe_prefill_q4k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
+    "prefill_q5k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
+    "moe_prefill_q5k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
     "pack": [_CS + "pack.hip", _CS + "q8k_device.h"],
 }
 
@@ -259,16 +261,21 @@ class MoE:
         return close(got, want, A)
 
 
-class Prefill:
-    """512 tokens through q8k_pack + qmatmul_prefill against a 4096 x 14336 Q4_K weight."""
+def _prefill_format(q, synth, fmt):
+    return {"q4k": (q.Q8K_Q4_K, synth.q4k_weights), "q5k": (q.Q8K_Q5_K, synth.q5k_weights)}[fmt]
 
-    def __init__(self, q, torch, rows=4096, K=14336, M=512, seed=4):
+
+class Prefill:
+    """512 tokens through q8k_pack + qmatmul_prefill against a 4096 x 14336 Q4_K (or Q5_K) weight."""
+
+    def __init__(self, q, torch, rows=4096, K=14336, M=512, seed=4, fmt="q4k"):
         import synth
 
-        self.q, self.torch, self.rows, self.K, self.M = q, torch, rows, K, M
+        self.q, self.torch, self.rows, self.K, self.M, self.fmt = q, torch, rows, K, M, fmt
+        self.qt, gen = _prefill_format(q, synth, fmt)
         g = np.random.default_rng(seed)
         dev = torch.device("cuda")
-        self.w_host = synth.q4k_weights(g, rows, K)
+        self.w_host = gen(g, rows, K)
         w0 = torch.from_numpy(self.w_host).to(dev)
         self.R = rotations(w0.numel())
         self.ws = [w0] + [w0.clone() for _ in range(self.R - 1)]
@@ -276,7 +283,7 @@ class Prefill:
         self.x = torch.from_numpy(self.x_host).to(dev)
         self.xq = torch.empty(q.q8k_act_bytes(M, K), dtype=torch.uint8, device=dev)
         self.y = torch.empty(M * rows, dtype=torch.float32, device=dev)
-        self.ws_bytes = q.qmatmul_prefill_workspace_bytes(q.Q8K_Q4_K, rows, K, M)
+        self.ws_bytes = q.qmatmul_prefill_workspace_bytes(self.qt, rows, K, M)
         self.wsp = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev) if self.ws_bytes else None
         self.ops = 2 * M * rows * K
         nb = K // 256
@@ -287,8 +294,8 @@ class Prefill:
         self.main(i)
 
     def main(self, i):
-        self.q.qmatmul_prefill(self.q.Q8K_Q4_K, self.ws[i % self.R], self.rows, self.K, self.xq, self.M, self.y,
-                               self.wsp, self.ws_bytes)
+        self.q.qmatmul_prefill(self.qt, self.ws[i % self.R], self.rows, self.K, self.xq, self.M, self.y, self.wsp,
+                               self.ws_bytes)
 
     def parity(self):
         import oracle
@@ -297,21 +304,23 @@ class Prefill:
         got = self.y.cpu().numpy().reshape(self.M, self.rows)
         qs, d, bs = oracle.q8k_pack(self.x_host)
         toks = np.array([0, 1, 255, 256, self.M - 1])
-        want, A = oracle.matvec(oracle.Q4_K, self.w_host, self.rows, self.K, qs[toks], d[toks], bs[toks],
-                                nthreads=ncores())
+        want, A = oracle.matvec(_oracle_qtype(oracle, self.fmt), self.w_host, self.rows, self.K, qs[toks], d[toks],
+                                bs[toks], nthreads=ncores())
         return bool(np.isfinite(got).all()) and close(got[toks], want, A)
 
 
 class MoEPrefill:
-    """512 tokens, top-2 of 8 Q4_K experts of 14336 x 4096: pack + qmatmul_prefill_moe."""
+    """512 tokens, top-2 of 8 Q4_K (or Q5_K) experts of 14336 x 4096: pack + qmatmul_prefill_moe."""
 
-    def __init__(self, q, torch, E=8, rows=14336, K=4096, T=512, topk=2, seed=7):
+    def __init__(self, q, torch, E=8, rows=14336, K=4096, T=512, topk=2, seed=7, fmt="q4k"):
         import synth
 
         self.q, self.torch, self.E, self.rows, self.K, self.T, self.topk = q, torch, E, rows, K, T, topk
+        self.fmt = fmt
+        self.qt, gen = _prefill_format(q, synth, fmt)
         g = np.random.default_rng(seed)
         dev = torch.device("cuda")
-        self.w_host = synth.q4k_weights(g, E * rows, K)
+        self.w_host = gen(g, E * rows, K)
         w0 = torch.from_numpy(self.w_host).to(dev)
         self.R = rotations(w0.numel())
         self.ws = [w0] + [w0.clone() for _ in range(self.R - 1)]
@@ -322,7 +331,7 @@ class MoEPrefill:
         self.rw = torch.from_numpy(self.rw_host).to(dev)
         self.xq = torch.empty(q.q8k_act_bytes(T, K), dtype=torch.uint8, device=dev)
         self.y = torch.empty(T * rows, dtype=torch.float32, device=dev)
-        self.ws_bytes = q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, E, rows, K, T, topk)
+        self.ws_bytes = q.qmatmul_prefill_moe_workspace_bytes(self.qt, E, rows, K, T, topk)
         self.wsp = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
         # useful int8 operations: every (token, slot) pair against its expert's rows
         self.ops = 2 * T * topk * rows * K
@@ -334,7 +343,7 @@ class MoEPrefill:
         self.main(i)
 
     def main(self, i):
-        self.q.qmatmul_prefill_moe(self.q.Q8K_Q4_K, self.ws[i % self.R], self.E, self.rows, self.K, self.xq, self.T,
+        self.q.qmatmul_prefill_moe(self.qt, self.ws[i % self.R], self.E, self.rows, self.K, self.xq, self.T,
                                    self.ids, self.rw, self.topk, self.y, self.wsp, self.ws_bytes)
 
     def parity(self):
@@ -345,8 +354,8 @@ class MoEPrefill:
         got = self.y.cpu().numpy().reshape(self.T, self.rows)
         qs, d, bs = oracle.q8k_pack(self.x_host)
         toks = np.array([0, 1, 200, self.T - 1])
-        want, A = oracle.moe(oracle.Q4_K, self.w_host, self.E, self.rows, self.K, qs[toks], d[toks], bs[toks],
-                             self.ids_host[toks], self.rw_host[toks], nthreads=ncores())
+        want, A = oracle.moe(_oracle_qtype(oracle, self.fmt), self.w_host, self.E, self.rows, self.K, qs[toks],
+                             d[toks], bs[toks], self.ids_host[toks], self.rw_host[toks], nthreads=ncores())
         return bool(np.isfinite(got).all()) and close(got[toks], want, A)
 
 
@@ -412,6 +421,8 @@ PROFILE_TARGETS = {
     "moe_q5k": "qmatvec_moe on the 8 x 14336x4096 Q5_K, 16-token top-2 workload",
     "prefill": "qmatmul_prefill on the 4096x14336 Q4_K, 512-token workload",
     "moe_prefill": "qmatmul_prefill_moe on the 8 x 14336x4096 Q4_K, 512-token top-2 workload",
+    "prefill_q5k": "qmatmul_prefill on the 4096x14336 Q5_K, 512-token workload",
+    "moe_prefill_q5k": "qmatmul_prefill_moe on the 8 x 14336x4096 Q5_K, 512-token top-2 workload",
     "pack": "q8k_pack of 512 x 14336 fp32 activations",
     "copy": "a plain 256 MiB device-to-device copy (torch), the counter calibration reference",
 }
@@ -434,6 +445,8 @@ def profile_run(q, torch, target, launches):
               "moe_q5k": lambda: MoE(q, torch, seed=6, fmt="q5k"),
               "prefill": lambda: Prefill(q, torch),
               "moe_prefill": lambda: MoEPrefill(q, torch),
+              "prefill_q5k": lambda: Prefill(q, torch, seed=8, fmt="q5k"),
+              "moe_prefill_q5k": lambda: MoEPrefill(q, torch, seed=9, fmt="q5k"),
               "pack": lambda: Prefill(q, torch)}[target]()
         wl.step(0)
         torch.cuda.synchronize()
@@ -547,28 +560,23 @@ def main():
         wl["moe_q5k_8x14336x4096_t16_top2"]["experts_hit"] = m.experts_hit
         del m
         torch.cuda.empty_cache()
-        log("workload: prefill_q4k_4096x14336_m512")
-        p = Prefill(q, torch)
-        ok = p.parity()
-        s, us = run_timed(torch, p, max(10, steps // 4), 3)
-        tops = p.ops / (us * 1e-6) / 1e12
-        wl["prefill_q4k_4096x14336_m512"] = {
-            "parity": "pass" if ok else "FAIL", "kernel_us": round(us, 2), "TOPS": round(tops, 1),
-            "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "step_ms": round(s * 1e3, 4),
-            "ops_per_launch": p.ops, "traffic": traffic_record("prefill_q4k")}
-        del p
-        torch.cuda.empty_cache()
-        log("workload: moe_prefill_q4k_8x14336x4096_t512_top2")
-        mp = MoEPrefill(q, torch)
-        ok = mp.parity()
-        s, us = run_timed(torch, mp, max(10, steps // 4), 3)
-        tops = mp.ops / (us * 1e-6) / 1e12
-        wl["moe_prefill_q4k_8x14336x4096_t512_top2"] = {
-            "parity": "pass" if ok else "FAIL", "kernel_us": round(us, 2), "TOPS": round(tops, 1),
-            "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "step_ms": round(s * 1e3, 4),
-            "ops_per_launch": mp.ops, "weight_copies_rotated": mp.R, "traffic": traffic_record("moe_prefill_q4k")}
-        del mp
-        torch.cuda.empty_cache()
+        for name, key, make in (
+                ("prefill_q4k_4096x14336_m512", "prefill_q4k", lambda: Prefill(q, torch)),
+                ("prefill_q5k_4096x14336_m512", "prefill_q5k", lambda: Prefill(q, torch, seed=8, fmt="q5k")),
+                ("moe_prefill_q4k_8x14336x4096_t512_top2", "moe_prefill_q4k", lambda: MoEPrefill(q, torch)),
+                ("moe_prefill_q5k_8x14336x4096_t512_top2", "moe_prefill_q5k",
+                 lambda: MoEPrefill(q, torch, seed=9, fmt="q5k"))):
+            log(f"workload: {name}")
+            p = make()
+            ok = p.parity()
+            s, us = run_timed(torch, p, max(10, steps // 4), 3)
+            tops = p.ops / (us * 1e-6) / 1e12
+            wl[name] = {
+                "parity": "pass" if ok else "FAIL", "kernel_us": round(us, 2), "TOPS": round(tops, 1),
+                "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "step_ms": round(s * 1e3, 4),
+                "ops_per_launch": p.ops, "weight_copies_rotated": p.R, "traffic": traffic_record(key)}
+            del p
+            torch.cuda.empty_cache()
         p = Prefill(q, torch)
         # q8_K pack of the 512 x 14336 batch, timed on its own
         gp = graph_of(torch, lambda i: q.q8k_pack(p.x, p.M, p.K, p.xq), 32)

@@ -140,8 +140,8 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
 
 /* qmatmul_prefill: y[m][n] = qmatvec's formula for every token m < M and
  * weight row n < rows, computed as a tiled int8 matrix-core GEMM.
- * qtype: Q8K_Q4_K (Q8K_Q5_K and Q8K_Q6_K_RELAID are refused with
- * Q8K_ERR_QTYPE: no prefill tile is built for them).  xq: q8_K buffer of M
+ * qtype: Q8K_Q4_K or Q8K_Q5_K (Q8K_Q6_K_RELAID is refused with
+ * Q8K_ERR_QTYPE: no Q6_K prefill tile is built).  xq: q8_K buffer of M
  * tokens.  y: fp32 [M][rows].
  * ws / ws_bytes: caller-owned workspace of at least
  * qmatmul_prefill_workspace_bytes(...) bytes (may be NULL when that is 0). */
@@ -155,10 +155,14 @@ int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const voi
  * Same weights, tokens, ids, router weights and result as qmatvec_moe,
  *   y[t][r] = sum_k rw[t][k] * (W_{ids[t][k]} x_t)[r],
  * for T tokens (0 <= T, T * K < 2^30) instead of at most 256.
- * qtype: Q8K_Q4_K.  1 <= topk <= min(E, Q8K_MOE_MAX_TOPK).  An id outside
- * [0, E) selects nothing.  ws / ws_bytes: caller-owned workspace of at least
- * qmatmul_prefill_moe_workspace_bytes(...) bytes (the fp32 result of every
- * (token, slot) pair), not overlapping y.  y: fp32 [T][rows]. */
+ * qtype: Q8K_Q4_K or Q8K_Q5_K.  1 <= E <= 4096;
+ * 1 <= topk <= min(E, Q8K_MOE_MAX_TOPK).  An id outside [0, E) selects
+ * nothing.  ws / ws_bytes: caller-owned workspace, 16-byte aligned, of at
+ * least qmatmul_prefill_moe_workspace_bytes(...) bytes, not overlapping y:
+ * the fp32 result of every (token, slot) pair, then the pairs grouped by
+ * expert and the chunk table (about 4 * T * topk * (rows + 1) bytes; 0 when
+ * T or rows is 0).  Its contents are scratch: stream-ordered calls may share
+ * one workspace, calls that overlap in time may not.  y: fp32 [T][rows]. */
 size_t qmatmul_prefill_moe_workspace_bytes(int qtype, int64_t E, int64_t rows, int64_t K, int64_t T, int32_t topk);
 int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq, int64_t T,
                         const int32_t* ids, const float* rw, int32_t topk, float* y, void* ws, size_t ws_bytes,

@@ -31,6 +31,7 @@ constexpr int64_t MAX_ROWS = (int64_t)1 << 30;
 constexpr int64_t MAX_K = (int64_t)1 << 24;
 constexpr int64_t MAX_TOKENS = (int64_t)1 << 24;
 constexpr int64_t MAX_EXPERTS = 4096;
+static_assert(MAX_EXPERTS <= MOE_GROUP_MAX_E, "the MoE prefill groups pairs of at most MOE_GROUP_MAX_E experts");
 
 // Every launch uses a 1-D grid of at most 2^31 - 1 workgroups.
 constexpr int64_t MAX_GRID = ((int64_t)1 << 31) - 1;
@@ -96,17 +97,17 @@ int launched(const char* fn, hipError_t e) {
     } while (0)
 
 // `decode`: the mat-vec family (Q4_K, Q5_K, relaid Q6_K); otherwise the
-// prefill tile (Q4_K only).
+// prefill tile (Q4_K, Q5_K).
 int check_weight(const char* fn, int qtype, const void* w, bool decode) {
-    if (qtype == Q8K_Q4_K || (decode && (qtype == Q8K_Q5_K || qtype == Q8K_Q6_K_RELAID)))
+    if (qtype == Q8K_Q4_K || qtype == Q8K_Q5_K || (decode && qtype == Q8K_Q6_K_RELAID))
         return check_ptr(fn, "w", w, 16);
     if (qtype == Q8K_Q6_K_GGUF)
         return fail(Q8K_ERR_QTYPE, "%s: raw GGUF Q6_K must be bound first (q8k_bind_q6k -> Q8K_Q6_K_RELAID)", fn);
-    if (!decode && (qtype == Q8K_Q5_K || qtype == Q8K_Q6_K_RELAID))
-        return fail(Q8K_ERR_QTYPE, "%s: no %s prefill tile is built (qmatvec_batched serves up to %d tokens)", fn,
-                    qtype == Q8K_Q5_K ? "Q5_K" : "Q6_K", Q8K_COLS_MAX);
+    if (!decode && qtype == Q8K_Q6_K_RELAID)
+        return fail(Q8K_ERR_QTYPE, "%s: no Q6_K prefill tile is built (qmatvec_batched serves up to %d tokens)", fn,
+                    Q8K_COLS_MAX);
     return fail(Q8K_ERR_QTYPE, "%s: qtype=%d not served here (use %s)", fn, qtype,
-                decode ? "Q8K_Q4_K=1, Q8K_Q6_K_RELAID=2 or Q8K_Q5_K=4" : "Q8K_Q4_K=1");
+                decode ? "Q8K_Q4_K=1, Q8K_Q6_K_RELAID=2 or Q8K_Q5_K=4" : "Q8K_Q4_K=1 or Q8K_Q5_K=4");
 }
 
 }  // namespace
@@ -255,13 +256,14 @@ int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const voi
     Q8K_TRY(check_grid(fn, ((rows + 31) / 32) * ((M + 63) / 64)));  // bound for every tile shape
     if (rows == 0 || M == 0) return Q8K_OK;
     const int nb = (int)(K / QK);
-    return launched(fn, launch_prefill_q4k(static_cast<const uint8_t*>(w), rows, nb, acts_of(xq, M, K), M, y,
-                                           (hipStream_t)stream));
+    return launched(fn, launch_prefill(qtype == Q8K_Q5_K, static_cast<const uint8_t*>(w), rows, nb, acts_of(xq, M, K),
+                                       M, y, (hipStream_t)stream));
 }
 
 size_t qmatmul_prefill_moe_workspace_bytes(int qtype, int64_t E, int64_t rows, int64_t K, int64_t T, int32_t topk) {
-    if (qtype != Q8K_Q4_K || E < 1 || rows < 0 || K <= 0 || K % QK != 0 || T < 0 || topk < 1) return 0;
-    return (size_t)T * (size_t)topk * (size_t)rows * sizeof(float);
+    if ((qtype != Q8K_Q4_K && qtype != Q8K_Q5_K) || E < 1 || rows < 0 || K <= 0 || K % QK != 0 || T < 0 || topk < 1)
+        return 0;
+    return (size_t)moe_prefill_ws(E, rows, T, topk).total;
 }
 
 int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq, int64_t T,
@@ -290,12 +292,13 @@ int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64
     if (ws_bytes < need)
         return fail(Q8K_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
     if (need > 0) Q8K_TRY(check_ptr(fn, "ws", ws, 16));
-    Q8K_TRY(check_grid(fn, E * ((rows + 63) / 64)));
+    Q8K_TRY(check_grid(fn, moe_prefill_ws(E, rows, T, topk).max_chunks * ((rows + 63) / 64)));
     Q8K_TRY(check_grid(fn, (T * rows + 255) / 256));
     if (rows == 0 || T == 0) return Q8K_OK;
     const int nb = (int)(K / QK);
-    return launched(fn, launch_prefill_moe_q4k(static_cast<const uint8_t*>(w), E, rows, nb, acts_of(xq, T, K), T, ids,
-                                               rw, topk, y, static_cast<float*>(ws), (hipStream_t)stream));
+    return launched(fn, launch_prefill_moe(qtype == Q8K_Q5_K, static_cast<const uint8_t*>(w), E, rows, nb,
+                                           acts_of(xq, T, K), T, ids, rw, topk, y, ws,
+                                           (hipStream_t)stream));
 }
 
 int q8k_debug_subblock_sums(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int32_t* S,

@@ -55,7 +55,21 @@ constexpr int PF_TM = 128;      // tokens per workgroup
 constexpr int PF_TN = 64;       // weight rows per workgroup
 constexpr int PF_LD = QK + 16;  // LDS row stride in bytes (bank spread)
 
-struct PrefillBuf {
+// Q5_K (a 5-bit quant q = l + 16h times a 6-bit scale does not split into
+// two int8 factors): the nibble l takes the two planes a*l and b*l as in
+// Q4_K, and the fifth bit h a third plane sc*h (<= 63), built by each
+// consumer in registers from the row's qh bytes and scales staged beside the
+// planes: I = 8 P_hi + P_lo + 16 P_h.
+template <bool Q5>
+struct PrefillQ5 {};
+template <>
+struct PrefillQ5<true> {
+    uint8_t qh[PF_TN][32];  // each row's fifth-bit plane (bit j of qh[l]: value l of sub-block j)
+    uint8_t sc[PF_TN][8];   // each row's sub-block scales
+};
+
+template <bool Q5>
+struct PrefillBuf : PrefillQ5<Q5> {
     int8_t whi[PF_TN * PF_LD];  // weight plane a*q
     int8_t wlo[PF_TN * PF_LD];  // weight plane b*q
     int8_t xa[PF_TM * PF_LD];   // token codes
@@ -64,9 +78,12 @@ struct PrefillBuf {
     uint16_t bj[PF_TN][16];     // dmin*m_j as bf16: [0..7] high, [8..15] low
     uint16_t aj[PF_TM][16];     // d8*bsum_j as bf16: [0..7] high, [8..15] low
 };
+template <bool Q5>
 struct PrefillSmem {
-    PrefillBuf buf[2];
+    PrefillBuf<Q5> buf[2];
 };
+template <bool Q5>
+constexpr int kblock() { return Q5 ? Q5K_BLOCK : Q4K_BLOCK; }
 
 // Four byte-wise products q_i * k (q_i <= 15, k <= 7: every product stays
 // inside its byte) as one packed 16-bit multiply.
@@ -118,6 +135,7 @@ __device__ __forceinline__ void lds_barrier() {
 //  * sub-block sums 4h..4h+3 (h = p&1) and the block scale of token p/2.
 struct PrefillRegs {
     uint4 hdr, q0, q1;
+    uint2 qh;  // Q5_K: qh bytes 8c..8c+7 of the row
     uint4 x[8];
     uint2 bsv;
     float d8;
@@ -135,11 +153,12 @@ struct PrefillSrc {
     int wo, xo[8], bso, d8o;
 };
 
+template <bool Q5>
 __device__ __forceinline__ void producer_src(PrefillSrc& S, const uint8_t* __restrict__ w, int64_t rows, int nb,
                                              const int8_t* __restrict__ qs, const float* __restrict__ d8,
                                              const int16_t* __restrict__ bs, int64_t K, int64_t M, int64_t n0,
                                              int64_t m0, int p) {
-    const int64_t wrow = (int64_t)nb * Q4K_BLOCK;
+    const int64_t wrow = (int64_t)nb * kblock<Q5>();
     S.w = w + n0 * wrow;
     S.x = qs + m0 * K;
     S.bs = bs + m0 * nb * 8;
@@ -161,11 +180,12 @@ __device__ __forceinline__ void producer_src(PrefillSrc& S, const uint8_t* __res
 // empty row).  An empty row's offsets point past every record, so its reads
 // return zeros.  Offsets stay 32-bit: T * K < 2^30 is checked by the caller.
 constexpr int PF_NONE = 0x7ffffff0;
+template <bool Q5>
 __device__ __forceinline__ void producer_src_gather(PrefillSrc& S, const uint8_t* __restrict__ w, int64_t rows,
                                                     int nb, const int8_t* __restrict__ qs,
                                                     const float* __restrict__ d8, const int16_t* __restrict__ bs,
                                                     int64_t K, int64_t T, int64_t n0, const int* tok, int p) {
-    const int64_t wrow = (int64_t)nb * Q4K_BLOCK;
+    const int64_t wrow = (int64_t)nb * kblock<Q5>();
     S.w = w + n0 * wrow;
     S.x = qs;
     S.bs = bs;
@@ -186,15 +206,17 @@ __device__ __forceinline__ void producer_src_gather(PrefillSrc& S, const uint8_t
     S.d8o = tb >= 0 ? tb * nb * 4 : PF_NONE;
 }
 
+template <bool Q5>
 __device__ __forceinline__ void producer_load(PrefillRegs& R, const PrefillSrc& S, int b, int p) {
-    const rsrc_t rw = make_rsrc(S.w + (int64_t)b * Q4K_BLOCK, S.wbytes - (int64_t)b * Q4K_BLOCK);
+    const rsrc_t rw = make_rsrc(S.w + (int64_t)b * kblock<Q5>(), S.wbytes - (int64_t)b * kblock<Q5>());
     const rsrc_t rx = make_rsrc(S.x + (int64_t)b * QK, S.xbytes - (int64_t)b * QK);
     const rsrc_t rb = make_rsrc(S.bs + (int64_t)b * 8, S.bsbytes - (int64_t)b * 16);
     const rsrc_t rd = make_rsrc(S.d8 + b, S.d8bytes - (int64_t)b * 4);
-    const int wq = S.wo + 32 * (p & 3);
+    const int wq = S.wo + (Q5 ? 48 : 16) + 32 * (p & 3);
     R.hdr = load16(rw, S.wo);
-    R.q0 = load16(rw, wq + 16);
-    R.q1 = load16(rw, wq + 32);
+    R.q0 = load16(rw, wq);
+    R.q1 = load16(rw, wq + 16);
+    if (Q5) R.qh = load8(rw, S.wo + 16 + 8 * (p & 3));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         R.x[i] = load16(rx, S.xo[i]);
@@ -202,7 +224,8 @@ __device__ __forceinline__ void producer_load(PrefillRegs& R, const PrefillSrc& 
     R.d8 = __builtin_bit_cast(float, load4(rd, S.d8o));
 }
 
-__device__ __forceinline__ void producer_store(const PrefillRegs& R, PrefillBuf& sm, int p) {
+template <bool Q5>
+__device__ __forceinline__ void producer_store(const PrefillRegs& R, PrefillBuf<Q5>& sm, int p) {
     // ---- weight planes and min-term operands of row p/4, sub-blocks 2c, 2c+1
     {
         const int r = p >> 2, c = p & 3;
@@ -239,6 +262,10 @@ __device__ __forceinline__ void producer_store(const PrefillRegs& R, PrefillBuf&
         *reinterpret_cast<uint32_t*>(&sm.bj[r][2 * c]) = h0 | (h1 << 16);
         *reinterpret_cast<uint32_t*>(&sm.bj[r][8 + 2 * c]) = l0 | (l1 << 16);
         if (c == 0) sm.dw[r] = half_bits_to_float(R.hdr.x & 0xffffu);
+        if constexpr (Q5) {
+            *reinterpret_cast<uint2*>(&sm.qh[r][8 * c]) = R.qh;
+            *reinterpret_cast<uint16_t*>(&sm.sc[r][2 * c]) = (uint16_t)(sc0 | (sc1 << 8));
+        }
     }
     // ---- token codes
     {
@@ -267,7 +294,8 @@ __device__ __forceinline__ void producer_store(const PrefillRegs& R, PrefillBuf&
 
 // ------------------------------------------------------------ consumers ----
 // Consumer wave: tokens tg0..tg0+63 (two MFMA tiles) x rows 32rg..32rg+31.
-__device__ __forceinline__ void consumer_block(const PrefillBuf& sm, int lane, int rg, int tg0, v16f (&accf)[2],
+template <bool Q5>
+__device__ __forceinline__ void consumer_block(const PrefillBuf<Q5>& sm, int lane, int rg, int tg0, v16f (&accf)[2],
                                                v16f (&accj)[2]) {
     const int kg = lane >> 5;
     const int nl = 32 * rg + (lane & 31);
@@ -275,7 +303,22 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf& sm, int lane, i
     const int8_t* bl = sm.wlo + nl * PF_LD + 16 * kg;
     const int8_t* a0p = sm.xa + (tg0 + (lane & 31)) * PF_LD + 16 * kg;
     const int8_t* a1p = a0p + 32 * PF_LD;
-    v16i ph[2], pl[2];
+    v16i ph[2], pl[2], pq[2];
+    // Q5_K: this lane's 16 values of each sub-block are positions 16kg..16kg+15,
+    // whose fifth bits are bit j of qh bytes 16kg..16kg+15
+    // (read from LDS at each use: keeping them in registers would spill the
+    // mixture-of-experts form)
+    auto hplane = [&](int j) {
+        v4i v = {0, 0, 0, 0};
+        if constexpr (Q5) {
+            const uint4 qhv = *reinterpret_cast<const uint4*>(&sm.qh[nl][16 * kg]);
+            const uint32_t scj = sm.sc[nl][j];
+            const uint32_t h[4] = {qhv.x, qhv.y, qhv.z, qhv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (int)mul_bytes(__builtin_rotateright32(h[i], j) & 0x01010101u, scj);
+        }
+        return v;
+    };
     {
         const v4i vh = *reinterpret_cast<const v4i*>(bh);
         const v4i vl = *reinterpret_cast<const v4i*>(bl);
@@ -286,6 +329,11 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf& sm, int lane, i
         pl[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, vl, z, 0, 0, 0);
         ph[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, vh, z, 0, 0, 0);
         pl[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, vl, z, 0, 0, 0);
+        if constexpr (Q5) {
+            const v4i vq = hplane(0);
+            pq[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, vq, z, 0, 0, 0);
+            pq[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, vq, z, 0, 0, 0);
+        }
     }
 #pragma unroll
     for (int j = 1; j < 8; ++j) {
@@ -297,6 +345,11 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf& sm, int lane, i
         pl[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, vl, pl[0], 0, 0, 0);
         ph[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, vh, ph[1], 0, 0, 0);
         pl[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, vl, pl[1], 0, 0, 0);
+        if constexpr (Q5) {
+            const v4i vq = hplane(j);
+            pq[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, vq, pq[0], 0, 0, 0);
+            pq[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, vq, pq[1], 0, 0, 0);
+        }
     }
     // min term: [ah | al] x [bh | bh] and [ah | al] x [bl | bl]; k-group 0 of
     // the token operand carries the high parts, k-group 1 the low parts
@@ -310,7 +363,7 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf& sm, int lane, i
             accj[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blv, accj[t], 0, 0, 0);
         }
     }
-    // block epilogue: acc += (d8 * float(8 P_hi + P_lo)) * d
+    // block epilogue: acc += (d8 * float(8 P_hi + P_lo (+ 16 P_h))) * d
     const float dd = sm.dw[nl];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -321,7 +374,8 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf& sm, int lane, i
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * g + i;
-                const float If = (float)((ph[t][r] << 3) + pl[t][r]);
+                const int I = (ph[t][r] << 3) + pl[t][r];
+                const float If = (float)(Q5 ? I + (pq[t][r] << 4) : I);
                 accf[t][r] = fmaf(If * d8a[i], dd, accf[t][r]);
             }
         }
@@ -331,9 +385,9 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf& sm, int lane, i
 // One 128-token x 64-row tile over all nb blocks.  The producers' sources are
 // in S (built by the caller); consumer output row m of the tile goes to
 // y[orow(m) * rows + n] when ok(m).
-template <class ORow, class OK>
-__device__ __forceinline__ void prefill_tile(PrefillSmem& sm, const PrefillSrc& S, int nb, int64_t rows, int64_t n0,
-                                             float* __restrict__ y, ORow orow, OK ok) {
+template <bool Q5, class ORow, class OK>
+__device__ __forceinline__ void prefill_tile(PrefillSmem<Q5>& sm, const PrefillSrc& S, int nb, int64_t rows,
+                                             int64_t n0, float* __restrict__ y, ORow orow, OK ok) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // Both roles run the same number of barriers: one before the first
     // block and one after each block (checked for every block count).
@@ -347,20 +401,20 @@ __device__ __forceinline__ void prefill_tile(PrefillSmem& sm, const PrefillSrc& 
         // have no records, so the reads return zeros without touching memory.
         // Branch-free loads keep the compiler's wait counts exact, so that a
         // store waits only for its own register set, two blocks old.
-        producer_load(RA, S, 0, p);
-        producer_load(RB, S, 1, p);
-        producer_store(RA, sm.buf[0], p);
-        producer_load(RA, S, 2, p);
+        producer_load<Q5>(RA, S, 0, p);
+        producer_load<Q5>(RB, S, 1, p);
+        producer_store<Q5>(RA, sm.buf[0], p);
+        producer_load<Q5>(RA, S, 2, p);
         lds_barrier();
         for (int b = 0; b < nb; b += 2) {
             // after block b is consumed: build block b+1 (RB), refill RB with b+3
-            if (b + 1 < nb) producer_store(RB, sm.buf[1], p);
-            producer_load(RB, S, b + 3, p);
+            if (b + 1 < nb) producer_store<Q5>(RB, sm.buf[1], p);
+            producer_load<Q5>(RB, S, b + 3, p);
             lds_barrier();
             if (b + 1 >= nb) break;
             // after block b+1 is consumed: build block b+2 (RA), refill RA with b+4
-            if (b + 2 < nb) producer_store(RA, sm.buf[0], p);
-            producer_load(RA, S, b + 4, p);
+            if (b + 2 < nb) producer_store<Q5>(RA, sm.buf[0], p);
+            producer_load<Q5>(RA, S, b + 4, p);
             lds_barrier();
         }
     } else {
@@ -373,7 +427,7 @@ __device__ __forceinline__ void prefill_tile(PrefillSmem& sm, const PrefillSrc& 
             for (int r = 0; r < 16; ++r) accf[i][r] = accj[i][r] = 0.0f;
         lds_barrier();
         for (int b = 0; b < nb; ++b) {
-            consumer_block(sm.buf[b & 1], lane, rg, tg0, accf, accj);
+            consumer_block<Q5>(sm.buf[b & 1], lane, rg, tg0, accf, accj);
             lds_barrier();
         }
         const int64_t n = n0 + 32 * rg + (lane & 31);
@@ -388,16 +442,17 @@ __device__ __forceinline__ void prefill_tile(PrefillSmem& sm, const PrefillSrc& 
     }
 }
 
+template <bool Q5>
 __global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
                                                           const int8_t* __restrict__ qs, const float* __restrict__ d8,
                                                           const int16_t* __restrict__ bs, int64_t K, int64_t M,
                                                           float* __restrict__ y) {
-    __shared__ __attribute__((aligned(16))) PrefillSmem sm;
+    __shared__ __attribute__((aligned(16))) PrefillSmem<Q5> sm;
     const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
     const int64_t n0 = ((int64_t)blockIdx.x % ntn) * PF_TN;
     const int64_t m0 = ((int64_t)blockIdx.x / ntn) * PF_TM;
     PrefillSrc S;
-    if (threadIdx.x >= 256) producer_src(S, w, rows, nb, qs, d8, bs, K, M, n0, m0, (int)threadIdx.x - 256);
+    if (threadIdx.x >= 256) producer_src<Q5>(S, w, rows, nb, qs, d8, bs, K, M, n0, m0, (int)threadIdx.x - 256);
     prefill_tile(
         sm, S, nb, rows, n0, y, [&](int m) { return m0 + m; }, [&](int m) { return m0 + m < M; });
 }
@@ -405,92 +460,112 @@ __global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restr
 // ----------------------------------------------------- mixture of experts ----
 // "Language models on the device", section 2.4: the prefill of an MoE layer
 // groups each expert's (token, slot) pairs into chunks and runs the prefill
-// tile per (expert, chunk), with a ragged last chunk.  Here workgroup
-// (e, row tile) walks the pairs in ascending order, collects the next 128
-// that chose expert e (a block-wide compaction of ids == e) and runs the
-// tile on them; pair p's dot products go to row p of the per-pair output
-// `out` [T * topk][rows].  A second kernel adds each token's pairs in slot
-// order: y[t][r] = sum_k rw[t][k] * out[t * topk + k][r], skipping ids
-// outside [0, E) (no workgroup writes those rows).
-struct MoeLists {
-    int tok[PF_TM];   // token of each tile row, -1 past the chunk's end
-    int pair[PF_TM];  // pair index of each tile row
-    int wcount[8];    // per-wave match counts of one 512-pair slab
-    int count, pos;   // pairs collected, next pair to examine
-};
+// tile per (expert, chunk), with a ragged last chunk.  Three launches:
+//   1. moe_group_kernel (one workgroup) counts the pairs of every expert,
+//      lists the pair indices grouped by expert in `order` and cuts each
+//      expert's run into chunks of at most 128 pairs (the chunk table);
+//   2. prefill_moe_q4k_kernel runs one prefill tile per (chunk, row tile):
+//      the chunk's tokens are gathered as the tile's 128 token rows and pair
+//      p's dot products go to row p of the per-pair output `out` [P][rows];
+//   3. moe_combine_kernel adds each token's pairs in slot order.
+// Within an expert the pairs may be listed in any order: every output
+// element is one row's own dot product, so the order changes no value.
 
-// Collect the next up-to-128 pairs p >= L.pos with ids[p] == e, in ascending
-// order.  Block-wide and barrier-synchronised; returns the count (uniform).
-__device__ __forceinline__ int moe_collect(MoeLists& L, const int32_t* __restrict__ ids, int64_t P, int64_t e,
-                                           int topk) {
+// Grouping of P pairs over E experts: pair counts and cursors in LDS.
+__global__ __launch_bounds__(1024) void moe_group_kernel(const int32_t* __restrict__ ids, int64_t P, int E,
+                                                         int32_t* __restrict__ nchunks, int4* __restrict__ chunks,
+                                                         int32_t* __restrict__ order) {
+    __shared__ int cnt[MOE_GROUP_MAX_E];
+    __shared__ int cur[MOE_GROUP_MAX_E];
+    __shared__ int wsum[16][2];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if (tid == 0) L.count = 0;
+    for (int e = tid; e < E; e += 1024) cnt[e] = 0;
     __syncthreads();
-    for (;;) {
-        const int count = L.count;
-        const int64_t pos = L.pos;
-        if (count >= PF_TM || pos >= P) break;  // uniform: read after a barrier
-        const int64_t p = pos + tid;
-        const bool m = p < P && ids[p] == (int32_t)e;
-        const uint64_t ball = __ballot(m);
-        const int below = __builtin_popcountll(ball & ((1ull << lane) - 1ull));
-        if (lane == 0) L.wcount[wv] = __builtin_popcountll(ball);
-        __syncthreads();
-        int before = 0, total = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = L.wcount[i];
-            before += i < wv ? c : 0;
-            total += c;
-        }
-        const int idx = count + before + below;
-        if (m && idx < PF_TM) {
-            L.tok[idx] = (int)(p / topk);
-            L.pair[idx] = (int)p;
-        }
-        __syncthreads();  // every thread has read count, pos and wcount
-        if (count + total <= PF_TM) {
-            if (tid == 0) {
-                L.count = count + total;
-                L.pos = pos + 512;
-            }
-        } else if (m && idx == PF_TM) {
-            // the first pair that did not fit: the next chunk starts there
-            L.count = PF_TM;
-            L.pos = p;
-        }
-        __syncthreads();
+    for (int64_t p = tid; p < P; p += 1024) {
+        const int32_t e = ids[p];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
-    const int count = L.count;
-    for (int i = count + (int)threadIdx.x; i < PF_TM; i += 512) L.tok[i] = -1;
     __syncthreads();
-    return count;
+    // Exclusive scans over experts of the pair counts and of the chunk counts
+    // ceil(cnt / 128); thread tid owns the experts [per * tid, per * tid + per).
+    const int per = (E + 1023) / 1024;
+    const int e0 = per * tid;
+    int sp = 0, sc = 0;
+    for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < E) {
+            sp += cnt[e];
+            sc += (cnt[e] + PF_TM - 1) / PF_TM;
+        }
+    }
+    int ip = sp, ic = sc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int tp = __shfl_up(ip, o), tc = __shfl_up(ic, o);
+        if (lane >= o) {
+            ip += tp;
+            ic += tc;
+        }
+    }
+    if (lane == 63) {
+        wsum[wv][0] = ip;
+        wsum[wv][1] = ic;
+    }
+    __syncthreads();
+    int pbase = ip - sp, cbase = ic - sc;
+    for (int i = 0; i < wv; ++i) {
+        pbase += wsum[i][0];
+        cbase += wsum[i][1];
+    }
+    for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < E) {
+            const int n = cnt[e];
+            cur[e] = pbase;
+            for (int c = 0; PF_TM * c < n; ++c)
+                chunks[cbase + c] = make_int4(e, pbase + PF_TM * c, min(PF_TM, n - PF_TM * c), 0);
+            pbase += n;
+            cbase += (n + PF_TM - 1) / PF_TM;
+        }
+    }
+    if (tid == 1023) *nchunks = cbase;  // the last thread ends on the total
+    __syncthreads();
+    for (int64_t p = tid; p < P; p += 1024) {
+        const int32_t e = ids[p];
+        if (e >= 0 && e < E) order[atomicAdd(&cur[e], 1)] = (int32_t)p;
+    }
 }
 
-__global__ __launch_bounds__(512) void prefill_moe_q4k_kernel(const uint8_t* __restrict__ w, int64_t E, int64_t rows,
-                                                              int nb, const int8_t* __restrict__ qs,
+template <bool Q5>
+__global__ __launch_bounds__(512) void prefill_moe_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
+                                                              const int8_t* __restrict__ qs,
                                                               const float* __restrict__ d8,
                                                               const int16_t* __restrict__ bs, int64_t K, int64_t T,
-                                                              const int32_t* __restrict__ ids, int topk,
+                                                              const int32_t* __restrict__ nchunks,
+                                                              const int4* __restrict__ chunks,
+                                                              const int32_t* __restrict__ order, int topk,
                                                               float* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) PrefillSmem sm;
-    __shared__ MoeLists L;
+    __shared__ __attribute__((aligned(16))) PrefillSmem<Q5> sm;
+    __shared__ int tok[PF_TM];   // token of each tile row, -1 past the chunk's end
+    __shared__ int pair[PF_TM];  // pair index of each tile row
     const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
-    const int64_t e = (int64_t)blockIdx.x / ntn;
+    const int64_t c = (int64_t)blockIdx.x / ntn;
+    if (c >= nchunks[0]) return;  // uniform: the grid covers the most chunks P pairs can make
     const int64_t n0 = ((int64_t)blockIdx.x % ntn) * PF_TN;
-    const uint8_t* we = w + e * rows * (int64_t)nb * Q4K_BLOCK;
-    const int64_t P = T * topk;
-    if (threadIdx.x == 0) L.pos = 0;
-    for (;;) {
-        const int count = moe_collect(L, ids, P, e, topk);
-        if (count == 0) break;  // uniform
-        PrefillSrc S;
-        if (threadIdx.x >= 256)
-            producer_src_gather(S, we, rows, nb, qs, d8, bs, K, T, n0, L.tok, (int)threadIdx.x - 256);
-        prefill_tile(
-            sm, S, nb, rows, n0, out, [&](int m) { return (int64_t)L.pair[m]; }, [&](int m) { return m < count; });
-        __syncthreads();  // the lists are rebuilt next
+    const int4 ch = chunks[c];
+    const int count = ch.z;
+    for (int i = threadIdx.x; i < PF_TM; i += 512) {
+        const int p = i < count ? order[ch.y + i] : -1;
+        pair[i] = p;
+        tok[i] = p < 0 ? -1 : p / topk;
     }
+    __syncthreads();
+    const uint8_t* we = w + (int64_t)ch.x * rows * (int64_t)nb * kblock<Q5>();
+    PrefillSrc S;
+    if (threadIdx.x >= 256)
+        producer_src_gather<Q5>(S, we, rows, nb, qs, d8, bs, K, T, n0, tok, (int)threadIdx.x - 256);
+    prefill_tile(
+        sm, S, nb, rows, n0, out, [&](int m) { return (int64_t)pair[m]; }, [&](int m) { return m < count; });
 }
 
 // y[t][r] = sum_k rw[t][k] * out[t * topk + k][r] over ids in [0, E), k ascending.
@@ -510,21 +585,37 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
     y[i] = s;
 }
 
-hipError_t launch_prefill_moe_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
-                                  const int32_t* ids, const float* rw, int topk, float* y, float* ws, hipStream_t s) {
+hipError_t launch_prefill_moe(bool q5, const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
+                              const int32_t* ids, const float* rw, int topk, float* y, void* ws, hipStream_t s) {
+    const MoePrefillWs L = moe_prefill_ws(E, rows, T, topk);
+    float* out = static_cast<float*>(ws);
+    int32_t* nchunks = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.meta);
+    int4* chunks = reinterpret_cast<int4*>(static_cast<char*>(ws) + L.chunks);
+    int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.order);
+    hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(1024), 0, s, ids, L.P, (int)E, nchunks, chunks, order);
     const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
-    hipLaunchKernelGGL(prefill_moe_q4k_kernel, dim3((unsigned)(E * ntn)), dim3(512), 0, s, w, E, rows, nb, a.qs, a.d,
-                       a.bs, a.K, T, ids, topk, ws);
+    const dim3 grid((unsigned)(L.max_chunks * ntn));
+    if (q5)
+        hipLaunchKernelGGL(prefill_moe_q4k_kernel<true>, grid, dim3(512), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K, T,
+                           nchunks, chunks, order, topk, out);
+    else
+        hipLaunchKernelGGL(prefill_moe_q4k_kernel<false>, grid, dim3(512), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K,
+                           T, nchunks, chunks, order, topk, out);
     const int64_t n = T * rows;
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws, rows, T, ids, rw,
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, out, rows, T, ids, rw,
                        topk, E, y);
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y, hipStream_t s) {
+hipError_t launch_prefill(bool q5, const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
+                          hipStream_t s) {
     const int64_t tiles = ((rows + PF_TN - 1) / PF_TN) * ((M + PF_TM - 1) / PF_TM);
-    hipLaunchKernelGGL(prefill_q4k_kernel, dim3((unsigned)tiles), dim3(512), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K,
-                       M, y);
+    if (q5)
+        hipLaunchKernelGGL(prefill_q4k_kernel<true>, dim3((unsigned)tiles), dim3(512), 0, s, w, rows, nb, a.qs, a.d,
+                           a.bs, a.K, M, y);
+    else
+        hipLaunchKernelGGL(prefill_q4k_kernel<false>, dim3((unsigned)tiles), dim3(512), 0, s, w, rows, nb, a.qs, a.d,
+                           a.bs, a.K, M, y);
     return hipGetLastError();
 }
 

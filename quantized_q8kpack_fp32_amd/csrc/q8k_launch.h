@@ -32,8 +32,35 @@ hipError_t launch_moe_q5k(const uint8_t* w, int64_t E, int64_t rows, int nb, Act
                           const float* rw, int topk, float* y, hipStream_t s);
 hipError_t launch_moe_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t E, int64_t rows, int nb, Acts a,
                           int64_t T, const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s);
-hipError_t launch_prefill_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y, hipStream_t s);
-hipError_t launch_prefill_moe_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
-                                  const int32_t* ids, const float* rw, int topk, float* y, float* ws, hipStream_t s);
+// Prefill tile for Q4_K (q5 = false) or Q5_K (q5 = true).
+hipError_t launch_prefill(bool q5, const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
+                          hipStream_t s);
+
+// Workspace of the MoE prefill, byte offsets from its start: the fp32 result
+// of every (token, slot) pair [P][rows]; then, 256-aligned, the chunk count
+// (int32, padded to 16 bytes), the chunk table (int4 {expert, first index in
+// order, count, 0} per chunk) and `order` (the P pair indices grouped by
+// expert).  P pairs over E experts make at most floor(P / 128) + min(E, P)
+// chunks of at most 128 pairs: each expert with n > 0 pairs makes
+// ceil(n / 128) <= floor(n / 128) + 1 of them.  No workspace is needed when
+// there are no pairs or no rows.
+constexpr int MOE_GROUP_MAX_E = 4096;  // most experts the grouping kernel counts in LDS
+struct MoePrefillWs {
+    int64_t P, max_chunks;
+    int64_t meta, chunks, order, total;
+};
+inline int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+inline MoePrefillWs moe_prefill_ws(int64_t E, int64_t rows, int64_t T, int64_t topk) {
+    MoePrefillWs L;
+    L.P = T * topk;
+    L.max_chunks = L.P / 128 + (E < L.P ? E : L.P);
+    L.meta = align256(L.P * rows * 4);
+    L.chunks = L.meta + 16;
+    L.order = L.chunks + 16 * L.max_chunks;
+    L.total = (L.P == 0 || rows == 0) ? 0 : align256(L.order + 4 * L.P);  // nothing is enqueued then
+    return L;
+}
+hipError_t launch_prefill_moe(bool q5, const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
+                              const int32_t* ids, const float* rw, int topk, float* y, void* ws, hipStream_t s);
 
 }  // namespace q8k

@@ -10,6 +10,7 @@ selection algorithm" (decline reasons, block alignment).
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -93,9 +94,11 @@ def test_qtype_refusals(q):
     msg = refused(q, "Q8K_ERR_QTYPE", q.qmatvec, q.Q8K_Q6_K_GGUF, A16, 4, 256, A16, A16, 0)
     assert "q8k_bind_q6k" in msg
     refused(q, "Q8K_ERR_QTYPE", q.qmatvec, 42, A16, 4, 256, A16, A16, 0)
-    refused(q, "Q8K_ERR_QTYPE", q.qmatmul_prefill, q.Q8K_Q6_K_RELAID, A16, 8, 256, A16, 4, A16, None, 0, 0)
-    msg = refused(q, "Q8K_ERR_QTYPE", q.qmatmul_prefill, q.Q8K_Q5_K, A16, 8, 256, A16, 4, A16, None, 0, 0)
-    assert "Q5_K" in msg
+    msg = refused(q, "Q8K_ERR_QTYPE", q.qmatmul_prefill, q.Q8K_Q6_K_RELAID, A16, 8, 256, A16, 4, A16, None, 0, 0)
+    assert "Q6_K" in msg
+    refused(q, "Q8K_ERR_QTYPE", q.qmatmul_prefill, q.Q8K_Q6_K_GGUF, A16, 8, 256, A16, 4, A16, None, 0, 0)
+    # Q5_K has a prefill tile: an empty call is accepted and enqueues nothing
+    q.qmatmul_prefill(q.Q8K_Q5_K, A16, 8, 256, A16, 0, A16, None, 0, 0)
 
 
 def test_batched_and_moe_arguments(q):
@@ -111,6 +114,38 @@ def test_batched_and_moe_arguments(q):
     refused(q, "Q8K_ERR_NULL", q.qmatvec_moe, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, None, A16, 2, A16, 0)
 
 
+def moe_prefill_ws_bytes(E, rows, T, topk):
+    """The documented MoE prefill workspace: fp32 per-pair results [P][rows],
+    then (256-aligned) a 16-byte chunk count, a 16-byte entry per possible
+    chunk and P int32 pair indices; P pairs over E experts make at most
+    P // 128 + min(E, P) chunks of at most 128 pairs."""
+    up = lambda b: -(-b // 256) * 256
+    P = T * topk
+    if P == 0 or rows == 0:
+        return 0
+    chunks = P // 128 + min(E, P)
+    return up(4 * P * rows) + up(16 + 16 * chunks + 4 * P)
+
+
+def test_moe_prefill_chunk_bound():
+    """The chunk bound P // 128 + min(E, P) holds for every split of P pairs
+    over E experts (ceil(n / 128) summed over the experts), and is reached;
+    brute force over small cases."""
+    import itertools
+
+    reached = False
+    for E in range(1, 4):
+        for P in range(0, 400, 43):
+            worst = 0
+            for cuts in itertools.combinations_with_replacement(range(P + 1), E - 1):
+                b = (0, *cuts, P)
+                worst = max(worst, sum(-(-(b[i + 1] - b[i]) // 128) for i in range(E)))
+            bound = P // 128 + min(E, P)
+            assert worst <= bound, (E, P, worst)
+            reached |= worst == bound
+    assert reached
+
+
 def test_prefill_moe_arguments(q):
     f = q.qmatmul_prefill_moe
     # E, topk, qtype, T*K, workspace
@@ -118,13 +153,21 @@ def test_prefill_moe_arguments(q):
     refused(q, "Q8K_ERR_ARG", f, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, A16, A16, 9, A16, A16, 1 << 20, 0)
     refused(q, "Q8K_ERR_ARG", f, q.Q8K_Q4_K, A16, 128, 4, 256, A16, 2, A16, A16, q.Q8K_MOE_MAX_TOPK + 1, A16,
             A16, 1 << 20, 0)
-    msg = refused(q, "Q8K_ERR_QTYPE", f, q.Q8K_Q5_K, A16, 8, 4, 256, A16, 16, A16, A16, 2, A16, A16, 1 << 20, 0)
-    assert "Q5_K" in msg
+    msg = refused(q, "Q8K_ERR_QTYPE", f, q.Q8K_Q6_K_RELAID, A16, 8, 4, 256, A16, 16, A16, A16, 2, A16, A16, 1 << 20,
+                  0)
+    assert "Q6_K" in msg
     msg = refused(q, "Q8K_ERR_SHAPE", f, q.Q8K_Q4_K, A16, 8, 4, 16384, A16, 1 << 16, A16, A16, 2, A16, A16,
                   1 << 40, 0)
     assert "2^30" in msg
     need = q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, 8, 4, 256, 16, 2)
-    assert need == 16 * 2 * 4 * 4
+    assert need == moe_prefill_ws_bytes(8, 4, 16, 2) == 1024
+    assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q5_K, 8, 4, 256, 16, 2) == need
+    # 512 tokens, top-2 of 8 experts of 14336 rows: the per-pair results dominate
+    assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, 8, 14336, 4096, 512, 2) == \
+        moe_prefill_ws_bytes(8, 14336, 512, 2)
+    assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, 4096, 8, 256, 3, 64) == moe_prefill_ws_bytes(4096, 8, 3, 64)
+    assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, 8, 4, 256, 0, 2) == 0
+    assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, 8, 0, 256, 16, 2) == 0
     refused(q, "Q8K_ERR_WORKSPACE", f, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, A16, A16, 2, A16, A16, need - 1, 0)
     refused(q, "Q8K_ERR_NULL", f, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, None, A16, 2, A16, A16, need, 0)
     assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q6_K_RELAID, 8, 4, 256, 16, 2) == 0

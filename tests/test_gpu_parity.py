@@ -328,36 +328,48 @@ def test_moe_crowded_expert_and_bad_ids(q):
 
 
 # ================================================================== MoE prefill (NEXT row)
-def moe_prefill_case(q, E, rows, K, T, topk, seed, ids=None):
+_PF_FMT = {"q4k": ("Q8K_Q4_K", oracle.Q4_K, synth.q4k_weights),
+           "q5k": ("Q8K_Q5_K", oracle.Q5_K, synth.q5k_weights)}
+
+
+def moe_prefill_case(q, E, rows, K, T, topk, seed, ids=None, fmt="q4k"):
+    qname, _, gen = _PF_FMT[fmt]
+    qt = getattr(q, qname)
     g = np.random.default_rng(seed)
-    w = synth.q4k_weights(g, E * rows, K)
+    w = gen(g, E * rows, K)
     x = synth.activations(g, T, K)
     r_ids, rw = synth.moe_routing(g, T, E, topk)
     if ids is None:
         ids = r_ids
     xq = pack_on_device(q, x)
     y = poisoned_f32(T, rows)
-    wsb = q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, E, rows, K, T, topk)
+    wsb = q.qmatmul_prefill_moe_workspace_bytes(qt, E, rows, K, T, topk)
     ws = poisoned(wsb)
-    q.qmatmul_prefill_moe(q.Q8K_Q4_K, to_dev(w), E, rows, K, xq, T, to_dev(ids.astype(np.int32)), to_dev(rw), topk,
-                          y, ws, wsb)
+    q.qmatmul_prefill_moe(qt, to_dev(w), E, rows, K, xq, T, to_dev(ids.astype(np.int32)), to_dev(rw), topk, y, ws,
+                          wsb)
     oqs, od, obs = oracle.q8k_pack(x)
     return host(y), w, oqs, od, obs, ids, rw
 
 
-@pytest.mark.parametrize("E,rows,K,T,topk,seed", [
-    (8, 512, 4096, 512, 2, 60),     # ~128 pairs per expert: one or two chunks each
-    (4, 130, 768, 37, 3, 61),       # ragged row tile, a few pairs per expert
-    (16, 64, 256, 200, 4, 62),      # many experts
-    (2, 96, 512, 1, 1, 63),         # one token
+@pytest.mark.parametrize("fmt,E,rows,K,T,topk,seed", [
+    ("q4k", 8, 512, 4096, 512, 2, 60),     # ~128 pairs per expert: one or two chunks each
+    ("q4k", 4, 130, 768, 37, 3, 61),       # ragged row tile, a few pairs per expert
+    ("q4k", 16, 64, 256, 200, 4, 62),      # many experts
+    ("q4k", 2, 96, 512, 1, 1, 63),         # one token
+    ("q4k", 300, 64, 256, 40, 8, 66),      # more experts than pairs: one-pair chunks
+    ("q4k", 2500, 8, 256, 64, 4, 73),      # more experts than grouping threads: several per thread
+    ("q5k", 8, 512, 4096, 512, 2, 67),
+    ("q5k", 4, 130, 768, 37, 3, 68),
+    ("q5k", 2, 96, 512, 1, 1, 69),
 ])
-def test_prefill_moe(q, E, rows, K, T, topk, seed):
-    got, w, oqs, od, obs, ids, rw = moe_prefill_case(q, E, rows, K, T, topk, seed)
-    want, A = oracle.moe(oracle.Q4_K, w, E, rows, K, oqs, od, obs, ids, rw, nthreads=NTH)
-    assert_close(got, want, A, f"moe prefill E={E} rows={rows} T={T}")
+def test_prefill_moe(q, fmt, E, rows, K, T, topk, seed):
+    got, w, oqs, od, obs, ids, rw = moe_prefill_case(q, E, rows, K, T, topk, seed, fmt=fmt)
+    want, A = oracle.moe(_PF_FMT[fmt][1], w, E, rows, K, oqs, od, obs, ids, rw, nthreads=NTH)
+    assert_close(got, want, A, f"moe prefill {fmt} E={E} rows={rows} T={T}")
 
 
-def test_prefill_moe_crowded_expert_and_bad_ids(q):
+@pytest.mark.parametrize("fmt", ["q4k", "q5k"])
+def test_prefill_moe_crowded_expert_and_bad_ids(q, fmt):
     """300 tokens all choose expert 0 first (three chunks, the last ragged);
     ids outside [0, E) select nothing."""
     E, rows, K, T, topk = 4, 100, 512, 300, 2
@@ -365,11 +377,20 @@ def test_prefill_moe_crowded_expert_and_bad_ids(q):
     ids = np.stack([np.zeros(T, np.int32), g.integers(1, E, T).astype(np.int32)], axis=1)
     ids[7, 1] = 9
     ids[11, 0] = -2
-    got, w, oqs, od, obs, ids, rw = moe_prefill_case(q, E, rows, K, T, topk, 64, ids=ids)
+    got, w, oqs, od, obs, ids, rw = moe_prefill_case(q, E, rows, K, T, topk, 64, ids=ids, fmt=fmt)
     ok = (ids >= 0) & (ids < E)
-    want, A = oracle.moe(oracle.Q4_K, w, E, rows, K, oqs, od, obs, np.where(ok, ids, 0),
+    want, A = oracle.moe(_PF_FMT[fmt][1], w, E, rows, K, oqs, od, obs, np.where(ok, ids, 0),
                          np.where(ok, rw, 0).astype(np.float32), nthreads=NTH)
-    assert_close(got, want, A, "moe prefill crowded")
+    assert_close(got, want, A, f"moe prefill crowded {fmt}")
+
+
+def test_prefill_moe_all_ids_out_of_range(q):
+    """No pair selects an expert: no chunk is made and y is all zeros."""
+    E, rows, K, T, topk = 4, 70, 256, 9, 2
+    ids = np.full((T, topk), 5, np.int32)
+    ids[0, 0] = -1
+    got, *_ = moe_prefill_case(q, E, rows, K, T, topk, 70, ids=ids)
+    assert np.array_equal(got, np.zeros((T, rows), np.float32))
 
 
 def test_prefill_moe_rows_equal_decode_moe(q):
@@ -388,47 +409,92 @@ def test_prefill_moe_rows_equal_decode_moe(q):
     assert_close(got, want, A, "prefill moe")
 
 
-# ================================================================== a7 prefill
-@pytest.mark.parametrize("M,rows,K,seed", [(1, 64, 256, 41), (17, 100, 512, 42), (64, 64, 256, 43),
-                                           (127, 256, 1024, 44), (200, 130, 768, 45), (65, 4096, 256, 46)])
-def test_prefill_full(q, M, rows, K, seed):
-    w = q4k(seed, rows, K)
-    x = acts(seed, M, K)
+# ================================================================== a7 prefill (+ Q5_K)
+def run_prefill(q, fmt, w, rows, K, x):
+    M = x.shape[0]
+    qt = getattr(q, _PF_FMT[fmt][0])
     xq = pack_on_device(q, x)
     y = poisoned_f32(M, rows)
-    ws_bytes = q.qmatmul_prefill_workspace_bytes(q.Q8K_Q4_K, rows, K, M)
+    ws_bytes = q.qmatmul_prefill_workspace_bytes(qt, rows, K, M)
     ws = poisoned(ws_bytes) if ws_bytes else None
-    q.qmatmul_prefill(q.Q8K_Q4_K, to_dev(w), rows, K, xq, M, y, ws, ws_bytes)
+    q.qmatmul_prefill(qt, to_dev(w), rows, K, xq, M, y, ws, ws_bytes)
+    return host(y)
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q5k"])
+@pytest.mark.parametrize("M,rows,K,seed", [(1, 64, 256, 41), (17, 100, 512, 42), (64, 64, 256, 43),
+                                           (127, 256, 1024, 44), (200, 130, 768, 45), (65, 4096, 256, 46)])
+def test_prefill_full(q, fmt, M, rows, K, seed):
+    w = _PF_FMT[fmt][2](np.random.default_rng(seed), rows, K)
+    x = acts(seed, M, K)
+    got = run_prefill(q, fmt, w, rows, K, x)
     oqs, od, obs = oracle.q8k_pack(x)
-    want, A = oracle.matvec(oracle.Q4_K, w, rows, K, oqs, od, obs, nthreads=NTH)
-    assert_close(host(y), want, A, f"prefill M={M} N={rows} K={K}")
+    want, A = oracle.matvec(_PF_FMT[fmt][1], w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(got, want, A, f"prefill {fmt} M={M} N={rows} K={K}")
 
 
-def test_prefill_down_projection_sampled(q):
+@pytest.mark.parametrize("fmt", ["q4k", "q5k"])
+def test_prefill_down_projection_sampled(q, fmt):
     """The 512-token x 4096-row x 14336 prefill: every output is finite and a
     sample of whole token rows and whole weight-row columns matches the oracle."""
     M, rows, K = 512, 4096, 14336
-    w = q4k(4, rows, K)
+    w = _PF_FMT[fmt][2](np.random.default_rng(4), rows, K)
     x = acts(4, M, K)
-    xq = pack_on_device(q, x)
-    y = poisoned_f32(M, rows)
-    ws_bytes = q.qmatmul_prefill_workspace_bytes(q.Q8K_Q4_K, rows, K, M)
-    ws = poisoned(ws_bytes) if ws_bytes else None
-    q.qmatmul_prefill(q.Q8K_Q4_K, to_dev(w), rows, K, xq, M, y, ws, ws_bytes)
-    got = host(y)
+    got = run_prefill(q, fmt, w, rows, K, x)
     assert np.isfinite(got).all()
+    ot = _PF_FMT[fmt][1]
     oqs, od, obs = oracle.q8k_pack(x)
     g = np.random.default_rng(123)
     toks = np.sort(g.choice(M, 6, replace=False))
     toks[0] = 0
     toks[-1] = M - 1
-    want, A = oracle.matvec(oracle.Q4_K, w, rows, K, oqs[toks], od[toks], obs[toks], nthreads=NTH)
-    assert_close(got[toks], want, A, "prefill token rows")
+    want, A = oracle.matvec(ot, w, rows, K, oqs[toks], od[toks], obs[toks], nthreads=NTH)
+    assert_close(got[toks], want, A, f"prefill {fmt} token rows")
     sel = np.sort(g.choice(rows, 24, replace=False))
     sel[-1] = rows - 1
     wsel = w.reshape(rows, -1)[sel].reshape(-1)
-    want, A = oracle.matvec(oracle.Q4_K, wsel, len(sel), K, oqs, od, obs, nthreads=NTH)
-    assert_close(got[:, sel], want, A, "prefill weight columns")
+    want, A = oracle.matvec(ot, wsel, len(sel), K, oqs, od, obs, nthreads=NTH)
+    assert_close(got[:, sel], want, A, f"prefill {fmt} weight columns")
+
+
+def test_prefill_q5k_largest_fields(q):
+    """Q5_K blocks at the top of every field (scales and mins 63, quants 31)
+    against tokens at +-127: the per-block integer sums reach their largest
+    magnitude, and every plane of the split scale is at its maximum."""
+    from gguf_pack import pack_q5k_block
+
+    rows, K, M = 64, 2048, 130
+    nb = K // 256
+    g = np.random.default_rng(71)
+    blocks = []
+    for r in range(rows * nb):
+        kind = r % 4
+        sc = np.full(8, 63) if kind < 2 else g.integers(0, 64, 8)
+        mn = np.full(8, 63) if kind in (0, 2) else g.integers(0, 64, 8)
+        qv = np.full(256, 31) if kind == 0 else g.integers(0, 32, 256)
+        blocks.append(pack_q5k_block(float(g.uniform(1e-3, 4e-3)), float(g.uniform(0, 8e-3)), sc, mn, qv))
+    w = np.concatenate(blocks)
+    x = np.where(g.random((M, K)) < 0.5, -1.0, 1.0).astype(np.float32) * 3.0
+    x[: M // 2] = np.abs(x[: M // 2])  # the first half: every value +3, so codes at +127
+    got = run_prefill(q, "q5k", w, rows, K, x)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(oracle.Q5_K, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(got, want, A, "prefill q5k largest fields")
+
+
+def test_prefill_q5k_without_fifth_bits_matches_q4k(q):
+    """A Q5_K weight with every qh byte zero gives the Q4_K prefill's outputs
+    on the same fields, bit for bit (the fifth-bit plane adds exact zeros)."""
+    rows, K, M = 130, 1024, 140
+    nb = K // 256
+    w4 = q4k(72, rows, K).reshape(rows * nb, 144)
+    w5 = np.zeros((rows * nb, 176), np.uint8)
+    w5[:, 0:16] = w4[:, 0:16]
+    w5[:, 48:176] = w4[:, 16:144]
+    x = acts(72, M, K)
+    y4 = run_prefill(q, "q4k", w4.reshape(-1), rows, K, x)
+    y5 = run_prefill(q, "q5k", w5.reshape(-1), rows, K, x)
+    assert np.array_equal(y4.view(np.uint32), y5.view(np.uint32))
 
 
 # ================================================================== empty inputs
