@@ -69,6 +69,8 @@ KERNEL_SOURCES = {
     "prefill_q4k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
     "moe_prefill_q4k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
     "prefill_q5k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
+    "prefill_q6k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
+    "moe_prefill_q6k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
     "moe_prefill_q5k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
     "pack": [_CS + "pack.hip", _CS + "q8k_device.h"],
 }
@@ -262,11 +264,22 @@ class MoE:
 
 
 def _prefill_format(q, synth, fmt):
-    return {"q4k": (q.Q8K_Q4_K, synth.q4k_weights), "q5k": (q.Q8K_Q5_K, synth.q5k_weights)}[fmt]
+    return {"q4k": (q.Q8K_Q4_K, synth.q4k_weights), "q5k": (q.Q8K_Q5_K, synth.q5k_weights),
+            "q6k": (q.Q8K_Q6_K_RELAID, synth.q6k_weights)}[fmt]
+
+
+def _device_weight(q, torch, fmt, w_host, nrows, K):
+    """GGUF blocks on the device in the form the kernels read (Q6_K: relaid at bind)."""
+    wg = torch.from_numpy(w_host).to(torch.device("cuda"))
+    if fmt != "q6k":
+        return wg
+    w0 = torch.empty(q.q8k_weight_bytes(q.Q8K_Q6_K_RELAID, nrows, K), dtype=torch.uint8, device=wg.device)
+    q.q8k_bind_q6k(wg, nrows, K, w0)
+    return w0
 
 
 class Prefill:
-    """512 tokens through q8k_pack + qmatmul_prefill against a 4096 x 14336 Q4_K (or Q5_K) weight."""
+    """512 tokens through q8k_pack + qmatmul_prefill against a 4096 x 14336 Q4_K (Q5_K, relaid Q6_K) weight."""
 
     def __init__(self, q, torch, rows=4096, K=14336, M=512, seed=4, fmt="q4k"):
         import synth
@@ -276,7 +289,7 @@ class Prefill:
         g = np.random.default_rng(seed)
         dev = torch.device("cuda")
         self.w_host = gen(g, rows, K)
-        w0 = torch.from_numpy(self.w_host).to(dev)
+        w0 = _device_weight(q, torch, fmt, self.w_host, rows, K)
         self.R = rotations(w0.numel())
         self.ws = [w0] + [w0.clone() for _ in range(self.R - 1)]
         self.x_host = synth.activations(g, M, K)
@@ -310,7 +323,7 @@ class Prefill:
 
 
 class MoEPrefill:
-    """512 tokens, top-2 of 8 Q4_K (or Q5_K) experts of 14336 x 4096: pack + qmatmul_prefill_moe."""
+    """512 tokens, top-2 of 8 Q4_K (Q5_K, relaid Q6_K) experts of 14336 x 4096: pack + qmatmul_prefill_moe."""
 
     def __init__(self, q, torch, E=8, rows=14336, K=4096, T=512, topk=2, seed=7, fmt="q4k"):
         import synth
@@ -321,7 +334,7 @@ class MoEPrefill:
         g = np.random.default_rng(seed)
         dev = torch.device("cuda")
         self.w_host = gen(g, E * rows, K)
-        w0 = torch.from_numpy(self.w_host).to(dev)
+        w0 = _device_weight(q, torch, fmt, self.w_host, E * rows, K)
         self.R = rotations(w0.numel())
         self.ws = [w0] + [w0.clone() for _ in range(self.R - 1)]
         self.x_host = synth.activations(g, T, K)
@@ -423,6 +436,8 @@ PROFILE_TARGETS = {
     "moe_prefill": "qmatmul_prefill_moe on the 8 x 14336x4096 Q4_K, 512-token top-2 workload",
     "prefill_q5k": "qmatmul_prefill on the 4096x14336 Q5_K, 512-token workload",
     "moe_prefill_q5k": "qmatmul_prefill_moe on the 8 x 14336x4096 Q5_K, 512-token top-2 workload",
+    "prefill_q6k": "qmatmul_prefill on the 4096x14336 relaid Q6_K, 512-token workload",
+    "moe_prefill_q6k": "qmatmul_prefill_moe on the 8 x 14336x4096 relaid Q6_K, 512-token top-2 workload",
     "pack": "q8k_pack of 512 x 14336 fp32 activations",
     "copy": "a plain 256 MiB device-to-device copy (torch), the counter calibration reference",
 }
@@ -447,6 +462,8 @@ def profile_run(q, torch, target, launches):
               "moe_prefill": lambda: MoEPrefill(q, torch),
               "prefill_q5k": lambda: Prefill(q, torch, seed=8, fmt="q5k"),
               "moe_prefill_q5k": lambda: MoEPrefill(q, torch, seed=9, fmt="q5k"),
+              "prefill_q6k": lambda: Prefill(q, torch, seed=10, fmt="q6k"),
+              "moe_prefill_q6k": lambda: MoEPrefill(q, torch, seed=11, fmt="q6k"),
               "pack": lambda: Prefill(q, torch)}[target]()
         wl.step(0)
         torch.cuda.synchronize()
@@ -563,9 +580,12 @@ def main():
         for name, key, make in (
                 ("prefill_q4k_4096x14336_m512", "prefill_q4k", lambda: Prefill(q, torch)),
                 ("prefill_q5k_4096x14336_m512", "prefill_q5k", lambda: Prefill(q, torch, seed=8, fmt="q5k")),
+                ("prefill_q6k_4096x14336_m512", "prefill_q6k", lambda: Prefill(q, torch, seed=10, fmt="q6k")),
                 ("moe_prefill_q4k_8x14336x4096_t512_top2", "moe_prefill_q4k", lambda: MoEPrefill(q, torch)),
                 ("moe_prefill_q5k_8x14336x4096_t512_top2", "moe_prefill_q5k",
-                 lambda: MoEPrefill(q, torch, seed=9, fmt="q5k"))):
+                 lambda: MoEPrefill(q, torch, seed=9, fmt="q5k")),
+                ("moe_prefill_q6k_8x14336x4096_t512_top2", "moe_prefill_q6k",
+                 lambda: MoEPrefill(q, torch, seed=11, fmt="q6k"))):
             log(f"workload: {name}")
             p = make()
             ok = p.parity()

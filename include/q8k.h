@@ -140,9 +140,9 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
 
 /* qmatmul_prefill: y[m][n] = qmatvec's formula for every token m < M and
  * weight row n < rows, computed as a tiled int8 matrix-core GEMM.
- * qtype: Q8K_Q4_K or Q8K_Q5_K (Q8K_Q6_K_RELAID is refused with
- * Q8K_ERR_QTYPE: no Q6_K prefill tile is built).  xq: q8_K buffer of M
- * tokens.  y: fp32 [M][rows].
+ * qtype: Q8K_Q4_K, Q8K_Q5_K or Q8K_Q6_K_RELAID (raw Q8K_Q6_K_GGUF is
+ * refused with Q8K_ERR_QTYPE: bind it first).  xq: q8_K buffer of M tokens.
+ * y: fp32 [M][rows].
  * ws / ws_bytes: caller-owned workspace of at least
  * qmatmul_prefill_workspace_bytes(...) bytes (may be NULL when that is 0). */
 size_t qmatmul_prefill_workspace_bytes(int qtype, int64_t rows, int64_t K, int64_t M);
@@ -155,7 +155,8 @@ int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const voi
  * Same weights, tokens, ids, router weights and result as qmatvec_moe,
  *   y[t][r] = sum_k rw[t][k] * (W_{ids[t][k]} x_t)[r],
  * for T tokens (0 <= T, T * K < 2^30) instead of at most 256.
- * qtype: Q8K_Q4_K or Q8K_Q5_K.  1 <= E <= 4096;
+ * qtype: Q8K_Q4_K, Q8K_Q5_K or Q8K_Q6_K_RELAID (w: E experts' weights
+ * bound as one E*rows-row matrix).  1 <= E <= 4096;
  * 1 <= topk <= min(E, Q8K_MOE_MAX_TOPK).  An id outside [0, E) selects
  * nothing.  ws / ws_bytes: caller-owned workspace, 16-byte aligned, of at
  * least qmatmul_prefill_moe_workspace_bytes(...) bytes, not overlapping y:

@@ -46,6 +46,13 @@ if not os.path.exists(LIB_PATH):
         "(python -m quantized_q8kpack_fp32_amd.build or __graft_entry__.build())"
     )
 
+# torch first: its HIP runtime carries the same soname (libamdhip64.so.7) as
+# the ROCm copy libq8k.so was linked against, so once torch has loaded it the
+# library binds to that same runtime.  Loaded the other way round, torch
+# would bring a second HIP runtime into the process, and the library's
+# launches would not see the device that torch's tensors live on.
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64

@@ -96,18 +96,27 @@ int launched(const char* fn, hipError_t e) {
         if (_st != Q8K_OK) return _st; \
     } while (0)
 
-// `decode`: the mat-vec family (Q4_K, Q5_K, relaid Q6_K); otherwise the
-// prefill tile (Q4_K, Q5_K).
-int check_weight(const char* fn, int qtype, const void* w, bool decode) {
-    if (qtype == Q8K_Q4_K || qtype == Q8K_Q5_K || (decode && qtype == Q8K_Q6_K_RELAID))
-        return check_ptr(fn, "w", w, 16);
+// Every operation serves Q4_K, Q5_K and relaid Q6_K weights.
+int check_weight(const char* fn, int qtype, const void* w) {
+    if (qtype == Q8K_Q4_K || qtype == Q8K_Q5_K || qtype == Q8K_Q6_K_RELAID) return check_ptr(fn, "w", w, 16);
     if (qtype == Q8K_Q6_K_GGUF)
         return fail(Q8K_ERR_QTYPE, "%s: raw GGUF Q6_K must be bound first (q8k_bind_q6k -> Q8K_Q6_K_RELAID)", fn);
-    if (!decode && qtype == Q8K_Q6_K_RELAID)
-        return fail(Q8K_ERR_QTYPE, "%s: no Q6_K prefill tile is built (qmatvec_batched serves up to %d tokens)", fn,
-                    Q8K_COLS_MAX);
-    return fail(Q8K_ERR_QTYPE, "%s: qtype=%d not served here (use %s)", fn, qtype,
-                decode ? "Q8K_Q4_K=1, Q8K_Q6_K_RELAID=2 or Q8K_Q5_K=4" : "Q8K_Q4_K=1 or Q8K_Q5_K=4");
+    return fail(Q8K_ERR_QTYPE, "%s: qtype=%d not served here (use Q8K_Q4_K=1, Q8K_Q6_K_RELAID=2 or Q8K_Q5_K=4)", fn,
+                qtype);
+}
+
+// The prefill tile's format index and weight streams (Q6_K: bodies and prefix).
+struct PrefillWeights {
+    int fmt;
+    const uint8_t* w;
+    const uint16_t* prefix;
+};
+PrefillWeights prefill_weights(int qtype, const void* w, int64_t nblocks) {
+    if (qtype == Q8K_Q6_K_RELAID) {
+        const Q6View v = q6_view(w, nblocks);
+        return PrefillWeights{PREFILL_Q6_K, v.bodies, v.prefix};
+    }
+    return PrefillWeights{qtype == Q8K_Q5_K ? PREFILL_Q5_K : PREFILL_Q4_K, static_cast<const uint8_t*>(w), nullptr};
 }
 
 }  // namespace
@@ -169,7 +178,7 @@ static int matvec_common(const char* fn, int qtype, const void* w, int64_t rows,
                          int64_t ncols, float* y, void* stream) {
     Q8K_TRY(check_k(fn, K));
     Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
-    Q8K_TRY(check_weight(fn, qtype, w, true));
+    Q8K_TRY(check_weight(fn, qtype, w));
     Q8K_TRY(check_ptr(fn, "xq", xq, 16));
     Q8K_TRY(check_ptr(fn, "y", y, 4));
     if (rows == 0) return Q8K_OK;
@@ -212,7 +221,7 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
     if (topk < 1 || topk > E || topk > Q8K_MOE_MAX_TOPK)
         return fail(Q8K_ERR_ARG, "%s: topk=%d must be in [1, min(E=%lld, %d)]", fn, topk, (long long)E,
                     Q8K_MOE_MAX_TOPK);
-    Q8K_TRY(check_weight(fn, qtype, w, true));
+    Q8K_TRY(check_weight(fn, qtype, w));
     Q8K_TRY(check_ptr(fn, "xq", xq, 16));
     Q8K_TRY(check_ptr(fn, "ids", ids, 4));
     Q8K_TRY(check_ptr(fn, "rw", rw, 4));
@@ -246,7 +255,7 @@ int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const voi
     Q8K_TRY(check_k(fn, K));
     Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
     Q8K_TRY(check_count(fn, "M", M, MAX_TOKENS));
-    Q8K_TRY(check_weight(fn, qtype, w, false));
+    Q8K_TRY(check_weight(fn, qtype, w));
     Q8K_TRY(check_ptr(fn, "xq", xq, 16));
     Q8K_TRY(check_ptr(fn, "y", y, 4));
     const size_t need = qmatmul_prefill_workspace_bytes(qtype, rows, K, M);
@@ -256,12 +265,14 @@ int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const voi
     Q8K_TRY(check_grid(fn, ((rows + 31) / 32) * ((M + 63) / 64)));  // bound for every tile shape
     if (rows == 0 || M == 0) return Q8K_OK;
     const int nb = (int)(K / QK);
-    return launched(fn, launch_prefill(qtype == Q8K_Q5_K, static_cast<const uint8_t*>(w), rows, nb, acts_of(xq, M, K),
-                                       M, y, (hipStream_t)stream));
+    const PrefillWeights pw = prefill_weights(qtype, w, rows * nb);
+    return launched(fn, launch_prefill(pw.fmt, pw.w, pw.prefix, rows, nb, acts_of(xq, M, K), M, y,
+                                       (hipStream_t)stream));
 }
 
 size_t qmatmul_prefill_moe_workspace_bytes(int qtype, int64_t E, int64_t rows, int64_t K, int64_t T, int32_t topk) {
-    if ((qtype != Q8K_Q4_K && qtype != Q8K_Q5_K) || E < 1 || rows < 0 || K <= 0 || K % QK != 0 || T < 0 || topk < 1)
+    if ((qtype != Q8K_Q4_K && qtype != Q8K_Q5_K && qtype != Q8K_Q6_K_RELAID) || E < 1 || rows < 0 || K <= 0 ||
+        K % QK != 0 || T < 0 || topk < 1)
         return 0;
     return (size_t)moe_prefill_ws(E, rows, T, topk).total;
 }
@@ -283,7 +294,7 @@ int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64
     if (topk < 1 || topk > E || topk > Q8K_MOE_MAX_TOPK)
         return fail(Q8K_ERR_ARG, "%s: topk=%d must be in [1, min(E=%lld, %d)]", fn, topk, (long long)E,
                     Q8K_MOE_MAX_TOPK);
-    Q8K_TRY(check_weight(fn, qtype, w, false));
+    Q8K_TRY(check_weight(fn, qtype, w));
     Q8K_TRY(check_ptr(fn, "xq", xq, 16));
     Q8K_TRY(check_ptr(fn, "ids", ids, 4));
     Q8K_TRY(check_ptr(fn, "rw", rw, 4));
@@ -296,9 +307,9 @@ int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64
     Q8K_TRY(check_grid(fn, (T * rows + 255) / 256));
     if (rows == 0 || T == 0) return Q8K_OK;
     const int nb = (int)(K / QK);
-    return launched(fn, launch_prefill_moe(qtype == Q8K_Q5_K, static_cast<const uint8_t*>(w), E, rows, nb,
-                                           acts_of(xq, T, K), T, ids, rw, topk, y, ws,
-                                           (hipStream_t)stream));
+    const PrefillWeights pw = prefill_weights(qtype, w, E * rows * nb);
+    return launched(fn, launch_prefill_moe(pw.fmt, pw.w, pw.prefix, E, rows, nb, acts_of(xq, T, K), T, ids, rw, topk,
+                                           y, ws, (hipStream_t)stream));
 }
 
 int q8k_debug_subblock_sums(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int32_t* S,
@@ -306,7 +317,7 @@ int q8k_debug_subblock_sums(int qtype, const void* w, int64_t rows, int64_t K, c
     const char* fn = "q8k_debug_subblock_sums";
     Q8K_TRY(check_k(fn, K));
     Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
-    Q8K_TRY(check_weight(fn, qtype, w, true));
+    Q8K_TRY(check_weight(fn, qtype, w));
     Q8K_TRY(check_ptr(fn, "xq", xq, 16));
     Q8K_TRY(check_ptr(fn, "S", S, 4));
     if (rows == 0) return Q8K_OK;

@@ -36,6 +36,13 @@
 // one barrier per block hands the buffers over.  The planes of a weight tile
 // are built once per workgroup, i.e. once per 128 tokens.
 //
+// Q6_K (relaid: fp16 d in a prefix, 208-byte body).  The value weight is
+// w = sc * (q - 32) with a signed 8-bit scale, an integer in [-4064, 4096]
+// that no product of two int8 factors covers.  The producers compute w in
+// 16-bit lanes (one packed multiply-add per two values) and stage its two
+// base-128 digits as the planes: w1 = w >> 7 in [-32, 32] and w0 = w & 127,
+// so I_b = 128 P_1 + P_0 exactly.  Q6_K has no min term.
+//
 // MFMA operand map (verified on gfx950): 32x32x32 int8 and 32x32x16 bf16 take
 // row l % 32 of A and column l % 32 of B from lane l, k-group l / 32; result
 // (i, j) is in lane j + 32 * ((i / 4) % 2), register (i % 4) + 4 * (i / 8).
@@ -60,30 +67,42 @@ constexpr int PF_LD = QK + 16;  // LDS row stride in bytes (bank spread)
 // Q4_K, and the fifth bit h a third plane sc*h (<= 63), built by each
 // consumer in registers from the row's qh bytes and scales staged beside the
 // planes: I = 8 P_hi + P_lo + 16 P_h.
-template <bool Q5>
+// Weight formats of the tile.
+constexpr int PF_Q4 = PREFILL_Q4_K, PF_Q5 = PREFILL_Q5_K, PF_Q6 = PREFILL_Q6_K;
+
+template <int F>
 struct PrefillQ5 {};
 template <>
-struct PrefillQ5<true> {
+struct PrefillQ5<PF_Q5> {
     uint8_t qh[PF_TN][32];  // each row's fifth-bit plane (bit j of qh[l]: value l of sub-block j)
     uint8_t sc[PF_TN][8];   // each row's sub-block scales
 };
+template <int F>
+struct PrefillMin {
+    uint16_t bj[PF_TN][16];  // dmin*m_j as bf16: [0..7] high, [8..15] low
+    uint16_t aj[PF_TM][16];  // d8*bsum_j as bf16: [0..7] high, [8..15] low
+};
+template <>
+struct PrefillMin<PF_Q6> {};  // Q6_K has no min term
 
-template <bool Q5>
-struct PrefillBuf : PrefillQ5<Q5> {
-    int8_t whi[PF_TN * PF_LD];  // weight plane a*q
-    int8_t wlo[PF_TN * PF_LD];  // weight plane b*q
+struct PrefillCore {
+    int8_t whi[PF_TN * PF_LD];  // weight plane a*q (Q6_K: w >> 7)
+    int8_t wlo[PF_TN * PF_LD];  // weight plane b*q (Q6_K: w & 127)
     int8_t xa[PF_TM * PF_LD];   // token codes
     float dw[PF_TN];            // row block scale d
     float d8[PF_TM];            // token block scale
-    uint16_t bj[PF_TN][16];     // dmin*m_j as bf16: [0..7] high, [8..15] low
-    uint16_t aj[PF_TM][16];     // d8*bsum_j as bf16: [0..7] high, [8..15] low
 };
-template <bool Q5>
+// Bases are laid out in order: the planes and codes first, then the format's
+// extra arrays.
+template <int F>
+struct PrefillBuf : PrefillCore, PrefillMin<F>, PrefillQ5<F> {};
+template <int F>
 struct PrefillSmem {
-    PrefillBuf<Q5> buf[2];
+    PrefillBuf<F> buf[2];
 };
-template <bool Q5>
-constexpr int kblock() { return Q5 ? Q5K_BLOCK : Q4K_BLOCK; }
+// Bytes per (row, block) in the weight stream the tile reads (Q6_K: the body).
+template <int F>
+constexpr int kblock() { return F == PF_Q5 ? Q5K_BLOCK : F == PF_Q6 ? Q6K_BODY : Q4K_BLOCK; }
 
 // Four byte-wise products q_i * k (q_i <= 15, k <= 7: every product stays
 // inside its byte) as one packed 16-bit multiply.
@@ -133,9 +152,14 @@ __device__ __forceinline__ void lds_barrier() {
 //    i = 0..7, at byte 16(l&15) of the block: one load instruction of a wave
 //    reads four tokens' 256 contiguous code bytes;
 //  * sub-block sums 4h..4h+3 (h = p&1) and the block scale of token p/2.
+//  Q6_K: row p/4, quarter c = p&3 (h = c>>1, t = c&1): ql bytes
+//    64h+32t..+31 (values 128h+32t+l and 128h+32t+64+l), qh bytes 32h..32h+31,
+//    scale bytes 8h..8h+7 and the row's d; no sub-block sums (no min term).
 struct PrefillRegs {
     uint4 hdr, q0, q1;
-    uint2 qh;  // Q5_K: qh bytes 8c..8c+7 of the row
+    uint2 qh;   // Q5_K: qh bytes 8c..8c+7 of the row; Q6_K: scale bytes 8h..8h+7
+    uint4 qh2;  // Q6_K: qh bytes 32h+16..32h+31 (hdr holds 32h..32h+15)
+    uint32_t dq;  // Q6_K: the row's fp16 d
     uint4 x[8];
     uint2 bsv;
     float d8;
@@ -146,29 +170,43 @@ struct PrefillRegs {
 // range check "offset < records" is exactly "inside the problem".
 struct PrefillSrc {
     const uint8_t* w;
+    const uint16_t* pf;  // Q6_K: the fp16 d prefix
     const int8_t* x;
     const int16_t* bs;
     const float* d8;
-    int64_t wbytes, xbytes, bsbytes, d8bytes;  // bytes from the tile's first row/token to the end
-    int wo, xo[8], bso, d8o;
+    int64_t wbytes, pfbytes, xbytes, bsbytes, d8bytes;  // bytes from the tile's first row/token to the end
+    int wo, pfo, xo[8], bso, d8o;
 };
 
-template <bool Q5>
-__device__ __forceinline__ void producer_src(PrefillSrc& S, const uint8_t* __restrict__ w, int64_t rows, int nb,
+template <int F>
+__device__ __forceinline__ void producer_src_weights(PrefillSrc& S, const uint8_t* __restrict__ w,
+                                                     const uint16_t* __restrict__ prefix, int64_t rows, int nb,
+                                                     int64_t n0, int p) {
+    const int64_t wrow = (int64_t)nb * kblock<F>();
+    S.w = w + n0 * wrow;
+    S.wbytes = (rows - n0) * wrow;
+    S.wo = (p >> 2) * (int)wrow;
+    if constexpr (F == PF_Q6) {
+        S.pf = prefix + n0 * nb;
+        S.pfbytes = (rows - n0) * nb * 2;
+        S.pfo = (p >> 2) * nb * 2;
+    }
+}
+
+template <int F>
+__device__ __forceinline__ void producer_src(PrefillSrc& S, const uint8_t* __restrict__ w,
+                                             const uint16_t* __restrict__ prefix, int64_t rows, int nb,
                                              const int8_t* __restrict__ qs, const float* __restrict__ d8,
                                              const int16_t* __restrict__ bs, int64_t K, int64_t M, int64_t n0,
                                              int64_t m0, int p) {
-    const int64_t wrow = (int64_t)nb * kblock<Q5>();
-    S.w = w + n0 * wrow;
+    producer_src_weights<F>(S, w, prefix, rows, nb, n0, p);
     S.x = qs + m0 * K;
     S.bs = bs + m0 * nb * 8;
     S.d8 = d8 + m0 * nb;
-    S.wbytes = (rows - n0) * wrow;
     S.xbytes = (M - m0) * K;
     S.bsbytes = (M - m0) * nb * 16;
     S.d8bytes = (M - m0) * nb * 4;
     const int wv = p >> 6, l = p & 63;
-    S.wo = (p >> 2) * (int)wrow;
 #pragma unroll
     for (int i = 0; i < 8; ++i) S.xo[i] = (16 * i + 4 * wv + (l >> 4)) * (int)K + 16 * (l & 15);
     S.bso = (p >> 1) * nb * 16 + 8 * (p & 1);
@@ -180,22 +218,20 @@ __device__ __forceinline__ void producer_src(PrefillSrc& S, const uint8_t* __res
 // empty row).  An empty row's offsets point past every record, so its reads
 // return zeros.  Offsets stay 32-bit: T * K < 2^30 is checked by the caller.
 constexpr int PF_NONE = 0x7ffffff0;
-template <bool Q5>
-__device__ __forceinline__ void producer_src_gather(PrefillSrc& S, const uint8_t* __restrict__ w, int64_t rows,
-                                                    int nb, const int8_t* __restrict__ qs,
-                                                    const float* __restrict__ d8, const int16_t* __restrict__ bs,
-                                                    int64_t K, int64_t T, int64_t n0, const int* tok, int p) {
-    const int64_t wrow = (int64_t)nb * kblock<Q5>();
-    S.w = w + n0 * wrow;
+template <int F>
+__device__ __forceinline__ void producer_src_gather(PrefillSrc& S, const uint8_t* __restrict__ w,
+                                                    const uint16_t* __restrict__ prefix, int64_t rows, int nb,
+                                                    const int8_t* __restrict__ qs, const float* __restrict__ d8,
+                                                    const int16_t* __restrict__ bs, int64_t K, int64_t T, int64_t n0,
+                                                    const int* tok, int p) {
+    producer_src_weights<F>(S, w, prefix, rows, nb, n0, p);
     S.x = qs;
     S.bs = bs;
     S.d8 = d8;
-    S.wbytes = (rows - n0) * wrow;
     S.xbytes = T * K;
     S.bsbytes = T * nb * 16;
     S.d8bytes = T * nb * 4;
     const int wv = p >> 6, l = p & 63;
-    S.wo = (p >> 2) * (int)wrow;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int t = tok[16 * i + 4 * wv + (l >> 4)];
@@ -206,28 +242,91 @@ __device__ __forceinline__ void producer_src_gather(PrefillSrc& S, const uint8_t
     S.d8o = tb >= 0 ? tb * nb * 4 : PF_NONE;
 }
 
-template <bool Q5>
+template <int F>
 __device__ __forceinline__ void producer_load(PrefillRegs& R, const PrefillSrc& S, int b, int p) {
-    const rsrc_t rw = make_rsrc(S.w + (int64_t)b * kblock<Q5>(), S.wbytes - (int64_t)b * kblock<Q5>());
+    constexpr bool Q5 = F == PF_Q5;
+    const rsrc_t rw = make_rsrc(S.w + (int64_t)b * kblock<F>(), S.wbytes - (int64_t)b * kblock<F>());
     const rsrc_t rx = make_rsrc(S.x + (int64_t)b * QK, S.xbytes - (int64_t)b * QK);
-    const rsrc_t rb = make_rsrc(S.bs + (int64_t)b * 8, S.bsbytes - (int64_t)b * 16);
     const rsrc_t rd = make_rsrc(S.d8 + b, S.d8bytes - (int64_t)b * 4);
-    const int wq = S.wo + (Q5 ? 48 : 16) + 32 * (p & 3);
-    R.hdr = load16(rw, S.wo);
-    R.q0 = load16(rw, wq);
-    R.q1 = load16(rw, wq + 16);
-    if (Q5) R.qh = load8(rw, S.wo + 16 + 8 * (p & 3));
+    if constexpr (F == PF_Q6) {
+        const rsrc_t rp = make_rsrc(S.pf + b, S.pfbytes - (int64_t)b * 2);
+        const int c = p & 3, h = c >> 1;
+        R.q0 = load16(rw, S.wo + 64 * h + 32 * (c & 1));
+        R.q1 = load16(rw, S.wo + 64 * h + 32 * (c & 1) + 16);
+        R.hdr = load16(rw, S.wo + 128 + 32 * h);
+        R.qh2 = load16(rw, S.wo + 128 + 32 * h + 16);
+        R.qh = load8(rw, S.wo + 192 + 8 * h);
+        R.dq = load2(rp, S.pfo);
+    } else {
+        const int wq = S.wo + (Q5 ? 48 : 16) + 32 * (p & 3);
+        R.hdr = load16(rw, S.wo);
+        R.q0 = load16(rw, wq);
+        R.q1 = load16(rw, wq + 16);
+        if (Q5) R.qh = load8(rw, S.wo + 16 + 8 * (p & 3));
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         R.x[i] = load16(rx, S.xo[i]);
-    R.bsv = load8(rb, S.bso);
+    if constexpr (F != PF_Q6) {
+        const rsrc_t rb = make_rsrc(S.bs + (int64_t)b * 8, S.bsbytes - (int64_t)b * 16);
+        R.bsv = load8(rb, S.bso);
+    }
     R.d8 = __builtin_bit_cast(float, load4(rd, S.d8o));
 }
 
-template <bool Q5>
-__device__ __forceinline__ void producer_store(const PrefillRegs& R, PrefillBuf<Q5>& sm, int p) {
-    // ---- weight planes and min-term operands of row p/4, sub-blocks 2c, 2c+1
-    {
+// Q6_K: the two base-128 digit planes of w = sc * (q - 32) for four values
+// q (bytes of q4, each 0..63) sharing one signed scale sc.  The values go to
+// 16-bit lanes in pairs (bytes 0, 2 and bytes 1, 3), one packed multiply-add
+// per pair forms w, and byte permutes put the four digits back in order.
+__device__ __forceinline__ void q6k_digits(uint32_t q4, int sc, uint32_t& w1, uint32_t& w0) {
+    const uint32_t qe = __builtin_amdgcn_perm(0u, q4, 0x0c020c00u);  // values 0, 2
+    const uint32_t qo = __builtin_amdgcn_perm(0u, q4, 0x0c030c01u);  // values 1, 3
+    const unsigned short s = (unsigned short)sc, o = (unsigned short)(-32 * sc);
+    const v2u16 ss = {s, s}, oo = {o, o};
+    const v2u16 we = __builtin_bit_cast(v2u16, qe) * ss + oo;
+    const v2u16 wo = __builtin_bit_cast(v2u16, qo) * ss + oo;
+    const v2u16 seven = {7, 7};
+    const uint32_t he = __builtin_bit_cast(uint32_t, we >> seven), ho = __builtin_bit_cast(uint32_t, wo >> seven);
+    // byte k of the result: value k's low byte (even values from `e`, odd from `o`)
+    w1 = __builtin_amdgcn_perm(ho, he, 0x06020400u);
+    w0 = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, wo), __builtin_bit_cast(uint32_t, we), 0x06020400u) &
+         0x7F7F7F7Fu;
+}
+
+template <int F>
+__device__ __forceinline__ void producer_store(const PrefillRegs& R, PrefillBuf<F>& sm, int p) {
+    constexpr bool Q5 = F == PF_Q5;
+    if constexpr (F == PF_Q6) {
+        // ---- digit planes of row p/4: values 128h+32t+l (low nibbles, quarter
+        // t, sub-blocks 8h+2t, 8h+2t+1) and 128h+32t+64+l (high nibbles,
+        // quarter t+2, sub-blocks 8h+2t+4, 8h+2t+5), l = 0..31
+        const int r = p >> 2, c = p & 3, h = c >> 1, t = c & 1;
+        const uint32_t ql[8] = {R.q0.x, R.q0.y, R.q0.z, R.q0.w, R.q1.x, R.q1.y, R.q1.z, R.q1.w};
+        const uint32_t qh[8] = {R.hdr.x, R.hdr.y, R.hdr.z, R.hdr.w, R.qh2.x, R.qh2.y, R.qh2.z, R.qh2.w};
+        const int sh = 16 * t;  // scale bytes 2t, 2t+1 of each half of the 8 loaded
+        const int s_lo0 = (int)(int8_t)(R.qh.x >> sh), s_lo1 = (int)(int8_t)(R.qh.x >> (sh + 8));
+        const int s_hi0 = (int)(int8_t)(R.qh.y >> sh), s_hi1 = (int)(int8_t)(R.qh.y >> (sh + 8));
+        uint32_t l1[8], l0[8], h1[8], h0[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t hb = qh[i] >> (2 * t);  // bits 2t, 2t+1 -> 0, 1; bits 2t+4, 2t+5 -> 4, 5
+            const uint32_t qlo = (ql[i] & 0x0F0F0F0Fu) | ((hb << 4) & 0x30303030u);
+            const uint32_t qhi = ((ql[i] >> 4) & 0x0F0F0F0Fu) | (hb & 0x30303030u);
+            q6k_digits(qlo, i < 4 ? s_lo0 : s_lo1, l1[i], l0[i]);
+            q6k_digits(qhi, i < 4 ? s_hi0 : s_hi1, h1[i], h0[i]);
+        }
+        int8_t* dh = sm.whi + r * PF_LD + 128 * h + 32 * t;
+        int8_t* dl = sm.wlo + r * PF_LD + 128 * h + 32 * t;
+        *reinterpret_cast<uint4*>(dh) = make_uint4(l1[0], l1[1], l1[2], l1[3]);
+        *reinterpret_cast<uint4*>(dh + 16) = make_uint4(l1[4], l1[5], l1[6], l1[7]);
+        *reinterpret_cast<uint4*>(dh + 64) = make_uint4(h1[0], h1[1], h1[2], h1[3]);
+        *reinterpret_cast<uint4*>(dh + 80) = make_uint4(h1[4], h1[5], h1[6], h1[7]);
+        *reinterpret_cast<uint4*>(dl) = make_uint4(l0[0], l0[1], l0[2], l0[3]);
+        *reinterpret_cast<uint4*>(dl + 16) = make_uint4(l0[4], l0[5], l0[6], l0[7]);
+        *reinterpret_cast<uint4*>(dl + 64) = make_uint4(h0[0], h0[1], h0[2], h0[3]);
+        *reinterpret_cast<uint4*>(dl + 80) = make_uint4(h0[4], h0[5], h0[6], h0[7]);
+        if (c == 0) sm.dw[r] = half_bits_to_float(R.dq & 0xffffu);
+    } else {
         const int r = p >> 2, c = p & 3;
         int sc0, mn0, sc1, mn1;
         q4k_scale_min(R.hdr, 2 * c, sc0, mn0);
@@ -275,7 +374,9 @@ __device__ __forceinline__ void producer_store(const PrefillRegs& R, PrefillBuf<
         for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(dst + 16 * i * PF_LD) = R.x[i];
     }
     // ---- token min-term operand d8 * bsum_j (j = 4h..4h+3) and scale
-    {
+    if constexpr (F == PF_Q6) {
+        if ((p & 1) == 0) sm.d8[p >> 1] = R.d8;
+    } else {
         const int t = p >> 1, h = p & 1;
         const uint32_t bw[2] = {R.bsv.x, R.bsv.y};
         uint32_t hb[4], lb[4];
@@ -294,9 +395,10 @@ __device__ __forceinline__ void producer_store(const PrefillRegs& R, PrefillBuf<
 
 // ------------------------------------------------------------ consumers ----
 // Consumer wave: tokens tg0..tg0+63 (two MFMA tiles) x rows 32rg..32rg+31.
-template <bool Q5>
-__device__ __forceinline__ void consumer_block(const PrefillBuf<Q5>& sm, int lane, int rg, int tg0, v16f (&accf)[2],
+template <int F>
+__device__ __forceinline__ void consumer_block(const PrefillBuf<F>& sm, int lane, int rg, int tg0, v16f (&accf)[2],
                                                v16f (&accj)[2]) {
+    constexpr bool Q5 = F == PF_Q5;
     const int kg = lane >> 5;
     const int nl = 32 * rg + (lane & 31);
     const int8_t* bh = sm.whi + nl * PF_LD + 16 * kg;
@@ -353,7 +455,7 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf<Q5>& sm, int lan
     }
     // min term: [ah | al] x [bh | bh] and [ah | al] x [bl | bl]; k-group 0 of
     // the token operand carries the high parts, k-group 1 the low parts
-    {
+    if constexpr (F != PF_Q6) {
         const v8bf bhv = *reinterpret_cast<const v8bf*>(&sm.bj[nl][0]);
         const v8bf blv = *reinterpret_cast<const v8bf*>(&sm.bj[nl][8]);
 #pragma unroll
@@ -364,6 +466,7 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf<Q5>& sm, int lan
         }
     }
     // block epilogue: acc += (d8 * float(8 P_hi + P_lo (+ 16 P_h))) * d
+    // (Q6_K: float(128 P_1 + P_0))
     const float dd = sm.dw[nl];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -374,7 +477,7 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf<Q5>& sm, int lan
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * g + i;
-                const int I = (ph[t][r] << 3) + pl[t][r];
+                const int I = (ph[t][r] << (F == PF_Q6 ? 7 : 3)) + pl[t][r];
                 const float If = (float)(Q5 ? I + (pq[t][r] << 4) : I);
                 accf[t][r] = fmaf(If * d8a[i], dd, accf[t][r]);
             }
@@ -385,8 +488,8 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf<Q5>& sm, int lan
 // One 128-token x 64-row tile over all nb blocks.  The producers' sources are
 // in S (built by the caller); consumer output row m of the tile goes to
 // y[orow(m) * rows + n] when ok(m).
-template <bool Q5, class ORow, class OK>
-__device__ __forceinline__ void prefill_tile(PrefillSmem<Q5>& sm, const PrefillSrc& S, int nb, int64_t rows,
+template <int F, class ORow, class OK>
+__device__ __forceinline__ void prefill_tile(PrefillSmem<F>& sm, const PrefillSrc& S, int nb, int64_t rows,
                                              int64_t n0, float* __restrict__ y, ORow orow, OK ok) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // Both roles run the same number of barriers: one before the first
@@ -401,20 +504,20 @@ __device__ __forceinline__ void prefill_tile(PrefillSmem<Q5>& sm, const PrefillS
         // have no records, so the reads return zeros without touching memory.
         // Branch-free loads keep the compiler's wait counts exact, so that a
         // store waits only for its own register set, two blocks old.
-        producer_load<Q5>(RA, S, 0, p);
-        producer_load<Q5>(RB, S, 1, p);
-        producer_store<Q5>(RA, sm.buf[0], p);
-        producer_load<Q5>(RA, S, 2, p);
+        producer_load<F>(RA, S, 0, p);
+        producer_load<F>(RB, S, 1, p);
+        producer_store<F>(RA, sm.buf[0], p);
+        producer_load<F>(RA, S, 2, p);
         lds_barrier();
         for (int b = 0; b < nb; b += 2) {
             // after block b is consumed: build block b+1 (RB), refill RB with b+3
-            if (b + 1 < nb) producer_store<Q5>(RB, sm.buf[1], p);
-            producer_load<Q5>(RB, S, b + 3, p);
+            if (b + 1 < nb) producer_store<F>(RB, sm.buf[1], p);
+            producer_load<F>(RB, S, b + 3, p);
             lds_barrier();
             if (b + 1 >= nb) break;
             // after block b+1 is consumed: build block b+2 (RA), refill RA with b+4
-            if (b + 2 < nb) producer_store<Q5>(RA, sm.buf[0], p);
-            producer_load<Q5>(RA, S, b + 4, p);
+            if (b + 2 < nb) producer_store<F>(RA, sm.buf[0], p);
+            producer_load<F>(RA, S, b + 4, p);
             lds_barrier();
         }
     } else {
@@ -427,7 +530,7 @@ __device__ __forceinline__ void prefill_tile(PrefillSmem<Q5>& sm, const PrefillS
             for (int r = 0; r < 16; ++r) accf[i][r] = accj[i][r] = 0.0f;
         lds_barrier();
         for (int b = 0; b < nb; ++b) {
-            consumer_block<Q5>(sm.buf[b & 1], lane, rg, tg0, accf, accj);
+            consumer_block<F>(sm.buf[b & 1], lane, rg, tg0, accf, accj);
             lds_barrier();
         }
         const int64_t n = n0 + 32 * rg + (lane & 31);
@@ -436,23 +539,25 @@ __device__ __forceinline__ void prefill_tile(PrefillSmem<Q5>& sm, const PrefillS
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = tg0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (ok(m) && n < rows) y[orow(m) * rows + n] = accf[i][r] - accj[i][r];
+                if (ok(m) && n < rows) y[orow(m) * rows + n] = F == PF_Q6 ? accf[i][r] : accf[i][r] - accj[i][r];
             }
         }
     }
 }
 
-template <bool Q5>
-__global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
+template <int F>
+__global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restrict__ w,
+                                                          const uint16_t* __restrict__ prefix, int64_t rows, int nb,
                                                           const int8_t* __restrict__ qs, const float* __restrict__ d8,
                                                           const int16_t* __restrict__ bs, int64_t K, int64_t M,
                                                           float* __restrict__ y) {
-    __shared__ __attribute__((aligned(16))) PrefillSmem<Q5> sm;
+    __shared__ __attribute__((aligned(16))) PrefillSmem<F> sm;
     const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
     const int64_t n0 = ((int64_t)blockIdx.x % ntn) * PF_TN;
     const int64_t m0 = ((int64_t)blockIdx.x / ntn) * PF_TM;
     PrefillSrc S;
-    if (threadIdx.x >= 256) producer_src<Q5>(S, w, rows, nb, qs, d8, bs, K, M, n0, m0, (int)threadIdx.x - 256);
+    if (threadIdx.x >= 256)
+        producer_src<F>(S, w, prefix, rows, nb, qs, d8, bs, K, M, n0, m0, (int)threadIdx.x - 256);
     prefill_tile(
         sm, S, nb, rows, n0, y, [&](int m) { return m0 + m; }, [&](int m) { return m0 + m < M; });
 }
@@ -536,8 +641,9 @@ __global__ __launch_bounds__(1024) void moe_group_kernel(const int32_t* __restri
     }
 }
 
-template <bool Q5>
-__global__ __launch_bounds__(512) void prefill_moe_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
+template <int F>
+__global__ __launch_bounds__(512) void prefill_moe_q4k_kernel(const uint8_t* __restrict__ w,
+                                                              const uint16_t* __restrict__ prefix, int64_t rows, int nb,
                                                               const int8_t* __restrict__ qs,
                                                               const float* __restrict__ d8,
                                                               const int16_t* __restrict__ bs, int64_t K, int64_t T,
@@ -545,7 +651,7 @@ __global__ __launch_bounds__(512) void prefill_moe_q4k_kernel(const uint8_t* __r
                                                               const int4* __restrict__ chunks,
                                                               const int32_t* __restrict__ order, int topk,
                                                               float* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) PrefillSmem<Q5> sm;
+    __shared__ __attribute__((aligned(16))) PrefillSmem<F> sm;
     __shared__ int tok[PF_TM];   // token of each tile row, -1 past the chunk's end
     __shared__ int pair[PF_TM];  // pair index of each tile row
     const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
@@ -560,10 +666,12 @@ __global__ __launch_bounds__(512) void prefill_moe_q4k_kernel(const uint8_t* __r
         tok[i] = p < 0 ? -1 : p / topk;
     }
     __syncthreads();
-    const uint8_t* we = w + (int64_t)ch.x * rows * (int64_t)nb * kblock<Q5>();
+    const int64_t eb = (int64_t)ch.x * rows * (int64_t)nb;  // the expert's first (row, block)
+    const uint8_t* we = w + eb * kblock<F>();
+    const uint16_t* pe = F == PF_Q6 ? prefix + eb : prefix;
     PrefillSrc S;
     if (threadIdx.x >= 256)
-        producer_src_gather<Q5>(S, we, rows, nb, qs, d8, bs, K, T, n0, tok, (int)threadIdx.x - 256);
+        producer_src_gather<F>(S, we, pe, rows, nb, qs, d8, bs, K, T, n0, tok, (int)threadIdx.x - 256);
     prefill_tile(
         sm, S, nb, rows, n0, out, [&](int m) { return (int64_t)pair[m]; }, [&](int m) { return m < count; });
 }
@@ -585,8 +693,9 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
     y[i] = s;
 }
 
-hipError_t launch_prefill_moe(bool q5, const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
-                              const int32_t* ids, const float* rw, int topk, float* y, void* ws, hipStream_t s) {
+hipError_t launch_prefill_moe(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t E, int64_t rows, int nb,
+                              Acts a, int64_t T, const int32_t* ids, const float* rw, int topk, float* y, void* ws,
+                              hipStream_t s) {
     const MoePrefillWs L = moe_prefill_ws(E, rows, T, topk);
     float* out = static_cast<float*>(ws);
     int32_t* nchunks = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.meta);
@@ -595,27 +704,33 @@ hipError_t launch_prefill_moe(bool q5, const uint8_t* w, int64_t E, int64_t rows
     hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(1024), 0, s, ids, L.P, (int)E, nchunks, chunks, order);
     const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
     const dim3 grid((unsigned)(L.max_chunks * ntn));
-    if (q5)
-        hipLaunchKernelGGL(prefill_moe_q4k_kernel<true>, grid, dim3(512), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K, T,
-                           nchunks, chunks, order, topk, out);
+    if (fmt == PF_Q6)
+        hipLaunchKernelGGL(prefill_moe_q4k_kernel<PF_Q6>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
+                           a.K, T, nchunks, chunks, order, topk, out);
+    else if (fmt == PF_Q5)
+        hipLaunchKernelGGL(prefill_moe_q4k_kernel<PF_Q5>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
+                           a.K, T, nchunks, chunks, order, topk, out);
     else
-        hipLaunchKernelGGL(prefill_moe_q4k_kernel<false>, grid, dim3(512), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K,
-                           T, nchunks, chunks, order, topk, out);
+        hipLaunchKernelGGL(prefill_moe_q4k_kernel<PF_Q4>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
+                           a.K, T, nchunks, chunks, order, topk, out);
     const int64_t n = T * rows;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, out, rows, T, ids, rw,
                        topk, E, y);
     return hipGetLastError();
 }
 
-hipError_t launch_prefill(bool q5, const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
-                          hipStream_t s) {
-    const int64_t tiles = ((rows + PF_TN - 1) / PF_TN) * ((M + PF_TM - 1) / PF_TM);
-    if (q5)
-        hipLaunchKernelGGL(prefill_q4k_kernel<true>, dim3((unsigned)tiles), dim3(512), 0, s, w, rows, nb, a.qs, a.d,
-                           a.bs, a.K, M, y);
+hipError_t launch_prefill(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a,
+                          int64_t M, float* y, hipStream_t s) {
+    const dim3 grid((unsigned)(((rows + PF_TN - 1) / PF_TN) * ((M + PF_TM - 1) / PF_TM)));
+    if (fmt == PF_Q6)
+        hipLaunchKernelGGL(prefill_q4k_kernel<PF_Q6>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
+                           a.K, M, y);
+    else if (fmt == PF_Q5)
+        hipLaunchKernelGGL(prefill_q4k_kernel<PF_Q5>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
+                           a.K, M, y);
     else
-        hipLaunchKernelGGL(prefill_q4k_kernel<false>, dim3((unsigned)tiles), dim3(512), 0, s, w, rows, nb, a.qs, a.d,
-                           a.bs, a.K, M, y);
+        hipLaunchKernelGGL(prefill_q4k_kernel<PF_Q4>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
+                           a.K, M, y);
     return hipGetLastError();
 }
 

@@ -32,9 +32,11 @@ hipError_t launch_moe_q5k(const uint8_t* w, int64_t E, int64_t rows, int nb, Act
                           const float* rw, int topk, float* y, hipStream_t s);
 hipError_t launch_moe_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t E, int64_t rows, int nb, Acts a,
                           int64_t T, const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s);
-// Prefill tile for Q4_K (q5 = false) or Q5_K (q5 = true).
-hipError_t launch_prefill(bool q5, const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
-                          hipStream_t s);
+// Prefill tile formats: Q4_K and Q5_K read one weight stream `w` (prefix
+// unused); relaid Q6_K reads the bodies as `w` and the fp16 d prefix.
+constexpr int PREFILL_Q4_K = 0, PREFILL_Q5_K = 1, PREFILL_Q6_K = 2;
+hipError_t launch_prefill(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a, int64_t M,
+                          float* y, hipStream_t s);
 
 // Workspace of the MoE prefill, byte offsets from its start: the fp32 result
 // of every (token, slot) pair [P][rows]; then, 256-aligned, the chunk count
@@ -60,7 +62,8 @@ inline MoePrefillWs moe_prefill_ws(int64_t E, int64_t rows, int64_t T, int64_t t
     L.total = (L.P == 0 || rows == 0) ? 0 : align256(L.order + 4 * L.P);  // nothing is enqueued then
     return L;
 }
-hipError_t launch_prefill_moe(bool q5, const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
-                              const int32_t* ids, const float* rw, int topk, float* y, void* ws, hipStream_t s);
+hipError_t launch_prefill_moe(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t E, int64_t rows, int nb,
+                              Acts a, int64_t T, const int32_t* ids, const float* rw, int topk, float* y, void* ws,
+                              hipStream_t s);
 
 }  // namespace q8k

@@ -94,11 +94,12 @@ def test_qtype_refusals(q):
     msg = refused(q, "Q8K_ERR_QTYPE", q.qmatvec, q.Q8K_Q6_K_GGUF, A16, 4, 256, A16, A16, 0)
     assert "q8k_bind_q6k" in msg
     refused(q, "Q8K_ERR_QTYPE", q.qmatvec, 42, A16, 4, 256, A16, A16, 0)
-    msg = refused(q, "Q8K_ERR_QTYPE", q.qmatmul_prefill, q.Q8K_Q6_K_RELAID, A16, 8, 256, A16, 4, A16, None, 0, 0)
-    assert "Q6_K" in msg
-    refused(q, "Q8K_ERR_QTYPE", q.qmatmul_prefill, q.Q8K_Q6_K_GGUF, A16, 8, 256, A16, 4, A16, None, 0, 0)
-    # Q5_K has a prefill tile: an empty call is accepted and enqueues nothing
-    q.qmatmul_prefill(q.Q8K_Q5_K, A16, 8, 256, A16, 0, A16, None, 0, 0)
+    msg = refused(q, "Q8K_ERR_QTYPE", q.qmatmul_prefill, q.Q8K_Q6_K_GGUF, A16, 8, 256, A16, 4, A16, None, 0, 0)
+    assert "q8k_bind_q6k" in msg
+    refused(q, "Q8K_ERR_QTYPE", q.qmatmul_prefill, 42, A16, 8, 256, A16, 4, A16, None, 0, 0)
+    # every served format has a prefill tile: empty calls are accepted and enqueue nothing
+    for qt in (q.Q8K_Q4_K, q.Q8K_Q5_K, q.Q8K_Q6_K_RELAID):
+        q.qmatmul_prefill(qt, A16, 8, 256, A16, 0, A16, None, 0, 0)
 
 
 def test_batched_and_moe_arguments(q):
@@ -153,15 +154,15 @@ def test_prefill_moe_arguments(q):
     refused(q, "Q8K_ERR_ARG", f, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, A16, A16, 9, A16, A16, 1 << 20, 0)
     refused(q, "Q8K_ERR_ARG", f, q.Q8K_Q4_K, A16, 128, 4, 256, A16, 2, A16, A16, q.Q8K_MOE_MAX_TOPK + 1, A16,
             A16, 1 << 20, 0)
-    msg = refused(q, "Q8K_ERR_QTYPE", f, q.Q8K_Q6_K_RELAID, A16, 8, 4, 256, A16, 16, A16, A16, 2, A16, A16, 1 << 20,
-                  0)
-    assert "Q6_K" in msg
+    msg = refused(q, "Q8K_ERR_QTYPE", f, q.Q8K_Q6_K_GGUF, A16, 8, 4, 256, A16, 16, A16, A16, 2, A16, A16, 1 << 20, 0)
+    assert "q8k_bind_q6k" in msg
     msg = refused(q, "Q8K_ERR_SHAPE", f, q.Q8K_Q4_K, A16, 8, 4, 16384, A16, 1 << 16, A16, A16, 2, A16, A16,
                   1 << 40, 0)
     assert "2^30" in msg
     need = q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, 8, 4, 256, 16, 2)
     assert need == moe_prefill_ws_bytes(8, 4, 16, 2) == 1024
     assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q5_K, 8, 4, 256, 16, 2) == need
+    assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q6_K_RELAID, 8, 4, 256, 16, 2) == need
     # 512 tokens, top-2 of 8 experts of 14336 rows: the per-pair results dominate
     assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, 8, 14336, 4096, 512, 2) == \
         moe_prefill_ws_bytes(8, 14336, 512, 2)
@@ -170,7 +171,7 @@ def test_prefill_moe_arguments(q):
     assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, 8, 0, 256, 16, 2) == 0
     refused(q, "Q8K_ERR_WORKSPACE", f, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, A16, A16, 2, A16, A16, need - 1, 0)
     refused(q, "Q8K_ERR_NULL", f, q.Q8K_Q4_K, A16, 8, 4, 256, A16, 16, None, A16, 2, A16, A16, need, 0)
-    assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q6_K_RELAID, 8, 4, 256, 16, 2) == 0
+    assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q6_K_GGUF, 8, 4, 256, 16, 2) == 0
 
 
 def test_empty_inputs_enqueue_nothing(q):

@@ -3,6 +3,8 @@ replay.  The bench times decode steps as graph replays, so this guards that
 the captured launches (no memset nodes: every output is fully overwritten by a
 kernel) reproduce eager execution exactly.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -89,3 +91,21 @@ def test_graph_replays_match_eager(q):
         y_side = torch.empty(rows, dtype=torch.float32, device=dev)
         q.qmatvec(q.Q8K_Q4_K, w4, rows, K, side, y_side)
         torch.cuda.synchronize()
+
+
+def test_package_imported_before_torch_launches(q):
+    """A fresh process that imports the package before torch still launches
+    on the device torch's tensors live on (one HIP runtime in the process)."""
+    import subprocess
+    import sys
+
+    code = ("import quantized_q8kpack_fp32_amd as q, torch, numpy as np\n"
+            "x = torch.ones(1, 256, device='cuda')\n"
+            "xq = torch.empty(q.q8k_act_bytes(1, 256), dtype=torch.uint8, device='cuda')\n"
+            "q.q8k_pack(x, 1, 256, xq)\n"
+            "torch.cuda.synchronize()\n"
+            "assert int(xq[0].item()) == 127, xq[:4]\n"
+            "print('ok')\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stderr[-2000:]

@@ -329,7 +329,17 @@ def test_moe_crowded_expert_and_bad_ids(q):
 
 # ================================================================== MoE prefill (NEXT row)
 _PF_FMT = {"q4k": ("Q8K_Q4_K", oracle.Q4_K, synth.q4k_weights),
-           "q5k": ("Q8K_Q5_K", oracle.Q5_K, synth.q5k_weights)}
+           "q5k": ("Q8K_Q5_K", oracle.Q5_K, synth.q5k_weights),
+           "q6k": ("Q8K_Q6_K_RELAID", oracle.Q6_K, synth.q6k_weights)}
+
+
+def pf_weights(q, fmt, w, nrows, K):
+    """Host GGUF blocks -> the device weight the prefill takes (Q6_K: bound by q8k_bind_q6k)."""
+    if fmt != "q6k":
+        return to_dev(w)
+    wd = poisoned(q.q8k_weight_bytes(q.Q8K_Q6_K_RELAID, nrows, K))
+    q.q8k_bind_q6k(to_dev(w), nrows, K, wd)
+    return wd
 
 
 def moe_prefill_case(q, E, rows, K, T, topk, seed, ids=None, fmt="q4k"):
@@ -345,8 +355,8 @@ def moe_prefill_case(q, E, rows, K, T, topk, seed, ids=None, fmt="q4k"):
     y = poisoned_f32(T, rows)
     wsb = q.qmatmul_prefill_moe_workspace_bytes(qt, E, rows, K, T, topk)
     ws = poisoned(wsb)
-    q.qmatmul_prefill_moe(qt, to_dev(w), E, rows, K, xq, T, to_dev(ids.astype(np.int32)), to_dev(rw), topk, y, ws,
-                          wsb)
+    q.qmatmul_prefill_moe(qt, pf_weights(q, fmt, w, E * rows, K), E, rows, K, xq, T, to_dev(ids.astype(np.int32)),
+                          to_dev(rw), topk, y, ws, wsb)
     oqs, od, obs = oracle.q8k_pack(x)
     return host(y), w, oqs, od, obs, ids, rw
 
@@ -361,6 +371,9 @@ def moe_prefill_case(q, E, rows, K, T, topk, seed, ids=None, fmt="q4k"):
     ("q5k", 8, 512, 4096, 512, 2, 67),
     ("q5k", 4, 130, 768, 37, 3, 68),
     ("q5k", 2, 96, 512, 1, 1, 69),
+    ("q6k", 8, 512, 4096, 512, 2, 74),
+    ("q6k", 4, 130, 768, 37, 3, 75),
+    ("q6k", 2, 96, 512, 1, 1, 76),
 ])
 def test_prefill_moe(q, fmt, E, rows, K, T, topk, seed):
     got, w, oqs, od, obs, ids, rw = moe_prefill_case(q, E, rows, K, T, topk, seed, fmt=fmt)
@@ -368,7 +381,7 @@ def test_prefill_moe(q, fmt, E, rows, K, T, topk, seed):
     assert_close(got, want, A, f"moe prefill {fmt} E={E} rows={rows} T={T}")
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q5k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 def test_prefill_moe_crowded_expert_and_bad_ids(q, fmt):
     """300 tokens all choose expert 0 first (three chunks, the last ragged);
     ids outside [0, E) select nothing."""
@@ -417,11 +430,11 @@ def run_prefill(q, fmt, w, rows, K, x):
     y = poisoned_f32(M, rows)
     ws_bytes = q.qmatmul_prefill_workspace_bytes(qt, rows, K, M)
     ws = poisoned(ws_bytes) if ws_bytes else None
-    q.qmatmul_prefill(qt, to_dev(w), rows, K, xq, M, y, ws, ws_bytes)
+    q.qmatmul_prefill(qt, pf_weights(q, fmt, w, rows, K), rows, K, xq, M, y, ws, ws_bytes)
     return host(y)
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q5k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,rows,K,seed", [(1, 64, 256, 41), (17, 100, 512, 42), (64, 64, 256, 43),
                                            (127, 256, 1024, 44), (200, 130, 768, 45), (65, 4096, 256, 46)])
 def test_prefill_full(q, fmt, M, rows, K, seed):
@@ -433,7 +446,7 @@ def test_prefill_full(q, fmt, M, rows, K, seed):
     assert_close(got, want, A, f"prefill {fmt} M={M} N={rows} K={K}")
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q5k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 def test_prefill_down_projection_sampled(q, fmt):
     """The 512-token x 4096-row x 14336 prefill: every output is finite and a
     sample of whole token rows and whole weight-row columns matches the oracle."""
@@ -480,6 +493,55 @@ def test_prefill_q5k_largest_fields(q):
     oqs, od, obs = oracle.q8k_pack(x)
     want, A = oracle.matvec(oracle.Q5_K, w, rows, K, oqs, od, obs, nthreads=NTH)
     assert_close(got, want, A, "prefill q5k largest fields")
+
+
+def test_prefill_q6k_extreme_scales_and_quants(q):
+    """Q6_K blocks at the corners of the value weight sc * (q - 32): scales
+    -128 and 127 against quants 0 and 63 (w = 4096, -4064, -4032, 3937),
+    zero scales, and tokens at +-127, so both digit planes reach their ends."""
+    from gguf_pack import pack_q6k_block
+
+    rows, K, M = 96, 1024, 130
+    nb = K // 256
+    g = np.random.default_rng(77)
+    corners = [(-128, 0), (-128, 63), (127, 0), (127, 63)]
+    blocks = []
+    for r in range(rows * nb):
+        kind = r % 5
+        if kind < 4:
+            sc, qq = corners[kind]
+            scv = np.full(16, sc)
+            qv = np.full(256, qq)
+            qv[::7] = g.integers(0, 64, qv[::7].shape)
+        else:
+            scv = np.where(g.random(16) < 0.3, 0, g.integers(-128, 128, 16))
+            qv = g.integers(0, 64, 256)
+        blocks.append(pack_q6k_block(float(g.uniform(1e-4, 1e-3)), scv, qv))
+    w = np.concatenate(blocks)
+    x = np.where(g.random((M, K)) < 0.5, -3.0, 3.0).astype(np.float32)
+    x[: M // 2] = 3.0
+    got = run_prefill(q, "q6k", w, rows, K, x)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(oracle.Q6_K, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(got, want, A, "prefill q6k extremes")
+
+
+def test_prefill_q6k_matches_batched_decode(q):
+    """The Q6_K prefill and eight-column batched decode of the same relaid
+    weight and tokens agree within the tolerance (integer sums are exact in
+    both; only the fp32 block sums run in different orders)."""
+    rows, K, M = 200, 2048, 8
+    w = synth.q6k_weights(np.random.default_rng(78), rows, K)
+    x = acts(78, M, K)
+    got = run_prefill(q, "q6k", w, rows, K, x)
+    wd = pf_weights(q, "q6k", w, rows, K)
+    xq = pack_on_device(q, x)
+    yb = poisoned_f32(M, rows)
+    q.qmatvec_batched(q.Q8K_Q6_K_RELAID, wd, rows, K, xq, M, yb)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(oracle.Q6_K, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(yb), want, A, "batched q6k")
+    assert_close(got, want, A, "prefill q6k")
 
 
 def test_prefill_q5k_without_fifth_bits_matches_q4k(q):
