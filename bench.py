@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Q4_K decode mat-vec HBM GB/s (% of peak); prefill int8 TOPS (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+HEADLINE_KERNEL = "matvec_f32_q4k_kernel<1, 2, false>"  # the one launch of the headline decode step
 MALL_BYTES = 256 << 20         # Infinity Cache
 TOL_REL, TOL_ABS = 1e-5, 1e-6
 
@@ -72,7 +73,10 @@ KERNEL_SOURCES = {
     "prefill_q6k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
     "moe_prefill_q6k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
     "moe_prefill_q5k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
-    "pack": [_CS + "pack.hip", _CS + "q8k_device.h"],
+    "pack": [_CS + "pack.hip", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
+    "fused_q4k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
+    "fused_q5k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
+    "fused_q6k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
 }
 
 
@@ -132,12 +136,13 @@ def _oracle_qtype(oracle, fmt):
 
 
 class Decode:
-    """One token through q8k_pack + qmatvec (Q4_K, Q5_K or relaid Q6_K)."""
+    """One token through q8k_pack + qmatvec (Q4_K, Q5_K or relaid Q6_K); with
+    fused=True through the one-launch qmatvec_f32 instead."""
 
-    def __init__(self, q, torch, fmt, rows, K, seed, R=None):
+    def __init__(self, q, torch, fmt, rows, K, seed, R=None, fused=False):
         import synth
 
-        self.q, self.torch, self.fmt, self.rows, self.K = q, torch, fmt, rows, K
+        self.q, self.torch, self.fmt, self.rows, self.K, self.fused = q, torch, fmt, rows, K, fused
         g = np.random.default_rng(seed)
         dev = torch.device("cuda")
         if fmt in ("q4k", "q5k"):
@@ -163,13 +168,20 @@ class Decode:
         self.mv_bytes = self.wbytes_alg + K + 4 * nb + (16 * nb if fmt != "q6k" else 0) + 4 * rows
         self.pack_bytes = 4 * K + K + 4 * nb + 16 * nb
         self.step_bytes = self.mv_bytes + self.pack_bytes
+        if fused:
+            # one launch: weight once, fp32 activations in, output out
+            self.mv_bytes = self.step_bytes = self.wbytes_alg + 4 * K + 4 * rows
 
     def step(self, i):
-        self.q.q8k_pack(self.x, 1, self.K, self.xq)
+        if not self.fused:
+            self.q.q8k_pack(self.x, 1, self.K, self.xq)
         self.main(i)
 
     def main(self, i):
-        self.q.qmatvec(self.qt, self.ws[i % self.R], self.rows, self.K, self.xq, self.y)
+        if self.fused:
+            self.q.qmatvec_f32(self.qt, self.ws[i % self.R], self.rows, self.K, self.x, 1, self.y, None)
+        else:
+            self.q.qmatvec(self.qt, self.ws[i % self.R], self.rows, self.K, self.xq, self.y)
 
     def parity(self):
         import oracle
@@ -431,6 +443,9 @@ PROFILE_TARGETS = {
     "decode_q6k": "qmatvec on the 32000x4096 relaid Q6_K workload",
     "moe": "qmatvec_moe on the 8 x 14336x4096 Q4_K, 16-token top-2 workload",
     "decode_q5k": "qmatvec on the 4096x4096 Q5_K decode workload",
+    "fused_q4k": "qmatvec_f32 (pack inside the launch) on the 4096x4096 Q4_K decode workload",
+    "fused_q5k": "qmatvec_f32 (pack inside the launch) on the 4096x4096 Q5_K decode workload",
+    "fused_q6k": "qmatvec_f32 (pack inside the launch) on the 32000x4096 relaid Q6_K workload",
     "moe_q5k": "qmatvec_moe on the 8 x 14336x4096 Q5_K, 16-token top-2 workload",
     "prefill": "qmatmul_prefill on the 4096x14336 Q4_K, 512-token workload",
     "moe_prefill": "qmatmul_prefill_moe on the 8 x 14336x4096 Q4_K, 512-token top-2 workload",
@@ -457,6 +472,9 @@ def profile_run(q, torch, target, launches):
               "decode_q6k": lambda: Decode(q, torch, "q6k", 32000, 4096, seed=2),
               "moe": lambda: MoE(q, torch),
               "decode_q5k": lambda: Decode(q, torch, "q5k", 4096, 4096, seed=5),
+              "fused_q4k": lambda: Decode(q, torch, "q4k", 4096, 4096, seed=1, fused=True),
+              "fused_q5k": lambda: Decode(q, torch, "q5k", 4096, 4096, seed=5, fused=True),
+              "fused_q6k": lambda: Decode(q, torch, "q6k", 32000, 4096, seed=2, fused=True),
               "moe_q5k": lambda: MoE(q, torch, seed=6, fmt="q5k"),
               "prefill": lambda: Prefill(q, torch),
               "moe_prefill": lambda: MoEPrefill(q, torch),
@@ -506,14 +524,14 @@ def main():
         profile_run(q, torch, args.profile, args.launches)
         return
 
-    # ---- headline: 4096x4096 Q4_K decode step
+    # ---- headline: 4096x4096 Q4_K decode step, one launch (q8_K pack inside)
     log("headline: decode_q4k_4096x4096")
-    hd = Decode(q, torch, "q4k", 4096, 4096, seed=1)
+    hd = Decode(q, torch, "q4k", 4096, 4096, seed=1, fused=True)
     parity = hd.parity()
     sec, mv_us = run_timed(torch, hd, args.steps, args.warmup)
     value = hd.step_bytes / sec / 1e9
     achieved = hd.mv_bytes / (mv_us * 1e-6) / 1e9
-    tr = traffic_record("matvec_q4k")
+    tr = traffic_record("fused_q4k")
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -529,11 +547,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_q4k_4096x4096", "rows": 4096, "K": 4096, "tokens": 1,
                    "weight": "GGUF Q4_K, 144 B per 256 values", "weight_copies_rotated": hd.R,
-                   "step": "q8k_pack + qmatvec", "step_bytes": hd.step_bytes, "timing": "hip graph replay",
+                   "step": "qmatvec_f32 (q8_K pack inside the launch)", "step_bytes": hd.step_bytes,
+                   "timing": "hip graph replay",
                    "parity": "pass" if parity else "FAIL"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
-                     "kernel": "matvec_q4k_kernel<1, 2, false>", "launch_us": round(mv_us, 3),
+                     "kernel": HEADLINE_KERNEL, "launch_us": round(mv_us, 3),
                      "algorithmic_bytes_per_launch": hd.mv_bytes},
     }
     del hd
@@ -554,6 +573,16 @@ def main():
             if kernel:
                 wl[name]["traffic"] = traffic_record(kernel)
 
+        # the same step as two launches: q8k_pack, then qmatvec on the packed token
+        log("workload: decode_q4k_4096x4096_pack_then_matvec")
+        decode_entry("decode_q4k_4096x4096_pack_then_matvec", Decode(q, torch, "q4k", 4096, 4096, seed=1),
+                     "matvec_q4k")
+        torch.cuda.empty_cache()
+        for name, fmt, rows, seed in (("decode_fused_q5k_4096x4096", "q5k", 4096, 5),
+                                      ("decode_fused_q6k_32000x4096", "q6k", 32000, 2)):
+            log(f"workload: {name}")
+            decode_entry(name, Decode(q, torch, fmt, rows, 4096, seed=seed, fused=True), "fused_" + fmt)
+            torch.cuda.empty_cache()
         log("workload: decode_q6k_32000x4096")
         decode_entry("decode_q6k_32000x4096", Decode(q, torch, "q6k", 32000, 4096, seed=2), "matvec_q6k")
         torch.cuda.empty_cache()

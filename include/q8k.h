@@ -128,7 +128,25 @@ int qmatvec(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, f
 int qmatvec_batched(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int64_t ncols, float* y,
                     void* stream);
 
-/* qmatvec_moe: expert-indexed decode.  w holds E experts, each a rows x K
+/* qmatvec_f32: the decode step in one launch, from fp32 activations.  Each
+ * workgroup first packs the ncols columns x [ncols][K] to q8_K in its own
+ * shared memory, with the same arithmetic as q8k_pack, then runs
+ * qmatvec_batched's arithmetic on them: y equals q8k_pack followed by
+ * qmatvec_batched bit for bit, without the packed activations' round trip
+ * through global memory or the second launch (the fused launches of
+ * "Language models on the device", sections 1 and 3.3; a q|k|v or gate|up
+ * weight concatenated row-wise is one weight here, so one launch serves all
+ * of its parts).
+ * qtype: Q8K_Q4_K, Q8K_Q5_K or Q8K_Q6_K_RELAID.  1 <= ncols <= Q8K_COLS_MAX
+ * and ncols * (K + K/256 * 20) <= 65536 bytes (the packed columns fit one
+ * workgroup's shared memory), else Q8K_ERR_ARG / Q8K_ERR_SHAPE.  x: fp32
+ * [ncols][K], 16-byte aligned.  xq_out: NULL, or a q8_K buffer of ncols
+ * tokens (q8k_act_bytes(ncols, K)) that also receives the packed columns,
+ * for further mat-vecs of the same tokens.  y: fp32 [ncols][rows]. */
+int qmatvec_f32(int qtype, const void* w, int64_t rows, int64_t K, const float* x, int64_t ncols, float* y,
+                void* xq_out, void* stream);
+
+/* qmatvec_moe: expert-indexed decode./* qmatvec_moe: expert-indexed decode.  w holds E experts, each a rows x K
  * weight in the given layout, expert e's blocks following expert e-1's.
  * xq: q8_K buffer of T tokens (0 <= T <= Q8K_MOE_MAX_TOKENS); ids int32
  * [T][topk]; rw fp32 [T][topk]; 1 <= topk <= min(E, Q8K_MOE_MAX_TOPK).

@@ -17,7 +17,7 @@ import os
 __all__ = [
     "Q8K_Q4_K", "Q8K_Q5_K", "Q8K_Q6_K_RELAID", "Q8K_Q6_K_GGUF", "Q8K_COLS_MAX", "Q8K_MOE_MAX_TOKENS", "Q8K_MOE_MAX_TOPK", "Q8KError",
     "lib", "LIB_PATH", "q8k_act_bytes", "q8k_act_layout", "q8k_weight_bytes", "q8k_pack", "q8k_bind_q6k",
-    "qmatvec", "qmatvec_batched", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
+    "qmatvec", "qmatvec_batched", "qmatvec_f32", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
     "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe",
     "q8k_debug_subblock_sums", "q8k_status_str", "q8k_last_error", "EXPORTED",
 ]
@@ -35,7 +35,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq8k.so")
 # every symbol declared in include/q8k.h
 EXPORTED = (
     "q8k_act_bytes", "q8k_act_layout", "q8k_weight_bytes", "q8k_pack", "q8k_bind_q6k", "qmatvec",
-    "qmatvec_batched", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
+    "qmatvec_batched", "qmatvec_f32", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
     "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe",
     "q8k_debug_subblock_sums", "q8k_status_str", "q8k_last_error",
 )
@@ -73,6 +73,8 @@ lib.qmatvec.restype = _INT
 lib.qmatvec.argtypes = [_INT, _P, _I64, _I64, _P, _P, _P]
 lib.qmatvec_batched.restype = _INT
 lib.qmatvec_batched.argtypes = [_INT, _P, _I64, _I64, _P, _I64, _P, _P]
+lib.qmatvec_f32.restype = _INT
+lib.qmatvec_f32.argtypes = [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P]
 lib.qmatvec_moe.restype = _INT
 lib.qmatvec_moe.argtypes = [_INT, _P, _I64, _I64, _I64, _P, _I64, _P, _P, ctypes.c_int32, _P, _P]
 lib.qmatmul_prefill_workspace_bytes.restype = _SZ
@@ -165,6 +167,10 @@ def qmatvec(qtype: int, w, rows: int, K: int, xq, y, stream=None) -> None:
 
 def qmatvec_batched(qtype: int, w, rows: int, K: int, xq, ncols: int, y, stream=None) -> None:
     _check(lib.qmatvec_batched(qtype, _ptr(w), rows, K, _ptr(xq), ncols, _ptr(y), _stream(stream)))
+
+
+def qmatvec_f32(qtype: int, w, rows: int, K: int, x, ncols: int, y, xq_out=None, stream=None) -> None:
+    _check(lib.qmatvec_f32(qtype, _ptr(w), rows, K, _ptr(x), ncols, _ptr(y), _ptr(xq_out), _stream(stream)))
 
 
 def qmatvec_moe(qtype: int, w, E: int, rows: int, K: int, xq, T: int, ids, rw, topk: int, y, stream=None) -> None:

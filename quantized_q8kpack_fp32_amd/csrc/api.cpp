@@ -114,9 +114,9 @@ struct PrefillWeights {
 PrefillWeights prefill_weights(int qtype, const void* w, int64_t nblocks) {
     if (qtype == Q8K_Q6_K_RELAID) {
         const Q6View v = q6_view(w, nblocks);
-        return PrefillWeights{PREFILL_Q6_K, v.bodies, v.prefix};
+        return PrefillWeights{WFMT_Q6_K, v.bodies, v.prefix};
     }
-    return PrefillWeights{qtype == Q8K_Q5_K ? PREFILL_Q5_K : PREFILL_Q4_K, static_cast<const uint8_t*>(w), nullptr};
+    return PrefillWeights{qtype == Q8K_Q5_K ? WFMT_Q5_K : WFMT_Q4_K, static_cast<const uint8_t*>(w), nullptr};
 }
 
 }  // namespace
@@ -194,6 +194,34 @@ static int matvec_common(const char* fn, int qtype, const void* w, int64_t rows,
         e = launch_matvec_q6k(v.prefix, v.bodies, rows, nb, a, (int)ncols, y, (hipStream_t)stream);
     }
     return launched(fn, e);
+}
+
+int qmatvec_f32(int qtype, const void* w, int64_t rows, int64_t K, const float* x, int64_t ncols, float* y,
+                void* xq_out, void* stream) {
+    const char* fn = "qmatvec_f32";
+    Q8K_TRY(check_k(fn, K));
+    Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
+    if (ncols < 1 || ncols > Q8K_COLS_MAX)
+        return fail(Q8K_ERR_ARG, "%s: ncols=%lld must be in [1, %d]", fn, (long long)ncols, Q8K_COLS_MAX);
+    if (fused_lds_bytes(ncols, K) > FUSED_LDS_MAX)
+        return fail(Q8K_ERR_SHAPE,
+                    "%s: ncols*K=%lld: the packed columns (%zu bytes) exceed one workgroup's %zu bytes of LDS "
+                    "(use q8k_pack + qmatvec_batched)",
+                    fn, (long long)(ncols * K), fused_lds_bytes(ncols, K), FUSED_LDS_MAX);
+    Q8K_TRY(check_weight(fn, qtype, w));
+    Q8K_TRY(check_ptr(fn, "x", x, 16));
+    Q8K_TRY(check_ptr(fn, "y", y, 4));
+    if (xq_out) Q8K_TRY(check_ptr(fn, "xq_out", xq_out, 16));
+    if (rows == 0) return Q8K_OK;
+    const int nb = (int)(K / QK);
+    PackedOut o{nullptr, nullptr, nullptr};
+    if (xq_out) {
+        const Acts a = acts_of(xq_out, ncols, K);
+        o = PackedOut{const_cast<int8_t*>(a.qs), const_cast<float*>(a.d), const_cast<int16_t*>(a.bs)};
+    }
+    const PrefillWeights pw = prefill_weights(qtype, w, rows * nb);
+    return launched(fn, launch_matvec_f32(pw.fmt, pw.w, pw.prefix, rows, nb, x, K, (int)ncols, y, o,
+                                          (hipStream_t)stream));
 }
 
 int qmatvec(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, float* y, void* stream) {

@@ -20,6 +20,7 @@
 // block and contribute nothing, which keeps the wave convergent.
 #include "kquant.h"
 #include "q8k_launch.h"
+#include "q8k_quant.h"
 
 namespace q8k {
 
@@ -141,6 +142,156 @@ __global__ __launch_bounds__(256) void sums_q4k_kernel(const uint8_t* __restrict
     }
 }
 
+// ------------------------------------------------- fused pack + mat-vec ----
+// One launch for a decode step from fp32 activations (the fused pack + GEMM
+// of "Language models on the device", section 1 and the fused launches of
+// section 3.3, which spare the packed activations a round trip through global
+// memory and a launch).  A workgroup of four rows first issues the weight
+// loads of its first loop trip, then its four waves quantise the activation
+// columns into LDS (wave w takes blocks w, w+4, ...) with the same lane
+// quantiser as q8k_pack, so the codes, sums and scales are the same bytes;
+// after one barrier each wave runs the mat-vec of its row with the
+// activations read from LDS.  Workgroup 0 also stores the packed columns when
+// the caller asks for them (to feed further mat-vecs of the same tokens).
+// The workgroup packs the NC activation columns x [NC][K] into LDS (codes
+// [NC][K], sums [NC][nb][8], scales [NC][nb]); workgroup 0 also stores them
+// to o when o.qs is not null.  Sixteen lanes take a block (16 values each),
+// so the 256 threads pack 16 blocks at once: a 4096-wide column in one pass.
+// The first pass (column 0, blocks 0..15) is loaded by pack_first, so that a
+// caller can issue its own loads behind it: loads complete in issue order,
+// and the packing must not wait for loads issued after its own.
+struct PackFirst {
+    float4 v[4];
+};
+// Workgroup size of the fused Q4_K/Q5_K kernel (one row per wave): every
+// workgroup packs the whole activation, so fewer, larger workgroups repeat
+// that work less often; up to two columns a wave's registers allow 16 waves.
+#ifndef Q8K_FUSED_WAVES
+#define Q8K_FUSED_WAVES 8
+#endif
+#ifndef Q8K_FUSED_WAVES_NARROW
+#define Q8K_FUSED_WAVES_NARROW 16
+#endif
+template <int NC>
+constexpr int fused_waves() { return NC <= 2 ? Q8K_FUSED_WAVES_NARROW : Q8K_FUSED_WAVES; }
+
+__device__ __forceinline__ void pack_first(PackFirst& P, const float* __restrict__ x, int nb) {
+    const int r = threadIdx.x & 15, b = threadIdx.x >> 4;
+    if (b < nb) {
+        const float4* src = reinterpret_cast<const float4*>(x + (int64_t)b * QK + 16 * r);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) P.v[i] = src[i];
+    }
+}
+
+__device__ __forceinline__ void pack_store(const float4 (&v)[4], int t, int b, int64_t K, int nb, int8_t* sqs,
+                                           int16_t* sbs, float* sd, const PackedOut& o, bool out) {
+    const int r = threadIdx.x & 15;
+    int sub;
+    float dd;
+    const uint4 codes = q8k_quant_lane16(v, sub, dd);
+    *reinterpret_cast<uint4*>(sqs + t * K + b * QK + 16 * r) = codes;
+    if ((r & 1) == 0) sbs[(t * nb + b) * 8 + (r >> 1)] = (int16_t)sub;
+    if (r == 0) sd[t * nb + b] = dd;
+    if (out) {
+        *reinterpret_cast<uint4*>(o.qs + t * K + (int64_t)b * QK + 16 * r) = codes;
+        if ((r & 1) == 0) o.bs[((int64_t)t * nb + b) * 8 + (r >> 1)] = (int16_t)sub;
+        if (r == 0) o.d[(int64_t)t * nb + b] = dd;
+    }
+}
+
+// Ends with a workgroup barrier.
+template <int NC>
+__device__ __forceinline__ void pack_to_lds(const PackFirst& P, const float* __restrict__ x, int64_t K, int nb,
+                                            int8_t* sqs, int16_t* sbs, float* sd, const PackedOut& o) {
+    const int r = threadIdx.x & 15, b0 = threadIdx.x >> 4, bstep = blockDim.x >> 4;
+    const bool out = o.qs != nullptr && blockIdx.x == 0;
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+        for (int b = b0; b < nb; b += bstep) {  // uniform per 16-lane row
+            if (t == 0 && b == b0) {
+                pack_store(P.v, 0, b, K, nb, sqs, sbs, sd, o, out);
+                continue;
+            }
+            const float4* src = reinterpret_cast<const float4*>(x + t * K + (int64_t)b * QK + 16 * r);
+            const float4 v[4] = {src[0], src[1], src[2], src[3]};
+            pack_store(v, t, b, K, nb, sqs, sbs, sd, o, out);
+        }
+    }
+    __syncthreads();
+}
+
+template <bool Q5>
+struct Q4Weights {
+    uint4 hdr, qv, qh;
+};
+
+template <bool Q5>
+__device__ __forceinline__ void q4k_load_w(Q4Weights<Q5>& W, const uint8_t* __restrict__ wr, int b, int ci) {
+    const uint8_t* blk = wr + (int64_t)b * kblock<Q5>();
+    W.hdr = *reinterpret_cast<const uint4*>(blk);
+    W.qv = *reinterpret_cast<const uint4*>(blk + (Q5 ? 48 : 16) + 16 * ci);
+    if (Q5) W.qh = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (ci & 1));
+}
+
+template <int NC, int U, bool Q5>
+__global__ __launch_bounds__(64 * fused_waves<NC>()) void matvec_f32_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
+                                                             const float* __restrict__ x, int64_t K,
+                                                             float* __restrict__ y, PackedOut o) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    int8_t* sqs = reinterpret_cast<int8_t*>(lds);                                // [NC][K]
+    int16_t* sbs = reinterpret_cast<int16_t*>(lds + (int64_t)NC * K);            // [NC][nb][8]
+    float* sd = reinterpret_cast<float*>(lds + (int64_t)NC * K + 16 * NC * nb);  // [NC][nb]
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * fused_waves<NC>() + wv;
+    const int ci = lane & 7, c = ci >> 1, half = ci & 1;
+    const int aoff = 64 * c + 16 * half, boff = 2 * c;
+    const uint8_t* wr = w + (row < rows ? row : rows - 1) * (int64_t)nb * kblock<Q5>();
+    PackFirst P;
+    pack_first(P, x, nb);
+    // weights of the first trip, in flight while the activations are packed
+    Q4Weights<Q5> W[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int b = (lane >> 3) + 8 * u;
+        q4k_load_w(W[u], wr, b < nb ? b : nb - 1, ci);
+    }
+    pack_to_lds<NC>(P, x, K, nb, sqs, sbs, sd, o);
+    if (row >= rows) return;  // uniform per wave, after the barrier
+    float acc[NC];
+#pragma unroll
+    for (int t = 0; t < NC; ++t) acc[t] = 0.0f;
+    for (int b0 = lane >> 3; b0 - (lane >> 3) < nb; b0 += 8 * U) {
+        Q4Chunk<NC, Q5> L[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int b = b0 + 8 * u;
+            const int bc = b < nb ? b : nb - 1;
+            L[u].hdr = W[u].hdr;
+            L[u].qv = W[u].qv;
+            L[u].qh = W[u].qh;
+#pragma unroll
+            for (int t = 0; t < NC; ++t) {
+                const int8_t* a = sqs + t * K + bc * QK + aoff;
+                L[u].alo[t] = *reinterpret_cast<const int4*>(a);
+                L[u].ahi[t] = *reinterpret_cast<const int4*>(a + 32);
+                L[u].bs[t] = *reinterpret_cast<const uint32_t*>(sbs + (t * nb + bc) * 8 + boff);
+                L[u].d8[t] = sd[t * nb + bc];
+            }
+            // the next trip's weights
+            const int bn = b + 8 * U;
+            if (b0 - (lane >> 3) + 8 * U < nb) q4k_load_w(W[u], wr, bn < nb ? bn : nb - 1, ci);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) q4k_accum(L[u], c, half, b0 + 8 * u < nb, acc);
+    }
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+        const float v = wave_sum_dpp(acc[t]);
+        if (lane == 0) y[(int64_t)t * rows + row] = v;
+    }
+}
+
 // ---------------------------------------------------------------- Q6_K ----
 // Lane map: lane l serves block b = 16k + (l >> 2) and the pair (h, lh) =
 // ((l >> 1) & 1, l & 1): the two ql chunks 4h + lh and 4h + 2 + lh (tt = 0
@@ -224,11 +375,26 @@ __device__ __forceinline__ void q6k_store(const float (&acc)[NC], int lane, int6
 #define Q8K_Q6_DEPTH 2
 #endif
 constexpr int Q6_DEPTH = Q8K_Q6_DEPTH;
-template <int NC>
+//
+// FUSED: the activations arrive as fp32 columns x and every workgroup packs
+// them into LDS first (as the fused Q4_K kernel does); qs and d8 are unused.
+template <int NC, bool FUSED>
 __global__ __launch_bounds__(256) void matvec_q6k_kernel(const uint16_t* __restrict__ prefix,
                                                          const uint8_t* __restrict__ bodies, int64_t rows, int nb,
                                                          const int8_t* __restrict__ qs, const float* __restrict__ d8,
-                                                         int64_t K, float* __restrict__ y) {
+                                                         int64_t K, float* __restrict__ y, const float* __restrict__ x,
+                                                         PackedOut o) {
+    if constexpr (FUSED) {
+        extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+        int8_t* sqs = reinterpret_cast<int8_t*>(lds);
+        int16_t* sbs = reinterpret_cast<int16_t*>(lds + (int64_t)NC * K);
+        float* sd = reinterpret_cast<float*>(lds + (int64_t)NC * K + 16 * NC * nb);
+        PackFirst P;
+        pack_first(P, x, nb);
+        pack_to_lds<NC>(P, x, K, nb, sqs, sbs, sd, o);
+        qs = sqs;
+        d8 = sd;
+    }
     const int64_t stride = (int64_t)gridDim.x * 4;
     int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -316,7 +482,8 @@ template <int NC>
 static void go_q6k(const uint16_t* p, const uint8_t* bodies, int64_t rows, int nb, Acts a, float* y, hipStream_t s) {
     const int64_t wgs = (rows + 3) / 4;
     const unsigned grid = (unsigned)(wgs < Q8K_Q6_GRID ? wgs : Q8K_Q6_GRID);
-    hipLaunchKernelGGL((matvec_q6k_kernel<NC>), dim3(grid), dim3(256), 0, s, p, bodies, rows, nb, a.qs, a.d, a.K, y);
+    hipLaunchKernelGGL((matvec_q6k_kernel<NC, false>), dim3(grid), dim3(256), 0, s, p, bodies, rows, nb, a.qs, a.d, a.K,
+                       y, nullptr, PackedOut{nullptr, nullptr, nullptr});
 }
 
 template <bool Q5>
@@ -342,6 +509,51 @@ hipError_t launch_matvec_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int
 
 hipError_t launch_matvec_q5k(const uint8_t* w, int64_t rows, int nb, Acts a, int ncols, float* y, hipStream_t s) {
     return launch_q4k_family<true>(w, rows, nb, a, ncols, y, s);
+}
+
+template <int NC, bool Q5>
+static void go_f32_q4k(const uint8_t* w, int64_t rows, int nb, const float* x, int64_t K, float* y, PackedOut o,
+                       hipStream_t s) {
+    constexpr int U = NC <= Q8K_MV_U2_MAXNC ? 2 : 1;
+    const size_t lds = fused_lds_bytes(NC, K);
+    constexpr int WV = fused_waves<NC>();
+    hipLaunchKernelGGL((matvec_f32_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + WV - 1) / WV)), dim3(64 * WV), lds,
+                       s, w, rows, nb, x, K, y, o);
+}
+
+template <int NC>
+static void go_f32_q6k(const uint16_t* p, const uint8_t* bodies, int64_t rows, int nb, const float* x, int64_t K,
+                       float* y, PackedOut o, hipStream_t s) {
+    const int64_t wgs = (rows + 3) / 4;
+    const unsigned grid = (unsigned)(wgs < Q8K_Q6_GRID ? wgs : Q8K_Q6_GRID);
+    hipLaunchKernelGGL((matvec_q6k_kernel<NC, true>), dim3(grid), dim3(256), fused_lds_bytes(NC, K), s, p, bodies,
+                       rows, nb, nullptr, nullptr, K, y, x, o);
+}
+
+hipError_t launch_matvec_f32(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, const float* x,
+                             int64_t K, int ncols, float* y, PackedOut o, hipStream_t s) {
+#define Q8K_F32_CASE(n)                                            \
+    case n:                                                        \
+        if (fmt == WFMT_Q6_K)                                   \
+            go_f32_q6k<n>(prefix, w, rows, nb, x, K, y, o, s);     \
+        else if (fmt == WFMT_Q5_K)                              \
+            go_f32_q4k<n, true>(w, rows, nb, x, K, y, o, s);       \
+        else                                                       \
+            go_f32_q4k<n, false>(w, rows, nb, x, K, y, o, s);      \
+        break;
+    switch (ncols) {
+        Q8K_F32_CASE(1)
+        Q8K_F32_CASE(2)
+        Q8K_F32_CASE(3)
+        Q8K_F32_CASE(4)
+        Q8K_F32_CASE(5)
+        Q8K_F32_CASE(6)
+        Q8K_F32_CASE(7)
+        Q8K_F32_CASE(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef Q8K_F32_CASE
+    return hipGetLastError();
 }
 
 hipError_t launch_matvec_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t rows, int nb, Acts a, int ncols,

@@ -7,6 +7,7 @@
 // that kernels read bodies with aligned 16-byte loads (same page, section 1).
 #include "q8k_device.h"
 #include "q8k_launch.h"
+#include "q8k_quant.h"
 
 namespace q8k {
 
@@ -19,32 +20,12 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ x, 
     const int lane = threadIdx.x & 63;
     if (blk >= nblocks) return;  // uniform per wave
     const float4 v = *reinterpret_cast<const float4*>(x + blk * QK + lane * 4);
-    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    amax = wave_max(amax);
-    int q[4] = {0, 0, 0, 0};
-    if (amax != 0.0f) {
-        // IEEE division (hipcc keeps fp32 '/' correctly rounded by default),
-        // then one multiply and round-half-even per value.
-        const float iscale = 127.0f / amax;
-        const float xs[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float r = __builtin_rintf(xs[i] * iscale);
-            if (r != r) r = 0.0f;  // 0 * inf when 127/amax overflows
-            r = r > 127.0f ? 127.0f : r;
-            r = r < -127.0f ? -127.0f : r;
-            q[i] = (int)r;
-        }
-    }
-    const uint32_t packed = (uint32_t)(q[0] & 255) | ((uint32_t)(q[1] & 255) << 8) | ((uint32_t)(q[2] & 255) << 16) |
-                            ((uint32_t)(q[3] & 255) << 24);
+    int s;
+    float dd;
+    const uint32_t packed = q8k_quant_lane(v, s, dd);
     *reinterpret_cast<uint32_t*>(qs + blk * QK + lane * 4) = packed;
-    int s = q[0] + q[1] + q[2] + q[3];
-    s += __shfl_xor(s, 1, WAVE);
-    s += __shfl_xor(s, 2, WAVE);
-    s += __shfl_xor(s, 4, WAVE);
     if ((lane & 7) == 0) bsums[blk * 8 + (lane >> 3)] = (int16_t)s;
-    if (lane == 0) d[blk] = amax != 0.0f ? amax / 127.0f : 0.0f;
+    if (lane == 0) d[blk] = dd;
 }
 
 hipError_t launch_pack(const float* x, int64_t nblocks, int8_t* qs, float* d, int16_t* bsums, hipStream_t s) {

@@ -68,7 +68,7 @@ constexpr int PF_LD = QK + 16;  // LDS row stride in bytes (bank spread)
 // consumer in registers from the row's qh bytes and scales staged beside the
 // planes: I = 8 P_hi + P_lo + 16 P_h.
 // Weight formats of the tile.
-constexpr int PF_Q4 = PREFILL_Q4_K, PF_Q5 = PREFILL_Q5_K, PF_Q6 = PREFILL_Q6_K;
+constexpr int PF_Q4 = WFMT_Q4_K, PF_Q5 = WFMT_Q5_K, PF_Q6 = WFMT_Q6_K;
 
 template <int F>
 struct PrefillQ5 {};

@@ -24,6 +24,23 @@ hipError_t launch_matvec_q6k(const uint16_t* prefix, const uint8_t* bodies, int6
 hipError_t launch_sums_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int32_t* S, hipStream_t s);
 hipError_t launch_matvec_q5k(const uint8_t* w, int64_t rows, int nb, Acts a, int ncols, float* y, hipStream_t s);
 hipError_t launch_sums_q5k(const uint8_t* w, int64_t rows, int nb, Acts a, int32_t* S, hipStream_t s);
+// Weight formats of the prefill and fused kernels: Q4_K and Q5_K read one
+// weight stream `w` (prefix unused); relaid Q6_K reads the bodies as `w` and
+// the fp16 d prefix.
+constexpr int WFMT_Q4_K = 0, WFMT_Q5_K = 1, WFMT_Q6_K = 2;
+
+// Fused pack + mat-vec from fp32 activations [ncols][K] (fmt: WFMT_*).  The packed
+// columns are also stored to `o` when o.qs is not null.  LDS per workgroup:
+// the packed columns, fused_lds_bytes(ncols, K) <= FUSED_LDS_MAX.
+struct PackedOut {
+    int8_t* qs;
+    float* d;
+    int16_t* bs;
+};
+inline size_t fused_lds_bytes(int64_t ncols, int64_t K) { return (size_t)(ncols * (K + K / 256 * 20)); }
+constexpr size_t FUSED_LDS_MAX = 65536;
+hipError_t launch_matvec_f32(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, const float* x,
+                             int64_t K, int ncols, float* y, PackedOut o, hipStream_t s);
 hipError_t launch_sums_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t rows, int nb, Acts a, int32_t* S,
                            hipStream_t s);
 hipError_t launch_moe_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T, const int32_t* ids,
@@ -32,9 +49,6 @@ hipError_t launch_moe_q5k(const uint8_t* w, int64_t E, int64_t rows, int nb, Act
                           const float* rw, int topk, float* y, hipStream_t s);
 hipError_t launch_moe_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t E, int64_t rows, int nb, Acts a,
                           int64_t T, const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s);
-// Prefill tile formats: Q4_K and Q5_K read one weight stream `w` (prefix
-// unused); relaid Q6_K reads the bodies as `w` and the fp16 d prefix.
-constexpr int PREFILL_Q4_K = 0, PREFILL_Q5_K = 1, PREFILL_Q6_K = 2;
 hipError_t launch_prefill(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a, int64_t M,
                           float* y, hipStream_t s);
 

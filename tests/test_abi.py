@@ -102,6 +102,21 @@ def test_qtype_refusals(q):
         q.qmatmul_prefill(qt, A16, 8, 256, A16, 0, A16, None, 0, 0)
 
 
+def test_fused_decode_arguments(q):
+    f = q.qmatvec_f32
+    refused(q, "Q8K_ERR_ARG", f, q.Q8K_Q4_K, A16, 4, 256, A16, 0, A16, None, 0)
+    refused(q, "Q8K_ERR_ARG", f, q.Q8K_Q4_K, A16, 4, 256, A16, q.Q8K_COLS_MAX + 1, A16, None, 0)
+    refused(q, "Q8K_ERR_SHAPE", f, q.Q8K_Q4_K, A16, 4, 1000, A16, 1, A16, None, 0)
+    # the packed columns must fit 64 KiB of LDS: ncols * (K + K/256*20) bytes
+    msg = refused(q, "Q8K_ERR_SHAPE", f, q.Q8K_Q4_K, A16, 4, 14336, A16, 5, A16, None, 0)
+    assert "LDS" in msg and "q8k_pack" in msg
+    f(q.Q8K_Q4_K, A16, 0, 14336, A16, 4, A16, None, 0)  # 4 * 15456 bytes fit; rows == 0 enqueues nothing
+    refused(q, "Q8K_ERR_ALIGN", f, q.Q8K_Q4_K, A16, 4, 256, A16 + 4, 1, A16, None, 0)
+    refused(q, "Q8K_ERR_ALIGN", f, q.Q8K_Q4_K, A16, 4, 256, A16, 1, A16, A16 + 8, 0)
+    refused(q, "Q8K_ERR_NULL", f, q.Q8K_Q4_K, A16, 4, 256, None, 1, A16, None, 0)
+    refused(q, "Q8K_ERR_QTYPE", f, q.Q8K_Q6_K_GGUF, A16, 4, 256, A16, 1, A16, None, 0)
+
+
 def test_batched_and_moe_arguments(q):
     refused(q, "Q8K_ERR_ARG", q.qmatvec_batched, q.Q8K_Q4_K, A16, 4, 256, A16, 0, A16, 0)
     refused(q, "Q8K_ERR_ARG", q.qmatvec_batched, q.Q8K_Q4_K, A16, 4, 256, A16, q.Q8K_COLS_MAX + 1, A16, 0)
@@ -177,6 +192,7 @@ def test_prefill_moe_arguments(q):
 def test_empty_inputs_enqueue_nothing(q):
     # zero rows / tokens are valid and return before any launch
     q.qmatvec(q.Q8K_Q4_K, A16, 0, 256, A16, A16, 0)
+    q.qmatvec_f32(q.Q8K_Q5_K, A16, 0, 256, A16, 2, A16, A16, 0)
     q.q8k_pack(A16, 0, 256, A16, 0)
     q.qmatvec_moe(q.Q8K_Q4_K, A16, 8, 4, 256, A16, 0, A16, A16, 2, A16, 0)
     q.qmatmul_prefill(q.Q8K_Q4_K, A16, 8, 256, A16, 0, A16, None, 0, 0)

@@ -273,6 +273,77 @@ def test_batched(q, ncols, fmt):
         assert np.array_equal(host(y1).view(np.uint32), got[c].view(np.uint32)), f"column {c}"
 
 
+# ================================================================== fused pack + decode (NEXT row)
+def fused_weights(q, fmt, seed, rows, K):
+    """-> (host GGUF bytes, device weight, C qtype, oracle qtype)."""
+    qname, ot, gen = _PF_FMT[fmt]
+    w = gen(np.random.default_rng(seed), rows, K)
+    return w, pf_weights(q, fmt, w, rows, K), getattr(q, qname), ot
+
+
+@pytest.mark.parametrize("fmt,rows,K,ncols,seed", [
+    ("q4k", 4096, 4096, 1, 80), ("q4k", 37, 256, 1, 81), ("q4k", 130, 14336, 1, 82), ("q4k", 1000, 4096, 4, 83),
+    ("q4k", 70, 1280, 8, 84), ("q4k", 9, 14336, 4, 85),
+    ("q5k", 4096, 4096, 1, 86), ("q5k", 13, 768, 3, 87), ("q5k", 70, 1280, 8, 88),
+    ("q6k", 1000, 4096, 1, 89), ("q6k", 37, 256, 2, 90), ("q6k", 130, 14336, 1, 91), ("q6k", 70, 4608, 8, 92),
+])
+def test_fused_decode_equals_pack_then_matvec(q, fmt, rows, K, ncols, seed):
+    """One fused launch from fp32 activations gives q8k_pack + qmatvec_batched
+    bit for bit, its packed copy equals q8k_pack's bytes, and both match the
+    oracle within the tolerance."""
+    w, wd, qt, ot = fused_weights(q, fmt, seed, rows, K)
+    x = acts(seed, ncols, K)
+    if ncols > 1:
+        x[1] = special_blocks(K)[0]
+    y = poisoned_f32(ncols, rows)
+    xq_f = poisoned(q.q8k_act_bytes(ncols, K))
+    q.qmatvec_f32(qt, wd, rows, K, to_dev(x), ncols, y, xq_f)
+    xq = pack_on_device(q, x)
+    y2 = poisoned_f32(ncols, rows)
+    q.qmatvec_batched(qt, wd, rows, K, xq, ncols, y2)
+    got = host(y)
+    assert np.array_equal(got.view(np.uint32), host(y2).view(np.uint32))
+    assert np.array_equal(host(xq_f), host(xq))
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(ot, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(got, want, A, f"fused {fmt} {rows}x{K} ncols={ncols}")
+
+
+def test_fused_decode_without_packed_copy(q):
+    """xq_out = NULL: the same outputs, nothing else written."""
+    rows, K = 300, 2048
+    w, wd, qt, _ = fused_weights(q, "q4k", 93, rows, K)
+    x = to_dev(acts(93, 2, K))
+    y1 = poisoned_f32(2, rows)
+    y2 = poisoned_f32(2, rows)
+    xq = poisoned(q.q8k_act_bytes(2, K))
+    q.qmatvec_f32(qt, wd, rows, K, x, 2, y1, xq)
+    q.qmatvec_f32(qt, wd, rows, K, x, 2, y2, None)
+    assert np.array_equal(host(y1).view(np.uint32), host(y2).view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_fused_qkv_one_launch_equals_three(q, fmt):
+    """q, k and v weights concatenated row-wise are one weight: one fused
+    launch gives each part's outputs bit for bit as three separate launches."""
+    K = 4096
+    parts = [(4096, 94), (1024, 95), (1024, 96)]
+    ws = [_PF_FMT[fmt][2](np.random.default_rng(sd), r, K) for r, sd in parts]
+    rows = sum(r for r, _ in parts)
+    wd = pf_weights(q, fmt, np.concatenate(ws), rows, K)
+    qt = getattr(q, _PF_FMT[fmt][0])
+    x = to_dev(acts(94, 1, K))
+    y = poisoned_f32(rows)
+    q.qmatvec_f32(qt, wd, rows, K, x, 1, y, None)
+    got = host(y)
+    r0 = 0
+    for (r, _), wp in zip(parts, ws):
+        yp = poisoned_f32(r)
+        q.qmatvec_f32(qt, pf_weights(q, fmt, wp, r, K), r, K, x, 1, yp, None)
+        assert np.array_equal(got[r0:r0 + r].view(np.uint32), host(yp).view(np.uint32))
+        r0 += r
+
+
 # ================================================================== a6 MoE decode
 def moe_case(q, fmt, E, rows, K, T, topk, seed, ids=None):
     g = np.random.default_rng(seed)
