@@ -632,7 +632,7 @@ def main():
         pus = replay_us(torch, gp, 32, reps=2)
         del gp
         wl["pack_512x14336"] = {"kernel_us": round(pus, 2), "GB/s": round(p.pack_bytes / (pus * 1e-6) / 1e9, 1),
-                                "bytes_per_launch": p.pack_bytes}
+                                "bytes_per_launch": p.pack_bytes, "traffic": traffic_record("pack")}
         del p
         out["workloads"] = wl
 

@@ -84,12 +84,24 @@ __device__ __forceinline__ void q4k_accum(const Q4Chunk<NC, Q5>& L, int c, int h
     }
 }
 
+// Rows (waves) per workgroup of the packed-activation mat-vec: up to two
+// columns (narrow) and more.
+#ifndef Q8K_MV_WAVES
+#define Q8K_MV_WAVES 8
+#endif
+#ifndef Q8K_MV_WAVES_NARROW
+#define Q8K_MV_WAVES_NARROW 4
+#endif
+template <int NC>
+constexpr int mv_waves() { return NC <= 2 ? Q8K_MV_WAVES_NARROW : Q8K_MV_WAVES; }
+
 template <int NC, int U, bool Q5>
-__global__ __launch_bounds__(256) void matvec_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
-                                                         const int8_t* __restrict__ qs, const float* __restrict__ d8,
-                                                         const int16_t* __restrict__ bs, int64_t K,
-                                                         float* __restrict__ y) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+__global__ __launch_bounds__(64 * mv_waves<NC>()) void matvec_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows,
+                                                                   int nb, const int8_t* __restrict__ qs,
+                                                                   const float* __restrict__ d8,
+                                                                   const int16_t* __restrict__ bs, int64_t K,
+                                                                   float* __restrict__ y) {
+    const int64_t row = (int64_t)blockIdx.x * mv_waves<NC>() + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;  // uniform per wave
     const int ci = lane & 7, c = ci >> 1, half = ci & 1;
@@ -472,8 +484,9 @@ __global__ __launch_bounds__(256) void sums_q6k_kernel(const uint8_t* __restrict
 template <int NC, bool Q5>
 static void go_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, float* y, hipStream_t s) {
     constexpr int U = NC <= Q8K_MV_U2_MAXNC ? 2 : 1;
-    hipLaunchKernelGGL((matvec_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb,
-                       a.qs, a.d, a.bs, a.K, y);
+    constexpr int WV = mv_waves<NC>();
+    hipLaunchKernelGGL((matvec_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + WV - 1) / WV)), dim3(64 * WV), 0, s, w,
+                       rows, nb, a.qs, a.d, a.bs, a.K, y);
 }
 #ifndef Q8K_Q6_GRID
 #define Q8K_Q6_GRID 512
