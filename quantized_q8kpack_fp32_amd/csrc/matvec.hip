@@ -246,30 +246,15 @@ __device__ __forceinline__ void q4k_load_w(Q4Weights<Q5>& W, const uint8_t* __re
     if (Q5) W.qh = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (ci & 1));
 }
 
+// The rows of one wave from activations in LDS (codes sqs [NC][K], sums sbs
+// [NC][nb][8], scales sd [NC][nb]); W holds the weights of the first trip.
 template <int NC, int U, bool Q5>
-__global__ __launch_bounds__(64 * fused_waves<NC>()) void matvec_f32_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
-                                                             const float* __restrict__ x, int64_t K,
-                                                             float* __restrict__ y, PackedOut o) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    int8_t* sqs = reinterpret_cast<int8_t*>(lds);                                // [NC][K]
-    int16_t* sbs = reinterpret_cast<int16_t*>(lds + (int64_t)NC * K);            // [NC][nb][8]
-    float* sd = reinterpret_cast<float*>(lds + (int64_t)NC * K + 16 * NC * nb);  // [NC][nb]
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * fused_waves<NC>() + wv;
+__device__ __forceinline__ void q4k_row_from_lds(Q4Weights<Q5> (&W)[U], const uint8_t* __restrict__ wr, int nb,
+                                                 const int8_t* sqs, const int16_t* sbs, const float* sd, int64_t K,
+                                                 int64_t rows, int64_t row, float* __restrict__ y) {
+    const int lane = threadIdx.x & 63;
     const int ci = lane & 7, c = ci >> 1, half = ci & 1;
     const int aoff = 64 * c + 16 * half, boff = 2 * c;
-    const uint8_t* wr = w + (row < rows ? row : rows - 1) * (int64_t)nb * kblock<Q5>();
-    PackFirst P;
-    pack_first(P, x, nb);
-    // weights of the first trip, in flight while the activations are packed
-    Q4Weights<Q5> W[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int b = (lane >> 3) + 8 * u;
-        q4k_load_w(W[u], wr, b < nb ? b : nb - 1, ci);
-    }
-    pack_to_lds<NC>(P, x, K, nb, sqs, sbs, sd, o);
-    if (row >= rows) return;  // uniform per wave, after the barrier
     float acc[NC];
 #pragma unroll
     for (int t = 0; t < NC; ++t) acc[t] = 0.0f;
@@ -302,6 +287,84 @@ __global__ __launch_bounds__(64 * fused_waves<NC>()) void matvec_f32_q4k_kernel(
         const float v = wave_sum_dpp(acc[t]);
         if (lane == 0) y[(int64_t)t * rows + row] = v;
     }
+}
+
+template <int NC, int U, bool Q5>
+__device__ __forceinline__ void q4k_first_weights(Q4Weights<Q5> (&W)[U], const uint8_t* __restrict__ wr, int nb) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int b = (lane >> 3) + 8 * u;
+        q4k_load_w(W[u], wr, b < nb ? b : nb - 1, lane & 7);
+    }
+}
+
+template <int NC, int U, bool Q5>
+__global__ __launch_bounds__(64 * fused_waves<NC>()) void matvec_f32_q4k_kernel(const uint8_t* __restrict__ w,
+                                                                                 int64_t rows, int nb,
+                                                                                 const float* __restrict__ x, int64_t K,
+                                                                                 float* __restrict__ y, PackedOut o) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    int8_t* sqs = reinterpret_cast<int8_t*>(lds);                                // [NC][K]
+    int16_t* sbs = reinterpret_cast<int16_t*>(lds + (int64_t)NC * K);            // [NC][nb][8]
+    float* sd = reinterpret_cast<float*>(lds + (int64_t)NC * K + 16 * NC * nb);  // [NC][nb]
+    const int64_t row = (int64_t)blockIdx.x * fused_waves<NC>() + (threadIdx.x >> 6);
+    const uint8_t* wr = w + (row < rows ? row : rows - 1) * (int64_t)nb * kblock<Q5>();
+    PackFirst P;
+    pack_first(P, x, nb);
+    // weights of the first trip, in flight while the activations are packed
+    Q4Weights<Q5> W[U];
+    q4k_first_weights<NC, U, Q5>(W, wr, nb);
+    pack_to_lds<NC>(P, x, K, nb, sqs, sbs, sd, o);
+    if (row >= rows) return;  // uniform per wave, after the barrier
+    q4k_row_from_lds<NC, U, Q5>(W, wr, nb, sqs, sbs, sd, K, rows, row, y);
+}
+
+// Packed-token form with the columns staged in LDS: the workgroup copies the
+// NC packed columns (codes, sums, scales) into LDS once, so its waves read
+// them there instead of each through the vector cache.  The first copy loads
+// are issued before the weights (loads complete in issue order).
+constexpr int STAGE_REGS = 4;  // 16-byte copy units per thread held across the weight loads
+template <int NC, int U, bool Q5>
+__global__ __launch_bounds__(64 * mv_waves<NC>()) void matvec_staged_q4k_kernel(
+    const uint8_t* __restrict__ w, int64_t rows, int nb, const int8_t* __restrict__ qs, const float* __restrict__ d8,
+    const int16_t* __restrict__ bs, int64_t K, float* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    int8_t* sqs = reinterpret_cast<int8_t*>(lds);
+    int16_t* sbs = reinterpret_cast<int16_t*>(lds + (int64_t)NC * K);
+    float* sd = reinterpret_cast<float*>(lds + (int64_t)NC * K + 16 * NC * nb);
+    const int T = 64 * mv_waves<NC>();
+    const int64_t row = (int64_t)blockIdx.x * mv_waves<NC>() + (threadIdx.x >> 6);
+    const uint8_t* wr = w + (row < rows ? row : rows - 1) * (int64_t)nb * kblock<Q5>();
+    // codes and sums as one run of 16-byte units: NC*K/16 of codes, then NC*nb of sums
+    const int ncode = (int)(NC * K / 16), nunit = ncode + NC * nb;
+    auto src = [&](int u) -> uint4 {
+        return u < ncode ? reinterpret_cast<const uint4*>(qs)[u] : reinterpret_cast<const uint4*>(bs)[u - ncode];
+    };
+    auto dst = [&](int u) -> uint4* {
+        return u < ncode ? reinterpret_cast<uint4*>(sqs) + u : reinterpret_cast<uint4*>(sbs) + (u - ncode);
+    };
+    uint4 R[STAGE_REGS];
+#pragma unroll
+    for (int i = 0; i < STAGE_REGS; ++i) {
+        const int u = (int)threadIdx.x + i * T;
+        if (u < nunit) R[i] = src(u);
+    }
+    float dv = 0.0f;
+    if ((int)threadIdx.x < NC * nb) dv = d8[threadIdx.x];
+    Q4Weights<Q5> W[U];
+    q4k_first_weights<NC, U, Q5>(W, wr, nb);
+#pragma unroll
+    for (int i = 0; i < STAGE_REGS; ++i) {
+        const int u = (int)threadIdx.x + i * T;
+        if (u < nunit) *dst(u) = R[i];
+    }
+    for (int u = (int)threadIdx.x + STAGE_REGS * T; u < nunit; u += T) *dst(u) = src(u);
+    if ((int)threadIdx.x < NC * nb) sd[threadIdx.x] = dv;
+    for (int i = (int)threadIdx.x + T; i < NC * nb; i += T) sd[i] = d8[i];
+    __syncthreads();
+    if (row >= rows) return;  // uniform per wave, after the barrier
+    q4k_row_from_lds<NC, U, Q5>(W, wr, nb, sqs, sbs, sd, K, rows, row, y);
 }
 
 // ---------------------------------------------------------------- Q6_K ----
@@ -481,10 +544,20 @@ __global__ __launch_bounds__(256) void sums_q6k_kernel(const uint8_t* __restrict
 // (a 4096-wide row in one trip); one group per trip for more columns, where
 // the activation registers of every column already give enough loads in
 // flight.  Q6_K: one 16-block pass per trip.
+// From this many columns the packed-token mat-vec stages the columns in LDS
+// (when they fit one workgroup's LDS).
+#ifndef Q8K_MV_STAGED_MINNC
+#define Q8K_MV_STAGED_MINNC 2
+#endif
 template <int NC, bool Q5>
 static void go_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, float* y, hipStream_t s) {
     constexpr int U = NC <= Q8K_MV_U2_MAXNC ? 2 : 1;
     constexpr int WV = mv_waves<NC>();
+    if (NC >= Q8K_MV_STAGED_MINNC && fused_lds_bytes(NC, a.K) <= FUSED_LDS_MAX) {
+        hipLaunchKernelGGL((matvec_staged_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + WV - 1) / WV)),
+                           dim3(64 * WV), fused_lds_bytes(NC, a.K), s, w, rows, nb, a.qs, a.d, a.bs, a.K, y);
+        return;
+    }
     hipLaunchKernelGGL((matvec_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + WV - 1) / WV)), dim3(64 * WV), 0, s, w,
                        rows, nb, a.qs, a.d, a.bs, a.K, y);
 }

@@ -273,6 +273,29 @@ def test_batched(q, ncols, fmt):
         assert np.array_equal(host(y1).view(np.uint32), got[c].view(np.uint32)), f"column {c}"
 
 
+@pytest.mark.parametrize("fmt,ncols", [("q4k", 4), ("q4k", 5), ("q5k", 2), ("q5k", 8)])
+def test_batched_long_rows(q, fmt, ncols):
+    """K = 14336: up to four columns are staged in LDS, five or more read the
+    packed token from global memory (they exceed one workgroup's LDS); both
+    match the oracle and the single-column mat-vec bit for bit."""
+    rows, K = 300, 14336
+    w = (q4k if fmt == "q4k" else q5k)(60 + ncols, rows, K)
+    qt, ot = (q.Q8K_Q4_K, oracle.Q4_K) if fmt == "q4k" else (q.Q8K_Q5_K, oracle.Q5_K)
+    wd = to_dev(w)
+    x = acts(61 + ncols, ncols, K)
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(ncols, rows)
+    q.qmatvec_batched(qt, wd, rows, K, xq, ncols, y)
+    got = host(y)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(ot, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(got, want, A, f"batched {fmt} K={K} ncols={ncols}")
+    for c in (0, ncols - 1):
+        y1 = poisoned_f32(rows)
+        q.qmatvec(qt, wd, rows, K, pack_on_device(q, x[c:c + 1]), y1)
+        assert np.array_equal(host(y1).view(np.uint32), got[c].view(np.uint32)), f"column {c}"
+
+
 # ================================================================== fused pack + decode (NEXT row)
 def fused_weights(q, fmt, seed, rows, K):
     """-> (host GGUF bytes, device weight, C qtype, oracle qtype)."""
