@@ -32,6 +32,7 @@ def test_graph_replays_match_eager(q):
     g = np.random.default_rng(5)
     rows, K, T, E, topk, M = 512, 1024, 4, 4, 2, 70
     w4 = to_dev(synth.q4k_weights(g, E * rows, K))
+    w5 = to_dev(synth.q5k_weights(g, rows, K))
     w6g = to_dev(synth.q6k_weights(g, rows, K))
     w6 = torch.empty(q.q8k_weight_bytes(q.Q8K_Q6_K_RELAID, rows, K), dtype=torch.uint8, device=dev)
     q.q8k_bind_q6k(w6g, rows, K, w6)
@@ -46,9 +47,18 @@ def test_graph_replays_match_eager(q):
     yb = torch.empty(T * rows, dtype=torch.float32, device=dev)
     ym = torch.empty(T * rows, dtype=torch.float32, device=dev)
     yp = torch.empty(M * rows, dtype=torch.float32, device=dev)
+    yp5 = torch.empty(M * rows, dtype=torch.float32, device=dev)
+    yp6 = torch.empty(M * rows, dtype=torch.float32, device=dev)
+    yf4 = torch.empty(rows, dtype=torch.float32, device=dev)
+    yf6 = torch.empty(rows, dtype=torch.float32, device=dev)
+    xqf = torch.empty(q.q8k_act_bytes(1, K), dtype=torch.uint8, device=dev)
+    yb5 = torch.empty(T * rows, dtype=torch.float32, device=dev)
+    ypm = torch.empty(T * rows, dtype=torch.float32, device=dev)
     ws_bytes = q.qmatmul_prefill_workspace_bytes(q.Q8K_Q4_K, rows, K, M)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    outs = [xq, xq1, xqT, y4, y6, yb, ym, yp]
+    wsm_bytes = q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, E, rows, K, T, topk)
+    wsm = torch.empty(wsm_bytes, dtype=torch.uint8, device=dev)
+    outs = [xq, xq1, xqT, y4, y6, yb, ym, yp, yp5, yp6, yf4, yf6, xqf, yb5, ypm]
 
     def path():
         q.q8k_pack(x, M, K, xq)
@@ -59,6 +69,12 @@ def test_graph_replays_match_eager(q):
         q.qmatvec_batched(q.Q8K_Q4_K, w4, rows, K, xqT, T, yb)
         q.qmatvec_moe(q.Q8K_Q4_K, w4, E, rows, K, xqT, T, ids, rw, topk, ym)
         q.qmatmul_prefill(q.Q8K_Q4_K, w4, rows, K, xq, M, yp, ws, ws_bytes)
+        q.qmatmul_prefill(q.Q8K_Q5_K, w5, rows, K, xq, M, yp5, ws, ws_bytes)
+        q.qmatmul_prefill(q.Q8K_Q6_K_RELAID, w6, rows, K, xq, M, yp6, ws, ws_bytes)
+        q.qmatvec_f32(q.Q8K_Q4_K, w4, rows, K, x[:1], 1, yf4, None)
+        q.qmatvec_f32(q.Q8K_Q6_K_RELAID, w6, rows, K, x[:1], 1, yf6, xqf)
+        q.qmatvec_batched(q.Q8K_Q5_K, w5, rows, K, xqT, T, yb5)
+        q.qmatmul_prefill_moe(q.Q8K_Q4_K, w4, E, rows, K, xqT, T, ids, rw, topk, ypm, wsm, wsm_bytes)
 
     path()
     torch.cuda.synchronize()
@@ -68,12 +84,12 @@ def test_graph_replays_match_eager(q):
         them is not written by any kernel), or the whole fp32 output."""
         if o.dtype != torch.uint8:
             return o.view(torch.uint8)
-        tok = {"xq": M, "xq1": 1, "xqT": T}[name]
+        tok = {"xq": M, "xq1": 1, "xqT": T, "xqf": 1}[name]
         total, od, ob = q.q8k_act_layout(tok, K)
         nb = K // 256
         return torch.cat([o[: tok * K], o[od: od + 4 * tok * nb], o[ob: ob + 16 * tok * nb]])
 
-    names = ["xq", "xq1", "xqT", "y4", "y6", "yb", "ym", "yp"]
+    names = ["xq", "xq1", "xqT", "y4", "y6", "yb", "ym", "yp", "yp5", "yp6", "yf4", "yf6", "xqf", "yb5", "ypm"]
     eager = [defined(n, o).clone() for n, o in zip(names, outs)]
 
     graph = torch.cuda.CUDAGraph()
