@@ -75,6 +75,8 @@ KERNEL_SOURCES = {
     "moe_prefill_q5k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
     "pack": [_CS + "pack.hip", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
     "fused_q4k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
+    "batched_q4k_c4": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
+    "batched_q4k_c8": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
     "fused_q5k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
     "fused_q6k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
 }
@@ -444,6 +446,8 @@ PROFILE_TARGETS = {
     "moe": "qmatvec_moe on the 8 x 14336x4096 Q4_K, 16-token top-2 workload",
     "decode_q5k": "qmatvec on the 4096x4096 Q5_K decode workload",
     "fused_q4k": "qmatvec_f32 (pack inside the launch) on the 4096x4096 Q4_K decode workload",
+    "batched4": "qmatvec_batched, 4 packed columns, on the 4096x4096 Q4_K workload",
+    "batched8": "qmatvec_batched, 8 packed columns, on the 4096x4096 Q4_K workload",
     "fused_q5k": "qmatvec_f32 (pack inside the launch) on the 4096x4096 Q5_K decode workload",
     "fused_q6k": "qmatvec_f32 (pack inside the launch) on the 32000x4096 relaid Q6_K workload",
     "moe_q5k": "qmatvec_moe on the 8 x 14336x4096 Q5_K, 16-token top-2 workload",
@@ -473,6 +477,8 @@ def profile_run(q, torch, target, launches):
               "moe": lambda: MoE(q, torch),
               "decode_q5k": lambda: Decode(q, torch, "q5k", 4096, 4096, seed=5),
               "fused_q4k": lambda: Decode(q, torch, "q4k", 4096, 4096, seed=1, fused=True),
+              "batched4": lambda: Batched(q, torch, "q4k", 4096, 4096, seed=1, ncols=4),
+              "batched8": lambda: Batched(q, torch, "q4k", 4096, 4096, seed=1, ncols=8),
               "fused_q5k": lambda: Decode(q, torch, "q5k", 4096, 4096, seed=5, fused=True),
               "fused_q6k": lambda: Decode(q, torch, "q6k", 32000, 4096, seed=2, fused=True),
               "moe_q5k": lambda: MoE(q, torch, seed=6, fmt="q5k"),
@@ -588,7 +594,8 @@ def main():
         torch.cuda.empty_cache()
         for nc in (4, 8):
             log(f"workload: batched_q4k_4096x4096_cols{nc}")
-            decode_entry(f"batched_q4k_4096x4096_cols{nc}", Batched(q, torch, "q4k", 4096, 4096, seed=1, ncols=nc))
+            decode_entry(f"batched_q4k_4096x4096_cols{nc}", Batched(q, torch, "q4k", 4096, 4096, seed=1, ncols=nc),
+                         f"batched_q4k_c{nc}")
             torch.cuda.empty_cache()
         log("workload: moe_q4k_8x14336x4096_t16_top2")
         m = MoE(q, torch)
