@@ -151,7 +151,7 @@ int q8k_pack(const float* x, int64_t T, int64_t K, void* xq, void* stream) {
     Q8K_TRY(check_count(fn, "T", T, MAX_TOKENS));
     Q8K_TRY(check_ptr(fn, "x", x, 16));
     Q8K_TRY(check_ptr(fn, "xq", xq, 16));
-    Q8K_TRY(check_grid(fn, (T * (K / QK) + 3) / 4));
+    Q8K_TRY(check_grid(fn, (T * (K / QK) + 15) / 16));  // 16 blocks per workgroup
     if (T == 0) return Q8K_OK;
     const ActLayout l = act_layout(T, K);
     uint8_t* base = static_cast<uint8_t*>(xq);

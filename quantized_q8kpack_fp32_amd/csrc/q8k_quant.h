@@ -1,52 +1,20 @@
-// q8_K quantisation of one 256-value block by one wavefront ("Language
-// models on the device: the cajeta-llm kernels", section 1: 256 values a
-// block, one scale and eight sub-block sums; the device quantiser of
-// section 2.6).  Shared by the pack kernel and the mat-vecs that pack their
-// own activations, so both produce the same bytes.
+// q8_K quantisation of one 256-value block ("Language models on the device:
+// the cajeta-llm kernels", section 1: 256 values a block, one scale and eight
+// sub-block sums; the device quantiser of section 2.6).  Shared by the pack
+// kernel and the mat-vecs that pack their own activations, so both produce
+// the same bytes.
 #pragma once
 #include "q8k_device.h"
 
 namespace q8k {
 
-// Lane l holds values 4l..4l+3 of the block (the eight lanes 8j..8j+7 hold
-// sub-block j).  Returns the lane's four codes packed little-endian; `sub`
-// is the sum of sub-block l/8's codes (the same in its eight lanes) and `d`
-// the block scale amax/127 (0 for an all-zero block), both wave-uniform in
-// their groups.
-__device__ __forceinline__ uint32_t q8k_quant_lane(float4 v, int& sub, float& d) {
-    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    amax = wave_max(amax);
-    int q[4] = {0, 0, 0, 0};
-    if (amax != 0.0f) {
-        // IEEE division (hipcc keeps fp32 '/' correctly rounded by default),
-        // then one multiply and round-half-even per value.
-        const float iscale = 127.0f / amax;
-        const float xs[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float r = __builtin_rintf(xs[i] * iscale);
-            if (r != r) r = 0.0f;  // 0 * inf when 127/amax overflows
-            r = r > 127.0f ? 127.0f : r;
-            r = r < -127.0f ? -127.0f : r;
-            q[i] = (int)r;
-        }
-    }
-    int s = q[0] + q[1] + q[2] + q[3];
-    s += __shfl_xor(s, 1, WAVE);
-    s += __shfl_xor(s, 2, WAVE);
-    s += __shfl_xor(s, 4, WAVE);
-    sub = s;
-    d = amax != 0.0f ? amax / 127.0f : 0.0f;
-    return (uint32_t)(q[0] & 255) | ((uint32_t)(q[1] & 255) << 8) | ((uint32_t)(q[2] & 255) << 16) |
-           ((uint32_t)(q[3] & 255) << 24);
-}
-
-// The same quantisation with 16 lanes per block: lane r of a 16-lane row
-// (DPP row) holds values 16r..16r+15 in v[0..3].  amax is a max and the sums
-// are integers, so the codes, sums and scale are the bytes q8k_quant_lane
-// gives for the block.  Returns the 16 codes; `sub` is the sum of sub-block
-// r/2 (lanes 2j and 2j+1 hold sub-block j).  Every lane of the row must be
-// active.
+// Sixteen lanes per block: lane r of a 16-lane row (DPP row) holds values
+// 16r..16r+15 in v[0..3].  The block scale is amax/127 (0 for an all-zero
+// block); each value is rounded half-to-even from x * (127/amax), both fp32
+// divisions correctly rounded, and clamped to [-127, 127].  amax is a max and
+// the sums are integers, so any lane layout gives the same bytes.  Returns the
+// 16 codes; `sub` is the sum of sub-block r/2 (lanes 2j and 2j+1 hold
+// sub-block j).  Every lane of the row must be active.
 __device__ __forceinline__ uint4 q8k_quant_lane16(const float4 (&v)[4], int& sub, float& d) {
     float amax = 0.0f;
 #pragma unroll
