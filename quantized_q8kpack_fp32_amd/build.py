@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libq8k.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "pack.hip", "matvec.hip", "moe.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "pack.hip", "matvec.hip", "moe.hip", "prefill.hip", "prefill_regw.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -35,9 +35,17 @@ _SCRATCH = re.compile(r"remark: Function Name: (\S+)")
 _SCRATCH_SIZE = re.compile(r"ScratchSize \[bytes/lane\]: (\d+)")
 
 
+# Per-source flags.  The prefill tile with register-resident weight planes
+# folds the matrix-core results with vector instructions, so its MFMAs must
+# write ordinary VGPRs (the accumulation-register form would add a copy per
+# result).
+SOURCE_FLAGS = {"prefill_regw.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> tuple[str, str]:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *[f"-D{d}" for d in defines], "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

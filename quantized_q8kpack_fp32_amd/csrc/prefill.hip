@@ -721,6 +721,9 @@ hipError_t launch_prefill_moe(int fmt, const uint8_t* w, const uint16_t* prefix,
 
 hipError_t launch_prefill(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a,
                           int64_t M, float* y, hipStream_t s) {
+#ifndef Q8K_PREFILL_PC_Q4
+    if (fmt == PF_Q4) return launch_prefill_regw_q4k(w, rows, nb, a, M, y, s);
+#endif
     const dim3 grid((unsigned)(((rows + PF_TN - 1) / PF_TN) * ((M + PF_TM - 1) / PF_TM)));
     if (fmt == PF_Q6)
         hipLaunchKernelGGL(prefill_q4k_kernel<PF_Q6>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,

@@ -1,0 +1,453 @@
+// Prefill GEMM with the weight planes built in registers: Q4_K weight
+// [N rows][K] times M packed q8_K tokens on the gfx950 matrix cores.
+//
+// "Language models on the device: the cajeta-llm kernels", section 2.3 (the
+// prefill tile: widen the weight nibbles to int8, stage ahead, multiply on
+// the matrix units, fold the per-sub-block scales through the accumulator
+// epilogue) and section 1 (the scale/min epilogue).  Per (token m, row n):
+//   y = sum_b d8_b * d_b * I_b  -  sum_b sum_j (d8_b * bsum_bj) * (dmin_b * m_bj)
+// with I_b = sum_j sc_j * S_j, the scale-weighted integer dot of block b.
+//
+// Arithmetic (as in the producer/consumer tile of prefill.hip): each 6-bit
+// scale is split sc = 8a + b and the weight enters the int8 matrix cores as
+// two planes a*q and b*q (each <= 105), so I_b = 8 P_hi + P_lo exactly from
+// two 32x32x32 int8 MFMA passes; the min term runs on the bf16 matrix cores
+// with both operands split into high and low bf16 parts, accumulating in
+// fp32 across blocks.
+//
+// Work split.  The int8 planes of a weight row are reused by every token of
+// the tile, and the token codes by every row.  Here the planes never leave
+// the registers of the wave that builds them: a workgroup of 8 waves (two per
+// SIMD, so one wave's vector work runs beside the other's matrix work) owns
+// 128 tokens x 64 rows; wave w takes rows 32 (w & 1) .. +31 for all 128
+// tokens (four 32-token MFMA tiles, so each plane fragment feeds eight MFMAs)
+// over the blocks b with b % 4 == w >> 1 (a quarter of K).  Only the token
+// codes go through LDS: the buffer unit copies them there (loads that write
+// LDS directly, no registers), double-buffered in stages of 64 tokens x one
+// block per quarter; a wave's planes serve the two stages of its block.  Every
+// token fragment read from LDS feeds two MFMAs (both planes).  The four
+// quarters meet at the end through LDS in a fixed order.
+//
+// Lane map.  32x32x32 int8 MFMA: A = tokens (row l % 32 from lane l), B =
+// weight rows (column l % 32), k-group g = l / 32 holds 16 of the 32 k.  The
+// k order inside a block is free as long as both operands follow it: lane
+// (j, g) owns quant bytes 64g .. 64g+63 of row j's block (values of
+// sub-blocks 4g .. 4g+3), and k-step kk (0..7) takes the low (kk even) or
+// high (kk odd) nibbles of its quant dwords 4(kk/2) .. 4(kk/2)+3: values
+// 64(2g + kk/4) + 32(kk%2) + 16((kk/2)%2) + 0..15, all in sub-block
+// 4g + 2(kk/4) + kk%2, the same 16 contiguous code bytes the token lane reads.
+//
+// Result (i, j) of a 32x32 MFMA is in lane j + 32 ((i / 4) % 2), register
+// (i % 4) + 4 (i / 8): each lane holds one weight row and 16 tokens.
+#include "q8k_device.h"
+#include "q8k_launch.h"
+
+namespace q8k {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+constexpr int RW_TM = 128;  // tokens per workgroup
+constexpr int RW_TN = 64;   // weight rows per workgroup
+constexpr int RW_KQ = 4;    // K quarters (waves per row group)
+constexpr int RW_SM = 64;   // tokens per stage
+constexpr int RW_THREADS = 512;
+
+// LDS, all double-buffered by stage parity: token codes (64 tokens x one
+// block per quarter), the raw block scales and sub-block sums (copied two
+// stages ahead, to build the min-term operands one stage ahead), and from
+// those the min-term operands and the block scales the epilogue reads.  A
+// stage's copies and its reads always touch opposite parities.  Token code
+// rows keep their 256 bytes together (one copy moves four whole rows, so its
+// global reads are contiguous) with the 16-byte chunks XOR-swizzled by the
+// token index: the 16 lanes of a read phase then hit 16 different bank
+// groups.  The min-term operands are stored fragment-major (64 lanes x 16
+// bytes in lane order).  The arrays written by buffer-unit copies and those
+// written by ds stores are separate objects.
+struct RwCopied {
+    int8_t codes[2][RW_KQ][RW_SM][QK];  // [parity][quarter][token][chunk ^ (token & 15)]
+    float d8raw[2][RW_KQ][RW_SM];       // [parity][quarter][token]
+    int16_t bs[2][RW_KQ][RW_SM][8];     // [parity][quarter][token][sub-block]
+};
+struct RwBuilt {
+    float d8[2][RW_KQ][RW_SM];     // [parity][quarter][token]
+    uint4 amin[2][RW_KQ][2][64];   // [parity][quarter][tile][lane (token i, g)]: bf16 d8*bsum_j, j = 4g..4g+3, high then low
+};
+static_assert(sizeof(RwCopied) + sizeof(RwBuilt) <= 160 * 1024, "LDS of one workgroup");
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ uint32_t lds_addr(void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
+
+// Buffer-unit copy of 16 (4) bytes per lane from `off` into LDS at base +
+// 16 (4) * lane; out-of-range reads write zeros.  Issued as inline assembly:
+// the compiler then does not count the copies among its own loads, so it
+// inserts no waits for them before unrelated LDS reads (it cannot tell the
+// two parities of a buffer apart).  Every read of copied data comes after a
+// stage_barrier(), whose vmcnt wait covers the copies.  (M0 holds the LDS
+// base; one wait state between writing M0 and the copy.)
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds_base, int off) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr(lds_base)), "v"(off), "s"(r)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(rsrc_t r, void* lds_base, int off) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr(lds_base)), "v"(off), "s"(r)
+                 : "memory", "m0");
+}
+
+// Four byte-wise products q_i * k (q_i <= 15, k <= 7: every product stays
+// inside its byte) as one packed 16-bit multiply.
+__device__ __forceinline__ uint32_t mul_bytes(uint32_t q, uint32_t k) {
+    const v2u16 kk = {(unsigned short)k, (unsigned short)k};
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2u16, q) * kk);
+}
+
+// bf16 high and low parts of v (round to nearest even both times): v - hi is
+// exact in fp32, so hi + lo carries 16 significant bits of v.
+__device__ __forceinline__ void bf16_split(float v, __bf16& hi, __bf16& lo) {
+    hi = (__bf16)v;
+    lo = (__bf16)(v - (float)hi);
+}
+
+// Sources of one workgroup: tokens m0.., rows n0...  Offsets stay 32-bit: a
+// tile's rows span at most 64 * (K / 256) * 144 bytes, its tokens 128 * K.
+// The byte counts from the tile's start to the end of each buffer are
+// clamped to 2^31 - 1 once, so every resource range below is one 32-bit
+// subtraction and a clamp at zero (scalar): no read the kernel issues lies
+// past 2^31 - 1 bytes from its tile's start.
+struct RwSrc {
+    const uint8_t* w;
+    const int8_t* x;
+    const float* d8;
+    const int16_t* bs;
+    int wbytes, xbytes, d8bytes, bsbytes;
+    int wrow;  // bytes per weight row
+    int nb;
+    int K;
+};
+__device__ __forceinline__ int clamp31(int64_t v) { return v <= 0 ? 0 : v < 0x7fffffff ? (int)v : 0x7fffffff; }
+// Raw buffer resource over [base, base + max(remaining, 0)).
+__device__ __forceinline__ rsrc_t rsrc32(const void* base, int remaining) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, remaining > 0 ? remaining : 0,
+                                             0x00020000 /* raw, untyped dwords */);
+}
+
+// Byte offset inside a 256-value block of the 16 codes lane (i, g) supplies at
+// k-step kk: values 64(2g + kk/4) + 32(kk%2) + 16((kk/2)%2) .. +15.
+__host__ __device__ constexpr int kstep_off(int g, int kk) {
+    return 128 * g + 64 * (kk >> 2) + 32 * (kk & 1) + 16 * ((kk >> 1) & 1);
+}
+
+// The buffer-unit copies of stage sg = 2 s + h (tokens 64 h .. 64 h + 63 of
+// the tile, block 4 s + q of quarter q) by wave wv: codes of 32 token rows of
+// quarter wv >> 1 (8 copies of four whole rows), and one copy of block scales
+// (waves 0..3) or sub-block sums (waves 4..7) of one quarter.
+__device__ __forceinline__ void issue_codes(RwCopied& sm, const RwSrc& S, int sg, int wv, int lane) {
+    const int s = sg >> 1, h = sg & 1;
+    const int q = wv >> 1, half = wv & 1;
+    const int tq = lane >> 4, pc = lane & 15;
+    // copy i covers stage tokens 32 half + 4i + tq; its resource starts at that
+    // group's first token (scalar), so the lane offsets repeat with period 4 in i
+    const int base = (RW_SM * h + 32 * half) * S.K + (4 * s + q) * QK;
+    int vo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vo[j] = tq * S.K + 16 * (pc ^ (4 * j + tq));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int o = base + 4 * i * S.K;
+        const rsrc_t rx = rsrc32(S.x + o, S.xbytes - o);
+        dma16(rx, &sm.codes[sg & 1][q][32 * half + 4 * i][0], vo[i & 3]);
+    }
+}
+__device__ __forceinline__ void issue_aux(RwCopied& sm, const RwSrc& S, int sg, int wv, int lane) {
+    const int s = sg >> 1, h = sg & 1, st = sg & 1;
+    const int q = wv & 3;
+    const int t0 = RW_SM * h;  // first token of the stage
+    const int off = lane * S.nb;  // token 64 h + lane, block 4 s + q, in units of one block's record
+    if (wv < 4) {
+        const int o = (t0 * S.nb + 4 * s + q) * 4;
+        dma4(rsrc32((const char*)S.d8 + o, S.d8bytes - o), &sm.d8raw[st][q][0], off * 4);
+    } else {
+        const int o = (t0 * S.nb + 4 * s + q) * 16;
+        dma16(rsrc32((const char*)S.bs + o, S.bsbytes - o), &sm.bs[st][q][0][0], off * 16);
+    }
+}
+
+// Raw weight bytes of one (row, block) for lane (j, g): the 16-byte header
+// (d, dmin, 12 scale bytes) and quant bytes 64g .. 64g+63.
+struct RwRaw {
+    uint4 hdr, q[4];
+};
+__device__ __forceinline__ void load_weights(RwRaw& R, const RwSrc& S, int b, int rg, int lane) {
+    // (blocks past the row's end read the next row's bytes or, past the last
+    // row, zeros: they are never multiplied)
+    const int boff = b * Q4K_BLOCK;
+    const rsrc_t rw = rsrc32(S.w + boff, S.wbytes - boff);
+    const int o = (32 * rg + (lane & 31)) * S.wrow;
+    R.hdr = load16(rw, o);
+    const int oq = o + 16 + 64 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) R.q[i] = load16(rw, oq + 16 * i);
+}
+
+// Min-term operands and block scales of the tokens of stage sg from the raw
+// scales and sums:
+// thread tid takes quarter (tid >> 6) & 3, token tid & 63, sub-blocks 4g ..
+// 4g+3 with g = tid >> 8.
+__device__ __forceinline__ void build_amin(const RwCopied& sm, RwBuilt& sb, int sg, int tid) {
+    const int q = (tid >> 6) & 3, t = tid & 63, g = tid >> 8;
+    const int st = sg & 1;
+    const float d8 = sm.d8raw[st][q][t];
+    if (g == 0) sb.d8[st][q][t] = d8;
+    const uint2 bv = *reinterpret_cast<const uint2*>(&sm.bs[st][q][t][4 * g]);
+    const uint32_t bw[2] = {bv.x, bv.y};
+    v8bf o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int sj = (int)(int16_t)(bw[j >> 1] >> (16 * (j & 1)));
+        __bf16 hi, lo;
+        bf16_split(d8 * (float)sj, hi, lo);
+        o[j] = hi;
+        o[4 + j] = lo;
+    }
+    *reinterpret_cast<v8bf*>(&sb.amin[sg & 1][q][t >> 5][(t & 31) + 32 * g]) = o;
+}
+
+// The operands of one (row, block) for lane (j, g), built from its raw bytes:
+// the two planes of the 8 k-steps, the row's min-term operands and its d.
+struct RwPlanes {
+    v4i ph[8], pl[8];
+    v8bf bh, bl;
+    float dd;
+};
+__device__ __forceinline__ void build_planes(RwPlanes& P, const RwRaw& R, int lane) {
+    const int g = lane >> 5;
+    // ---- scales and mins of sub-blocks 4g .. 4g+3 as bytes
+    const uint32_t y = R.hdr.y, z = R.hdr.z, wq = R.hdr.w;
+    // (branch-free: g differs between the two halves of the wave)
+    const uint32_t hm = 0u - (uint32_t)g;
+    const uint32_t sc = (hm & ((wq & 0x0F0F0F0Fu) | ((y >> 2) & 0x30303030u))) | (~hm & y & 0x3F3F3F3Fu);
+    const uint32_t mn = (hm & (((wq >> 4) & 0x0F0F0F0Fu) | ((z >> 2) & 0x30303030u))) | (~hm & z & 0x3F3F3F3Fu);
+    const uint32_t av = (sc >> 3) & 0x07070707u, bvv = sc & 0x07070707u;
+    P.dd = half_bits_to_float(R.hdr.x & 0xffffu);
+    const float dmin = half_bits_to_float(R.hdr.x >> 16);
+    // ---- row min-term operands: -dmin * m_j (exact in fp32), high / low bf16
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        __bf16 hi, lo;
+        bf16_split(-dmin * (float)((mn >> (8 * e)) & 0xffu), hi, lo);
+        P.bh[e] = P.bh[4 + e] = hi;
+        P.bl[e] = P.bl[4 + e] = lo;
+    }
+    // ---- the two planes of the 8 k-steps
+    const uint32_t raw[16] = {R.q[0].x, R.q[0].y, R.q[0].z, R.q[0].w, R.q[1].x, R.q[1].y, R.q[1].z, R.q[1].w,
+                              R.q[2].x, R.q[2].y, R.q[2].z, R.q[2].w, R.q[3].x, R.q[3].y, R.q[3].z, R.q[3].w};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const int e = 2 * (kk >> 2) + (kk & 1);
+        const uint32_t ka = (av >> (8 * e)) & 0xffu, kb = (bvv >> (8 * e)) & 0xffu;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const uint32_t r = raw[4 * (kk >> 1) + x];
+            const uint32_t nib = (kk & 1) ? ((r >> 4) & 0x0F0F0F0Fu) : (r & 0x0F0F0F0Fu);
+            P.ph[kk][x] = (int)mul_bytes(nib, ka);
+            P.pl[kk][x] = (int)mul_bytes(nib, kb);
+        }
+    }
+}
+
+// One stage of one wave: 64 tokens x 32 rows of block 4 s + q, two MFMA tiles
+// of 32 tokens, into the accumulators of tiles 2h and 2h + 1.
+__device__ __forceinline__ void wave_stage(const RwCopied& sm, const RwBuilt& sb, const RwPlanes& P, int sg, int q,
+                                           int lane,
+                                           v16f (&acc)[4]) {
+    const int g = lane >> 5, h = sg & 1;
+    // Code fragment of lane (i, g) at k-step kk: row i of the tile, logical
+    // chunk kstep_off(g, kk) / 16 stored at chunk ^ (i & 15): one XOR per read.
+    const int i = lane & 31;
+    const int8_t* rowp = &sm.codes[sg & 1][q][i][0];
+    const int y16 = 16 * (i & 15) ^ 128 * g;
+    auto frag = [&](int t, int kk) {
+        return *reinterpret_cast<const v4i*>(rowp + (y16 ^ kstep_off(0, kk)) + t * 32 * QK);
+    };
+    const float* d8row = &sb.d8[sg & 1][q][0];
+    // The eight code fragments of a tile are read before its MFMAs (one LDS
+    // latency per tile).  Both planes use them: the high plane's chain first,
+    // then its sum times 8, then the low plane's chain into the same
+    // accumulator, which then holds I = 8 P_hi + P_lo.
+    auto chains = [&](int t, v16i& I) {
+        v4i a[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) a[kk] = frag(t, kk);
+        {
+            const v16i zero = {};
+            I = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0], P.ph[0], zero, 0, 0, 0);
+        }
+#pragma unroll
+        for (int kk = 1; kk < 8; ++kk) I = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[kk], P.ph[kk], I, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) I[r] <<= 3;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) I = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[kk], P.pl[kk], I, 0, 0, 0);
+    };
+    // min term: [ah | al] x [bh | bh] and [ah | al] x [bl | bl]
+    auto minterm = [&](int t) {
+        v16f& ac = acc[2 * h + t];
+        const v8bf am = *reinterpret_cast<const v8bf*>(&sb.amin[sg & 1][q][t][lane]);
+        ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, P.bh, ac, 0, 0, 0);
+        ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, P.bl, ac, 0, 0, 0);
+    };
+    // block epilogue: acc += (d8 * float(I)) * d
+    auto fold = [&](int t, const v16i& I) {
+        v16f& ac = acc[2 * h + t];
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+            const float4 dv = *reinterpret_cast<const float4*>(d8row + 32 * t + 8 * G + 4 * g);
+            const float d8a[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * G + e;
+                ac[r] = fmaf((float)I[r] * d8a[e], P.dd, ac[r]);
+            }
+        }
+    };
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        v16i I;
+        chains(t, I);
+        minterm(t);
+        fold(t, I);
+    }
+}
+
+// The stage's LDS writes (ds stores of this wave and buffer-unit copies) done,
+// then the workgroup barrier.  `keep` loads issued last may stay in flight
+// (the next block's weight bytes, which land in registers).
+template <int keep>
+__device__ __forceinline__ void stage_barrier() {
+    if constexpr (keep == 0)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(keep) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+constexpr int RW_RAW_LOADS = 5;  // load_weights() issues five loads
+
+__global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
+    const uint8_t* __restrict__ w, int64_t rows, int nb, const int8_t* __restrict__ qs,
+    const float* __restrict__ d8, const int16_t* __restrict__ bs, int64_t K, int64_t M, float* __restrict__ y) {
+    __shared__ __attribute__((aligned(16))) RwCopied sm;
+    __shared__ __attribute__((aligned(16))) RwBuilt sb;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int rg = wv & 1, q = wv >> 1;
+    // Tiles of one XCD (workgroups b, b + 8, ...) take consecutive tile indices,
+    // so they share token tiles in their L2.
+    const int64_t ntn = (rows + RW_TN - 1) / RW_TN, ntm = (M + RW_TM - 1) / RW_TM;
+    const int64_t G = ntn * ntm;
+    const int64_t L = (G % 8 == 0) ? ((int64_t)(blockIdx.x % 8) * (G / 8) + blockIdx.x / 8) : (int64_t)blockIdx.x;
+    const int64_t n0 = (L % ntn) * RW_TN, m0 = (L / ntn) * RW_TM;
+
+    RwSrc S;
+    S.nb = nb;
+    S.K = (int)K;
+    S.wrow = nb * Q4K_BLOCK;
+    S.w = w + n0 * S.wrow;
+    S.wbytes = clamp31((rows - n0) * S.wrow);
+    S.x = qs + m0 * K;
+    S.xbytes = clamp31((M - m0) * K);
+    S.d8 = d8 + m0 * nb;
+    S.d8bytes = clamp31((M - m0) * nb * 4);
+    S.bs = bs + m0 * nb * 8;
+    S.bsbytes = clamp31((M - m0) * nb * 16);
+
+    const int steps = (nb + RW_KQ - 1) / RW_KQ;
+    const int nst = 2 * steps;                        // stages
+    const bool half2 = M - m0 > RW_SM;                // the tile's second 64 tokens exist
+    v16f acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+
+    RwRaw R;
+    issue_codes(sm, S, 0, wv, lane);
+    issue_aux(sm, S, 0, wv, lane);
+    issue_aux(sm, S, 1, wv, lane);
+    load_weights(R, S, q, rg, lane);
+    stage_barrier<0>();
+    build_amin(sm, sb, 0, tid);
+    stage_barrier<0>();
+    RwPlanes PL;
+    for (int sg = 0; sg < nst; sg += 2) {
+        const int b = 2 * sg + q;  // block of this wave in step sg / 2
+        // ---- first 64 tokens: copies of the next stage (codes) and the one
+        // after (scales, sums); this block's operands, then the next block's raw
+        // bytes into the same registers (issued last: they may stay in flight
+        // across the barrier)
+        // (R landed at the last barrier; the empty use makes the compiler place
+        // its own wait for R here, before copies it does not know about)
+        asm volatile("" ::"v"(__builtin_bit_cast(v4i, R.hdr)), "v"(__builtin_bit_cast(v4i, R.q[0])),
+                     "v"(__builtin_bit_cast(v4i, R.q[1])), "v"(__builtin_bit_cast(v4i, R.q[2])),
+                     "v"(__builtin_bit_cast(v4i, R.q[3])));
+        issue_codes(sm, S, sg + 1, wv, lane);
+        if (sg + 2 < nst) issue_aux(sm, S, sg + 2, wv, lane);
+        build_planes(PL, R, lane);
+        load_weights(R, S, b + RW_KQ, rg, lane);
+        if (b < nb) wave_stage(sm, sb, PL, sg, q, lane, acc);
+        build_amin(sm, sb, sg + 1, tid);
+        stage_barrier<RW_RAW_LOADS>();
+        // ---- second 64 tokens
+        if (sg + 2 < nst) issue_codes(sm, S, sg + 2, wv, lane);
+        if (sg + 3 < nst) issue_aux(sm, S, sg + 3, wv, lane);
+        if (b < nb && half2) wave_stage(sm, sb, PL, sg + 1, q, lane, acc);
+        if (sg + 2 < nst) build_amin(sm, sb, sg + 2, tid);
+        stage_barrier<0>();
+    }
+    // quarters 1..3 hand their sums to quarter 0 (fixed order q = 0, 1, 2, 3).
+    // The lane index is read afresh (mbcnt) so that nothing lane-dependent
+    // stays live across the loop for this epilogue.
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    float* red = reinterpret_cast<float*>(&sm.codes[0][0][0][0]);
+    if (q > 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[((((q - 1) * 2 + rg) * 4 + t) * 16 + r) * 64 + ln] = acc[t][r];
+    }
+    __syncthreads();
+    if (q == 0) {
+        const int64_t n = n0 + 32 * rg + (ln & 31);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + 32 * t + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+                float v = acc[t][r];
+#pragma unroll
+                for (int qq = 1; qq < RW_KQ; ++qq) v += red[((((qq - 1) * 2 + rg) * 4 + t) * 16 + r) * 64 + ln];
+                if (m < M && n < rows) y[m * rows + n] = v;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_regw_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
+                                   hipStream_t s) {
+    const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * ((M + RW_TM - 1) / RW_TM)));
+    hipLaunchKernelGGL(prefill_regw_q4k_kernel, grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K, M,
+                       y);
+    return hipGetLastError();
+}
+
+}  // namespace q8k

@@ -51,6 +51,10 @@ hipError_t launch_moe_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t
                           int64_t T, const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s);
 hipError_t launch_prefill(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a, int64_t M,
                           float* y, hipStream_t s);
+// Q4_K prefill with the weight planes built in the registers of the waves that
+// multiply them (prefill_regw.hip).
+hipError_t launch_prefill_regw_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
+                                   hipStream_t s);
 
 // Workspace of the MoE prefill, byte offsets from its start: the fp32 result
 // of every (token, slot) pair [P][rows]; then, 256-aligned, the chunk count
