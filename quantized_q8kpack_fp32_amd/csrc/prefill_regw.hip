@@ -349,12 +349,12 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int rg = wv & 1, q = wv >> 1;
-    // Tiles of one XCD (workgroups b, b + 8, ...) take consecutive tile indices,
-    // so they share token tiles in their L2.
-    const int64_t ntn = (rows + RW_TN - 1) / RW_TN, ntm = (M + RW_TM - 1) / RW_TM;
-    const int64_t G = ntn * ntm;
-    const int64_t L = (G % 8 == 0) ? ((int64_t)(blockIdx.x % 8) * (G / 8) + blockIdx.x / 8) : (int64_t)blockIdx.x;
-    const int64_t n0 = (L % ntn) * RW_TN, m0 = (L / ntn) * RW_TM;
+    // Row tiles vary fastest: the workgroups on one XCD (b, b + 8, ...) then
+    // cover every token tile and a set of row tiles, so each weight row is
+    // fetched into one L2 (measured: fewer L2 misses and faster than giving
+    // each XCD one token tile).
+    const int64_t ntn = (rows + RW_TN - 1) / RW_TN;
+    const int64_t n0 = ((int64_t)blockIdx.x % ntn) * RW_TN, m0 = ((int64_t)blockIdx.x / ntn) * RW_TM;
 
     RwSrc S;
     S.nb = nb;
