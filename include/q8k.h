@@ -146,7 +146,7 @@ int qmatvec_batched(int qtype, const void* w, int64_t rows, int64_t K, const voi
 int qmatvec_f32(int qtype, const void* w, int64_t rows, int64_t K, const float* x, int64_t ncols, float* y,
                 void* xq_out, void* stream);
 
-/* qmatvec_moe: expert-indexed decode./* qmatvec_moe: expert-indexed decode.  w holds E experts, each a rows x K
+/* qmatvec_moe: expert-indexed decode.  w holds E experts, each a rows x K
  * weight in the given layout, expert e's blocks following expert e-1's.
  * xq: q8_K buffer of T tokens (0 <= T <= Q8K_MOE_MAX_TOKENS); ids int32
  * [T][topk]; rw fp32 [T][topk]; 1 <= topk <= min(E, Q8K_MOE_MAX_TOPK).

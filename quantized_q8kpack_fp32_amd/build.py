@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libq8k.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "pack.hip", "matvec.hip", "moe.hip", "prefill.hip", "prefill_regw.hip"]
+SOURCES = ["api.cpp", "pack.hip", "matvec.hip", "moe.hip", "moe_mfma.hip", "prefill.hip", "prefill_regw.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -35,11 +35,12 @@ _SCRATCH = re.compile(r"remark: Function Name: (\S+)")
 _SCRATCH_SIZE = re.compile(r"ScratchSize \[bytes/lane\]: (\d+)")
 
 
-# Per-source flags.  The prefill tile with register-resident weight planes
-# folds the matrix-core results with vector instructions, so its MFMAs must
-# write ordinary VGPRs (the accumulation-register form would add a copy per
+# Per-source flags.  The tiles with register-resident weight planes (prefill,
+# mixture-of-experts decode) fold the matrix-core results with vector
+# instructions, so their MFMAs must write ordinary VGPRs (the accumulation-register form would add a copy per
 # result).
-SOURCE_FLAGS = {"prefill_regw.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"prefill_regw.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "moe_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> tuple[str, str]:

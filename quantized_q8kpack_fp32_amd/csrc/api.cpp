@@ -259,7 +259,14 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
     const Acts a = acts_of(xq, T, K);
     hipError_t e;
     if (qtype == Q8K_Q4_K) {
-        e = launch_moe_q4k(static_cast<const uint8_t*>(w), E, rows, nb, a, T, ids, rw, topk, y, (hipStream_t)stream);
+        // matrix-core kernel while a packed token fits its LDS stage (K up to
+        // about 119k), the one-lane-per-row kernel beyond
+        if (moe_mfma_q4k_fits(K))
+            e = launch_moe_mfma_q4k(static_cast<const uint8_t*>(w), E, rows, nb, a, T, ids, rw, topk, y,
+                                    (hipStream_t)stream);
+        else
+            e = launch_moe_q4k(static_cast<const uint8_t*>(w), E, rows, nb, a, T, ids, rw, topk, y,
+                               (hipStream_t)stream);
     } else if (qtype == Q8K_Q5_K) {
         e = launch_moe_q5k(static_cast<const uint8_t*>(w), E, rows, nb, a, T, ids, rw, topk, y, (hipStream_t)stream);
     } else {

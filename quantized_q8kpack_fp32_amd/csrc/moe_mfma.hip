@@ -1,0 +1,343 @@
+// Mixture-of-experts decode for Q4_K on the int8 matrix cores.
+//
+// "Language models on the device: the cajeta-llm kernels", section 2.4: for a
+// decode, every token's selected experts are visited in one launch and each
+// token's expert outputs are summed as they are produced; weights are read
+// through the index of which expert each token chose (section intro).
+//
+// A workgroup owns 32 consecutive rows of every expert; its MM_WAVES waves take
+// the experts w, w + MM_WAVES, ... .  For expert e a wave lists the (token,
+// slot) pairs that chose e (a ballot over ids) and multiplies its 32 rows
+// against up to 32 of those pairs at a time as one 32x32 int8 MFMA tile per
+// k-step: the pairs' q8_K codes are the A operand (row i = pair i of the
+// group), the rows' Q4_K blocks the B operand, built in registers as the two
+// planes a*q and b*q of the split scale sc = 8a + b (q4k_planes.h), so one
+// weight read serves every pair of the group.  Per block: the high plane's
+// chain of eight MFMAs, its sum times 8, the low plane's chain into the same
+// int32 accumulator (I = 8 P_hi + P_lo, exact); the min term on the bf16
+// matrix path (both operands split in high and low parts) into the fp32
+// accumulator; then acc += (d8 * float(I)) * d for the pairs present.
+//
+// The dot of pair p and row r lands in an LDS slot owned by p; once every wave
+// is done the workgroup adds each token's slots in slot order,
+//   y[t][r] = sum_k rw[t][k] * dot(ids[t][k], t, r),
+// so the order of the sum is fixed and no atomics or global workspace are
+// used.  Tokens are taken in slabs of at most MM_SLOT pairs whose packed
+// tokens fit the workgroup's LDS stage (codes, sub-block sums and scales of
+// every slab token, copied once per slab): the pairs' operands are then LDS
+// reads, so the only vector-memory loads in flight during the block walk are
+// the weight blocks, and each wave keeps the next two in flight while it
+// multiplies the current one (vector loads complete in issue order, so token
+// loads interleaved with them would cut that depth to one).  An expert nobody
+// chose is never read; an id outside [0, E) matches no expert and its slot is
+// skipped.
+#include "q4k_planes.h"
+#include "q8k.h"
+#include "q8k_launch.h"
+
+#include <atomic>
+
+namespace q8k {
+namespace {
+
+constexpr int MM_WAVES = 8;   // waves per workgroup
+constexpr int MM_ROWS = 32;   // rows per workgroup (the MFMA's B columns)
+constexpr int MM_SLOT = 128;  // (token, slot) pairs per slab
+static_assert(MM_SLOT >= Q8K_MOE_MAX_TOPK, "a slab holds at least one token's pairs");
+constexpr int MM_TOK_BYTES = 98304;  // LDS stage of the slab's packed tokens
+constexpr int MM_TILE = MM_ROWS * Q4K_BLOCK;  // one block of the workgroup's rows: 4608 bytes
+
+// LDS bytes of one staged token: codes padded by 16 bytes (consecutive tokens
+// start 4 banks apart), sub-block sums, block scales.
+__host__ __device__ constexpr int64_t mm_tok_bytes(int64_t K) { return (K + 16) + K / 16 + K / 64; }
+
+struct MmWave {
+    int plist[64];  // pair indices of the current 64-pair window that chose the wave's expert, by rank
+    float d8[32];   // the group's block scales (pair i at i) for the epilogue
+    __attribute__((aligned(16))) uint8_t tile[MM_TILE];  // block b of rows r0..r0+31, [row][144 B]
+};
+struct MmSmem {
+    MmWave wave[MM_WAVES];
+    float slot[MM_SLOT * MM_ROWS];  // dot of (pair, row), pair-major
+    // slab tokens: codes [ts][K + 16], then sums [ts][K / 32] int16, then scales [ts][K / 256] fp32
+    int8_t tok[MM_TOK_BYTES];
+};
+
+// One block of the workgroup's 32 rows, loaded by hand in a sector-contiguous
+// lane map: load x of lane l takes 16-byte chunk c = 64x + l of the 288 chunks
+// (row c / 9, chunk c % 9 of its 144-byte block; the fifth load's upper half
+// repeats the lower half), so consecutive lanes read consecutive bytes and a
+// load instruction touches 2-3 cache lines per row instead of 32 scattered
+// pieces.  The wave then moves the block through its LDS tile into the
+// matrix-core lane map.  The walk keeps two blocks in flight behind the one it
+// multiplies and waits for that one with an explicit count (it issues no other
+// vector-memory load); the wait names the registers it covers, so the compiler
+// neither reads them earlier nor reuses them while a load into them is in
+// flight.
+struct MmW {
+    v4i c[5];
+};
+constexpr int MM_W_LOADS = 5;  // loads per block and lane
+template <int IMM>
+__device__ __forceinline__ v4i mm_vload16(rsrc_t r, int off) {
+    v4i v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3" : "=v"(v) : "v"(off), "s"(r), "n"(IMM));
+    return v;
+}
+// Lane l's five chunk offsets inside a row-major run of 32 rows (block 0).
+struct MmLane {
+    int go[MM_W_LOADS];  // global: row * row_bytes + 16 * chunk
+    int lo[MM_W_LOADS];  // LDS tile: 16 * c
+};
+__device__ __forceinline__ MmLane mm_lane(int lane, int64_t wrow) {
+    MmLane m;
+#pragma unroll
+    for (int x = 0; x < MM_W_LOADS; ++x) {
+        const int c = x < 4 ? 64 * x + lane : 256 + (lane & 31);
+        m.go[x] = (c / 9) * (int)wrow + 16 * (c % 9);
+        m.lo[x] = 16 * c;
+    }
+    return m;
+}
+__device__ __forceinline__ void mm_issue_w(MmW& W, rsrc_t wr, const MmLane& m, int b) {
+    const int boff = b * Q4K_BLOCK;
+    W.c[0] = mm_vload16<0>(wr, m.go[0] + boff);
+    W.c[1] = mm_vload16<0>(wr, m.go[1] + boff);
+    W.c[2] = mm_vload16<0>(wr, m.go[2] + boff);
+    W.c[3] = mm_vload16<0>(wr, m.go[3] + boff);
+    W.c[4] = mm_vload16<0>(wr, m.go[4] + boff);
+}
+template <int N>
+__device__ __forceinline__ void mm_wait_w(MmW& W) {
+    asm volatile("s_waitcnt vmcnt(%5)" : "+v"(W.c[0]), "+v"(W.c[1]), "+v"(W.c[2]), "+v"(W.c[3]), "+v"(W.c[4]) : "n"(N));
+}
+
+// The wave hands data between its own lanes through LDS.  The hardware runs
+// one wave's LDS instructions in order, but the compiler reasons per thread:
+// the memory clobbers keep a lane's reads behind the other lanes' writes and
+// the next writes behind the reads.
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
+    const uint8_t* __restrict__ w, int64_t E, int64_t rows, int nb, const int8_t* __restrict__ qs,
+    const float* __restrict__ d8, const int16_t* __restrict__ bs, int64_t K, int64_t T,
+    const int32_t* __restrict__ ids, const float* __restrict__ rw, int topk, float* __restrict__ y, int rt,
+    int64_t ntiles) {
+    __shared__ __attribute__((aligned(16))) MmSmem sm;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: expert and rsrc are scalar
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 31, g = lane >> 5;
+    const int64_t wrow = (int64_t)nb * Q4K_BLOCK;
+    MmWave& L = sm.wave[wv];
+    const MmLane ml = mm_lane(lane, wrow);  // rows past `live` read zeros
+    const int64_t KS = K + 16, cpt = K / 16;  // staged code row stride; 16-byte chunks of codes per token
+    const int64_t tsl = MM_TOK_BYTES / mm_tok_bytes(K);  // >= 1 (checked by the launcher)
+    const int64_t ts = MM_SLOT / topk < tsl ? MM_SLOT / topk : tsl;  // tokens per slab
+    int8_t* const tokc = sm.tok;
+    int8_t* const tokb = sm.tok + ts * KS;
+    float* const tokd = reinterpret_cast<float*>(sm.tok + ts * KS + ts * cpt);
+    for (int64_t t0 = 0; t0 < T; t0 += ts) {
+        const int64_t t1 = t0 + ts < T ? t0 + ts : T;
+        const int64_t pb = t0 * topk, pe = t1 * topk;
+        // ---- stage the slab's packed tokens
+        {
+            const int64_t nt = t1 - t0;
+            for (int64_t c = threadIdx.x; c < nt * cpt; c += 64 * MM_WAVES) {
+                const int64_t t = c / cpt, o = c - t * cpt;
+                *reinterpret_cast<v4i*>(tokc + t * KS + 16 * o) =
+                    *reinterpret_cast<const v4i*>(qs + (t0 + t) * K + 16 * o);
+            }
+            // sums: one 16-byte chunk per block; scales: one fp32 per block
+            for (int64_t c = threadIdx.x; c < nt * nb; c += 64 * MM_WAVES) {
+                *reinterpret_cast<v4i*>(tokb + 16 * c) = *reinterpret_cast<const v4i*>(bs + (t0 * nb + c) * 8);
+                tokd[c] = d8[t0 * nb + c];
+            }
+        }
+        __syncthreads();
+        for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t r0 = tile * rt;
+        const int64_t live = rows - r0 < rt ? rows - r0 : rt;  // rows of this tile
+        for (int64_t e = wv; e < E; e += MM_WAVES) {
+            const rsrc_t wr = make_rsrc(w + (e * rows + r0) * wrow, live * wrow);
+            for (int64_t p0 = pb; p0 < pe; p0 += 64) {
+                const int64_t p = p0 + lane;
+                const bool hit = p < pe && ids[p] == (int32_t)e;
+                const uint64_t mask = __ballot(hit);
+                if (mask == 0) continue;
+                const int count = __popcll(mask);
+                // pair indices by rank in the window
+                wave_lds_fence();
+                if (hit) L.plist[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u))] = (int)p;
+                wave_lds_fence();
+                for (int k0 = 0; k0 < count; k0 += 32) {
+                    const int n = count - k0 < 32 ? count - k0 : 32;  // pairs of this group
+                    // code lane (i, g) takes pair k0 + i (pair k0 when the group has fewer)
+                    const int pi = L.plist[k0 + (i < n ? i : 0)];
+                    const int tl = (int)(pi / topk - t0);  // the pair's token in the slab stage
+                    const int8_t* xrow = tokc + tl * KS;
+                    const int8_t* bsrow = tokb + tl * cpt + 8 * g;
+                    const float* d8row = tokd + tl * nb;
+                    v16f acc = {};
+                    // The weights of three blocks are in registers at once: block b's
+                    // (multiplied now) and blocks b+1, b+2 (in flight).  Block j lives in
+                    // W[j mod 3] (W0, W1, W2 named apart: no register copies); the walk
+                    // starts at b = -2 with two load-only steps.  The last two steps
+                    // reload the row's last block (a cache hit, never used) and the
+                    // walk ends by draining them: no load outlives it.
+                    MmW W0, W1, W2;
+                    auto step = [&](int b, MmW& Wc, MmW& Wfree) {
+                        mm_issue_w(Wfree, wr, ml, b + 2 < nb ? b + 2 : nb - 1);
+                        if (b < 0) return;
+                        mm_wait_w<2 * MM_W_LOADS>(Wc);
+                        // block b through the tile: lane (i, g) takes row i's header
+                        // and its quant bytes 64g .. 64g+63
+                        Q4kRaw R;
+                        wave_lds_fence();
+#pragma unroll
+                        for (int x = 0; x < MM_W_LOADS; ++x) *reinterpret_cast<v4i*>(L.tile + ml.lo[x]) = Wc.c[x];
+                        wave_lds_fence();
+                        {
+                            const uint8_t* tr = L.tile + i * Q4K_BLOCK;
+                            R.hdr = *reinterpret_cast<const uint4*>(tr);
+#pragma unroll
+                            for (int x = 0; x < 4; ++x) R.q[x] = *reinterpret_cast<const uint4*>(tr + 16 + 64 * g + 16 * x);
+                        }
+                        // the pair's operand: codes of sub-blocks 4g..4g+3, their sums, the block scale
+                        v4i A[8];
+#pragma unroll
+                        for (int kk = 0; kk < 8; ++kk)
+                            A[kk] = *reinterpret_cast<const v4i*>(xrow + b * QK + kstep_off(g, kk));
+                        const uint2 bsv = *reinterpret_cast<const uint2*>(bsrow + 16 * b);
+                        const float a8 = d8row[b];
+                        Q4kPlanes P;
+                        build_q4k_planes(P, R, lane);
+                        // ---- integer chains
+                        v16i I;
+                        {
+                            const v16i zero = {};
+                            I = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[0], P.ph[0], zero, 0, 0, 0);
+                        }
+#pragma unroll
+                        for (int kk = 1; kk < 8; ++kk)
+                            I = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[kk], P.ph[kk], I, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) I[r] <<= 3;
+                        // the low chain reads the codes again: holding them across both
+                        // chains costs the registers the third weight block needs
+                        asm volatile("" ::: "memory");
+#pragma unroll
+                        for (int kk = 0; kk < 8; ++kk) {
+                            const v4i a2 = *reinterpret_cast<const v4i*>(xrow + b * QK + kstep_off(g, kk));
+                            I = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2, P.pl[kk], I, 0, 0, 0);
+                        }
+                        // ---- min term: the pair's d8 * bsum_j (j = 4g..4g+3), high
+                        // then low bf16 parts, against [bh | bh] and [bl | bl]
+                        {
+                            v8bf am;
+                            const uint32_t bw[2] = {bsv.x, bsv.y};
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const int sj = (int)(int16_t)(bw[j >> 1] >> (16 * (j & 1)));
+                                __bf16 hi, lo;
+                                bf16_split(a8 * (float)sj, hi, lo);
+                                am[j] = hi;
+                                am[4 + j] = lo;
+                            }
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, P.bh, acc, 0, 0, 0);
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, P.bl, acc, 0, 0, 0);
+                        }
+                        // ---- epilogue: acc += (d8 * float(I)) * d for the pairs
+                        // present; register r of lane l holds pair 8(r/4) + 4g + r%4
+                        wave_lds_fence();
+                        if (g == 0) L.d8[i] = a8;
+                        wave_lds_fence();
+#pragma unroll
+                        for (int G = 0; G < 4; ++G) {
+                            if (8 * G < n) {  // wave-uniform
+                                const float4 dv = *reinterpret_cast<const float4*>(&L.d8[8 * G + 4 * g]);
+                                const float d8a[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+                                for (int e2 = 0; e2 < 4; ++e2) {
+                                    const int r = 4 * G + e2;
+                                    acc[r] = fmaf((float)I[r] * d8a[e2], P.dd, acc[r]);
+                                }
+                            }
+                        }
+                    };
+                    for (int b = -2; b < nb; b += 3) {
+                        step(b, W1, W0);
+                        if (b + 1 == nb) break;
+                        step(b + 1, W2, W1);
+                        if (b + 2 == nb) break;
+                        step(b + 2, W0, W2);
+                    }
+                    mm_wait_w<0>(W0);
+                    mm_wait_w<0>(W1);
+                    mm_wait_w<0>(W2);
+                    // ---- the group's dots into their pairs' slots (row i of the
+                    // workgroup is this lane's weight row)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int pr = 8 * (r >> 2) + 4 * g + (r & 3);  // pair of register r
+                        if (pr < n) sm.slot[(L.plist[k0 + pr] - (int)pb) * MM_ROWS + i] = acc[r];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // ---- each token's slots, added in slot order
+        for (int idx = threadIdx.x; idx < (int)(t1 - t0) * MM_ROWS; idx += 64 * MM_WAVES) {
+            const int64_t t = t0 + idx / MM_ROWS;
+            const int r = idx % MM_ROWS;
+            if (r < live) {
+                float s = 0.0f;
+                for (int k = 0; k < topk; ++k) {
+                    const int64_t pp = t * topk + k;
+                    const int32_t id = ids[pp];
+                    if (id >= 0 && id < E) s += rw[pp] * sm.slot[(pp - pb) * MM_ROWS + r];
+                }
+                y[t * rows + r0 + r] = s;
+            }
+        }
+        __syncthreads();
+        }
+    }
+}
+
+// Compute units of the current device, asked once per device.
+int64_t device_cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    const int slot = dev >= 0 && dev < 64 ? dev : 0;
+    int n = cached[slot].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[slot].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+}  // namespace
+
+bool moe_mfma_q4k_fits(int64_t K) { return mm_tok_bytes(K) <= MM_TOK_BYTES; }
+
+hipError_t launch_moe_mfma_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
+                               const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s) {
+    if (!moe_mfma_q4k_fits(a.K)) return hipErrorInvalidValue;
+    // One workgroup per compute unit (its LDS allows no second), each walking
+    // row tiles of rt <= 32 rows: rt is chosen so the tiles come out as whole
+    // rounds over the compute units (14336 rows: 512 tiles of 28 on 256 units)
+    // and a workgroup stages its tokens once for all its tiles.
+    const int64_t cus = device_cu_count();
+    const int64_t rounds = ((rows + MM_ROWS - 1) / MM_ROWS + cus - 1) / cus;
+    int64_t rt = (rows + rounds * cus - 1) / (rounds * cus);
+    rt = rt < 16 ? 16 : rt > MM_ROWS ? MM_ROWS : rt;
+    const int64_t ntiles = (rows + rt - 1) / rt;
+    const unsigned grid = (unsigned)(ntiles < cus ? ntiles : cus);
+    hipLaunchKernelGGL(moe_mfma_q4k_kernel, dim3(grid), dim3(64 * MM_WAVES), 0, s, w, E, rows, nb, a.qs, a.d, a.bs,
+                       a.K, T, ids, rw, topk, y, (int)rt, ntiles);
+    return hipGetLastError();
+}
+
+}  // namespace q8k

@@ -39,17 +39,11 @@
 //
 // Result (i, j) of a 32x32 MFMA is in lane j + 32 ((i / 4) % 2), register
 // (i % 4) + 4 (i / 8): each lane holds one weight row and 16 tokens.
-#include "q8k_device.h"
+#include "q4k_planes.h"
 #include "q8k_launch.h"
 
 namespace q8k {
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 
 constexpr int RW_TM = 128;  // tokens per workgroup
 constexpr int RW_TN = 64;   // weight rows per workgroup
@@ -102,20 +96,6 @@ __device__ __forceinline__ void dma4(rsrc_t r, void* lds_base, int off) {
                  : "memory", "m0");
 }
 
-// Four byte-wise products q_i * k (q_i <= 15, k <= 7: every product stays
-// inside its byte) as one packed 16-bit multiply.
-__device__ __forceinline__ uint32_t mul_bytes(uint32_t q, uint32_t k) {
-    const v2u16 kk = {(unsigned short)k, (unsigned short)k};
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2u16, q) * kk);
-}
-
-// bf16 high and low parts of v (round to nearest even both times): v - hi is
-// exact in fp32, so hi + lo carries 16 significant bits of v.
-__device__ __forceinline__ void bf16_split(float v, __bf16& hi, __bf16& lo) {
-    hi = (__bf16)v;
-    lo = (__bf16)(v - (float)hi);
-}
-
 // Sources of one workgroup: tokens m0.., rows n0...  Offsets stay 32-bit: a
 // tile's rows span at most 64 * (K / 256) * 144 bytes, its tokens 128 * K.
 // The byte counts from the tile's start to the end of each buffer are
@@ -137,12 +117,6 @@ __device__ __forceinline__ int clamp31(int64_t v) { return v <= 0 ? 0 : v < 0x7f
 __device__ __forceinline__ rsrc_t rsrc32(const void* base, int remaining) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, remaining > 0 ? remaining : 0,
                                              0x00020000 /* raw, untyped dwords */);
-}
-
-// Byte offset inside a 256-value block of the 16 codes lane (i, g) supplies at
-// k-step kk: values 64(2g + kk/4) + 32(kk%2) + 16((kk/2)%2) .. +15.
-__host__ __device__ constexpr int kstep_off(int g, int kk) {
-    return 128 * g + 64 * (kk >> 2) + 32 * (kk & 1) + 16 * ((kk >> 1) & 1);
 }
 
 // The buffer-unit copies of stage sg = 2 s + h (tokens 64 h .. 64 h + 63 of
@@ -180,12 +154,7 @@ __device__ __forceinline__ void issue_aux(RwCopied& sm, const RwSrc& S, int sg, 
     }
 }
 
-// Raw weight bytes of one (row, block) for lane (j, g): the 16-byte header
-// (d, dmin, 12 scale bytes) and quant bytes 64g .. 64g+63.
-struct RwRaw {
-    uint4 hdr, q[4];
-};
-__device__ __forceinline__ void load_weights(RwRaw& R, const RwSrc& S, int b, int rg, int lane) {
+__device__ __forceinline__ void load_weights(Q4kRaw& R, const RwSrc& S, int b, int rg, int lane) {
     // (blocks past the row's end read the next row's bytes or, past the last
     // row, zeros: they are never multiplied)
     const int boff = b * Q4K_BLOCK;
@@ -220,52 +189,9 @@ __device__ __forceinline__ void build_amin(const RwCopied& sm, RwBuilt& sb, int 
     *reinterpret_cast<v8bf*>(&sb.amin[sg & 1][q][t >> 5][(t & 31) + 32 * g]) = o;
 }
 
-// The operands of one (row, block) for lane (j, g), built from its raw bytes:
-// the two planes of the 8 k-steps, the row's min-term operands and its d.
-struct RwPlanes {
-    v4i ph[8], pl[8];
-    v8bf bh, bl;
-    float dd;
-};
-__device__ __forceinline__ void build_planes(RwPlanes& P, const RwRaw& R, int lane) {
-    const int g = lane >> 5;
-    // ---- scales and mins of sub-blocks 4g .. 4g+3 as bytes
-    const uint32_t y = R.hdr.y, z = R.hdr.z, wq = R.hdr.w;
-    // (branch-free: g differs between the two halves of the wave)
-    const uint32_t hm = 0u - (uint32_t)g;
-    const uint32_t sc = (hm & ((wq & 0x0F0F0F0Fu) | ((y >> 2) & 0x30303030u))) | (~hm & y & 0x3F3F3F3Fu);
-    const uint32_t mn = (hm & (((wq >> 4) & 0x0F0F0F0Fu) | ((z >> 2) & 0x30303030u))) | (~hm & z & 0x3F3F3F3Fu);
-    const uint32_t av = (sc >> 3) & 0x07070707u, bvv = sc & 0x07070707u;
-    P.dd = half_bits_to_float(R.hdr.x & 0xffffu);
-    const float dmin = half_bits_to_float(R.hdr.x >> 16);
-    // ---- row min-term operands: -dmin * m_j (exact in fp32), high / low bf16
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        __bf16 hi, lo;
-        bf16_split(-dmin * (float)((mn >> (8 * e)) & 0xffu), hi, lo);
-        P.bh[e] = P.bh[4 + e] = hi;
-        P.bl[e] = P.bl[4 + e] = lo;
-    }
-    // ---- the two planes of the 8 k-steps
-    const uint32_t raw[16] = {R.q[0].x, R.q[0].y, R.q[0].z, R.q[0].w, R.q[1].x, R.q[1].y, R.q[1].z, R.q[1].w,
-                              R.q[2].x, R.q[2].y, R.q[2].z, R.q[2].w, R.q[3].x, R.q[3].y, R.q[3].z, R.q[3].w};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        const int e = 2 * (kk >> 2) + (kk & 1);
-        const uint32_t ka = (av >> (8 * e)) & 0xffu, kb = (bvv >> (8 * e)) & 0xffu;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const uint32_t r = raw[4 * (kk >> 1) + x];
-            const uint32_t nib = (kk & 1) ? ((r >> 4) & 0x0F0F0F0Fu) : (r & 0x0F0F0F0Fu);
-            P.ph[kk][x] = (int)mul_bytes(nib, ka);
-            P.pl[kk][x] = (int)mul_bytes(nib, kb);
-        }
-    }
-}
-
 // One stage of one wave: 64 tokens x 32 rows of block 4 s + q, two MFMA tiles
 // of 32 tokens, into the accumulators of tiles 2h and 2h + 1.
-__device__ __forceinline__ void wave_stage(const RwCopied& sm, const RwBuilt& sb, const RwPlanes& P, int sg, int q,
+__device__ __forceinline__ void wave_stage(const RwCopied& sm, const RwBuilt& sb, const Q4kPlanes& P, int sg, int q,
                                            int lane,
                                            v16f (&acc)[4]) {
     const int g = lane >> 5, h = sg & 1;
@@ -378,7 +304,7 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 
-    RwRaw R;
+    Q4kRaw R;
     issue_codes(sm, S, 0, wv, lane);
     issue_aux(sm, S, 0, wv, lane);
     issue_aux(sm, S, 1, wv, lane);
@@ -386,7 +312,7 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     stage_barrier<0>();
     build_amin(sm, sb, 0, tid);
     stage_barrier<0>();
-    RwPlanes PL;
+    Q4kPlanes PL;
     for (int sg = 0; sg < nst; sg += 2) {
         const int b = 2 * sg + q;  // block of this wave in step sg / 2
         // ---- first 64 tokens: copies of the next stage (codes) and the one
@@ -400,7 +326,7 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
                      "v"(__builtin_bit_cast(v4i, R.q[3])));
         issue_codes(sm, S, sg + 1, wv, lane);
         if (sg + 2 < nst) issue_aux(sm, S, sg + 2, wv, lane);
-        build_planes(PL, R, lane);
+        build_q4k_planes(PL, R, lane);
         load_weights(R, S, b + RW_KQ, rg, lane);
         if (b < nb) wave_stage(sm, sb, PL, sg, q, lane, acc);
         build_amin(sm, sb, sg + 1, tid);
