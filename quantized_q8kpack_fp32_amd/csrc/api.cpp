@@ -339,7 +339,7 @@ int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64
         return fail(Q8K_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
     if (need > 0) Q8K_TRY(check_ptr(fn, "ws", ws, 16));
     Q8K_TRY(check_grid(fn, moe_prefill_ws(E, rows, T, topk).max_chunks * ((rows + 63) / 64)));
-    Q8K_TRY(check_grid(fn, (T * rows + 255) / 256));
+    Q8K_TRY(check_grid(fn, T * ((rows + 255) / 256)));  // the combine's workgroups, at most
     if (rows == 0 || T == 0) return Q8K_OK;
     const int nb = (int)(K / QK);
     const PrefillWeights pw = prefill_weights(qtype, w, E * rows * nb);

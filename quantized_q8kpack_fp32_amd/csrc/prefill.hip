@@ -677,20 +677,26 @@ __global__ __launch_bounds__(512) void prefill_moe_q4k_kernel(const uint8_t* __r
 }
 
 // y[t][r] = sum_k rw[t][k] * out[t * topk + k][r] over ids in [0, E), k ascending.
+// A workgroup takes one token and 256 * V consecutive rows (V = 4 when rows is
+// a multiple of 4 and y 16-byte aligned: 16-byte loads and stores); the
+// token's ids and router weights are the same for all its threads.
+template <int V>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ out, int64_t rows, int64_t T,
                                                           const int32_t* __restrict__ ids,
                                                           const float* __restrict__ rw, int topk, int64_t E,
                                                           float* __restrict__ y) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= T * rows) return;
-    const int64_t t = i / rows, r = i % rows;
-    float s = 0.0f;
+    typedef float fv __attribute__((ext_vector_type(V)));
+    const int64_t nrb = (rows + 256 * V - 1) / (256 * V);
+    const int64_t t = (int64_t)blockIdx.x / nrb;
+    const int64_t r = ((int64_t)blockIdx.x % nrb * 256 + threadIdx.x) * V;
+    if (r >= rows) return;
+    fv s = {};
     for (int k = 0; k < topk; ++k) {
         const int64_t pp = t * topk + k;
         const int32_t id = ids[pp];
-        if (id >= 0 && id < E) s += rw[pp] * out[pp * rows + r];
+        if (id >= 0 && id < E) s += rw[pp] * *reinterpret_cast<const fv*>(out + pp * rows + r);
     }
-    y[i] = s;
+    *reinterpret_cast<fv*>(y + t * rows + r) = s;
 }
 
 hipError_t launch_prefill_moe(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t E, int64_t rows, int nb,
@@ -704,18 +710,20 @@ hipError_t launch_prefill_moe(int fmt, const uint8_t* w, const uint16_t* prefix,
     hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(1024), 0, s, ids, L.P, (int)E, nchunks, chunks, order);
     const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
     const dim3 grid((unsigned)(L.max_chunks * ntn));
-    if (fmt == PF_Q6)
+    if (fmt == PF_Q4)
+        launch_prefill_regw_moe_q4k(w, rows, nb, a, T, L.max_chunks, nchunks, chunks, order, topk, out, s);
+    else if (fmt == PF_Q6)
         hipLaunchKernelGGL(prefill_moe_q4k_kernel<PF_Q6>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
                            a.K, T, nchunks, chunks, order, topk, out);
     else if (fmt == PF_Q5)
         hipLaunchKernelGGL(prefill_moe_q4k_kernel<PF_Q5>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
                            a.K, T, nchunks, chunks, order, topk, out);
+    if (rows % 4 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0)
+        hipLaunchKernelGGL(moe_combine_kernel<4>, dim3((unsigned)(T * ((rows + 1023) / 1024))), dim3(256), 0, s, out,
+                           rows, T, ids, rw, topk, E, y);
     else
-        hipLaunchKernelGGL(prefill_moe_q4k_kernel<PF_Q4>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
-                           a.K, T, nchunks, chunks, order, topk, out);
-    const int64_t n = T * rows;
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, out, rows, T, ids, rw,
-                       topk, E, y);
+        hipLaunchKernelGGL(moe_combine_kernel<1>, dim3((unsigned)(T * ((rows + 255) / 256))), dim3(256), 0, s, out,
+                           rows, T, ids, rw, topk, E, y);
     return hipGetLastError();
 }
 

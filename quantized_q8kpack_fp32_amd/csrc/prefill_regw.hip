@@ -71,7 +71,15 @@ struct RwBuilt {
     float d8[2][RW_KQ][RW_SM];     // [parity][quarter][token]
     uint4 amin[2][RW_KQ][2][64];   // [parity][quarter][tile][lane (token i, g)]: bf16 d8*bsum_j, j = 4g..4g+3, high then low
 };
-static_assert(sizeof(RwCopied) + sizeof(RwBuilt) <= 160 * 1024, "LDS of one workgroup");
+// Mixture-of-experts tiles: the tile's 128 rows are the pairs of one chunk
+// (pairs of one expert, grouped beforehand), so token rows are gathered: the
+// byte offset of each tile row's token in the q8_K codes, and its pair index
+// (the row of the per-pair result).
+struct RwGather {
+    int tokoff[RW_TM];
+    int pair[RW_TM];
+};
+static_assert(sizeof(RwCopied) + sizeof(RwBuilt) + sizeof(RwGather) <= 160 * 1024, "LDS of one workgroup");
 
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ uint32_t lds_addr(void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
@@ -111,6 +119,7 @@ struct RwSrc {
     int wrow;  // bytes per weight row
     int nb;
     int K;
+    const int* tokoff;  // gathered tiles: LDS offsets of the tile's token rows
 };
 __device__ __forceinline__ int clamp31(int64_t v) { return v <= 0 ? 0 : v < 0x7fffffff ? (int)v : 0x7fffffff; }
 // Raw buffer resource over [base, base + max(remaining, 0)).
@@ -123,10 +132,22 @@ __device__ __forceinline__ rsrc_t rsrc32(const void* base, int remaining) {
 // the tile, block 4 s + q of quarter q) by wave wv: codes of 32 token rows of
 // quarter wv >> 1 (8 copies of four whole rows), and one copy of block scales
 // (waves 0..3) or sub-block sums (waves 4..7) of one quarter.
+template <bool GATHER>
 __device__ __forceinline__ void issue_codes(RwCopied& sm, const RwSrc& S, int sg, int wv, int lane) {
     const int s = sg >> 1, h = sg & 1;
     const int q = wv >> 1, half = wv & 1;
     const int tq = lane >> 4, pc = lane & 15;
+    if constexpr (GATHER) {
+        // copy i covers stage tokens 32 half + 4i + tq, each at its own row
+        const int bo = (4 * s + q) * QK;
+        const rsrc_t rx = rsrc32(S.x + bo, S.xbytes - bo);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int m = RW_SM * h + 32 * half + 4 * i + tq;
+            dma16(rx, &sm.codes[sg & 1][q][32 * half + 4 * i][0], S.tokoff[m] + 16 * (pc ^ (4 * (i & 3) + tq)));
+        }
+        return;
+    }
     // copy i covers stage tokens 32 half + 4i + tq; its resource starts at that
     // group's first token (scalar), so the lane offsets repeat with period 4 in i
     const int base = (RW_SM * h + 32 * half) * S.K + (4 * s + q) * QK;
@@ -140,10 +161,24 @@ __device__ __forceinline__ void issue_codes(RwCopied& sm, const RwSrc& S, int sg
         dma16(rx, &sm.codes[sg & 1][q][32 * half + 4 * i][0], vo[i & 3]);
     }
 }
+template <bool GATHER>
 __device__ __forceinline__ void issue_aux(RwCopied& sm, const RwSrc& S, int sg, int wv, int lane) {
     const int s = sg >> 1, h = sg & 1, st = sg & 1;
     const int q = wv & 3;
     const int t0 = RW_SM * h;  // first token of the stage
+    if constexpr (GATHER) {
+        // token row r's records start at r * nb * 4 (scales) and r * nb * 16
+        // (sums) bytes, i.e. at its code offset r * K over 64 and over 16
+        const int tok = S.tokoff[t0 + lane];
+        if (wv < 4) {
+            const int o = (4 * s + q) * 4;
+            dma4(rsrc32((const char*)S.d8 + o, S.d8bytes - o), &sm.d8raw[st][q][0], tok >> 6);
+        } else {
+            const int o = (4 * s + q) * 16;
+            dma16(rsrc32((const char*)S.bs + o, S.bsbytes - o), &sm.bs[st][q][0][0], tok >> 4);
+        }
+        return;
+    }
     const int off = lane * S.nb;  // token 64 h + lane, block 4 s + q, in units of one block's record
     if (wv < 4) {
         const int o = (t0 * S.nb + 4 * s + q) * 4;
@@ -267,11 +302,20 @@ __device__ __forceinline__ void stage_barrier() {
 }
 constexpr int RW_RAW_LOADS = 5;  // load_weights() issues five loads
 
+// GATHER = false: y[m][n] for tokens m0 .. m0+127 of M.  GATHER = true (the
+// mixture-of-experts prefill): workgroup (chunk c, row tile) multiplies the
+// chunk's expert by the tokens of its pairs (chunks[c] = {expert, first index
+// in order, count}); the result of pair p goes to row p of y ([P][rows]);
+// workgroups past the chunk count return at once.
+template <bool GATHER>
 __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     const uint8_t* __restrict__ w, int64_t rows, int nb, const int8_t* __restrict__ qs,
-    const float* __restrict__ d8, const int16_t* __restrict__ bs, int64_t K, int64_t M, float* __restrict__ y) {
+    const float* __restrict__ d8, const int16_t* __restrict__ bs, int64_t K, int64_t M, float* __restrict__ y,
+    const int32_t* __restrict__ nchunks, const int4* __restrict__ chunks, const int32_t* __restrict__ order,
+    int topk) {
     __shared__ __attribute__((aligned(16))) RwCopied sm;
     __shared__ __attribute__((aligned(16))) RwBuilt sb;
+    __shared__ RwGather gat;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int rg = wv & 1, q = wv >> 1;
@@ -286,18 +330,42 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     S.nb = nb;
     S.K = (int)K;
     S.wrow = nb * Q4K_BLOCK;
-    S.w = w + n0 * S.wrow;
+    S.tokoff = gat.tokoff;
+    int64_t live;  // tokens of the tile
+    if constexpr (GATHER) {
+        const int64_t c = (int64_t)blockIdx.x / ntn;
+        if (c >= *nchunks) return;  // the whole workgroup
+        const int4 ch = chunks[c];
+        live = ch.z;
+        // rows past the chunk's count repeat its first pair (never stored)
+        for (int m = tid; m < RW_TM; m += RW_THREADS) {
+            const int p = order[ch.y + (m < ch.z ? m : 0)];
+            gat.pair[m] = p;
+            gat.tokoff[m] = (int)((int64_t)(p / topk) * K);
+        }
+        S.w = w + ((int64_t)ch.x * rows + n0) * S.wrow;
+        S.x = qs;
+        S.xbytes = clamp31(M * K);
+        S.d8 = d8;
+        S.d8bytes = clamp31(M * nb * 4);
+        S.bs = bs;
+        S.bsbytes = clamp31(M * nb * 16);
+        __syncthreads();
+    } else {
+        live = M - m0;
+        S.w = w + n0 * S.wrow;
+        S.x = qs + m0 * K;
+        S.xbytes = clamp31((M - m0) * K);
+        S.d8 = d8 + m0 * nb;
+        S.d8bytes = clamp31((M - m0) * nb * 4);
+        S.bs = bs + m0 * nb * 8;
+        S.bsbytes = clamp31((M - m0) * nb * 16);
+    }
     S.wbytes = clamp31((rows - n0) * S.wrow);
-    S.x = qs + m0 * K;
-    S.xbytes = clamp31((M - m0) * K);
-    S.d8 = d8 + m0 * nb;
-    S.d8bytes = clamp31((M - m0) * nb * 4);
-    S.bs = bs + m0 * nb * 8;
-    S.bsbytes = clamp31((M - m0) * nb * 16);
 
     const int steps = (nb + RW_KQ - 1) / RW_KQ;
     const int nst = 2 * steps;                        // stages
-    const bool half2 = M - m0 > RW_SM;                // the tile's second 64 tokens exist
+    const bool half2 = live > RW_SM;                  // the tile's second 64 tokens exist
     v16f acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -305,9 +373,9 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 
     Q4kRaw R;
-    issue_codes(sm, S, 0, wv, lane);
-    issue_aux(sm, S, 0, wv, lane);
-    issue_aux(sm, S, 1, wv, lane);
+    issue_codes<GATHER>(sm, S, 0, wv, lane);
+    issue_aux<GATHER>(sm, S, 0, wv, lane);
+    issue_aux<GATHER>(sm, S, 1, wv, lane);
     load_weights(R, S, q, rg, lane);
     stage_barrier<0>();
     build_amin(sm, sb, 0, tid);
@@ -324,16 +392,16 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         asm volatile("" ::"v"(__builtin_bit_cast(v4i, R.hdr)), "v"(__builtin_bit_cast(v4i, R.q[0])),
                      "v"(__builtin_bit_cast(v4i, R.q[1])), "v"(__builtin_bit_cast(v4i, R.q[2])),
                      "v"(__builtin_bit_cast(v4i, R.q[3])));
-        issue_codes(sm, S, sg + 1, wv, lane);
-        if (sg + 2 < nst) issue_aux(sm, S, sg + 2, wv, lane);
+        issue_codes<GATHER>(sm, S, sg + 1, wv, lane);
+        if (sg + 2 < nst) issue_aux<GATHER>(sm, S, sg + 2, wv, lane);
         build_q4k_planes(PL, R, lane);
         load_weights(R, S, b + RW_KQ, rg, lane);
         if (b < nb) wave_stage(sm, sb, PL, sg, q, lane, acc);
         build_amin(sm, sb, sg + 1, tid);
         stage_barrier<RW_RAW_LOADS>();
         // ---- second 64 tokens
-        if (sg + 2 < nst) issue_codes(sm, S, sg + 2, wv, lane);
-        if (sg + 3 < nst) issue_aux(sm, S, sg + 3, wv, lane);
+        if (sg + 2 < nst) issue_codes<GATHER>(sm, S, sg + 2, wv, lane);
+        if (sg + 3 < nst) issue_aux<GATHER>(sm, S, sg + 3, wv, lane);
         if (b < nb && half2) wave_stage(sm, sb, PL, sg + 1, q, lane, acc);
         if (sg + 2 < nst) build_amin(sm, sb, sg + 2, tid);
         stage_barrier<0>();
@@ -356,11 +424,16 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + 32 * t + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+                const int mt = 32 * t + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);  // tile row
                 float v = acc[t][r];
 #pragma unroll
                 for (int qq = 1; qq < RW_KQ; ++qq) v += red[((((qq - 1) * 2 + rg) * 4 + t) * 16 + r) * 64 + ln];
-                if (m < M && n < rows) y[m * rows + n] = v;
+                if (mt < live && n < rows) {
+                    if constexpr (GATHER)
+                        y[(int64_t)gat.pair[mt] * rows + n] = v;
+                    else
+                        y[(m0 + mt) * rows + n] = v;
+                }
             }
         }
     }
@@ -371,8 +444,17 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
 hipError_t launch_prefill_regw_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
                                    hipStream_t s) {
     const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * ((M + RW_TM - 1) / RW_TM)));
-    hipLaunchKernelGGL(prefill_regw_q4k_kernel, grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K, M,
-                       y);
+    hipLaunchKernelGGL(prefill_regw_q4k_kernel<false>, grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs,
+                       a.K, M, y, nullptr, nullptr, nullptr, 1);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_regw_moe_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t T, int64_t max_chunks,
+                                       const int32_t* nchunks, const int4* chunks, const int32_t* order, int topk,
+                                       float* out, hipStream_t s) {
+    const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * max_chunks));
+    hipLaunchKernelGGL(prefill_regw_q4k_kernel<true>, grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs,
+                       a.K, T, out, nchunks, chunks, order, topk);
     return hipGetLastError();
 }
 

@@ -60,6 +60,11 @@ hipError_t launch_prefill(int fmt, const uint8_t* w, const uint16_t* prefix, int
 // multiply them (prefill_regw.hip).
 hipError_t launch_prefill_regw_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
                                    hipStream_t s);
+// The same tile over the chunks of a mixture-of-experts prefill (T tokens;
+// chunk table and pair order as in the workspace below; out: [P][rows]).
+hipError_t launch_prefill_regw_moe_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t T, int64_t max_chunks,
+                                       const int32_t* nchunks, const int4* chunks, const int32_t* order, int topk,
+                                       float* out, hipStream_t s);
 
 // Workspace of the MoE prefill, byte offsets from its start: the fp32 result
 // of every (token, slot) pair [P][rows]; then, 256-aligned, the chunk count
