@@ -5,18 +5,20 @@
 // token's expert outputs are summed as they are produced; weights are read
 // through the index of which expert each token chose (section intro).
 //
-// A workgroup owns 32 consecutive rows of every expert; its MM_WAVES waves take
-// the experts w, w + MM_WAVES, ... .  For expert e a wave lists the (token,
-// slot) pairs that chose e (a ballot over ids) and multiplies its 32 rows
-// against up to 32 of those pairs at a time as one 32x32 int8 MFMA tile per
-// k-step: the pairs' q8_K codes are the A operand (row i = pair i of the
-// group), the rows' Q4_K blocks the B operand, built in registers as the two
-// planes a*q and b*q of the split scale sc = 8a + b (q4k_planes.h), so one
-// weight read serves every pair of the group.  Per block: the high plane's
-// chain of eight MFMAs, its sum times 8, the low plane's chain into the same
-// int32 accumulator (I = 8 P_hi + P_lo, exact); the min term on the bf16
-// matrix path (both operands split in high and low parts) into the fp32
-// accumulator; then acc += (d8 * float(I)) * d for the pairs present.
+// A workgroup walks row tiles of at most 32 rows of every expert; its
+// MM_WAVES waves take the experts w, w + MM_WAVES, ... .  For expert e a wave
+// lists the (token, slot) pairs that chose e (a ballot over ids) and
+// multiplies its tile's rows against up to MM_GROUP of those pairs at a time
+// on the int8 matrix cores, one 32x32x32 MFMA per 32-value sub-block: the
+// pairs' q8_K codes are the A operand (row i = pair i of the group), the
+// rows' raw 4-bit quants the B operand, and the result is the integer sum S_j
+// of sub-block j for every (pair, row), exactly.  The six-bit scales then
+// fold in int32 on the vector unit, I = sum_j sc_j * S_j, in the four result
+// registers that hold the group's pairs; the min term runs on the bf16 matrix
+// path (both operands split in high and low parts) into the fp32
+// accumulator; then acc += (d8 * float(I)) * d.  One weight read serves every
+// pair of the group, and the vector work per weight byte is a nibble mask and
+// a quarter of a multiply-add.
 //
 // The dot of pair p and row r lands in an LDS slot owned by p; once every wave
 // is done the workgroup adds each token's slots in slot order,
@@ -26,12 +28,12 @@
 // tokens fit the workgroup's LDS stage (codes, sub-block sums and scales of
 // every slab token, copied once per slab): the pairs' operands are then LDS
 // reads, so the only vector-memory loads in flight during the block walk are
-// the weight blocks, and each wave keeps the next two in flight while it
+// the weight blocks, and each wave keeps the next one in flight while it
 // multiplies the current one (vector loads complete in issue order, so token
-// loads interleaved with them would cut that depth to one).  An expert nobody
+// loads interleaved with them would be waited for with every block).  An expert nobody
 // chose is never read; an id outside [0, E) matches no expert and its slot is
 // skipped.
-#include "q4k_planes.h"
+#include "q4k_planes.h"  // vector types, bf16 split
 #include "q8k.h"
 #include "q8k_launch.h"
 
@@ -43,6 +45,7 @@ namespace {
 constexpr int MM_WAVES = 8;   // waves per workgroup
 constexpr int MM_ROWS = 32;   // rows per workgroup (the MFMA's B columns)
 constexpr int MM_SLOT = 128;  // (token, slot) pairs per slab
+constexpr int MM_GROUP = 8;   // pairs per MFMA tile (its first 8 rows; the rest repeat pair 0)
 static_assert(MM_SLOT >= Q8K_MOE_MAX_TOPK, "a slab holds at least one token's pairs");
 constexpr int MM_TOK_BYTES = 98304;  // LDS stage of the slab's packed tokens
 constexpr int MM_TILE = MM_ROWS * Q4K_BLOCK;  // one block of the workgroup's rows: 4608 bytes
@@ -63,17 +66,17 @@ struct MmSmem {
     int8_t tok[MM_TOK_BYTES];
 };
 
-// One block of the workgroup's 32 rows, loaded by hand in a sector-contiguous
-// lane map: load x of lane l takes 16-byte chunk c = 64x + l of the 288 chunks
+// One block of the tile's 32 rows, loaded by hand in a sector-contiguous lane
+// map: load x of lane l takes 16-byte chunk c = 64x + l of the 288 chunks
 // (row c / 9, chunk c % 9 of its 144-byte block; the fifth load's upper half
 // repeats the lower half), so consecutive lanes read consecutive bytes and a
 // load instruction touches 2-3 cache lines per row instead of 32 scattered
 // pieces.  The wave then moves the block through its LDS tile into the
-// matrix-core lane map.  The walk keeps two blocks in flight behind the one it
-// multiplies and waits for that one with an explicit count (it issues no other
-// vector-memory load); the wait names the registers it covers, so the compiler
-// neither reads them earlier nor reuses them while a load into them is in
-// flight.
+// matrix-core lane map.  The walk keeps the next block in flight behind the
+// one it multiplies and waits for that one with an explicit count (it issues
+// no other vector-memory load); the wait names the registers it covers, so
+// the compiler neither reads them earlier nor reuses them while a load into
+// them is in flight.
 struct MmW {
     v4i c[5];
 };
@@ -169,66 +172,94 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
                 wave_lds_fence();
                 if (hit) L.plist[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u))] = (int)p;
                 wave_lds_fence();
-                for (int k0 = 0; k0 < count; k0 += 32) {
-                    const int n = count - k0 < 32 ? count - k0 : 32;  // pairs of this group
+                for (int k0 = 0; k0 < count; k0 += MM_GROUP) {
+                    const int n = count - k0 < MM_GROUP ? count - k0 : MM_GROUP;  // pairs of this group
                     // code lane (i, g) takes pair k0 + i (pair k0 when the group has fewer)
                     const int pi = L.plist[k0 + (i < n ? i : 0)];
                     const int tl = (int)(pi / topk - t0);  // the pair's token in the slab stage
                     const int8_t* xrow = tokc + tl * KS;
                     const int8_t* bsrow = tokb + tl * cpt + 8 * g;
                     const float* d8row = tokd + tl * nb;
+                    // The block walk.  The weights of two blocks are in registers at
+                    // once: block b's (multiplied now) and block b+1's (in flight), in W0
+                    // and W1 by parity (no register copies); the walk starts at b = -1
+                    // with a load-only step.  The last step reloads the row's last block
+                    // (a cache hit, never used) and the walk ends by draining it: no load
+                    // outlives it.
                     v16f acc = {};
-                    // The weights of three blocks are in registers at once: block b's
-                    // (multiplied now) and blocks b+1, b+2 (in flight).  Block j lives in
-                    // W[j mod 3] (W0, W1, W2 named apart: no register copies); the walk
-                    // starts at b = -2 with two load-only steps.  The last two steps
-                    // reload the row's last block (a cache hit, never used) and the
-                    // walk ends by draining them: no load outlives it.
-                    MmW W0, W1, W2;
-                    auto step = [&](int b, MmW& Wc, MmW& Wfree) {
-                        mm_issue_w(Wfree, wr, ml, b + 2 < nb ? b + 2 : nb - 1);
+                    MmW W0, W1;
+                    auto step = [&](int b, MmW& Wc, MmW& Wfree) __attribute__((always_inline)) {
+                        mm_issue_w(Wfree, wr, ml, b + 1 < nb ? b + 1 : nb - 1);
                         if (b < 0) return;
-                        mm_wait_w<2 * MM_W_LOADS>(Wc);
-                        // block b through the tile: lane (i, g) takes row i's header
-                        // and its quant bytes 64g .. 64g+63
-                        Q4kRaw R;
+                        mm_wait_w<MM_W_LOADS>(Wc);
+                        // block b through the tile into this wave's lane map
                         wave_lds_fence();
 #pragma unroll
-                        for (int x = 0; x < MM_W_LOADS; ++x) *reinterpret_cast<v4i*>(L.tile + ml.lo[x]) = Wc.c[x];
+                        for (int x = 0; x < MM_W_LOADS; ++x)
+                            *reinterpret_cast<v4i*>(L.tile + ml.lo[x]) = Wc.c[x];
                         wave_lds_fence();
-                        {
-                            const uint8_t* tr = L.tile + i * Q4K_BLOCK;
-                            R.hdr = *reinterpret_cast<const uint4*>(tr);
-#pragma unroll
-                            for (int x = 0; x < 4; ++x) R.q[x] = *reinterpret_cast<const uint4*>(tr + 16 + 64 * g + 16 * x);
-                        }
-                        // the pair's operand: codes of sub-blocks 4g..4g+3, their sums, the block scale
-                        v4i A[8];
-#pragma unroll
-                        for (int kk = 0; kk < 8; ++kk)
-                            A[kk] = *reinterpret_cast<const v4i*>(xrow + b * QK + kstep_off(g, kk));
+                        const uint8_t* tr = L.tile + i * Q4K_BLOCK;
+                        const uint4 hdr = *reinterpret_cast<const uint4*>(tr);
                         const uint2 bsv = *reinterpret_cast<const uint2*>(bsrow + 16 * b);
                         const float a8 = d8row[b];
-                        Q4kPlanes P;
-                        build_q4k_planes(P, R, lane);
-                        // ---- integer chains
+                        // the row's min-term operands for sub-blocks 4g..4g+3 (-dmin *
+                        // m_j, high and low bf16 parts, repeated in both fragment
+                        // halves) and d
+                        const uint32_t hy = hdr.y, hz = hdr.z, hw = hdr.w;
+                        const uint32_t hm = 0u - (uint32_t)g;  // (branch-free: g differs inside the wave)
+                        const uint32_t mn = (hm & (((hw >> 4) & 0x0F0F0F0Fu) | ((hz >> 2) & 0x30303030u))) |
+                                            (~hm & hz & 0x3F3F3F3Fu);
+                        const float dd = half_bits_to_float(hdr.x & 0xffffu);
+                        const float dmin = half_bits_to_float(hdr.x >> 16);
+                        v8bf bh, bl;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            __bf16 hi, lo;
+                            bf16_split(-dmin * (float)((mn >> (8 * e)) & 0xffu), hi, lo);
+                            bh[e] = bh[4 + e] = hi;
+                            bl[e] = bl[4 + e] = lo;
+                        }
                         v16i I;
                         {
-                            const v16i zero = {};
-                            I = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[0], P.ph[0], zero, 0, 0, 0);
-                        }
+                            // One MFMA per 32-value sub-block j on the raw nibbles gives
+                            // the sums S_j of every (pair, row); the six-bit scales fold
+                            // in int32 in the registers that hold pairs: I = sum_j sc_j *
+                            // S_j (|S_j| <= 127*15*32, sc_j <= 63: 24-bit products).  Lane
+                            // (i, g) holds quant bytes 32m + 16g .. +15 (m = 0..3): values
+                            // 16g .. 16g+15 of sub-blocks 2m (low nibbles) and 2m + 1
+                            // (high nibbles).  Sub-block j + 1's MFMA is issued before
+                            // sub-block j's fold.
+                            v4i qb[4];
 #pragma unroll
-                        for (int kk = 1; kk < 8; ++kk)
-                            I = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[kk], P.ph[kk], I, 0, 0, 0);
+                            for (int m = 0; m < 4; ++m)
+                                qb[m] = *reinterpret_cast<const v4i*>(tr + 16 + 32 * m + 16 * g);
+                            const uint32_t sc03 = hy & 0x3F3F3F3Fu;
+                            const uint32_t sc47 = (hw & 0x0F0F0F0Fu) | ((hy >> 2) & 0x30303030u);
+                            auto sums = [&](int j) {
+                                const v4i aj = *reinterpret_cast<const v4i*>(xrow + b * QK + 32 * j + 16 * g);
+                                v4i bj;
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) I[r] <<= 3;
-                        // the low chain reads the codes again: holding them across both
-                        // chains costs the registers the third weight block needs
-                        asm volatile("" ::: "memory");
+                                for (int x = 0; x < 4; ++x)
+                                    bj[x] = (j & 1) ? ((qb[j >> 1][x] >> 4) & 0x0F0F0F0F) : (qb[j >> 1][x] & 0x0F0F0F0F);
+                                const v16i zero = {};
+                                return __builtin_amdgcn_mfma_i32_32x32x32_i8(aj, bj, zero, 0, 0, 0);
+                            };
+                            auto fold = [&](int j, const v16i& S) {
+                                const int sc = (int)(((j < 4 ? sc03 : sc47) >> (8 * (j & 3))) & 0xffu);
 #pragma unroll
-                        for (int kk = 0; kk < 8; ++kk) {
-                            const v4i a2 = *reinterpret_cast<const v4i*>(xrow + b * QK + kstep_off(g, kk));
-                            I = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2, P.pl[kk], I, 0, 0, 0);
+                                for (int r = 0; r < 4; ++r)
+                                    I[r] = j == 0 ? __mul24(sc, S[r]) : I[r] + __mul24(sc, S[r]);
+                            };
+                            v16i S0 = sums(0), S1;
+#pragma unroll
+                            for (int j = 0; j < 8; j += 2) {
+                                S1 = sums(j + 1);
+                                fold(j, S0);
+                                __builtin_amdgcn_sched_barrier(0);
+                                if (j + 2 < 8) S0 = sums(j + 2);
+                                fold(j + 1, S1);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
                         }
                         // ---- min term: the pair's d8 * bsum_j (j = 4g..4g+3), high
                         // then low bf16 parts, against [bh | bh] and [bl | bl]
@@ -243,37 +274,29 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
                                 am[j] = hi;
                                 am[4 + j] = lo;
                             }
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, P.bh, acc, 0, 0, 0);
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, P.bl, acc, 0, 0, 0);
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bh, acc, 0, 0, 0);
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bl, acc, 0, 0, 0);
                         }
-                        // ---- epilogue: acc += (d8 * float(I)) * d for the pairs
-                        // present; register r of lane l holds pair 8(r/4) + 4g + r%4
+                        // ---- epilogue: acc += (d8 * float(I)) * d; register r < 4 of
+                        // lane (i, g) holds pair 4g + r (the other registers hold the
+                        // tile's repeated rows)
                         wave_lds_fence();
                         if (g == 0) L.d8[i] = a8;
                         wave_lds_fence();
+                        {
+                            const float4 dv = *reinterpret_cast<const float4*>(&L.d8[4 * g]);
+                            const float d8a[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
-                        for (int G = 0; G < 4; ++G) {
-                            if (8 * G < n) {  // wave-uniform
-                                const float4 dv = *reinterpret_cast<const float4*>(&L.d8[8 * G + 4 * g]);
-                                const float d8a[4] = {dv.x, dv.y, dv.z, dv.w};
-#pragma unroll
-                                for (int e2 = 0; e2 < 4; ++e2) {
-                                    const int r = 4 * G + e2;
-                                    acc[r] = fmaf((float)I[r] * d8a[e2], P.dd, acc[r]);
-                                }
-                            }
+                            for (int r = 0; r < 4; ++r) acc[r] = fmaf((float)I[r] * d8a[r], dd, acc[r]);
                         }
                     };
-                    for (int b = -2; b < nb; b += 3) {
+                    for (int b = -1; b < nb; b += 2) {
                         step(b, W1, W0);
                         if (b + 1 == nb) break;
-                        step(b + 1, W2, W1);
-                        if (b + 2 == nb) break;
-                        step(b + 2, W0, W2);
+                        step(b + 1, W0, W1);
                     }
                     mm_wait_w<0>(W0);
                     mm_wait_w<0>(W1);
-                    mm_wait_w<0>(W2);
                     // ---- the group's dots into their pairs' slots (row i of the
                     // workgroup is this lane's weight row)
 #pragma unroll
