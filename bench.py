@@ -66,7 +66,7 @@ KERNEL_SOURCES = {
     "matvec_q6k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
     "moe": [_CS + "moe_mfma.hip", _CS + "q4k_planes.h", _CS + "q8k_device.h"],
     "matvec_q5k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
-    "moe_q5k": [_CS + "moe.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
+    "moe_q5k": [_CS + "moe_mfma.hip", _CS + "q4k_planes.h", _CS + "q8k_device.h"],
     "prefill_q4k": [_CS + "prefill_regw.hip", _CS + "q4k_planes.h", _CS + "q8k_device.h"],
     "moe_prefill_q4k": [_CS + "prefill_regw.hip", _CS + "q4k_planes.h", _CS + "prefill.hip", _CS + "q8k_device.h"],
     "prefill_q5k": [_CS + "prefill.hip", _CS + "q8k_device.h"],

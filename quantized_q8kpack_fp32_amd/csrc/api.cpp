@@ -260,7 +260,7 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
     hipError_t e;
     if (qtype == Q8K_Q4_K) {
         // matrix-core kernel while a packed token fits its LDS stage (K up to
-        // about 119k), the one-lane-per-row kernel beyond
+        // about 89k), the one-lane-per-row kernel beyond
         if (moe_mfma_q4k_fits(K))
             e = launch_moe_mfma_q4k(static_cast<const uint8_t*>(w), E, rows, nb, a, T, ids, rw, topk, y,
                                     (hipStream_t)stream);
@@ -268,7 +268,12 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
             e = launch_moe_q4k(static_cast<const uint8_t*>(w), E, rows, nb, a, T, ids, rw, topk, y,
                                (hipStream_t)stream);
     } else if (qtype == Q8K_Q5_K) {
-        e = launch_moe_q5k(static_cast<const uint8_t*>(w), E, rows, nb, a, T, ids, rw, topk, y, (hipStream_t)stream);
+        if (moe_mfma_q4k_fits(K))
+            e = launch_moe_mfma_q5k(static_cast<const uint8_t*>(w), E, rows, nb, a, T, ids, rw, topk, y,
+                                    (hipStream_t)stream);
+        else
+            e = launch_moe_q5k(static_cast<const uint8_t*>(w), E, rows, nb, a, T, ids, rw, topk, y,
+                               (hipStream_t)stream);
     } else {
         const Q6View v = q6_view(w, E * rows * nb);
         e = launch_moe_q6k(v.prefix, v.bodies, E, rows, nb, a, T, ids, rw, topk, y, (hipStream_t)stream);

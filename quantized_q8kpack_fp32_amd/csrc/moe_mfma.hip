@@ -48,19 +48,34 @@ constexpr int MM_SLOT = 128;  // (token, slot) pairs per slab
 constexpr int MM_GROUP = 8;   // pairs per MFMA tile (its first 8 rows; the rest repeat pair 0)
 static_assert(MM_SLOT >= Q8K_MOE_MAX_TOPK, "a slab holds at least one token's pairs");
 constexpr int MM_TOK_BYTES = 98304;  // LDS stage of the slab's packed tokens
-constexpr int MM_TILE = MM_ROWS * Q4K_BLOCK;  // one block of the workgroup's rows: 4608 bytes
+
+// Block formats: Q4_K (144 bytes: d, dmin, 12 scale bytes, 128 quant bytes) and
+// Q5_K (176 bytes: the same 16-byte header, 32 bytes of fifth bits, then the
+// 128 low-nibble bytes).  A tile of 32 rows' blocks is CH 16-byte chunks per
+// row, NL loads per lane.
+template <bool Q5>
+struct MmFmt {
+    static constexpr int BLK = Q5 ? Q5K_BLOCK : Q4K_BLOCK;
+    static constexpr int CH = BLK / 16;    // 9 or 11
+    static constexpr int NL = Q5 ? 6 : 5;  // ceil(32 * CH / 64)
+    static constexpr int QOFF = Q5 ? 48 : 16;
+    static constexpr int TILE = MM_ROWS * BLK;
+    static_assert(32 * CH - 64 * (NL - 1) == 32, "the last load takes the last 32 chunks");
+};
 
 // LDS bytes of one staged token: codes padded by 16 bytes (consecutive tokens
 // start 4 banks apart), sub-block sums, block scales.
 __host__ __device__ constexpr int64_t mm_tok_bytes(int64_t K) { return (K + 16) + K / 16 + K / 64; }
 
+template <bool Q5>
 struct MmWave {
     int plist[64];  // pair indices of the current 64-pair window that chose the wave's expert, by rank
     float d8[32];   // the group's block scales (pair i at i) for the epilogue
-    __attribute__((aligned(16))) uint8_t tile[MM_TILE];  // block b of rows r0..r0+31, [row][144 B]
+    __attribute__((aligned(16))) uint8_t tile[MmFmt<Q5>::TILE];  // block b of the tile's rows, [row][block]
 };
+template <bool Q5>
 struct MmSmem {
-    MmWave wave[MM_WAVES];
+    MmWave<Q5> wave[MM_WAVES];
     float slot[MM_SLOT * MM_ROWS];  // dot of (pair, row), pair-major
     // slab tokens: codes [ts][K + 16], then sums [ts][K / 32] int16, then scales [ts][K / 256] fp32
     int8_t tok[MM_TOK_BYTES];
@@ -77,42 +92,49 @@ struct MmSmem {
 // no other vector-memory load); the wait names the registers it covers, so
 // the compiler neither reads them earlier nor reuses them while a load into
 // them is in flight.
+template <int NL>
 struct MmW {
-    v4i c[5];
+    v4i c[NL];
 };
-constexpr int MM_W_LOADS = 5;  // loads per block and lane
-template <int IMM>
 __device__ __forceinline__ v4i mm_vload16(rsrc_t r, int off) {
     v4i v;
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3" : "=v"(v) : "v"(off), "s"(r), "n"(IMM));
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(r));
     return v;
 }
-// Lane l's five chunk offsets inside a row-major run of 32 rows (block 0).
+// Lane l's chunk offsets inside a row-major run of 32 rows (block 0).
+template <int NL>
 struct MmLane {
-    int go[MM_W_LOADS];  // global: row * row_bytes + 16 * chunk
-    int lo[MM_W_LOADS];  // LDS tile: 16 * c
+    int go[NL];  // global: row * row_bytes + 16 * chunk
+    int lo[NL];  // LDS tile: 16 * c
 };
-__device__ __forceinline__ MmLane mm_lane(int lane, int64_t wrow) {
-    MmLane m;
+template <bool Q5>
+__device__ __forceinline__ MmLane<MmFmt<Q5>::NL> mm_lane(int lane, int64_t wrow) {
+    using F = MmFmt<Q5>;
+    MmLane<F::NL> m;
 #pragma unroll
-    for (int x = 0; x < MM_W_LOADS; ++x) {
-        const int c = x < 4 ? 64 * x + lane : 256 + (lane & 31);
-        m.go[x] = (c / 9) * (int)wrow + 16 * (c % 9);
+    for (int x = 0; x < F::NL; ++x) {
+        const int c = x < F::NL - 1 ? 64 * x + lane : 64 * (F::NL - 1) + (lane & 31);
+        m.go[x] = (c / F::CH) * (int)wrow + 16 * (c % F::CH);
         m.lo[x] = 16 * c;
     }
     return m;
 }
-__device__ __forceinline__ void mm_issue_w(MmW& W, rsrc_t wr, const MmLane& m, int b) {
-    const int boff = b * Q4K_BLOCK;
-    W.c[0] = mm_vload16<0>(wr, m.go[0] + boff);
-    W.c[1] = mm_vload16<0>(wr, m.go[1] + boff);
-    W.c[2] = mm_vload16<0>(wr, m.go[2] + boff);
-    W.c[3] = mm_vload16<0>(wr, m.go[3] + boff);
-    W.c[4] = mm_vload16<0>(wr, m.go[4] + boff);
+template <bool Q5>
+__device__ __forceinline__ void mm_issue_w(MmW<MmFmt<Q5>::NL>& W, rsrc_t wr, const MmLane<MmFmt<Q5>::NL>& m,
+                                           int b) {
+    const int boff = b * MmFmt<Q5>::BLK;
+#pragma unroll
+    for (int x = 0; x < MmFmt<Q5>::NL; ++x) W.c[x] = mm_vload16(wr, m.go[x] + boff);
 }
 template <int N>
-__device__ __forceinline__ void mm_wait_w(MmW& W) {
+__device__ __forceinline__ void mm_wait_w(MmW<5>& W) {
     asm volatile("s_waitcnt vmcnt(%5)" : "+v"(W.c[0]), "+v"(W.c[1]), "+v"(W.c[2]), "+v"(W.c[3]), "+v"(W.c[4]) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void mm_wait_w(MmW<6>& W) {
+    asm volatile("s_waitcnt vmcnt(%6)"
+                 : "+v"(W.c[0]), "+v"(W.c[1]), "+v"(W.c[2]), "+v"(W.c[3]), "+v"(W.c[4]), "+v"(W.c[5])
+                 : "n"(N));
 }
 
 // The wave hands data between its own lanes through LDS.  The hardware runs
@@ -121,18 +143,20 @@ __device__ __forceinline__ void mm_wait_w(MmW& W) {
 // the next writes behind the reads.
 __device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+template <bool Q5>
 __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
     const uint8_t* __restrict__ w, int64_t E, int64_t rows, int nb, const int8_t* __restrict__ qs,
     const float* __restrict__ d8, const int16_t* __restrict__ bs, int64_t K, int64_t T,
     const int32_t* __restrict__ ids, const float* __restrict__ rw, int topk, float* __restrict__ y, int rt,
     int64_t ntiles) {
-    __shared__ __attribute__((aligned(16))) MmSmem sm;
+    using F = MmFmt<Q5>;
+    __shared__ __attribute__((aligned(16))) MmSmem<Q5> sm;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: expert and rsrc are scalar
     const int lane = threadIdx.x & 63;
     const int i = lane & 31, g = lane >> 5;
-    const int64_t wrow = (int64_t)nb * Q4K_BLOCK;
-    MmWave& L = sm.wave[wv];
-    const MmLane ml = mm_lane(lane, wrow);  // rows past `live` read zeros
+    const int64_t wrow = (int64_t)nb * F::BLK;
+    MmWave<Q5>& L = sm.wave[wv];
+    const MmLane<F::NL> ml = mm_lane<Q5>(lane, wrow);  // rows past `live` read zeros
     const int64_t KS = K + 16, cpt = K / 16;  // staged code row stride; 16-byte chunks of codes per token
     const int64_t tsl = MM_TOK_BYTES / mm_tok_bytes(K);  // >= 1 (checked by the launcher)
     const int64_t ts = MM_SLOT / topk < tsl ? MM_SLOT / topk : tsl;  // tokens per slab
@@ -187,18 +211,18 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
                     // (a cache hit, never used) and the walk ends by draining it: no load
                     // outlives it.
                     v16f acc = {};
-                    MmW W0, W1;
-                    auto step = [&](int b, MmW& Wc, MmW& Wfree) __attribute__((always_inline)) {
-                        mm_issue_w(Wfree, wr, ml, b + 1 < nb ? b + 1 : nb - 1);
+                    MmW<F::NL> W0, W1;
+                    auto step = [&](int b, MmW<F::NL>& Wc, MmW<F::NL>& Wfree) __attribute__((always_inline)) {
+                        mm_issue_w<Q5>(Wfree, wr, ml, b + 1 < nb ? b + 1 : nb - 1);
                         if (b < 0) return;
-                        mm_wait_w<MM_W_LOADS>(Wc);
+                        mm_wait_w<F::NL>(Wc);
                         // block b through the tile into this wave's lane map
                         wave_lds_fence();
 #pragma unroll
-                        for (int x = 0; x < MM_W_LOADS; ++x)
+                        for (int x = 0; x < F::NL; ++x)
                             *reinterpret_cast<v4i*>(L.tile + ml.lo[x]) = Wc.c[x];
                         wave_lds_fence();
-                        const uint8_t* tr = L.tile + i * Q4K_BLOCK;
+                        const uint8_t* tr = L.tile + i * F::BLK;
                         const uint4 hdr = *reinterpret_cast<const uint4*>(tr);
                         const uint2 bsv = *reinterpret_cast<const uint2*>(bsrow + 16 * b);
                         const float a8 = d8row[b];
@@ -232,7 +256,10 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
                             v4i qb[4];
 #pragma unroll
                             for (int m = 0; m < 4; ++m)
-                                qb[m] = *reinterpret_cast<const v4i*>(tr + 16 + 32 * m + 16 * g);
+                                qb[m] = *reinterpret_cast<const v4i*>(tr + F::QOFF + 32 * m + 16 * g);
+                            // Q5_K: fifth bits of values 16g .. 16g+15 (bit j of byte t: sub-block j)
+                            v4i qh = {};
+                            if constexpr (Q5) qh = *reinterpret_cast<const v4i*>(tr + 16 + 16 * g);
                             const uint32_t sc03 = hy & 0x3F3F3F3Fu;
                             const uint32_t sc47 = (hw & 0x0F0F0F0Fu) | ((hy >> 2) & 0x30303030u);
                             auto sums = [&](int j) {
@@ -240,7 +267,8 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
                                 v4i bj;
 #pragma unroll
                                 for (int x = 0; x < 4; ++x)
-                                    bj[x] = (j & 1) ? ((qb[j >> 1][x] >> 4) & 0x0F0F0F0F) : (qb[j >> 1][x] & 0x0F0F0F0F);
+                                    bj[x] = ((j & 1) ? ((qb[j >> 1][x] >> 4) & 0x0F0F0F0F) : (qb[j >> 1][x] & 0x0F0F0F0F)) |
+                                            (Q5 ? ((qh[x] >> j) & 0x01010101) << 4 : 0);
                                 const v16i zero = {};
                                 return __builtin_amdgcn_mfma_i32_32x32x32_i8(aj, bj, zero, 0, 0, 0);
                             };
@@ -345,8 +373,9 @@ int64_t device_cu_count() {
 
 bool moe_mfma_q4k_fits(int64_t K) { return mm_tok_bytes(K) <= MM_TOK_BYTES; }
 
-hipError_t launch_moe_mfma_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
-                               const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s) {
+template <bool Q5>
+hipError_t launch_moe_mfma(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T, const int32_t* ids,
+                           const float* rw, int topk, float* y, hipStream_t s) {
     if (!moe_mfma_q4k_fits(a.K)) return hipErrorInvalidValue;
     // One workgroup per compute unit (its LDS allows no second), each walking
     // row tiles of rt <= 32 rows: rt is chosen so the tiles come out as whole
@@ -358,9 +387,18 @@ hipError_t launch_moe_mfma_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb
     rt = rt < 16 ? 16 : rt > MM_ROWS ? MM_ROWS : rt;
     const int64_t ntiles = (rows + rt - 1) / rt;
     const unsigned grid = (unsigned)(ntiles < cus ? ntiles : cus);
-    hipLaunchKernelGGL(moe_mfma_q4k_kernel, dim3(grid), dim3(64 * MM_WAVES), 0, s, w, E, rows, nb, a.qs, a.d, a.bs,
+    hipLaunchKernelGGL(moe_mfma_q4k_kernel<Q5>, dim3(grid), dim3(64 * MM_WAVES), 0, s, w, E, rows, nb, a.qs, a.d, a.bs,
                        a.K, T, ids, rw, topk, y, (int)rt, ntiles);
     return hipGetLastError();
+}
+
+hipError_t launch_moe_mfma_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
+                               const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s) {
+    return launch_moe_mfma<false>(w, E, rows, nb, a, T, ids, rw, topk, y, s);
+}
+hipError_t launch_moe_mfma_q5k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
+                               const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s) {
+    return launch_moe_mfma<true>(w, E, rows, nb, a, T, ids, rw, topk, y, s);
 }
 
 }  // namespace q8k

@@ -50,6 +50,8 @@ hipError_t launch_moe_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Act
 bool moe_mfma_q4k_fits(int64_t K);
 hipError_t launch_moe_mfma_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
                                const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s);
+hipError_t launch_moe_mfma_q5k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
+                               const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s);
 hipError_t launch_moe_q5k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T, const int32_t* ids,
                           const float* rw, int topk, float* y, hipStream_t s);
 hipError_t launch_moe_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t E, int64_t rows, int nb, Acts a,
