@@ -279,11 +279,16 @@ __device__ __forceinline__ void wave_stage(const RwCopied& sm, const RwBuilt& sb
             }
         }
     };
+    // The matrix chains run at raised wave priority: the SIMD's other wave,
+    // usually in its vector phase (plane build, folds), then fills the issue
+    // slots between them instead of competing for the matrix unit.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         v16i I;
+        __builtin_amdgcn_s_setprio(1);
         chains(t, I);
         minterm(t);
+        __builtin_amdgcn_s_setprio(0);
         fold(t, I);
     }
 }
