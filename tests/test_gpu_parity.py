@@ -403,6 +403,8 @@ def moe_case(q, fmt, E, rows, K, T, topk, seed, ids=None):
     ("q5k", 8, 14336, 4096, 16, 2, 35),    # the MoE decode layer shape in Q5_K
     ("q5k", 4, 100, 512, 5, 3, 36),
     ("q5k", 16, 64, 256, 200, 4, 37),
+    ("q4k", 64, 40, 512, 5, 64, 42),       # topk at its limit: two tokens per slab, every expert hit
+    ("q5k", 1, 29, 256, 3, 1, 43),         # one expert, one slot, fewer rows than a tile
     ("q5k", 2, 40, 88064, 3, 2, 40),       # one packed token per LDS stage: a slab per token
     ("q5k", 2, 40, 131072, 3, 2, 41),      # a packed token beyond the LDS stage: one lane per row
 ])
