@@ -182,175 +182,179 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
         }
         __syncthreads();
         for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int64_t r0 = tile * rt;
-        const int64_t live = rows - r0 < rt ? rows - r0 : rt;  // rows of this tile
-        for (int64_t e = wv; e < E; e += MM_WAVES) {
-            const rsrc_t wr = make_rsrc(w + (e * rows + r0) * wrow, live * wrow);
-            for (int64_t p0 = pb; p0 < pe; p0 += 64) {
-                const int64_t p = p0 + lane;
-                const bool hit = p < pe && ids[p] == (int32_t)e;
-                const uint64_t mask = __ballot(hit);
-                if (mask == 0) continue;
-                const int count = __popcll(mask);
-                // pair indices by rank in the window
-                wave_lds_fence();
-                if (hit) L.plist[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u))] = (int)p;
-                wave_lds_fence();
-                for (int k0 = 0; k0 < count; k0 += MM_GROUP) {
-                    const int n = count - k0 < MM_GROUP ? count - k0 : MM_GROUP;  // pairs of this group
-                    // code lane (i, g) takes pair k0 + i (pair k0 when the group has fewer)
-                    const int pi = L.plist[k0 + (i < n ? i : 0)];
-                    const int tl = (int)(pi / topk - t0);  // the pair's token in the slab stage
-                    const int8_t* xrow = tokc + tl * KS;
-                    const int8_t* bsrow = tokb + tl * cpt + 8 * g;
-                    const float* d8row = tokd + tl * nb;
-                    // The block walk.  The weights of two blocks are in registers at
-                    // once: block b's (multiplied now) and block b+1's (in flight), in W0
-                    // and W1 by parity (no register copies); the walk starts at b = -1
-                    // with a load-only step.  The last step reloads the row's last block
-                    // (a cache hit, never used) and the walk ends by draining it: no load
-                    // outlives it.
-                    v16f acc = {};
-                    MmW<F::NL> W0, W1;
-                    auto step = [&](int b, MmW<F::NL>& Wc, MmW<F::NL>& Wfree) __attribute__((always_inline)) {
-                        mm_issue_w<Q5>(Wfree, wr, ml, b + 1 < nb ? b + 1 : nb - 1);
-                        if (b < 0) return;
-                        mm_wait_w<F::NL>(Wc);
-                        // block b through the tile into this wave's lane map
-                        wave_lds_fence();
+            const int64_t r0 = tile * rt;
+            const int64_t live = rows - r0 < rt ? rows - r0 : rt;  // rows of this tile
+            for (int64_t e = wv; e < E; e += MM_WAVES) {
+                const rsrc_t wr = make_rsrc(w + (e * rows + r0) * wrow, live * wrow);
+                for (int64_t p0 = pb; p0 < pe; p0 += 64) {
+                    const int64_t p = p0 + lane;
+                    const bool hit = p < pe && ids[p] == (int32_t)e;
+                    const uint64_t mask = __ballot(hit);
+                    if (mask == 0) continue;
+                    const int count = __popcll(mask);
+                    // pair indices by rank in the window
+                    wave_lds_fence();
+                    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                    if (hit) L.plist[rank] = (int)p;
+                    wave_lds_fence();
+                    for (int k0 = 0; k0 < count; k0 += MM_GROUP) {
+                        const int n = count - k0 < MM_GROUP ? count - k0 : MM_GROUP;  // pairs of this group
+                        // code lane (i, g) takes pair k0 + i (pair k0 when the group has fewer)
+                        const int pi = L.plist[k0 + (i < n ? i : 0)];
+                        const int tl = (int)(pi / topk - t0);  // the pair's token in the slab stage
+                        const int8_t* xrow = tokc + tl * KS;
+                        const int8_t* bsrow = tokb + tl * cpt + 8 * g;
+                        const float* d8row = tokd + tl * nb;
+                        // The block walk.  The weights of two blocks are in registers at
+                        // once: block b's (multiplied now) and block b+1's (in flight), in W0
+                        // and W1 by parity (no register copies); the walk starts at b = -1
+                        // with a load-only step.  The last step reloads the row's last block
+                        // (a cache hit, never used) and the walk ends by draining it: no load
+                        // outlives it.
+                        v16f acc = {};
+                        MmW<F::NL> W0, W1;
+                        auto step = [&](int b, MmW<F::NL>& Wc, MmW<F::NL>& Wfree) __attribute__((always_inline)) {
+                            mm_issue_w<Q5>(Wfree, wr, ml, b + 1 < nb ? b + 1 : nb - 1);
+                            if (b < 0) return;
+                            mm_wait_w<F::NL>(Wc);
+                            // block b through the tile into this wave's lane map
+                            wave_lds_fence();
 #pragma unroll
-                        for (int x = 0; x < F::NL; ++x)
-                            *reinterpret_cast<v4i*>(L.tile + ml.lo[x]) = Wc.c[x];
-                        wave_lds_fence();
-                        const uint8_t* tr = L.tile + i * F::BLK;
-                        const uint4 hdr = *reinterpret_cast<const uint4*>(tr);
-                        const uint2 bsv = *reinterpret_cast<const uint2*>(bsrow + 16 * b);
-                        const float a8 = d8row[b];
-                        // the row's min-term operands for sub-blocks 4g..4g+3 (-dmin *
-                        // m_j, high and low bf16 parts, repeated in both fragment
-                        // halves) and d
-                        const uint32_t hy = hdr.y, hz = hdr.z, hw = hdr.w;
-                        const uint32_t hm = 0u - (uint32_t)g;  // (branch-free: g differs inside the wave)
-                        const uint32_t mn = (hm & (((hw >> 4) & 0x0F0F0F0Fu) | ((hz >> 2) & 0x30303030u))) |
-                                            (~hm & hz & 0x3F3F3F3Fu);
-                        const float dd = half_bits_to_float(hdr.x & 0xffffu);
-                        const float dmin = half_bits_to_float(hdr.x >> 16);
-                        v8bf bh, bl;
+                            for (int x = 0; x < F::NL; ++x)
+                                *reinterpret_cast<v4i*>(L.tile + ml.lo[x]) = Wc.c[x];
+                            wave_lds_fence();
+                            const uint8_t* tr = L.tile + i * F::BLK;
+                            const uint4 hdr = *reinterpret_cast<const uint4*>(tr);
+                            const uint2 bsv = *reinterpret_cast<const uint2*>(bsrow + 16 * b);
+                            const float a8 = d8row[b];
+                            // the row's min-term operands for sub-blocks 4g..4g+3 (-dmin *
+                            // m_j, high and low bf16 parts, repeated in both fragment
+                            // halves) and d
+                            const uint32_t hy = hdr.y, hz = hdr.z, hw = hdr.w;
+                            const uint32_t hm = 0u - (uint32_t)g;  // (branch-free: g differs inside the wave)
+                            const uint32_t mn = (hm & (((hw >> 4) & 0x0F0F0F0Fu) | ((hz >> 2) & 0x30303030u))) |
+                                                (~hm & hz & 0x3F3F3F3Fu);
+                            const float dd = half_bits_to_float(hdr.x & 0xffffu);
+                            const float dmin = half_bits_to_float(hdr.x >> 16);
+                            v8bf bh, bl;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            __bf16 hi, lo;
-                            bf16_split(-dmin * (float)((mn >> (8 * e)) & 0xffu), hi, lo);
-                            bh[e] = bh[4 + e] = hi;
-                            bl[e] = bl[4 + e] = lo;
-                        }
-                        v16i I;
-                        {
-                            // One MFMA per 32-value sub-block j on the raw nibbles gives
-                            // the sums S_j of every (pair, row); the six-bit scales fold
-                            // in int32 in the registers that hold pairs: I = sum_j sc_j *
-                            // S_j (|S_j| <= 127*15*32, sc_j <= 63: 24-bit products).  Lane
-                            // (i, g) holds quant bytes 32m + 16g .. +15 (m = 0..3): values
-                            // 16g .. 16g+15 of sub-blocks 2m (low nibbles) and 2m + 1
-                            // (high nibbles).  Sub-block j + 1's MFMA is issued before
-                            // sub-block j's fold.
-                            v4i qb[4];
-#pragma unroll
-                            for (int m = 0; m < 4; ++m)
-                                qb[m] = *reinterpret_cast<const v4i*>(tr + F::QOFF + 32 * m + 16 * g);
-                            // Q5_K: fifth bits of values 16g .. 16g+15 (bit j of byte t: sub-block j)
-                            v4i qh = {};
-                            if constexpr (Q5) qh = *reinterpret_cast<const v4i*>(tr + 16 + 16 * g);
-                            const uint32_t sc03 = hy & 0x3F3F3F3Fu;
-                            const uint32_t sc47 = (hw & 0x0F0F0F0Fu) | ((hy >> 2) & 0x30303030u);
-                            auto sums = [&](int j) {
-                                const v4i aj = *reinterpret_cast<const v4i*>(xrow + b * QK + 32 * j + 16 * g);
-                                v4i bj;
-#pragma unroll
-                                for (int x = 0; x < 4; ++x)
-                                    bj[x] = ((j & 1) ? ((qb[j >> 1][x] >> 4) & 0x0F0F0F0F) : (qb[j >> 1][x] & 0x0F0F0F0F)) |
-                                            (Q5 ? ((qh[x] >> j) & 0x01010101) << 4 : 0);
-                                const v16i zero = {};
-                                return __builtin_amdgcn_mfma_i32_32x32x32_i8(aj, bj, zero, 0, 0, 0);
-                            };
-                            auto fold = [&](int j, const v16i& S) {
-                                const int sc = (int)(((j < 4 ? sc03 : sc47) >> (8 * (j & 3))) & 0xffu);
-#pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    I[r] = j == 0 ? __mul24(sc, S[r]) : I[r] + __mul24(sc, S[r]);
-                            };
-                            v16i S0 = sums(0), S1;
-#pragma unroll
-                            for (int j = 0; j < 8; j += 2) {
-                                S1 = sums(j + 1);
-                                fold(j, S0);
-                                __builtin_amdgcn_sched_barrier(0);
-                                if (j + 2 < 8) S0 = sums(j + 2);
-                                fold(j + 1, S1);
-                                __builtin_amdgcn_sched_barrier(0);
-                            }
-                        }
-                        // ---- min term: the pair's d8 * bsum_j (j = 4g..4g+3), high
-                        // then low bf16 parts, against [bh | bh] and [bl | bl]
-                        {
-                            v8bf am;
-                            const uint32_t bw[2] = {bsv.x, bsv.y};
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const int sj = (int)(int16_t)(bw[j >> 1] >> (16 * (j & 1)));
+                            for (int e = 0; e < 4; ++e) {
                                 __bf16 hi, lo;
-                                bf16_split(a8 * (float)sj, hi, lo);
-                                am[j] = hi;
-                                am[4 + j] = lo;
+                                bf16_split(-dmin * (float)((mn >> (8 * e)) & 0xffu), hi, lo);
+                                bh[e] = bh[4 + e] = hi;
+                                bl[e] = bl[4 + e] = lo;
                             }
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bh, acc, 0, 0, 0);
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bl, acc, 0, 0, 0);
-                        }
-                        // ---- epilogue: acc += (d8 * float(I)) * d; register r < 4 of
-                        // lane (i, g) holds pair 4g + r (the other registers hold the
-                        // tile's repeated rows)
-                        wave_lds_fence();
-                        if (g == 0) L.d8[i] = a8;
-                        wave_lds_fence();
-                        {
-                            const float4 dv = *reinterpret_cast<const float4*>(&L.d8[4 * g]);
-                            const float d8a[4] = {dv.x, dv.y, dv.z, dv.w};
+                            v16i I;
+                            {
+                                // One MFMA per 32-value sub-block j on the raw nibbles gives
+                                // the sums S_j of every (pair, row); the six-bit scales fold
+                                // in int32 in the registers that hold pairs: I = sum_j sc_j *
+                                // S_j (|S_j| <= 127*15*32, sc_j <= 63: 24-bit products).  Lane
+                                // (i, g) holds quant bytes 32m + 16g .. +15 (m = 0..3): values
+                                // 16g .. 16g+15 of sub-blocks 2m (low nibbles) and 2m + 1
+                                // (high nibbles).  Sub-block j + 1's MFMA is issued before
+                                // sub-block j's fold.
+                                v4i qb[4];
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) acc[r] = fmaf((float)I[r] * d8a[r], dd, acc[r]);
-                        }
-                    };
-                    for (int b = -1; b < nb; b += 2) {
-                        step(b, W1, W0);
-                        if (b + 1 == nb) break;
-                        step(b + 1, W0, W1);
-                    }
-                    mm_wait_w<0>(W0);
-                    mm_wait_w<0>(W1);
-                    // ---- the group's dots into their pairs' slots (row i of the
-                    // workgroup is this lane's weight row)
+                                for (int m = 0; m < 4; ++m)
+                                    qb[m] = *reinterpret_cast<const v4i*>(tr + F::QOFF + 32 * m + 16 * g);
+                                // Q5_K: fifth bits of values 16g .. 16g+15 (bit j of byte t: sub-block j)
+                                v4i qh = {};
+                                if constexpr (Q5) qh = *reinterpret_cast<const v4i*>(tr + 16 + 16 * g);
+                                const uint32_t sc03 = hy & 0x3F3F3F3Fu;
+                                const uint32_t sc47 = (hw & 0x0F0F0F0Fu) | ((hy >> 2) & 0x30303030u);
+                                auto sums = [&](int j) {
+                                    const v4i aj = *reinterpret_cast<const v4i*>(xrow + b * QK + 32 * j + 16 * g);
+                                    v4i bj;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int pr = 8 * (r >> 2) + 4 * g + (r & 3);  // pair of register r
-                        if (pr < n) sm.slot[(L.plist[k0 + pr] - (int)pb) * MM_ROWS + i] = acc[r];
+                                    for (int x = 0; x < 4; ++x) {
+                                        const int q4 = qb[j >> 1][x];
+                                        const int nib = (j & 1) ? ((q4 >> 4) & 0x0F0F0F0F) : (q4 & 0x0F0F0F0F);
+                                        bj[x] = nib | (Q5 ? ((qh[x] >> j) & 0x01010101) << 4 : 0);
+                                    }
+                                    const v16i zero = {};
+                                    return __builtin_amdgcn_mfma_i32_32x32x32_i8(aj, bj, zero, 0, 0, 0);
+                                };
+                                auto fold = [&](int j, const v16i& S) {
+                                    const int sc = (int)(((j < 4 ? sc03 : sc47) >> (8 * (j & 3))) & 0xffu);
+#pragma unroll
+                                    for (int r = 0; r < 4; ++r)
+                                        I[r] = j == 0 ? __mul24(sc, S[r]) : I[r] + __mul24(sc, S[r]);
+                                };
+                                v16i S0 = sums(0), S1;
+#pragma unroll
+                                for (int j = 0; j < 8; j += 2) {
+                                    S1 = sums(j + 1);
+                                    fold(j, S0);
+                                    __builtin_amdgcn_sched_barrier(0);
+                                    if (j + 2 < 8) S0 = sums(j + 2);
+                                    fold(j + 1, S1);
+                                    __builtin_amdgcn_sched_barrier(0);
+                                }
+                            }
+                            // ---- min term: the pair's d8 * bsum_j (j = 4g..4g+3), high
+                            // then low bf16 parts, against [bh | bh] and [bl | bl]
+                            {
+                                v8bf am;
+                                const uint32_t bw[2] = {bsv.x, bsv.y};
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) {
+                                    const int sj = (int)(int16_t)(bw[j >> 1] >> (16 * (j & 1)));
+                                    __bf16 hi, lo;
+                                    bf16_split(a8 * (float)sj, hi, lo);
+                                    am[j] = hi;
+                                    am[4 + j] = lo;
+                                }
+                                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bh, acc, 0, 0, 0);
+                                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bl, acc, 0, 0, 0);
+                            }
+                            // ---- epilogue: acc += (d8 * float(I)) * d; register r < 4 of
+                            // lane (i, g) holds pair 4g + r (the other registers hold the
+                            // tile's repeated rows)
+                            wave_lds_fence();
+                            if (g == 0) L.d8[i] = a8;
+                            wave_lds_fence();
+                            {
+                                const float4 dv = *reinterpret_cast<const float4*>(&L.d8[4 * g]);
+                                const float d8a[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) acc[r] = fmaf((float)I[r] * d8a[r], dd, acc[r]);
+                            }
+                        };
+                        for (int b = -1; b < nb; b += 2) {
+                            step(b, W1, W0);
+                            if (b + 1 == nb) break;
+                            step(b + 1, W0, W1);
+                        }
+                        mm_wait_w<0>(W0);
+                        mm_wait_w<0>(W1);
+                        // ---- the group's dots into their pairs' slots (row i of the
+                        // workgroup is this lane's weight row)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int pr = 8 * (r >> 2) + 4 * g + (r & 3);  // pair of register r
+                            if (pr < n) sm.slot[(L.plist[k0 + pr] - (int)pb) * MM_ROWS + i] = acc[r];
+                        }
                     }
                 }
             }
-        }
-        __syncthreads();
-        // ---- each token's slots, added in slot order
-        for (int idx = threadIdx.x; idx < (int)(t1 - t0) * MM_ROWS; idx += 64 * MM_WAVES) {
-            const int64_t t = t0 + idx / MM_ROWS;
-            const int r = idx % MM_ROWS;
-            if (r < live) {
-                float s = 0.0f;
-                for (int k = 0; k < topk; ++k) {
-                    const int64_t pp = t * topk + k;
-                    const int32_t id = ids[pp];
-                    if (id >= 0 && id < E) s += rw[pp] * sm.slot[(pp - pb) * MM_ROWS + r];
+            __syncthreads();
+            // ---- each token's slots, added in slot order
+            for (int idx = threadIdx.x; idx < (int)(t1 - t0) * MM_ROWS; idx += 64 * MM_WAVES) {
+                const int64_t t = t0 + idx / MM_ROWS;
+                const int r = idx % MM_ROWS;
+                if (r < live) {
+                    float s = 0.0f;
+                    for (int k = 0; k < topk; ++k) {
+                        const int64_t pp = t * topk + k;
+                        const int32_t id = ids[pp];
+                        if (id >= 0 && id < E) s += rw[pp] * sm.slot[(pp - pb) * MM_ROWS + r];
+                    }
+                    y[t * rows + r0 + r] = s;
                 }
-                y[t * rows + r0 + r] = s;
             }
-        }
-        __syncthreads();
+            __syncthreads();
         }
     }
 }
