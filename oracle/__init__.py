@@ -70,6 +70,8 @@ def _load():
     lib.or_moe.restype = ctypes.c_int
     lib.or_moe.argtypes = [ctypes.c_int, P, I64, I64, I64, P, P, P, I64, P, P, I64, P, P, ctypes.c_int]
     lib.or_q6k_relayout.argtypes = [P, I64, P, P]
+    lib.or_block_sums.restype = ctypes.c_int
+    lib.or_block_sums.argtypes = [ctypes.c_int, P, I64, I64, P, I64, P]
     _lib = lib
     return lib
 
@@ -174,6 +176,20 @@ def subblock_sums(qtype: int, w: np.ndarray, rows: int, K: int, qs_row: np.ndarr
         S = np.empty((rows, K // 16), np.int32)
         _load().or_subblock_sums_q6k(_p(w), rows, K, _p(qs_row), _p(S))
     return S
+
+
+def block_sums(qtype: int, w: np.ndarray, rows: int, K: int, qs) -> np.ndarray:
+    """Exact integer block sums I[T, rows, K/256] = sum_j sc_j * S_j (Q6_K:
+    sum_s sc_s * S_s): each block's scale-weighted integer dot, before the
+    floating-point epilogue.  qs: int8 [T, K] (or [K])."""
+    w = _c(w, np.uint8)
+    qs = _c(qs, np.int8)
+    T = qs.shape[0] if qs.ndim == 2 else 1
+    I = np.empty((T, rows, K // QK), np.int64)
+    rc = _load().or_block_sums(qtype, _p(w), rows, K, _p(qs), T, _p(I))
+    if rc != 0:
+        raise ValueError(f"or_block_sums refused ({rc})")
+    return I
 
 
 def matvec(qtype: int, w: np.ndarray, rows: int, K: int, qs, d8, bsums, nthreads: int = 1):

@@ -265,6 +265,52 @@ void or_subblock_sums_q6k(const uint8_t* w, int64_t rows, int64_t K, const int8_
 }
 
 /* ------------------------------------------------------------------------ */
+/* O5b. Exact integer block sums: the scale-weighted integer dot of each     */
+/* block before the floating-point epilogue ("Language models on the        */
+/* device", section 1: the integer dot product does the arithmetic, the      */
+/* sub-block scales fold in afterwards).                                     */
+/*   Q4_K, Q5_K: I[t][r][b] = sum_j sc_j * S_j over the 8 sub-blocks;        */
+/*   Q6_K:       I[t][r][b] = sum_s sc_s * S_s over the 16 sub-blocks.       */
+/* qtype as in or_matvec (1 Q4_K, 2 Q6_K, 3 Q5_K; GGUF blocks); qs holds T   */
+/* tokens' K codes.  The min term (sum_j m_j * bsum_j) is not part of I.     */
+/* ------------------------------------------------------------------------ */
+int or_block_sums(int qtype, const uint8_t* w, int64_t rows, int64_t K, const int8_t* qs, int64_t T, int64_t* I) {
+    if (qtype < 1 || qtype > 3 || rows < 0 || T < 0 || K % QK) return -1;
+    int64_t nb = K / QK;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t b = 0; b < nb; ++b) {
+                const int8_t* x = qs + t * K + b * QK;
+                int64_t acc = 0;
+                if (qtype == 2) {
+                    float d;
+                    int8_t sc[16];
+                    uint8_t q[QK];
+                    or_q6k_fields(w + (r * nb + b) * 210, &d, sc, q);
+                    for (int s = 0; s < 16; ++s) {
+                        int64_t S = 0;
+                        for (int i = 0; i < 16; ++i) S += ((int64_t)q[16 * s + i] - 32) * x[16 * s + i];
+                        acc += (int64_t)sc[s] * S;
+                    }
+                } else {
+                    float d, dmin;
+                    uint8_t sc[8], mn[8], q[QK];
+                    if (qtype == 3)
+                        or_q5k_fields(w + (r * nb + b) * 176, &d, &dmin, sc, mn, q);
+                    else
+                        or_q4k_fields(w + (r * nb + b) * 144, &d, &dmin, sc, mn, q);
+                    for (int j = 0; j < 8; ++j) {
+                        int64_t S = 0;
+                        for (int i = 0; i < 32; ++i) S += (int64_t)q[32 * j + i] * x[32 * j + i];
+                        acc += (int64_t)sc[j] * S;
+                    }
+                }
+                I[(t * rows + r) * nb + b] = acc;
+            }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* O6. One output element: weight row `wr` (nb blocks) against one packed    */
 /* token (qs, d8, bsums of that token).  fp64 epilogue over exact integers;  */
 /* *A receives the sum of |terms| at sub-block granularity.                  */

@@ -356,3 +356,90 @@ def test_moe_routing_generator_shape():
     ids, rw = synth.moe_routing(g, 16, 8, 2)
     assert ids.shape == (16, 2) and all(len(set(r)) == 2 for r in ids.tolist())
     assert np.allclose(rw.sum(1), 1.0, atol=1e-6) and (rw > 0).all()
+
+
+# --------------------------------------------------------------------------- tolerance terms and block sums
+def _golden_terms():
+    with open(os.path.join(GOLDEN, "tolerance_terms.json")) as f:
+        return json.load(f)
+
+
+def _golden_token(gt):
+    """The two hand-worked token blocks (fp32 values chosen so the codes are exact)."""
+    blk = np.zeros(256, np.float32)
+    blk[0] = 127.0
+    blk[1:32] = -1.0
+    for j, c in enumerate(gt["group_values"]):
+        blk[32 * (j + 1):32 * (j + 2)] = c
+    return np.concatenate([blk, 0.5 * blk])[None, :]
+
+
+def _golden_block(fmt, b):
+    if fmt == "q6k":
+        return pack_q6k_block(b["d"], b["sc"], [b["q_all"]] * 256)
+    pk = pack_q5k_block if fmt == "q5k" else pack_q4k_block
+    return pk(b["d"], b["dmin"], b["sc"], b["m"], [b["q_all"]] * 256)
+
+
+_FMT_Q = {"q4k": 1, "q6k": 2, "q5k": 3}
+
+
+def test_golden_token_codes(orc):
+    gt = _golden_terms()["token"]
+    qs, d8, bs = orc.q8k_pack(_golden_token(gt))
+    assert list(d8[0]) == gt["d8"]
+    assert list(bs[0, :8]) == gt["bsums"] and list(bs[0, 8:]) == gt["bsums"]
+    assert np.array_equal(qs[0, :256], qs[0, 256:])
+
+
+@pytest.mark.parametrize("name", ["q4k_two_blocks", "q5k_two_blocks", "q6k_two_blocks"])
+def test_golden_sum_of_terms(orc, name):
+    """y, the tolerance scale A = sum|terms|, the sub-block sums S and the block
+    sums I of hand-worked blocks, exactly (a scaled, dropped or signed term
+    changes A)."""
+    g = _golden_terms()
+    cs = next(c for c in g["cases"] if c["name"] == name)
+    qt = _FMT_Q[cs["fmt"]]
+    blk = _golden_block(cs["fmt"], cs["block"])
+    w = np.concatenate([blk, blk])
+    qs, d8, bs = orc.q8k_pack(_golden_token(g["token"]))
+    y, A = orc.matvec(qt, w, 1, 512, qs, d8, bs)
+    assert y[0, 0] == cs["y"] and A[0, 0] == cs["A"]
+    S = orc.subblock_sums(qt, w, 1, 512, qs[0])
+    assert list(S[0, :len(cs["S"])]) == cs["S"] and list(S[0, len(cs["S"]):]) == cs["S"]
+    assert list(orc.block_sums(qt, w, 1, 512, qs)[0, 0]) == cs["I"]
+
+
+def test_golden_moe_sum_of_terms(orc):
+    """Two experts with a negative router weight: A sums |rw| times each expert's terms."""
+    g = _golden_terms()
+    cs = next(c for c in g["cases"] if c["name"] == "moe_q4k_signed_router")
+    w = np.concatenate([np.concatenate([_golden_block("q4k", e)] * 2) for e in cs["experts"]])
+    qs, d8, bs = orc.q8k_pack(_golden_token(g["token"]))
+    ids = np.array([cs["ids"]], np.int32)
+    rw = np.array([cs["rw"]], np.float32)
+    y, A = orc.moe(orc.Q4_K, w, 2, 1, 512, qs, d8, bs, ids, rw)
+    assert y[0, 0] == cs["y"] and A[0, 0] == cs["A"]
+
+
+@pytest.mark.parametrize("qtype", [1, 2, 3])
+def test_block_sums_equal_integer_dot_of_dequantised_block(orc, qtype):
+    """With d = 1 (and dmin = 0) the dequantised block is sc_j * q (Q6_K:
+    sc_s * (q - 32)), integer valued: I_b is then its plain integer dot with the
+    codes (brute force over the pinned dequantisation)."""
+    g = np.random.default_rng(40 + qtype)
+    rows, K, T = 4, 768, 3
+    w = _GEN[qtype](g, rows, K).reshape(rows * (K // 256), _BB[qtype]).copy()
+    one = np.array([1.0], np.float16).view(np.uint8)
+    if qtype == 2:
+        w[:, 208:210] = one
+    else:
+        w[:, 0:2] = one
+        w[:, 2:4] = 0
+    w = w.reshape(-1)
+    qs = g.integers(-127, 128, (T, K)).astype(np.int8)
+    I = orc.block_sums(qtype, w, rows, K, qs)
+    W = orc.dequant(qtype, w, rows, K)
+    assert np.array_equal(W, np.round(W))
+    want = (qs.astype(np.int64)[:, None, :] * W.astype(np.int64)[None, :, :]).reshape(T, rows, K // 256, 256).sum(-1)
+    assert np.array_equal(I, want)
