@@ -330,10 +330,9 @@ class Prefill:
         self.step(0)
         got = self.y.cpu().numpy().reshape(self.M, self.rows)
         qs, d, bs = oracle.q8k_pack(self.x_host)
-        toks = np.array([0, 1, 255, 256, self.M - 1])
-        want, A = oracle.matvec(_oracle_qtype(oracle, self.fmt), self.w_host, self.rows, self.K, qs[toks], d[toks],
-                                bs[toks], nthreads=ncores())
-        return bool(np.isfinite(got).all()) and close(got[toks], want, A)
+        want, A = oracle.matvec(_oracle_qtype(oracle, self.fmt), self.w_host, self.rows, self.K, qs, d, bs,
+                                nthreads=ncores())
+        return close(got, want, A)  # every output
 
 
 class MoEPrefill:
@@ -374,16 +373,15 @@ class MoEPrefill:
                                    self.ids, self.rw, self.topk, self.y, self.wsp, self.ws_bytes)
 
     def parity(self):
-        """Sampled tokens against the oracle's MoE (the same per-token formula)."""
+        """Every token against the oracle's MoE (the same per-token formula)."""
         import oracle
 
         self.step(0)
         got = self.y.cpu().numpy().reshape(self.T, self.rows)
         qs, d, bs = oracle.q8k_pack(self.x_host)
-        toks = np.array([0, 1, 200, self.T - 1])
-        want, A = oracle.moe(_oracle_qtype(oracle, self.fmt), self.w_host, self.E, self.rows, self.K, qs[toks],
-                             d[toks], bs[toks], self.ids_host[toks], self.rw_host[toks], nthreads=ncores())
-        return bool(np.isfinite(got).all()) and close(got[toks], want, A)
+        want, A = oracle.moe(_oracle_qtype(oracle, self.fmt), self.w_host, self.E, self.rows, self.K, qs, d, bs,
+                             self.ids_host, self.rw_host, nthreads=ncores())
+        return close(got, want, A)
 
 
 def ncores() -> int:

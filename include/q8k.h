@@ -16,9 +16,9 @@
  *   - section 2.2: batched decode, one pass over a weight row serves several
  *     activation columns;
  *   - section 2.3: prefill, a tiled matrix-core GEMM with a scale epilogue;
- *     a Q5_K member is the Q4_K one with the fifth-bit plane OR-ed into bit
- *     four of each staged value (here: the Q5_K mat-vec, batched and MoE
- *     forms; the Q5_K prefill is not built and is refused);
+ *     a Q5_K member is the Q4_K one with the fifth-bit plane supplying bit
+ *     four of each value (every operation here serves Q4_K, Q5_K and relaid
+ *     Q6_K weights, the prefill and its MoE form included);
  *   - section 2.4: mixture of experts, a decode mat-vec that visits each
  *     token's selected experts and sums their weighted outputs, and the
  *     prefill form that runs the prefill tile per expert chunk;
@@ -27,9 +27,11 @@
  *
  * Conventions for every entry point
  *   - Buffers are device pointers owned by the caller; the library never
- *     allocates, never synchronises and keeps no state besides the calling
- *     thread's last-error text.  Buffers must stay alive until the work
- *     enqueued on `stream` has finished.
+ *     allocates and never synchronises.  Its only state: the calling
+ *     thread's last-error text and launch record (q8k_debug_last_launches),
+ *     and the compute-unit count of each device, asked of the runtime once
+ *     (it sizes the MoE decode grid).  Buffers must stay alive until the
+ *     work enqueued on `stream` has finished.
  *   - `stream` is a hipStream_t (NULL = the default stream).
  *   - Arguments are validated on the host before anything is enqueued.  A
  *     refusal returns a non-zero q8k_status, enqueues nothing, leaves every
@@ -187,12 +189,44 @@ int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64
                         const int32_t* ids, const float* rw, int32_t topk, float* y, void* ws, size_t ws_bytes,
                         void* stream);
 
-/* Test support: the exact int32 sub-block sums of every weight row against
- * one packed token, computed by the same device code as qmatvec.
- * S: int32 [rows][K/32] for Q8K_Q4_K and Q8K_Q5_K, [rows][K/16] for
- * Q8K_Q6_K_RELAID. */
-int q8k_debug_subblock_sums(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int32_t* S,
+/* ---------------------------------------------------------- test support --
+ * The exact integer sums of the path ("Language models on the device",
+ * section 1: the integer dot product does the arithmetic, the sub-block
+ * scales and mins fold in afterwards), exported by the kernels that ship:
+ * each call runs the operation's own kernel, instantiated with a flag that
+ * also stores its integer sums, and writes y exactly as the operation does.
+ * Validation, refusals and ownership as for the operations.
+ *
+ * q8k_debug_subblock_sums: qmatvec's kernel for one packed token (xq, T = 1).
+ *   y: fp32 [rows]; S: int32 sub-block sums of quant x code, [rows][K/32]
+ *   for Q8K_Q4_K and Q8K_Q5_K, [rows][K/16] (quants minus 32) for
+ *   Q8K_Q6_K_RELAID. */
+int q8k_debug_subblock_sums(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, float* y, int32_t* S,
                             void* stream);
+
+/* q8k_debug_prefill_block_sums: qmatmul_prefill's tile for M packed tokens.
+ *   y: fp32 [M][rows]; I: int32 block sums [M][rows][K/256], the integer the
+ *   tile folds into y per block: sum_j sc_j * S_j (Q4_K, Q5_K; 8 sub-blocks)
+ *   or sum_s sc_s * S_s (Q6_K; 16 sub-blocks). */
+int q8k_debug_prefill_block_sums(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int64_t M,
+                                 float* y, int32_t* I, void* stream);
+
+/* q8k_debug_moe_subblock_sums: qmatvec_moe's matrix-core kernel (Q8K_Q4_K or
+ *   Q8K_Q5_K; K small enough that a packed token fits its shared-memory
+ *   stage, else Q8K_ERR_SHAPE).  y: fp32 [T][rows]; S: int32 sub-block sums
+ *   [T * topk][rows][K/32] of pair (t, k) against expert ids[t][k]; entries
+ *   of pairs whose id is outside [0, E) are not written. */
+int q8k_debug_moe_subblock_sums(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq,
+                                int64_t T, const int32_t* ids, const float* rw, int32_t topk, float* y, int32_t* S,
+                                void* stream);
+
+/* q8k_debug_last_launches: the kernels the calling thread's last operation
+ * (any call above that takes a stream) enqueued, as host kernel handles in
+ * launch order: the first min(count, max) go to handles.  Returns the count.
+ * A test maps each handle to its kernel's name through the library's symbol
+ * table ("One kernel, any device", section 5: the census of value-checked
+ * kernels). */
+int q8k_debug_last_launches(const void** handles, int max);
 
 /* ---------------------------------------------------------------- errors -- */
 const char* q8k_status_str(int status);

@@ -19,7 +19,8 @@ __all__ = [
     "lib", "LIB_PATH", "q8k_act_bytes", "q8k_act_layout", "q8k_weight_bytes", "q8k_pack", "q8k_bind_q6k",
     "qmatvec", "qmatvec_batched", "qmatvec_f32", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
     "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe",
-    "q8k_debug_subblock_sums", "q8k_status_str", "q8k_last_error", "EXPORTED",
+    "q8k_debug_subblock_sums", "q8k_debug_prefill_block_sums", "q8k_debug_moe_subblock_sums",
+    "q8k_debug_last_launches", "q8k_status_str", "q8k_last_error", "EXPORTED",
 ]
 
 Q8K_Q4_K = 1
@@ -37,7 +38,8 @@ EXPORTED = (
     "q8k_act_bytes", "q8k_act_layout", "q8k_weight_bytes", "q8k_pack", "q8k_bind_q6k", "qmatvec",
     "qmatvec_batched", "qmatvec_f32", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
     "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe",
-    "q8k_debug_subblock_sums", "q8k_status_str", "q8k_last_error",
+    "q8k_debug_subblock_sums", "q8k_debug_prefill_block_sums", "q8k_debug_moe_subblock_sums",
+    "q8k_debug_last_launches", "q8k_status_str", "q8k_last_error",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -86,7 +88,13 @@ lib.qmatmul_prefill_moe_workspace_bytes.argtypes = [_INT, _I64, _I64, _I64, _I64
 lib.qmatmul_prefill_moe.restype = _INT
 lib.qmatmul_prefill_moe.argtypes = [_INT, _P, _I64, _I64, _I64, _P, _I64, _P, _P, ctypes.c_int32, _P, _P, _SZ, _P]
 lib.q8k_debug_subblock_sums.restype = _INT
-lib.q8k_debug_subblock_sums.argtypes = [_INT, _P, _I64, _I64, _P, _P, _P]
+lib.q8k_debug_subblock_sums.argtypes = [_INT, _P, _I64, _I64, _P, _P, _P, _P]
+lib.q8k_debug_prefill_block_sums.restype = _INT
+lib.q8k_debug_prefill_block_sums.argtypes = [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P]
+lib.q8k_debug_moe_subblock_sums.restype = _INT
+lib.q8k_debug_moe_subblock_sums.argtypes = [_INT, _P, _I64, _I64, _I64, _P, _I64, _P, _P, ctypes.c_int32, _P, _P, _P]
+lib.q8k_debug_last_launches.restype = _INT
+lib.q8k_debug_last_launches.argtypes = [ctypes.POINTER(_P), _INT]
 lib.q8k_status_str.restype = ctypes.c_char_p
 lib.q8k_status_str.argtypes = [_INT]
 lib.q8k_last_error.restype = ctypes.c_char_p
@@ -194,5 +202,23 @@ def qmatmul_prefill_moe(qtype: int, w, E: int, rows: int, K: int, xq, T: int, id
                                    _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def q8k_debug_subblock_sums(qtype: int, w, rows: int, K: int, xq, S, stream=None) -> None:
-    _check(lib.q8k_debug_subblock_sums(qtype, _ptr(w), rows, K, _ptr(xq), _ptr(S), _stream(stream)))
+def q8k_debug_subblock_sums(qtype: int, w, rows: int, K: int, xq, y, S, stream=None) -> None:
+    _check(lib.q8k_debug_subblock_sums(qtype, _ptr(w), rows, K, _ptr(xq), _ptr(y), _ptr(S), _stream(stream)))
+
+
+def q8k_debug_prefill_block_sums(qtype: int, w, rows: int, K: int, xq, M: int, y, I, stream=None) -> None:
+    _check(lib.q8k_debug_prefill_block_sums(qtype, _ptr(w), rows, K, _ptr(xq), M, _ptr(y), _ptr(I),
+                                            _stream(stream)))
+
+
+def q8k_debug_moe_subblock_sums(qtype: int, w, E: int, rows: int, K: int, xq, T: int, ids, rw, topk: int, y, S,
+                                stream=None) -> None:
+    _check(lib.q8k_debug_moe_subblock_sums(qtype, _ptr(w), E, rows, K, _ptr(xq), T, _ptr(ids), _ptr(rw), topk,
+                                           _ptr(y), _ptr(S), _stream(stream)))
+
+
+def q8k_debug_last_launches() -> list:
+    """Host kernel handles the calling thread's last operation enqueued, in order."""
+    buf = (_P * 16)()
+    n = int(lib.q8k_debug_last_launches(buf, 16))
+    return [int(buf[i] or 0) for i in range(min(n, 16))] + [0] * max(0, n - 16)

@@ -17,6 +17,14 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// The launch record of the calling thread's last operation (test support: the
+// kernel census).  Every operation clears it first; each launch appends its
+// kernel's host handle.
+constexpr int LAUNCH_RECORD_MAX = 16;
+thread_local const void* g_launched[LAUNCH_RECORD_MAX];
+thread_local int g_nlaunched = 0;
+void begin_call() { g_nlaunched = 0; }
+
 int fail(int status, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
@@ -121,6 +129,11 @@ PrefillWeights prefill_weights(int qtype, const void* w, int64_t nblocks) {
 
 }  // namespace
 
+void q8k::note_launch(const void* kernel) {
+    if (g_nlaunched < LAUNCH_RECORD_MAX) g_launched[g_nlaunched] = kernel;
+    ++g_nlaunched;  // counts past the record's end too, so an overflow is visible
+}
+
 extern "C" {
 
 size_t q8k_act_layout(int64_t T, int64_t K, size_t* off_d, size_t* off_bsums) {
@@ -146,6 +159,7 @@ size_t q8k_weight_bytes(int qtype, int64_t rows, int64_t K) {
 }
 
 int q8k_pack(const float* x, int64_t T, int64_t K, void* xq, void* stream) {
+    begin_call();
     const char* fn = "q8k_pack";
     Q8K_TRY(check_k(fn, K));
     Q8K_TRY(check_count(fn, "T", T, MAX_TOKENS));
@@ -161,6 +175,7 @@ int q8k_pack(const float* x, int64_t T, int64_t K, void* xq, void* stream) {
 }
 
 int q8k_bind_q6k(const void* w_gguf, int64_t rows, int64_t K, void* w_relaid, void* stream) {
+    begin_call();
     const char* fn = "q8k_bind_q6k";
     Q8K_TRY(check_k(fn, K));
     Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
@@ -198,6 +213,7 @@ static int matvec_common(const char* fn, int qtype, const void* w, int64_t rows,
 
 int qmatvec_f32(int qtype, const void* w, int64_t rows, int64_t K, const float* x, int64_t ncols, float* y,
                 void* xq_out, void* stream) {
+    begin_call();
     const char* fn = "qmatvec_f32";
     Q8K_TRY(check_k(fn, K));
     Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
@@ -225,11 +241,13 @@ int qmatvec_f32(int qtype, const void* w, int64_t rows, int64_t K, const float* 
 }
 
 int qmatvec(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, float* y, void* stream) {
+    begin_call();
     return matvec_common("qmatvec", qtype, w, rows, K, xq, 1, y, stream);
 }
 
 int qmatvec_batched(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int64_t ncols, float* y,
                     void* stream) {
+    begin_call();
     if (ncols < 1 || ncols > Q8K_COLS_MAX)
         return fail(Q8K_ERR_ARG, "qmatvec_batched: ncols=%lld must be in [1, %d]", (long long)ncols, Q8K_COLS_MAX);
     return matvec_common("qmatvec_batched", qtype, w, rows, K, xq, ncols, y, stream);
@@ -237,6 +255,7 @@ int qmatvec_batched(int qtype, const void* w, int64_t rows, int64_t K, const voi
 
 int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq, int64_t T,
                 const int32_t* ids, const float* rw, int32_t topk, float* y, void* stream) {
+    begin_call();
     const char* fn = "qmatvec_moe";
     Q8K_TRY(check_k(fn, K));
     Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
@@ -291,6 +310,7 @@ size_t qmatmul_prefill_workspace_bytes(int qtype, int64_t rows, int64_t K, int64
 
 int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int64_t M, float* y, void* ws,
                     size_t ws_bytes, void* stream) {
+    begin_call();
     const char* fn = "qmatmul_prefill";
     Q8K_TRY(check_k(fn, K));
     Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
@@ -320,6 +340,7 @@ size_t qmatmul_prefill_moe_workspace_bytes(int qtype, int64_t E, int64_t rows, i
 int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq, int64_t T,
                         const int32_t* ids, const float* rw, int32_t topk, float* y, void* ws, size_t ws_bytes,
                         void* stream) {
+    begin_call();
     const char* fn = "qmatmul_prefill_moe";
     Q8K_TRY(check_k(fn, K));
     Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
@@ -352,27 +373,78 @@ int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64
                                            y, ws, (hipStream_t)stream));
 }
 
-int q8k_debug_subblock_sums(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int32_t* S,
+int q8k_debug_subblock_sums(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, float* y, int32_t* S,
                             void* stream) {
+    begin_call();
     const char* fn = "q8k_debug_subblock_sums";
     Q8K_TRY(check_k(fn, K));
     Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
     Q8K_TRY(check_weight(fn, qtype, w));
     Q8K_TRY(check_ptr(fn, "xq", xq, 16));
+    Q8K_TRY(check_ptr(fn, "y", y, 4));
     Q8K_TRY(check_ptr(fn, "S", S, 4));
     if (rows == 0) return Q8K_OK;
     const int nb = (int)(K / QK);
-    const Acts a = acts_of(xq, 1, K);
-    hipError_t e;
-    if (qtype == Q8K_Q4_K) {
-        e = launch_sums_q4k(static_cast<const uint8_t*>(w), rows, nb, a, S, (hipStream_t)stream);
-    } else if (qtype == Q8K_Q5_K) {
-        e = launch_sums_q5k(static_cast<const uint8_t*>(w), rows, nb, a, S, (hipStream_t)stream);
-    } else {
-        const Q6View v = q6_view(w, rows * nb);
-        e = launch_sums_q6k(v.prefix, v.bodies, rows, nb, a, S, (hipStream_t)stream);
-    }
-    return launched(fn, e);
+    const PrefillWeights pw = prefill_weights(qtype, w, rows * nb);
+    return launched(fn, launch_matvec_sums(pw.fmt, pw.w, pw.prefix, rows, nb, acts_of(xq, 1, K), y, S,
+                                           (hipStream_t)stream));
+}
+
+int q8k_debug_prefill_block_sums(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int64_t M,
+                                 float* y, int32_t* I, void* stream) {
+    begin_call();
+    const char* fn = "q8k_debug_prefill_block_sums";
+    Q8K_TRY(check_k(fn, K));
+    Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
+    Q8K_TRY(check_count(fn, "M", M, MAX_TOKENS));
+    Q8K_TRY(check_weight(fn, qtype, w));
+    Q8K_TRY(check_ptr(fn, "xq", xq, 16));
+    Q8K_TRY(check_ptr(fn, "y", y, 4));
+    Q8K_TRY(check_ptr(fn, "I", I, 4));
+    Q8K_TRY(check_grid(fn, ((rows + 31) / 32) * ((M + 63) / 64)));
+    if (rows == 0 || M == 0) return Q8K_OK;
+    const int nb = (int)(K / QK);
+    const PrefillWeights pw = prefill_weights(qtype, w, rows * nb);
+    return launched(fn, launch_prefill_sums(pw.fmt, pw.w, pw.prefix, rows, nb, acts_of(xq, M, K), M, y, I,
+                                            (hipStream_t)stream));
+}
+
+int q8k_debug_moe_subblock_sums(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq,
+                                int64_t T, const int32_t* ids, const float* rw, int32_t topk, float* y, int32_t* S,
+                                void* stream) {
+    begin_call();
+    const char* fn = "q8k_debug_moe_subblock_sums";
+    Q8K_TRY(check_k(fn, K));
+    Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
+    if (qtype != Q8K_Q4_K && qtype != Q8K_Q5_K)
+        return fail(Q8K_ERR_QTYPE, "%s: qtype=%d: the matrix-core MoE kernel serves Q8K_Q4_K and Q8K_Q5_K", fn, qtype);
+    if (!moe_mfma_q4k_fits(K))
+        return fail(Q8K_ERR_SHAPE, "%s: K=%lld: a packed token exceeds the matrix-core MoE kernel's LDS stage", fn,
+                    (long long)K);
+    if (E < 1 || E > MAX_EXPERTS)
+        return fail(Q8K_ERR_ARG, "%s: E=%lld must be in [1, %lld]", fn, (long long)E, (long long)MAX_EXPERTS);
+    if (E * rows > MAX_ROWS)
+        return fail(Q8K_ERR_SHAPE, "%s: E*rows=%lld exceeds %lld", fn, (long long)(E * rows), (long long)MAX_ROWS);
+    if (T < 0 || T > Q8K_MOE_MAX_TOKENS)
+        return fail(Q8K_ERR_ARG, "%s: T=%lld must be in [0, %d]", fn, (long long)T, Q8K_MOE_MAX_TOKENS);
+    if (topk < 1 || topk > E || topk > Q8K_MOE_MAX_TOPK)
+        return fail(Q8K_ERR_ARG, "%s: topk=%d must be in [1, min(E=%lld, %d)]", fn, topk, (long long)E,
+                    Q8K_MOE_MAX_TOPK);
+    Q8K_TRY(check_ptr(fn, "w", w, 16));
+    Q8K_TRY(check_ptr(fn, "xq", xq, 16));
+    Q8K_TRY(check_ptr(fn, "ids", ids, 4));
+    Q8K_TRY(check_ptr(fn, "rw", rw, 4));
+    Q8K_TRY(check_ptr(fn, "y", y, 4));
+    Q8K_TRY(check_ptr(fn, "S", S, 4));
+    if (rows == 0 || T == 0) return Q8K_OK;
+    return launched(fn, launch_moe_mfma_sums(qtype == Q8K_Q5_K, static_cast<const uint8_t*>(w), E, rows, (int)(K / QK),
+                                             acts_of(xq, T, K), T, ids, rw, topk, y, S, (hipStream_t)stream));
+}
+
+int q8k_debug_last_launches(const void** handles, int max) {
+    const int n = g_nlaunched < LAUNCH_RECORD_MAX ? g_nlaunched : LAUNCH_RECORD_MAX;
+    for (int i = 0; i < n && i < max; ++i) handles[i] = g_launched[i];
+    return g_nlaunched;
 }
 
 const char* q8k_status_str(int status) {

@@ -62,8 +62,12 @@ __device__ __forceinline__ void q4k_load(Q4Chunk<NC, Q5>& L, const uint8_t* __re
     }
 }
 
-template <int NC, bool Q5>
-__device__ __forceinline__ void q4k_accum(const Q4Chunk<NC, Q5>& L, int c, int half, bool valid, float (&acc)[NC]) {
+// SUMS (test support, one column): also store the chunk's two exact sub-block
+// sums to Sb[2c], Sb[2c + 1] (Sb: the block's eight sums); the two halves of
+// each sub-block sit in lanes ci and ci ^ 1.
+template <int NC, bool Q5, bool SUMS = false>
+__device__ __forceinline__ void q4k_accum(const Q4Chunk<NC, Q5>& L, int c, int half, bool valid, float (&acc)[NC],
+                                          int32_t* Sb = nullptr) {
     int sc0, sc1, m0, m1;
     q4k_scales(L.hdr, c, sc0, sc1, m0, m1);
     const float dd = half_bits_to_float(L.hdr.x & 0xffffu);
@@ -75,6 +79,13 @@ __device__ __forceinline__ void q4k_accum(const Q4Chunk<NC, Q5>& L, int c, int h
     for (int t = 0; t < NC; ++t) {
         int S0, S1;
         q4k_chunk_sums(lo, hi, L.alo[t], L.ahi[t], S0, S1);
+        if constexpr (SUMS) {
+            const int f0 = S0 + __shfl_xor(S0, 1, WAVE), f1 = S1 + __shfl_xor(S1, 1, WAVE);
+            if (valid && !half) {
+                Sb[2 * c] = f0;
+                Sb[2 * c + 1] = f1;
+            }
+        }
         const int isum = sc0 * S0 + sc1 * S1;
         // the min term uses whole sub-block sums: counted once per chunk pair
         const int msum =
@@ -95,12 +106,15 @@ __device__ __forceinline__ void q4k_accum(const Q4Chunk<NC, Q5>& L, int c, int h
 template <int NC>
 constexpr int mv_waves() { return NC <= 2 ? Q8K_MV_WAVES_NARROW : Q8K_MV_WAVES; }
 
-template <int NC, int U, bool Q5>
+// SUMS (test support, NC = 1): the same kernel also stores the exact
+// sub-block sums S [rows][nb][8].
+template <int NC, int U, bool Q5, bool SUMS = false>
 __global__ __launch_bounds__(64 * mv_waves<NC>()) void matvec_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows,
                                                                    int nb, const int8_t* __restrict__ qs,
                                                                    const float* __restrict__ d8,
                                                                    const int16_t* __restrict__ bs, int64_t K,
-                                                                   float* __restrict__ y) {
+                                                                   float* __restrict__ y, int32_t* __restrict__ S) {
+    static_assert(!SUMS || NC == 1, "sums of one column");
     const int64_t row = (int64_t)blockIdx.x * mv_waves<NC>() + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;  // uniform per wave
@@ -118,39 +132,14 @@ __global__ __launch_bounds__(64 * mv_waves<NC>()) void matvec_q4k_kernel(const u
             q4k_load(L[u], wr, b < nb ? b : nb - 1, ci, aoff, boff, qs, d8, bs, K, nb);
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) q4k_accum(L[u], c, half, b0 + 8 * u < nb, acc);
+        for (int u = 0; u < U; ++u)
+            q4k_accum<NC, Q5, SUMS>(L[u], c, half, b0 + 8 * u < nb, acc,
+                                    SUMS ? S + (row * nb + b0 + 8 * u) * 8 : nullptr);
     }
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
         const float v = wave_sum_dpp(acc[t]);
         if (lane == 0) y[(int64_t)t * rows + row] = v;
-    }
-}
-
-template <bool Q5>
-__global__ __launch_bounds__(256) void sums_q4k_kernel(const uint8_t* __restrict__ w, int64_t rows, int nb,
-                                                       const int8_t* __restrict__ qs, int32_t* __restrict__ S) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (row >= rows) return;
-    const int ci = lane & 7, c = ci >> 1, half = ci & 1;
-    const uint8_t* wr = w + row * (int64_t)nb * kblock<Q5>();
-    for (int b = lane >> 3; b < nb; b += 8) {
-        const uint8_t* blk = wr + (int64_t)b * kblock<Q5>();
-        const uint4 qv = *reinterpret_cast<const uint4*>(blk + (Q5 ? 48 : 16) + 16 * ci);
-        const int8_t* a = qs + (int64_t)b * QK + 64 * c + 16 * half;
-        uint32_t lo[4], hi[4];
-        q4k_unpack(qv, lo, hi);
-        if (Q5) q5k_fifth_bits(*reinterpret_cast<const uint4*>(blk + 16 + 16 * half), c, lo, hi);
-        int S0, S1;
-        q4k_chunk_sums(lo, hi, *reinterpret_cast<const int4*>(a), *reinterpret_cast<const int4*>(a + 32), S0, S1);
-        // the two halves of each sub-block sit in lanes ci and ci^1
-        S0 += __shfl_xor(S0, 1, WAVE);
-        S1 += __shfl_xor(S1, 1, WAVE);
-        if (!half) {
-            S[(row * nb + b) * 8 + 2 * c] = S0;
-            S[(row * nb + b) * 8 + 2 * c + 1] = S1;
-        }
     }
 }
 
@@ -411,8 +400,12 @@ __device__ __forceinline__ void q6k_load_a(Q6A<NC>& A, int b, int h, int lh, con
     }
 }
 
-template <int NC>
-__device__ __forceinline__ void q6k_accum(const Q6W& W, const Q6A<NC>& A, int lh, bool valid, float (&acc)[NC]) {
+// SUMS (test support, one column): also store the lane's four exact
+// sub-block sums to Sb[lh], Sb[2 + lh], Sb[4 + lh], Sb[6 + lh] (Sb: the
+// block's sums from sub-block 8h on).
+template <int NC, bool SUMS = false>
+__device__ __forceinline__ void q6k_accum(const Q6W& W, const Q6A<NC>& A, int lh, bool valid, float (&acc)[NC],
+                                          int32_t* Sb = nullptr) {
     // scale bytes (relative to 8h): sub-blocks 8h + 2tt + lh and +4
     const uint32_t sw0 = W.scv.x >> (8 * lh), sw1 = W.scv.y >> (8 * lh);
     const int sc00 = (int)(int8_t)(sw0 & 0xffu), sc01 = (int)(int8_t)(sw1 & 0xffu);                  // tt = 0
@@ -423,8 +416,17 @@ __device__ __forceinline__ void q6k_accum(const Q6W& W, const Q6A<NC>& A, int lh
     q6k_unpack(W.ql1, W.qhv, 1, lo1, hi1);
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
-        const int I = sc00 * q6k_sum16(lo0, A.a[t][0]) + sc01 * q6k_sum16(hi0, A.a[t][1]) +
-                      sc10 * q6k_sum16(lo1, A.a[t][2]) + sc11 * q6k_sum16(hi1, A.a[t][3]);
+        const int s00 = q6k_sum16(lo0, A.a[t][0]), s01 = q6k_sum16(hi0, A.a[t][1]);
+        const int s10 = q6k_sum16(lo1, A.a[t][2]), s11 = q6k_sum16(hi1, A.a[t][3]);
+        if constexpr (SUMS) {
+            if (valid) {
+                Sb[lh] = s00;
+                Sb[4 + lh] = s01;
+                Sb[2 + lh] = s10;
+                Sb[6 + lh] = s11;
+            }
+        }
+        const int I = sc00 * s00 + sc01 * s01 + sc10 * s10 + sc11 * s11;
         const float v = A.d8[t] * dd * (float)I;
         acc[t] += valid ? v : 0.0f;
     }
@@ -453,12 +455,16 @@ constexpr int Q6_DEPTH = Q8K_Q6_DEPTH;
 //
 // FUSED: the activations arrive as fp32 columns x and every workgroup packs
 // them into LDS first (as the fused Q4_K kernel does); qs and d8 are unused.
-template <int NC, bool FUSED>
+//
+// SUMS (test support, NC = 1, packed token): the same kernel also stores the
+// exact sub-block sums S [rows][nb][16].
+template <int NC, bool FUSED, bool SUMS = false>
 __global__ __launch_bounds__(256) void matvec_q6k_kernel(const uint16_t* __restrict__ prefix,
                                                          const uint8_t* __restrict__ bodies, int64_t rows, int nb,
                                                          const int8_t* __restrict__ qs, const float* __restrict__ d8,
                                                          int64_t K, float* __restrict__ y, const float* __restrict__ x,
-                                                         PackedOut o) {
+                                                         PackedOut o, int32_t* __restrict__ S) {
+    static_assert(!SUMS || (NC == 1 && !FUSED), "sums of one packed column");
     if constexpr (FUSED) {
         extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
         int8_t* sqs = reinterpret_cast<int8_t*>(lds);
@@ -496,7 +502,7 @@ __global__ __launch_bounds__(256) void matvec_q6k_kernel(const uint16_t* __restr
                 float acc[NC];
 #pragma unroll
                 for (int t = 0; t < NC; ++t) acc[t] = 0.0f;
-                q6k_accum(W[i], A, lh, valid, acc);
+                q6k_accum<NC, SUMS>(W[i], A, lh, valid, acc, SUMS ? S + (cur * nb + b) * 16 + 8 * h : nullptr);
                 q6k_store(acc, lane, rows, cur, y);
                 if (cur + stride >= rows) return;
             }
@@ -513,29 +519,9 @@ __global__ __launch_bounds__(256) void matvec_q6k_kernel(const uint16_t* __restr
             Q6A<NC> A;
             q6k_load_w(W, prefix, bodies, row, b, h, lh, nb);
             q6k_load_a(A, b, h, lh, qs, d8, K, nb);
-            q6k_accum(W, A, lh, b0 < nb, acc);
+            q6k_accum<NC, SUMS>(W, A, lh, b0 < nb, acc, SUMS ? S + (row * nb + b) * 16 + 8 * h : nullptr);
         }
         q6k_store(acc, lane, rows, row, y);
-    }
-}
-
-__global__ __launch_bounds__(256) void sums_q6k_kernel(const uint8_t* __restrict__ bodies, int64_t rows, int nb,
-                                                       const int8_t* __restrict__ qs, int32_t* __restrict__ S) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (row >= rows) return;
-    const int ci = lane & 7, h = ci >> 2, tt = (ci >> 1) & 1, lh = ci & 1;
-    const int s0 = 8 * h + 2 * tt + lh;
-    const int aoff = 128 * h + 32 * tt + 16 * lh;
-    for (int b = lane >> 3; b < nb; b += 8) {
-        const int64_t ib = row * nb + b;
-        const uint8_t* body = bodies + ib * Q6K_BODY;
-        uint32_t lo[4], hi[4];
-        q6k_unpack(*reinterpret_cast<const uint4*>(body + 16 * ci),
-                   *reinterpret_cast<const uint4*>(body + 128 + 16 * (2 * h + lh)), tt, lo, hi);
-        const int8_t* a = qs + (int64_t)b * QK + aoff;
-        S[ib * 16 + s0] = q6k_sum16(lo, *reinterpret_cast<const int4*>(a));
-        S[ib * 16 + s0 + 4] = q6k_sum16(hi, *reinterpret_cast<const int4*>(a + 64));
     }
 }
 
@@ -554,12 +540,12 @@ static void go_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, float* y, hip
     constexpr int U = NC <= Q8K_MV_U2_MAXNC ? 2 : 1;
     constexpr int WV = mv_waves<NC>();
     if (NC >= Q8K_MV_STAGED_MINNC && fused_lds_bytes(NC, a.K) <= FUSED_LDS_MAX) {
-        hipLaunchKernelGGL((matvec_staged_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + WV - 1) / WV)),
-                           dim3(64 * WV), fused_lds_bytes(NC, a.K), s, w, rows, nb, a.qs, a.d, a.bs, a.K, y);
+        Q8K_LAUNCH((matvec_staged_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + WV - 1) / WV)), dim3(64 * WV),
+                   fused_lds_bytes(NC, a.K), s, w, rows, nb, a.qs, a.d, a.bs, a.K, y);
         return;
     }
-    hipLaunchKernelGGL((matvec_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + WV - 1) / WV)), dim3(64 * WV), 0, s, w,
-                       rows, nb, a.qs, a.d, a.bs, a.K, y);
+    Q8K_LAUNCH((matvec_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + WV - 1) / WV)), dim3(64 * WV), 0, s, w, rows, nb,
+               a.qs, a.d, a.bs, a.K, y, nullptr);
 }
 #ifndef Q8K_Q6_GRID
 #define Q8K_Q6_GRID 512
@@ -568,8 +554,8 @@ template <int NC>
 static void go_q6k(const uint16_t* p, const uint8_t* bodies, int64_t rows, int nb, Acts a, float* y, hipStream_t s) {
     const int64_t wgs = (rows + 3) / 4;
     const unsigned grid = (unsigned)(wgs < Q8K_Q6_GRID ? wgs : Q8K_Q6_GRID);
-    hipLaunchKernelGGL((matvec_q6k_kernel<NC, false>), dim3(grid), dim3(256), 0, s, p, bodies, rows, nb, a.qs, a.d, a.K,
-                       y, nullptr, PackedOut{nullptr, nullptr, nullptr});
+    Q8K_LAUNCH((matvec_q6k_kernel<NC, false>), dim3(grid), dim3(256), 0, s, p, bodies, rows, nb, a.qs, a.d, a.K, y,
+               nullptr, PackedOut{nullptr, nullptr, nullptr}, nullptr);
 }
 
 template <bool Q5>
@@ -603,8 +589,8 @@ static void go_f32_q4k(const uint8_t* w, int64_t rows, int nb, const float* x, i
     constexpr int U = NC <= Q8K_MV_U2_MAXNC ? 2 : 1;
     const size_t lds = fused_lds_bytes(NC, K);
     constexpr int WV = fused_waves<NC>();
-    hipLaunchKernelGGL((matvec_f32_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + WV - 1) / WV)), dim3(64 * WV), lds,
-                       s, w, rows, nb, x, K, y, o);
+    Q8K_LAUNCH((matvec_f32_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + WV - 1) / WV)), dim3(64 * WV), lds, s, w,
+               rows, nb, x, K, y, o);
 }
 
 template <int NC>
@@ -612,8 +598,8 @@ static void go_f32_q6k(const uint16_t* p, const uint8_t* bodies, int64_t rows, i
                        float* y, PackedOut o, hipStream_t s) {
     const int64_t wgs = (rows + 3) / 4;
     const unsigned grid = (unsigned)(wgs < Q8K_Q6_GRID ? wgs : Q8K_Q6_GRID);
-    hipLaunchKernelGGL((matvec_q6k_kernel<NC, true>), dim3(grid), dim3(256), fused_lds_bytes(NC, K), s, p, bodies,
-                       rows, nb, nullptr, nullptr, K, y, x, o);
+    Q8K_LAUNCH((matvec_q6k_kernel<NC, true>), dim3(grid), dim3(256), fused_lds_bytes(NC, K), s, p, bodies, rows, nb,
+               nullptr, nullptr, K, y, x, o, nullptr);
 }
 
 hipError_t launch_matvec_f32(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, const float* x,
@@ -658,22 +644,23 @@ hipError_t launch_matvec_q6k(const uint16_t* prefix, const uint8_t* bodies, int6
     return hipGetLastError();
 }
 
-hipError_t launch_sums_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int32_t* S, hipStream_t s) {
-    hipLaunchKernelGGL(sums_q4k_kernel<false>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb, a.qs,
-                       S);
-    return hipGetLastError();
-}
-
-hipError_t launch_sums_q5k(const uint8_t* w, int64_t rows, int nb, Acts a, int32_t* S, hipStream_t s) {
-    hipLaunchKernelGGL(sums_q4k_kernel<true>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, nb, a.qs,
-                       S);
-    return hipGetLastError();
-}
-
-hipError_t launch_sums_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t rows, int nb, Acts a, int32_t* S,
-                           hipStream_t s) {
-    (void)prefix;
-    hipLaunchKernelGGL(sums_q6k_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, bodies, rows, nb, a.qs, S);
+hipError_t launch_matvec_sums(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a,
+                              float* y, int32_t* S, hipStream_t s) {
+    // qmatvec's launch shapes for one column (go_q4k, go_q6k)
+    constexpr int WV = mv_waves<1>();
+    const dim3 g4((unsigned)((rows + WV - 1) / WV));
+    if (fmt == WFMT_Q4_K) {
+        Q8K_LAUNCH((matvec_q4k_kernel<1, 2, false, true>), g4, dim3(64 * WV), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K,
+                   y, S);
+    } else if (fmt == WFMT_Q5_K) {
+        Q8K_LAUNCH((matvec_q4k_kernel<1, 2, true, true>), g4, dim3(64 * WV), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K,
+                   y, S);
+    } else {
+        const int64_t wgs = (rows + 3) / 4;
+        const unsigned grid = (unsigned)(wgs < Q8K_Q6_GRID ? wgs : Q8K_Q6_GRID);
+        Q8K_LAUNCH((matvec_q6k_kernel<1, false, true>), dim3(grid), dim3(256), 0, s, prefix, w, rows, nb, a.qs, a.d,
+                   a.K, y, nullptr, PackedOut{nullptr, nullptr, nullptr}, S);
+    }
     return hipGetLastError();
 }
 

@@ -502,16 +502,16 @@ __global__ __launch_bounds__(256) void moe_chunk_kernel(const uint8_t* __restric
 hipError_t launch_moe_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T, const int32_t* ids,
                           const float* rw, int topk, float* y, hipStream_t s) {
     const unsigned grid = (unsigned)((rows + MQ_ROWS - 1) / MQ_ROWS);
-    hipLaunchKernelGGL(moe_rows_q4k_kernel<false>, dim3(grid), dim3(64 * MQ_WAVES), 0, s, w, E, rows, nb, a.qs, a.d,
-                       a.bs, a.K, T, ids, rw, topk, y);
+    Q8K_LAUNCH(moe_rows_q4k_kernel<false>, dim3(grid), dim3(64 * MQ_WAVES), 0, s, w, E, rows, nb, a.qs, a.d, a.bs,
+               a.K, T, ids, rw, topk, y);
     return hipGetLastError();
 }
 
 hipError_t launch_moe_q5k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T, const int32_t* ids,
                           const float* rw, int topk, float* y, hipStream_t s) {
     const unsigned grid = (unsigned)((rows + MQ_ROWS - 1) / MQ_ROWS);
-    hipLaunchKernelGGL(moe_rows_q4k_kernel<true>, dim3(grid), dim3(64 * MQ_WAVES), 0, s, w, E, rows, nb, a.qs, a.d,
-                       a.bs, a.K, T, ids, rw, topk, y);
+    Q8K_LAUNCH(moe_rows_q4k_kernel<true>, dim3(grid), dim3(64 * MQ_WAVES), 0, s, w, E, rows, nb, a.qs, a.d, a.bs,
+               a.K, T, ids, rw, topk, y);
     return hipGetLastError();
 }
 
@@ -519,8 +519,8 @@ hipError_t launch_moe_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t
                           int64_t T, const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s) {
     const int64_t waves = (rows + MC_ROWS - 1) / MC_ROWS;
     const unsigned grid = (unsigned)((waves + 3) / 4);
-    hipLaunchKernelGGL(moe_chunk_kernel<true>, dim3(grid), dim3(256), 0, s, bodies, prefix, E, rows, nb, a.qs, a.d,
-                       a.bs, a.K, T, ids, rw, topk, y);
+    Q8K_LAUNCH(moe_chunk_kernel<true>, dim3(grid), dim3(256), 0, s, bodies, prefix, E, rows, nb, a.qs, a.d, a.bs,
+               a.K, T, ids, rw, topk, y);
     return hipGetLastError();
 }
 

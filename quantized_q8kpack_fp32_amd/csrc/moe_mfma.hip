@@ -143,12 +143,14 @@ __device__ __forceinline__ void mm_wait_w(MmW<6>& W) {
 // the next writes behind the reads.
 __device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <bool Q5>
+// SUMS (test support): the same kernel also stores each pair's exact sub-block
+// sums, Sout [T * topk][rows][nb][8], as its matrix cores produce them.
+template <bool Q5, bool SUMS = false>
 __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
     const uint8_t* __restrict__ w, int64_t E, int64_t rows, int nb, const int8_t* __restrict__ qs,
     const float* __restrict__ d8, const int16_t* __restrict__ bs, int64_t K, int64_t T,
     const int32_t* __restrict__ ids, const float* __restrict__ rw, int topk, float* __restrict__ y, int rt,
-    int64_t ntiles) {
+    int64_t ntiles, int32_t* __restrict__ Sout) {
     using F = MmFmt<Q5>;
     __shared__ __attribute__((aligned(16))) MmSmem<Q5> sm;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: expert and rsrc are scalar
@@ -277,6 +279,14 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
                                     return __builtin_amdgcn_mfma_i32_32x32x32_i8(aj, bj, zero, 0, 0, 0);
                                 };
                                 auto fold = [&](int j, const v16i& S) {
+                                    if constexpr (SUMS) {
+                                        // register r < 4 of lane (i, g) holds pair 4g + r of the group, row i
+#pragma unroll
+                                        for (int r = 0; r < 4; ++r)
+                                            if (4 * g + r < n && i < live)
+                                                Sout[((int64_t)L.plist[k0 + 4 * g + r] * rows + r0 + i) * (nb * 8) +
+                                                     8 * b + j] = S[r];
+                                    }
                                     const int sc = (int)(((j < 4 ? sc03 : sc47) >> (8 * (j & 3))) & 0xffu);
 #pragma unroll
                                     for (int r = 0; r < 4; ++r)
@@ -377,9 +387,9 @@ int64_t device_cu_count() {
 
 bool moe_mfma_q4k_fits(int64_t K) { return mm_tok_bytes(K) <= MM_TOK_BYTES; }
 
-template <bool Q5>
+template <bool Q5, bool SUMS = false>
 hipError_t launch_moe_mfma(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T, const int32_t* ids,
-                           const float* rw, int topk, float* y, hipStream_t s) {
+                           const float* rw, int topk, float* y, hipStream_t s, int32_t* Sout = nullptr) {
     if (!moe_mfma_q4k_fits(a.K)) return hipErrorInvalidValue;
     // One workgroup per compute unit (its LDS allows no second), each walking
     // row tiles of rt <= 32 rows: rt is chosen so the tiles come out as whole
@@ -391,8 +401,8 @@ hipError_t launch_moe_mfma(const uint8_t* w, int64_t E, int64_t rows, int nb, Ac
     rt = rt < 16 ? 16 : rt > MM_ROWS ? MM_ROWS : rt;
     const int64_t ntiles = (rows + rt - 1) / rt;
     const unsigned grid = (unsigned)(ntiles < cus ? ntiles : cus);
-    hipLaunchKernelGGL(moe_mfma_q4k_kernel<Q5>, dim3(grid), dim3(64 * MM_WAVES), 0, s, w, E, rows, nb, a.qs, a.d, a.bs,
-                       a.K, T, ids, rw, topk, y, (int)rt, ntiles);
+    Q8K_LAUNCH((moe_mfma_q4k_kernel<Q5, SUMS>), dim3(grid), dim3(64 * MM_WAVES), 0, s, w, E, rows, nb, a.qs, a.d, a.bs,
+               a.K, T, ids, rw, topk, y, (int)rt, ntiles, Sout);
     return hipGetLastError();
 }
 
@@ -403,6 +413,11 @@ hipError_t launch_moe_mfma_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb
 hipError_t launch_moe_mfma_q5k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
                                const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s) {
     return launch_moe_mfma<true>(w, E, rows, nb, a, T, ids, rw, topk, y, s);
+}
+hipError_t launch_moe_mfma_sums(bool q5, const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
+                                const int32_t* ids, const float* rw, int topk, float* y, int32_t* S, hipStream_t s) {
+    return q5 ? launch_moe_mfma<true, true>(w, E, rows, nb, a, T, ids, rw, topk, y, s, S)
+              : launch_moe_mfma<false, true>(w, E, rows, nb, a, T, ids, rw, topk, y, s, S);
 }
 
 }  // namespace q8k

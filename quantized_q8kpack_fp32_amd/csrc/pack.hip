@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ x, 
 }
 
 hipError_t launch_pack(const float* x, int64_t nblocks, int8_t* qs, float* d, int16_t* bsums, hipStream_t s) {
-    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((nblocks + 15) / 16)), dim3(256), 0, s, x, nblocks, qs, d, bsums);
+    Q8K_LAUNCH(pack_kernel, dim3((unsigned)((nblocks + 15) / 16)), dim3(256), 0, s, x, nblocks, qs, d, bsums);
     return hipGetLastError();
 }
 
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void bind_q6k_kernel(const uint8_t* __restrict
 
 hipError_t launch_bind_q6k(const uint8_t* src, int64_t nblocks, uint16_t* prefix, uint8_t* bodies, hipStream_t s) {
     const int64_t grid = (nblocks + 3) / 4;
-    hipLaunchKernelGGL(bind_q6k_kernel, dim3((unsigned)grid), dim3(256), 0, s, src, nblocks, prefix, bodies);
+    Q8K_LAUNCH(bind_q6k_kernel, dim3((unsigned)grid), dim3(256), 0, s, src, nblocks, prefix, bodies);
     return hipGetLastError();
 }
 

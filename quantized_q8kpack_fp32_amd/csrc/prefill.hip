@@ -394,10 +394,19 @@ __device__ __forceinline__ void producer_store(const PrefillRegs& R, PrefillBuf<
 }
 
 // ------------------------------------------------------------ consumers ----
+// Test support (SUMS): where the block sums I_b go, [M][rows][nb] from the
+// tile's first token and row (int32).
+struct PfSums {
+    int32_t* I;
+    int64_t rows, live, nrow;  // problem rows; tokens and rows of this tile still inside the problem
+    int nb;
+};
+
 // Consumer wave: tokens tg0..tg0+63 (two MFMA tiles) x rows 32rg..32rg+31.
-template <int F>
+// SUMS: also store each (token, row)'s exact block sum I_b of block b to D.
+template <int F, bool SUMS = false>
 __device__ __forceinline__ void consumer_block(const PrefillBuf<F>& sm, int lane, int rg, int tg0, v16f (&accf)[2],
-                                               v16f (&accj)[2]) {
+                                               v16f (&accj)[2], const PfSums& D = PfSums{}, int b = 0) {
     constexpr bool Q5 = F == PF_Q5;
     const int kg = lane >> 5;
     const int nl = 32 * rg + (lane & 31);
@@ -478,7 +487,12 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf<F>& sm, int lane
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * g + i;
                 const int I = (ph[t][r] << (F == PF_Q6 ? 7 : 3)) + pl[t][r];
-                const float If = (float)(Q5 ? I + (pq[t][r] << 4) : I);
+                const int Ib = Q5 ? I + (pq[t][r] << 4) : I;
+                if constexpr (SUMS) {
+                    const int m = tg0 + 32 * t + 8 * g + 4 * kg + i;
+                    if (m < D.live && nl < D.nrow) D.I[((int64_t)m * D.rows + nl) * D.nb + b] = Ib;
+                }
+                const float If = (float)Ib;
                 accf[t][r] = fmaf(If * d8a[i], dd, accf[t][r]);
             }
         }
@@ -488,9 +502,10 @@ __device__ __forceinline__ void consumer_block(const PrefillBuf<F>& sm, int lane
 // One 128-token x 64-row tile over all nb blocks.  The producers' sources are
 // in S (built by the caller); consumer output row m of the tile goes to
 // y[orow(m) * rows + n] when ok(m).
-template <int F, class ORow, class OK>
+template <int F, bool SUMS = false, class ORow, class OK>
 __device__ __forceinline__ void prefill_tile(PrefillSmem<F>& sm, const PrefillSrc& S, int nb, int64_t rows,
-                                             int64_t n0, float* __restrict__ y, ORow orow, OK ok) {
+                                             int64_t n0, float* __restrict__ y, ORow orow, OK ok,
+                                             const PfSums& D = PfSums{}) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // Both roles run the same number of barriers: one before the first
     // block and one after each block (checked for every block count).
@@ -530,7 +545,7 @@ __device__ __forceinline__ void prefill_tile(PrefillSmem<F>& sm, const PrefillSr
             for (int r = 0; r < 16; ++r) accf[i][r] = accj[i][r] = 0.0f;
         lds_barrier();
         for (int b = 0; b < nb; ++b) {
-            consumer_block<F>(sm.buf[b & 1], lane, rg, tg0, accf, accj);
+            consumer_block<F, SUMS>(sm.buf[b & 1], lane, rg, tg0, accf, accj, D, b);
             lds_barrier();
         }
         const int64_t n = n0 + 32 * rg + (lane & 31);
@@ -545,12 +560,14 @@ __device__ __forceinline__ void prefill_tile(PrefillSmem<F>& sm, const PrefillSr
     }
 }
 
-template <int F>
+// SUMS (test support): the same kernel also stores every block's exact
+// integer sum I_b to Isum [M][rows][nb].
+template <int F, bool SUMS = false>
 __global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restrict__ w,
                                                           const uint16_t* __restrict__ prefix, int64_t rows, int nb,
                                                           const int8_t* __restrict__ qs, const float* __restrict__ d8,
                                                           const int16_t* __restrict__ bs, int64_t K, int64_t M,
-                                                          float* __restrict__ y) {
+                                                          float* __restrict__ y, int32_t* __restrict__ Isum) {
     __shared__ __attribute__((aligned(16))) PrefillSmem<F> sm;
     const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
     const int64_t n0 = ((int64_t)blockIdx.x % ntn) * PF_TN;
@@ -558,8 +575,10 @@ __global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restr
     PrefillSrc S;
     if (threadIdx.x >= 256)
         producer_src<F>(S, w, prefix, rows, nb, qs, d8, bs, K, M, n0, m0, (int)threadIdx.x - 256);
-    prefill_tile(
-        sm, S, nb, rows, n0, y, [&](int m) { return m0 + m; }, [&](int m) { return m0 + m < M; });
+    PfSums D{};
+    if constexpr (SUMS) D = PfSums{Isum + (m0 * rows + n0) * nb, rows, M - m0, rows - n0, nb};
+    prefill_tile<F, SUMS>(
+        sm, S, nb, rows, n0, y, [&](int m) { return m0 + m; }, [&](int m) { return m0 + m < M; }, D);
 }
 
 // ----------------------------------------------------- mixture of experts ----
@@ -707,41 +726,51 @@ hipError_t launch_prefill_moe(int fmt, const uint8_t* w, const uint16_t* prefix,
     int32_t* nchunks = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.meta);
     int4* chunks = reinterpret_cast<int4*>(static_cast<char*>(ws) + L.chunks);
     int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.order);
-    hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(1024), 0, s, ids, L.P, (int)E, nchunks, chunks, order);
+    Q8K_LAUNCH(moe_group_kernel, dim3(1), dim3(1024), 0, s, ids, L.P, (int)E, nchunks, chunks, order);
     const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
     const dim3 grid((unsigned)(L.max_chunks * ntn));
     if (fmt == PF_Q4)
         launch_prefill_regw_moe_q4k(w, rows, nb, a, T, L.max_chunks, nchunks, chunks, order, topk, out, s);
     else if (fmt == PF_Q6)
-        hipLaunchKernelGGL(prefill_moe_q4k_kernel<PF_Q6>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
-                           a.K, T, nchunks, chunks, order, topk, out);
+        Q8K_LAUNCH(prefill_moe_q4k_kernel<PF_Q6>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K, T,
+                   nchunks, chunks, order, topk, out);
     else if (fmt == PF_Q5)
-        hipLaunchKernelGGL(prefill_moe_q4k_kernel<PF_Q5>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
-                           a.K, T, nchunks, chunks, order, topk, out);
+        Q8K_LAUNCH(prefill_moe_q4k_kernel<PF_Q5>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K, T,
+                   nchunks, chunks, order, topk, out);
     if (rows % 4 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0)
-        hipLaunchKernelGGL(moe_combine_kernel<4>, dim3((unsigned)(T * ((rows + 1023) / 1024))), dim3(256), 0, s, out,
-                           rows, T, ids, rw, topk, E, y);
+        Q8K_LAUNCH(moe_combine_kernel<4>, dim3((unsigned)(T * ((rows + 1023) / 1024))), dim3(256), 0, s, out, rows, T,
+                   ids, rw, topk, E, y);
     else
-        hipLaunchKernelGGL(moe_combine_kernel<1>, dim3((unsigned)(T * ((rows + 255) / 256))), dim3(256), 0, s, out,
-                           rows, T, ids, rw, topk, E, y);
+        Q8K_LAUNCH(moe_combine_kernel<1>, dim3((unsigned)(T * ((rows + 255) / 256))), dim3(256), 0, s, out, rows, T,
+                   ids, rw, topk, E, y);
     return hipGetLastError();
 }
 
+// Q4_K runs the register-plane tile (prefill_regw.hip); Q5_K and relaid Q6_K
+// the producer/consumer tile above.
 hipError_t launch_prefill(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a,
                           int64_t M, float* y, hipStream_t s) {
-#ifndef Q8K_PREFILL_PC_Q4
     if (fmt == PF_Q4) return launch_prefill_regw_q4k(w, rows, nb, a, M, y, s);
-#endif
     const dim3 grid((unsigned)(((rows + PF_TN - 1) / PF_TN) * ((M + PF_TM - 1) / PF_TM)));
     if (fmt == PF_Q6)
-        hipLaunchKernelGGL(prefill_q4k_kernel<PF_Q6>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
-                           a.K, M, y);
-    else if (fmt == PF_Q5)
-        hipLaunchKernelGGL(prefill_q4k_kernel<PF_Q5>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
-                           a.K, M, y);
+        Q8K_LAUNCH(prefill_q4k_kernel<PF_Q6>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K, M, y,
+                   nullptr);
     else
-        hipLaunchKernelGGL(prefill_q4k_kernel<PF_Q4>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs,
-                           a.K, M, y);
+        Q8K_LAUNCH(prefill_q4k_kernel<PF_Q5>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K, M, y,
+                   nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_sums(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a,
+                               int64_t M, float* y, int32_t* I, hipStream_t s) {
+    if (fmt == PF_Q4) return launch_prefill_regw_q4k_sums(w, rows, nb, a, M, y, I, s);
+    const dim3 grid((unsigned)(((rows + PF_TN - 1) / PF_TN) * ((M + PF_TM - 1) / PF_TM)));
+    if (fmt == PF_Q6)
+        Q8K_LAUNCH((prefill_q4k_kernel<PF_Q6, true>), grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K,
+                   M, y, I);
+    else
+        Q8K_LAUNCH((prefill_q4k_kernel<PF_Q5, true>), grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K,
+                   M, y, I);
     return hipGetLastError();
 }
 

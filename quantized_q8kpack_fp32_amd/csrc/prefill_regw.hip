@@ -105,27 +105,36 @@ __device__ __forceinline__ void dma4(rsrc_t r, void* lds_base, int off) {
 }
 
 // Sources of one workgroup: tokens m0.., rows n0...  Offsets stay 32-bit: a
-// tile's rows span at most 64 * (K / 256) * 144 bytes, its tokens 128 * K.
-// The byte counts from the tile's start to the end of each buffer are
-// clamped to 2^31 - 1 once, so every resource range below is one 32-bit
-// subtraction and a clamp at zero (scalar): no read the kernel issues lies
-// past 2^31 - 1 bytes from its tile's start.
+// tile's rows span at most 64 * (K / 256) * 144 bytes, its tokens 128 * K <=
+// 2^31 bytes.  The byte counts from the tile's start to the end of each
+// buffer are unsigned 32-bit (the largest token span, 2^31, included; the
+// resource's record count is an unsigned 32-bit field), so every resource
+// range below is the count left after the copy's own start offset: one
+// scalar compare and subtraction.
 struct RwSrc {
     const uint8_t* w;
     const int8_t* x;
     const float* d8;
     const int16_t* bs;
-    int wbytes, xbytes, d8bytes, bsbytes;
+    uint32_t wbytes, xbytes, d8bytes, bsbytes;
     int wrow;  // bytes per weight row
     int nb;
     int K;
     const int* tokoff;  // gathered tiles: LDS offsets of the tile's token rows
 };
-__device__ __forceinline__ int clamp31(int64_t v) { return v <= 0 ? 0 : v < 0x7fffffff ? (int)v : 0x7fffffff; }
-// Raw buffer resource over [base, base + max(remaining, 0)).
-__device__ __forceinline__ rsrc_t rsrc32(const void* base, int remaining) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, remaining > 0 ? remaining : 0,
-                                             0x00020000 /* raw, untyped dwords */);
+// Byte span as an unsigned 32-bit count (0 if negative, 2^32 - 1 at most).
+__device__ __forceinline__ uint32_t span32(int64_t v) {
+    return v <= 0 ? 0u : v < 0xffffffffLL ? (uint32_t)v : 0xffffffffu;
+}
+// Raw buffer resource over [base + off, base + total): the records left after
+// the start offset `off` (none when off >= total).  The difference is taken in
+// signed 64 bits: an unsigned compare-and-subtract becomes a saturating
+// subtract, which only the vector unit has, and the descriptor must stay in
+// scalar registers for the copies' inline assembly.
+__device__ __forceinline__ rsrc_t rsrc32(const void* base, uint32_t total, uint32_t off) {
+    const int64_t left = (int64_t)total - (int64_t)off;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base)) + off, (short)0,
+                                             (int)(uint32_t)(left > 0 ? left : 0), 0x00020000 /* raw, untyped dwords */);
 }
 
 // The buffer-unit copies of stage sg = 2 s + h (tokens 64 h .. 64 h + 63 of
@@ -140,7 +149,7 @@ __device__ __forceinline__ void issue_codes(RwCopied& sm, const RwSrc& S, int sg
     if constexpr (GATHER) {
         // copy i covers stage tokens 32 half + 4i + tq, each at its own row
         const int bo = (4 * s + q) * QK;
-        const rsrc_t rx = rsrc32(S.x + bo, S.xbytes - bo);
+        const rsrc_t rx = rsrc32(S.x, S.xbytes, (uint32_t)bo);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int m = RW_SM * h + 32 * half + 4 * i + tq;
@@ -157,7 +166,7 @@ __device__ __forceinline__ void issue_codes(RwCopied& sm, const RwSrc& S, int sg
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int o = base + 4 * i * S.K;
-        const rsrc_t rx = rsrc32(S.x + o, S.xbytes - o);
+        const rsrc_t rx = rsrc32(S.x, S.xbytes, (uint32_t)o);
         dma16(rx, &sm.codes[sg & 1][q][32 * half + 4 * i][0], vo[i & 3]);
     }
 }
@@ -172,20 +181,20 @@ __device__ __forceinline__ void issue_aux(RwCopied& sm, const RwSrc& S, int sg, 
         const int tok = S.tokoff[t0 + lane];
         if (wv < 4) {
             const int o = (4 * s + q) * 4;
-            dma4(rsrc32((const char*)S.d8 + o, S.d8bytes - o), &sm.d8raw[st][q][0], tok >> 6);
+            dma4(rsrc32(S.d8, S.d8bytes, (uint32_t)o), &sm.d8raw[st][q][0], tok >> 6);
         } else {
             const int o = (4 * s + q) * 16;
-            dma16(rsrc32((const char*)S.bs + o, S.bsbytes - o), &sm.bs[st][q][0][0], tok >> 4);
+            dma16(rsrc32(S.bs, S.bsbytes, (uint32_t)o), &sm.bs[st][q][0][0], tok >> 4);
         }
         return;
     }
     const int off = lane * S.nb;  // token 64 h + lane, block 4 s + q, in units of one block's record
     if (wv < 4) {
         const int o = (t0 * S.nb + 4 * s + q) * 4;
-        dma4(rsrc32((const char*)S.d8 + o, S.d8bytes - o), &sm.d8raw[st][q][0], off * 4);
+        dma4(rsrc32(S.d8, S.d8bytes, (uint32_t)o), &sm.d8raw[st][q][0], off * 4);
     } else {
         const int o = (t0 * S.nb + 4 * s + q) * 16;
-        dma16(rsrc32((const char*)S.bs + o, S.bsbytes - o), &sm.bs[st][q][0][0], off * 16);
+        dma16(rsrc32(S.bs, S.bsbytes, (uint32_t)o), &sm.bs[st][q][0][0], off * 16);
     }
 }
 
@@ -193,7 +202,7 @@ __device__ __forceinline__ void load_weights(Q4kRaw& R, const RwSrc& S, int b, i
     // (blocks past the row's end read the next row's bytes or, past the last
     // row, zeros: they are never multiplied)
     const int boff = b * Q4K_BLOCK;
-    const rsrc_t rw = rsrc32(S.w + boff, S.wbytes - boff);
+    const rsrc_t rw = rsrc32(S.w, S.wbytes, (uint32_t)boff);
     const int o = (32 * rg + (lane & 31)) * S.wrow;
     R.hdr = load16(rw, o);
     const int oq = o + 16 + 64 * (lane >> 5);
@@ -224,11 +233,20 @@ __device__ __forceinline__ void build_amin(const RwCopied& sm, RwBuilt& sb, int 
     *reinterpret_cast<v8bf*>(&sb.amin[sg & 1][q][t >> 5][(t & 31) + 32 * g]) = o;
 }
 
+// Test support (SUMS): where the block sums I_b go, [M][rows][nb] from the
+// tile's first token and row (int32).
+struct RwSums {
+    int32_t* I;
+    int64_t rows, live, nrow;  // problem rows; tokens and rows of this tile still inside the problem
+    int nb;
+};
+
 // One stage of one wave: 64 tokens x 32 rows of block 4 s + q, two MFMA tiles
-// of 32 tokens, into the accumulators of tiles 2h and 2h + 1.
+// of 32 tokens, into the accumulators of tiles 2h and 2h + 1.  SUMS: also
+// store each (token, row)'s exact block sum I_b to D.
+template <bool SUMS = false>
 __device__ __forceinline__ void wave_stage(const RwCopied& sm, const RwBuilt& sb, const Q4kPlanes& P, int sg, int q,
-                                           int lane,
-                                           v16f (&acc)[4]) {
+                                           int lane, v16f (&acc)[4], const RwSums& D = RwSums{}, int rg = 0) {
     const int g = lane >> 5, h = sg & 1;
     // Code fragment of lane (i, g) at k-step kk: row i of the tile, logical
     // chunk kstep_off(g, kk) / 16 stored at chunk ^ (i & 15): one XOR per read.
@@ -289,6 +307,17 @@ __device__ __forceinline__ void wave_stage(const RwCopied& sm, const RwBuilt& sb
         chains(t, I);
         minterm(t);
         __builtin_amdgcn_s_setprio(0);
+        if constexpr (SUMS) {
+            // lane (j, g) register r: row 32 rg + j, token 8 (r / 4) + 4 g + r % 4 of tile t
+            const int b = 2 * (sg & ~1) + q;
+            const int j = lane & 31;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = 64 * h + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (m < D.live && 32 * rg + j < D.nrow)
+                    D.I[((int64_t)m * D.rows + 32 * rg + j) * D.nb + b] = I[r];
+            }
+        }
         fold(t, I);
     }
 }
@@ -312,12 +341,16 @@ constexpr int RW_RAW_LOADS = 5;  // load_weights() issues five loads
 // chunk's expert by the tokens of its pairs (chunks[c] = {expert, first index
 // in order, count}); the result of pair p goes to row p of y ([P][rows]);
 // workgroups past the chunk count return at once.
-template <bool GATHER>
+//
+// SUMS (test support, dense tiles): the same kernel also stores every block's
+// exact integer sum I_b = 8 P_hi + P_lo to Isum [M][rows][nb].
+template <bool GATHER, bool SUMS = false>
 __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     const uint8_t* __restrict__ w, int64_t rows, int nb, const int8_t* __restrict__ qs,
     const float* __restrict__ d8, const int16_t* __restrict__ bs, int64_t K, int64_t M, float* __restrict__ y,
     const int32_t* __restrict__ nchunks, const int4* __restrict__ chunks, const int32_t* __restrict__ order,
-    int topk) {
+    int topk, int32_t* __restrict__ Isum) {
+    static_assert(!(SUMS && GATHER), "block sums of the dense tile");
     __shared__ __attribute__((aligned(16))) RwCopied sm;
     __shared__ __attribute__((aligned(16))) RwBuilt sb;
     __shared__ RwGather gat;
@@ -350,23 +383,25 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         }
         S.w = w + ((int64_t)ch.x * rows + n0) * S.wrow;
         S.x = qs;
-        S.xbytes = clamp31(M * K);
+        S.xbytes = span32(M * K);
         S.d8 = d8;
-        S.d8bytes = clamp31(M * nb * 4);
+        S.d8bytes = span32(M * nb * 4);
         S.bs = bs;
-        S.bsbytes = clamp31(M * nb * 16);
+        S.bsbytes = span32(M * nb * 16);
         __syncthreads();
     } else {
         live = M - m0;
         S.w = w + n0 * S.wrow;
         S.x = qs + m0 * K;
-        S.xbytes = clamp31((M - m0) * K);
+        S.xbytes = span32((M - m0) * K);
         S.d8 = d8 + m0 * nb;
-        S.d8bytes = clamp31((M - m0) * nb * 4);
+        S.d8bytes = span32((M - m0) * nb * 4);
         S.bs = bs + m0 * nb * 8;
-        S.bsbytes = clamp31((M - m0) * nb * 16);
+        S.bsbytes = span32((M - m0) * nb * 16);
     }
-    S.wbytes = clamp31((rows - n0) * S.wrow);
+    S.wbytes = span32((rows - n0) * S.wrow);
+    RwSums D{};
+    if constexpr (SUMS) D = RwSums{Isum + (m0 * rows + n0) * nb, rows, live, rows - n0, nb};
 
     const int steps = (nb + RW_KQ - 1) / RW_KQ;
     const int nst = 2 * steps;                        // stages
@@ -401,13 +436,13 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         if (sg + 2 < nst) issue_aux<GATHER>(sm, S, sg + 2, wv, lane);
         build_q4k_planes(PL, R, lane);
         load_weights(R, S, b + RW_KQ, rg, lane);
-        if (b < nb) wave_stage(sm, sb, PL, sg, q, lane, acc);
+        if (b < nb) wave_stage<SUMS>(sm, sb, PL, sg, q, lane, acc, D, rg);
         build_amin(sm, sb, sg + 1, tid);
         stage_barrier<RW_RAW_LOADS>();
         // ---- second 64 tokens
         if (sg + 2 < nst) issue_codes<GATHER>(sm, S, sg + 2, wv, lane);
         if (sg + 3 < nst) issue_aux<GATHER>(sm, S, sg + 3, wv, lane);
-        if (b < nb && half2) wave_stage(sm, sb, PL, sg + 1, q, lane, acc);
+        if (b < nb && half2) wave_stage<SUMS>(sm, sb, PL, sg + 1, q, lane, acc, D, rg);
         if (sg + 2 < nst) build_amin(sm, sb, sg + 2, tid);
         stage_barrier<0>();
     }
@@ -449,8 +484,16 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
 hipError_t launch_prefill_regw_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
                                    hipStream_t s) {
     const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * ((M + RW_TM - 1) / RW_TM)));
-    hipLaunchKernelGGL(prefill_regw_q4k_kernel<false>, grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs,
-                       a.K, M, y, nullptr, nullptr, nullptr, 1);
+    Q8K_LAUNCH((prefill_regw_q4k_kernel<false>), grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K, M, y,
+               nullptr, nullptr, nullptr, 1, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_regw_q4k_sums(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
+                                        int32_t* I, hipStream_t s) {
+    const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * ((M + RW_TM - 1) / RW_TM)));
+    Q8K_LAUNCH((prefill_regw_q4k_kernel<false, true>), grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K,
+               M, y, nullptr, nullptr, nullptr, 1, I);
     return hipGetLastError();
 }
 
@@ -458,8 +501,8 @@ hipError_t launch_prefill_regw_moe_q4k(const uint8_t* w, int64_t rows, int nb, A
                                        const int32_t* nchunks, const int4* chunks, const int32_t* order, int topk,
                                        float* out, hipStream_t s) {
     const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * max_chunks));
-    hipLaunchKernelGGL(prefill_regw_q4k_kernel<true>, grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs,
-                       a.K, T, out, nchunks, chunks, order, topk);
+    Q8K_LAUNCH((prefill_regw_q4k_kernel<true>), grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K, T,
+               out, nchunks, chunks, order, topk, nullptr);
     return hipGetLastError();
 }
 

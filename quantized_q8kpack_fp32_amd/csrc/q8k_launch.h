@@ -7,6 +7,18 @@
 
 namespace q8k {
 
+// Launch census: every launch notes its kernel's host handle for the calling
+// thread (the C ABI resets the record at the start of each call), so a test
+// can tell which kernels produced the values it checks ("One kernel, any
+// device", section 5: every registered kernel must be value-checked by some
+// test).
+void note_launch(const void* kernel);
+#define Q8K_LAUNCH(kernel, grid, block, lds, stream, ...)                         \
+    do {                                                                          \
+        ::q8k::note_launch(reinterpret_cast<const void*>(&kernel));               \
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);        \
+    } while (0)
+
 hipError_t launch_pack(const float* x, int64_t nblocks, int8_t* qs, float* d, int16_t* bsums, hipStream_t s);
 hipError_t launch_bind_q6k(const uint8_t* src, int64_t nblocks, uint16_t* prefix, uint8_t* bodies, hipStream_t s);
 
@@ -21,9 +33,7 @@ struct Acts {
 hipError_t launch_matvec_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int ncols, float* y, hipStream_t s);
 hipError_t launch_matvec_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t rows, int nb, Acts a, int ncols,
                              float* y, hipStream_t s);
-hipError_t launch_sums_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int32_t* S, hipStream_t s);
 hipError_t launch_matvec_q5k(const uint8_t* w, int64_t rows, int nb, Acts a, int ncols, float* y, hipStream_t s);
-hipError_t launch_sums_q5k(const uint8_t* w, int64_t rows, int nb, Acts a, int32_t* S, hipStream_t s);
 // Weight formats of the prefill and fused kernels: Q4_K and Q5_K read one
 // weight stream `w` (prefix unused); relaid Q6_K reads the bodies as `w` and
 // the fp16 d prefix.
@@ -41,8 +51,6 @@ inline size_t fused_lds_bytes(int64_t ncols, int64_t K) { return (size_t)(ncols 
 constexpr size_t FUSED_LDS_MAX = 65536;
 hipError_t launch_matvec_f32(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, const float* x,
                              int64_t K, int ncols, float* y, PackedOut o, hipStream_t s);
-hipError_t launch_sums_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t rows, int nb, Acts a, int32_t* S,
-                           hipStream_t s);
 hipError_t launch_moe_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T, const int32_t* ids,
                           const float* rw, int topk, float* y, hipStream_t s);
 // Q4_K mixture-of-experts decode on the int8 matrix cores (moe_mfma.hip); it
@@ -95,5 +103,23 @@ inline MoePrefillWs moe_prefill_ws(int64_t E, int64_t rows, int64_t T, int64_t t
 hipError_t launch_prefill_moe(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t E, int64_t rows, int nb,
                               Acts a, int64_t T, const int32_t* ids, const float* rw, int topk, float* y, void* ws,
                               hipStream_t s);
+
+// ---- test support: the shipped kernels' integer sums (template flags of the
+// same kernels, which also write y as they ship)
+// qmatvec's kernel for one packed token: y [rows] and the exact sub-block sums
+// S [rows][nb][8] (Q4_K, Q5_K) or [rows][nb][16] (relaid Q6_K).
+hipError_t launch_matvec_sums(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a,
+                              float* y, int32_t* S, hipStream_t s);
+// qmatmul_prefill's tile: y [M][rows] and the block sums I [M][rows][nb]
+// (sum_j sc_j * S_j per block, the integer the tile folds into y).
+hipError_t launch_prefill_sums(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a,
+                               int64_t M, float* y, int32_t* I, hipStream_t s);
+hipError_t launch_prefill_regw_q4k_sums(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
+                                        int32_t* I, hipStream_t s);
+// qmatvec_moe's matrix-core kernel (Q4_K, Q5_K): y [T][rows] and the sub-block
+// sums S [T * topk][rows][nb][8] of every (token, slot) pair that selects an
+// expert in [0, E) (other pairs' entries are not written).
+hipError_t launch_moe_mfma_sums(bool q5, const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
+                                const int32_t* ids, const float* rw, int topk, float* y, int32_t* S, hipStream_t s);
 
 }  // namespace q8k

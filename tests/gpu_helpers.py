@@ -1,7 +1,14 @@
-"""Device-side helpers for the GPU parity tests (torch for memory only)."""
+"""Device-side helpers for the GPU parity tests (torch for memory only).
+
+The value checks here (assert_close, assert_exact) compare a GPU result with
+the oracle; a passing check credits the kernels that the test's calls have
+launched since the last check (census.CENSUS).
+"""
 from __future__ import annotations
 
 import numpy as np
+
+from census import CENSUS
 
 TOL_REL = 1e-5  # |err| <= 1e-5 * sum|terms| + 1e-6  (fp32 outputs)
 TOL_ABS = 1e-6
@@ -63,7 +70,27 @@ def split_act(q, xq_host: np.ndarray, T: int, K: int):
     return qs, d, bs
 
 
+def assert_exact(got: np.ndarray, want: np.ndarray, what: str = ""):
+    """Bit-exact equality with an oracle value (integers, bytes); credits the
+    pending kernels."""
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    if got.dtype.kind == "f":
+        same = np.array_equal(got.view(np.uint32 if got.itemsize == 4 else np.uint64),
+                              want.astype(got.dtype).view(np.uint32 if got.itemsize == 4 else np.uint64))
+    else:
+        same = np.array_equal(got.astype(np.int64), want.astype(np.int64))
+    if not same:
+        bad = np.argwhere(got != want)
+        raise AssertionError(f"{what}: {len(bad)} entries differ from the oracle; first at {tuple(bad[0])}: "
+                             f"got {got[tuple(bad[0])]!r} want {want[tuple(bad[0])]!r}")
+    CENSUS.credit()
+
+
 def assert_close(got: np.ndarray, want: np.ndarray, A: np.ndarray, what: str = ""):
+    """|err| <= 1e-5 * A + 1e-6 against the oracle (fp32 outputs); credits the
+    pending kernels."""
     got = np.asarray(got, np.float64)
     assert got.shape == want.shape, (got.shape, want.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output (an unwritten element?)"
@@ -74,3 +101,4 @@ def assert_close(got: np.ndarray, want: np.ndarray, A: np.ndarray, what: str = "
         i = np.unravel_index(np.argmax(err / bound), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} outputs out of tolerance; worst at {i}: got {got[i]!r} "
                              f"want {want[i]!r} err {err[i]:.3g} bound {bound[i]:.3g}")
+    CENSUS.credit()

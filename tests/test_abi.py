@@ -204,3 +204,26 @@ def test_status_strings(q):
     assert q.q8k_status_str(0) == "Q8K_OK"
     assert q.q8k_status_str(7) == "Q8K_ERR_LAUNCH"
     assert q.q8k_status_str(99) == "Q8K_ERR_UNKNOWN"
+
+
+def test_refused_call_records_no_launch(q):
+    """A refusal enqueues nothing: the launch record of the call is empty."""
+    refused(q, "Q8K_ERR_SHAPE", q.qmatvec, q.Q8K_Q4_K, A16, 4, 1000, A16, A16, 0)
+    assert q.q8k_debug_last_launches() == []
+    refused(q, "Q8K_ERR_QTYPE", q.q8k_debug_moe_subblock_sums, q.Q8K_Q6_K_RELAID, A16, 2, 4, 256, A16, 1, A16, A16, 1,
+            A16, A16, 0)
+    assert q.q8k_debug_last_launches() == []
+
+
+def test_census_reads_the_kernel_table(q):
+    """The census maps launch records to kernels through the library's symbol
+    table: it must find the kernels of every family."""
+    import census
+
+    names = {census.short(n) for n in census.kernel_names(q).values()}
+    for k in ("pack_kernel", "bind_q6k_kernel", "matvec_q4k_kernel<1, 2, false, false>",
+              "matvec_q6k_kernel<1, false, false>", "matvec_f32_q4k_kernel<1, 2, false>",
+              "moe_mfma_q4k_kernel<false, false>", "prefill_regw_q4k_kernel<false, false>",
+              "prefill_q4k_kernel<2, false>", "moe_group_kernel", "moe_combine_kernel<4>"):
+        assert k in names, k
+    assert not any(n.startswith("prefill_q4k_kernel<0") for n in names), "the Q4_K prefill runs the register tile"

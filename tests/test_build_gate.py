@@ -26,7 +26,21 @@ csrc/moe.hip:201:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=ker
 def test_spilling_kernel_is_named():
     b = _build_module()
     bad = b._check_scratch(LOG, "moe.hip")
-    assert bad == ["moe.hip: _ZN3q8k10moe_kernelILb0EEEvPKh: 376 bytes/lane of scratch"]
+    assert bad == ["moe.hip: void q8k::moe_kernel<false>(unsigned char const*): 376 bytes/lane of scratch"]
+
+
+def test_only_named_test_kernels_may_spill():
+    """The exemption names test-support instantiations only: the product
+    kernel of the same template still fails the gate."""
+    b = _build_module()
+    log = LOG.replace("_ZN3q8k10moe_kernelILb0EEEvPKh",
+                      "_ZN3q8k12_GLOBAL__N_123prefill_regw_q4k_kernelILb0ELb1EEEvPKhliPKaPKfPKsllPfPKiPK15HIP_vector_"
+                      "typeIiLj4EESC_iPi")
+    assert b._check_scratch(log, "prefill_regw.hip") == []
+    log = LOG.replace("_ZN3q8k10moe_kernelILb0EEEvPKh",
+                      "_ZN3q8k12_GLOBAL__N_123prefill_regw_q4k_kernelILb0ELb0EEEvPKhliPKaPKfPKsllPfPKiPK15HIP_vector_"
+                      "typeIiLj4EESC_iPi")
+    assert len(b._check_scratch(log, "prefill_regw.hip")) == 1
 
 
 def test_clean_log_passes():

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import synth
+from census import tracked
 from gpu_helpers import pack_on_device, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -22,7 +23,7 @@ def q():
         pytest.skip("no GPU")
     import quantized_q8kpack_fp32_amd as q
 
-    return q
+    return tracked(q)
 
 
 def test_graph_replays_match_eager(q):

@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import assert_close, host, pack_on_device, poisoned, poisoned_f32, to_dev
+from census import tracked
+from gpu_helpers import assert_close, assert_exact, host, pack_on_device, poisoned, poisoned_f32, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +29,7 @@ def q():
     import quantized_q8kpack_fp32_amd as q
 
     oracle.build()
-    return q
+    return tracked(q)
 
 
 def _weights(q, fmt, g, rows, K):
@@ -109,7 +110,34 @@ def test_prefill_largest_k_full_tile(q, fmt):
         assert_close(got[t], want[0], A[0], f"prefill {fmt} K=2^24 token {t}")
     zero = np.ones(M, bool)
     zero[list(xr)] = False
-    assert np.array_equal(got[zero], np.zeros((zero.sum(), rows), np.float32))
+    assert_exact(got[zero], np.zeros((zero.sum(), rows), np.float32), "zero tokens")
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_prefill_largest_k_last_code_bytes(q, fmt):
+    """A full 128-token tile at K = 2^24 spans exactly 2^31 code bytes.  Token
+    127 is zero except the last 16 values of its last block, so its output
+    depends only on the tile's last 16 code bytes: a buffer range one byte
+    short would drop the last dword of codes."""
+    import torch
+
+    rows, K, M = 3, K_MAX, 128
+    g = np.random.default_rng(204)
+    w, wd, qt, ot = _weights(q, fmt, g, rows, K)
+    tail = np.zeros((1, K), np.float32)
+    tail[0, K - 16:] = g.standard_normal(16).astype(np.float32)
+    x = torch.zeros((M, K), dtype=torch.float32, device="cuda")
+    x[M - 1, K - 16:] = to_dev(tail[0, K - 16:])
+    xq = poisoned(q.q8k_act_bytes(M, K))
+    q.q8k_pack(x, M, K, xq)
+    del x
+    y = poisoned_f32(M, rows)
+    q.qmatmul_prefill(qt, wd, rows, K, xq, M, y, None, 0)
+    got = host(y)
+    oqs, od, obs = oracle.q8k_pack(tail)
+    want, A = oracle.matvec(ot, w, rows, K, oqs, od, obs)
+    assert_close(got[M - 1], want[0], A[0], f"prefill {fmt} K=2^24, token 127's last 16 values")
+    assert_exact(got[:M - 1], np.zeros((M - 1, rows), np.float32), "zero tokens")
 
 
 def test_prefill_moe_largest_tk(q):
@@ -138,4 +166,4 @@ def test_prefill_moe_largest_tk(q):
         assert_close(got[t:t + 1], want, A, f"moe prefill K={K} token {t}")
     zero = np.ones(T, bool)
     zero[list(xr)] = False
-    assert np.array_equal(got[zero], np.zeros((zero.sum(), rows), np.float32))
+    assert_exact(got[zero], np.zeros((zero.sum(), rows), np.float32), "zero tokens")

@@ -16,8 +16,9 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import (assert_close, host, pack_on_device, poisoned, poisoned_f32, poisoned_i32, split_act,
-                         to_dev)
+from census import tracked
+from gpu_helpers import (assert_close, assert_exact, host, pack_on_device, poisoned, poisoned_f32, poisoned_i32,
+                         split_act, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +34,7 @@ def q():
     import quantized_q8kpack_fp32_amd as q
 
     oracle.build()
-    return q
+    return tracked(q)
 
 
 def q4k(seed, rows, K):
@@ -74,9 +75,9 @@ def test_pack_bit_exact(q, T, K):
     xq = pack_on_device(q, x)
     qs, d, bs = split_act(q, host(xq), T, K)
     oqs, od, obs = oracle.q8k_pack(x)
-    assert np.array_equal(qs, oqs)
-    assert np.array_equal(d.view(np.uint32), od.view(np.uint32))
-    assert np.array_equal(bs, obs)
+    assert_exact(qs, oqs, "codes")
+    assert_exact(d, od, "scales")
+    assert_exact(bs, obs, "sums")
 
 
 @pytest.mark.parametrize("K", [2048, 4096])
@@ -85,22 +86,30 @@ def test_pack_special_blocks_bit_exact(q, K):
     xq = pack_on_device(q, x)
     qs, d, bs = split_act(q, host(xq), 1, K)
     oqs, od, obs = oracle.q8k_pack(x)
-    assert np.array_equal(qs, oqs)
-    assert np.array_equal(d.view(np.uint32), od.view(np.uint32))
-    assert np.array_equal(bs, obs)
+    assert_exact(qs, oqs, "codes")
+    assert_exact(d, od, "scales")
+    assert_exact(bs, obs, "sums")
 
 
 # ================================================================== a3 Q4_K decode
 @pytest.mark.parametrize("rows,K,seed", [(256, 1024, 0), (4096, 4096, 1), (37, 256, 5), (13, 768, 6),
                                          (70, 1280, 7), (9, 14336, 8)])
 def test_q4k_subblock_sums_bit_exact(q, rows, K, seed):
+    """qmatvec's own kernel, with its sums flag: int32 sub-block sums equal the
+    oracle's bit for bit, and its y equals qmatvec's bit for bit."""
     w = q4k(seed, rows, K)
     x = acts(seed, 1, K)
     xq = pack_on_device(q, x)
     S = poisoned_i32(rows, K // 32)
-    q.q8k_debug_subblock_sums(q.Q8K_Q4_K, to_dev(w), rows, K, xq, S)
-    oqs, _, _ = oracle.q8k_pack(x)
-    assert np.array_equal(host(S), oracle.subblock_sums(oracle.Q4_K, w, rows, K, oqs[0]))
+    y = poisoned_f32(rows)
+    q.q8k_debug_subblock_sums(q.Q8K_Q4_K, to_dev(w), rows, K, xq, y, S)
+    oqs, od, obs = oracle.q8k_pack(x)
+    assert_exact(host(S), oracle.subblock_sums(oracle.Q4_K, w, rows, K, oqs[0]), "S")
+    want, A = oracle.matvec(oracle.Q4_K, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(y), want[0], A[0], "y of the sums kernel")
+    y1 = poisoned_f32(rows)
+    q.qmatvec(q.Q8K_Q4_K, to_dev(w), rows, K, xq, y1)
+    assert np.array_equal(host(y1).view(np.uint32), host(y).view(np.uint32))
 
 
 @pytest.mark.parametrize("rows,K,seed", [(256, 1024, 0), (4096, 4096, 1), (37, 256, 5), (13, 768, 6),
@@ -147,9 +156,12 @@ def test_q5k_subblock_sums_bit_exact(q, rows, K, seed):
     x = acts(seed, 1, K)
     xq = pack_on_device(q, x)
     S = poisoned_i32(rows, K // 32)
-    q.q8k_debug_subblock_sums(q.Q8K_Q5_K, to_dev(w), rows, K, xq, S)
-    oqs, _, _ = oracle.q8k_pack(x)
-    assert np.array_equal(host(S), oracle.subblock_sums(oracle.Q5_K, w, rows, K, oqs[0]))
+    y = poisoned_f32(rows)
+    q.q8k_debug_subblock_sums(q.Q8K_Q5_K, to_dev(w), rows, K, xq, y, S)
+    oqs, od, obs = oracle.q8k_pack(x)
+    assert_exact(host(S), oracle.subblock_sums(oracle.Q5_K, w, rows, K, oqs[0]), "S")
+    want, A = oracle.matvec(oracle.Q5_K, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(y), want[0], A[0], "y of the sums kernel")
 
 
 @pytest.mark.parametrize("rows,K,seed", [(256, 1024, 50), (4096, 4096, 51), (37, 256, 52), (13, 768, 53),
@@ -216,19 +228,27 @@ def test_q6k_bind_bit_exact(q, rows, K):
     got = host(wr)
     prefix, bodies = oracle.q6k_relayout(w, nblk)
     pad = ((2 * nblk + 255) // 256) * 256
-    assert np.array_equal(got[: 2 * nblk].view(np.uint16), prefix)
-    assert np.array_equal(got[pad: pad + 208 * nblk], bodies)
+    assert_exact(got[: 2 * nblk].view(np.uint16), prefix, "prefix")
+    assert_exact(got[pad: pad + 208 * nblk], bodies, "bodies")
 
 
 @pytest.mark.parametrize("rows,K,seed", [(32000, 4096, 2), (37, 256, 11), (100, 1280, 12), (7, 14336, 13)])
 def test_q6k_subblock_sums_bit_exact(q, rows, K, seed):
+    """qmatvec's Q6_K kernel as it ships (4 lanes per block, the (h, lh) lane
+    map, the row walk), with its sums flag."""
     w, wr = q6k_bound(q, seed, rows, K)
     x = acts(seed, 1, K)
     xq = pack_on_device(q, x)
     S = poisoned_i32(rows, K // 16)
-    q.q8k_debug_subblock_sums(q.Q8K_Q6_K_RELAID, wr, rows, K, xq, S)
-    oqs, _, _ = oracle.q8k_pack(x)
-    assert np.array_equal(host(S), oracle.subblock_sums(oracle.Q6_K, w, rows, K, oqs[0]))
+    y = poisoned_f32(rows)
+    q.q8k_debug_subblock_sums(q.Q8K_Q6_K_RELAID, wr, rows, K, xq, y, S)
+    oqs, od, obs = oracle.q8k_pack(x)
+    assert_exact(host(S), oracle.subblock_sums(oracle.Q6_K, w, rows, K, oqs[0]), "S")
+    want, A = oracle.matvec(oracle.Q6_K, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(y), want[0], A[0], "y of the sums kernel")
+    y1 = poisoned_f32(rows)
+    q.qmatvec(q.Q8K_Q6_K_RELAID, wr, rows, K, xq, y1)
+    assert np.array_equal(host(y1).view(np.uint32), host(y).view(np.uint32))
 
 
 @pytest.mark.parametrize("rows,K,seed", [(32000, 4096, 2), (37, 256, 11), (100, 1280, 12), (7, 14336, 13)])
@@ -503,7 +523,7 @@ def test_prefill_moe_all_ids_out_of_range(q):
     ids = np.full((T, topk), 5, np.int32)
     ids[0, 0] = -1
     got, *_ = moe_prefill_case(q, E, rows, K, T, topk, 70, ids=ids)
-    assert np.array_equal(got, np.zeros((T, rows), np.float32))
+    assert_exact(got, np.zeros((T, rows), np.float32), "no pair selects an expert")
 
 
 def test_prefill_moe_rows_equal_decode_moe(q):
@@ -547,27 +567,111 @@ def test_prefill_full(q, fmt, M, rows, K, seed):
 
 
 @pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
-def test_prefill_down_projection_sampled(q, fmt):
-    """The 512-token x 4096-row x 14336 prefill: every output is finite and a
-    sample of whole token rows and whole weight-row columns matches the oracle."""
+def test_prefill_down_projection_full(q, fmt):
+    """The 512-token x 4096-row x 14336 prefill: all 2,097,152 outputs against
+    the oracle."""
     M, rows, K = 512, 4096, 14336
     w = _PF_FMT[fmt][2](np.random.default_rng(4), rows, K)
     x = acts(4, M, K)
     got = run_prefill(q, fmt, w, rows, K, x)
-    assert np.isfinite(got).all()
-    ot = _PF_FMT[fmt][1]
     oqs, od, obs = oracle.q8k_pack(x)
-    g = np.random.default_rng(123)
-    toks = np.sort(g.choice(M, 6, replace=False))
-    toks[0] = 0
-    toks[-1] = M - 1
-    want, A = oracle.matvec(ot, w, rows, K, oqs[toks], od[toks], obs[toks], nthreads=NTH)
-    assert_close(got[toks], want, A, f"prefill {fmt} token rows")
-    sel = np.sort(g.choice(rows, 24, replace=False))
-    sel[-1] = rows - 1
-    wsel = w.reshape(rows, -1)[sel].reshape(-1)
-    want, A = oracle.matvec(ot, wsel, len(sel), K, oqs, od, obs, nthreads=NTH)
-    assert_close(got[:, sel], want, A, f"prefill {fmt} weight columns")
+    want, A = oracle.matvec(_PF_FMT[fmt][1], w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(got, want, A, f"prefill {fmt} 512x4096x14336")
+
+
+# ================================================================== integer sums of the shipped tiles
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("M,rows,K,seed", [(130, 130, 768, 140), (200, 70, 1024, 141), (129, 65, 256, 142),
+                                           (1, 64, 512, 143)])
+def test_prefill_block_sums_bit_exact(q, fmt, M, rows, K, seed):
+    """qmatmul_prefill's own tile with its sums flag: every block's integer
+    sum I_b = sum_j sc_j S_j (the value the tile folds into y) equals the
+    oracle's bit for bit, and y equals qmatmul_prefill's bit for bit."""
+    w = _PF_FMT[fmt][2](np.random.default_rng(seed), rows, K)
+    x = acts(seed, M, K)
+    qt = getattr(q, _PF_FMT[fmt][0])
+    wd = pf_weights(q, fmt, w, rows, K)
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(M, rows)
+    I = poisoned_i32(M, rows, K // 256)
+    q.q8k_debug_prefill_block_sums(qt, wd, rows, K, xq, M, y, I)
+    oqs, od, obs = oracle.q8k_pack(x)
+    assert_exact(host(I), oracle.block_sums(_PF_FMT[fmt][1], w, rows, K, oqs), f"I {fmt}")
+    want, A = oracle.matvec(_PF_FMT[fmt][1], w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(y), want, A, f"y of the sums tile {fmt}")
+    y1 = poisoned_f32(M, rows)
+    q.qmatmul_prefill(qt, wd, rows, K, xq, M, y1, None, 0)
+    assert np.array_equal(host(y1).view(np.uint32), host(y).view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt,E,rows,K,T,topk,seed", [
+    ("q4k", 4, 100, 512, 5, 3, 150), ("q4k", 8, 300, 1024, 16, 2, 151), ("q4k", 2, 40, 256, 20, 2, 152),
+    ("q5k", 4, 100, 512, 5, 3, 153), ("q5k", 8, 300, 1024, 16, 2, 154),
+])
+def test_moe_subblock_sums_bit_exact(q, fmt, E, rows, K, T, topk, seed):
+    """qmatvec_moe's matrix-core kernel with its sums flag: each (token, slot)
+    pair's sub-block sums S_j against its expert equal the oracle's bit for
+    bit (more than 8 pairs per expert in the 20-token case: several groups);
+    an out-of-range id's entries stay unwritten."""
+    g = np.random.default_rng(seed)
+    gen, qt, ot = (synth.q4k_weights, q.Q8K_Q4_K, oracle.Q4_K) if fmt == "q4k" else \
+        (synth.q5k_weights, q.Q8K_Q5_K, oracle.Q5_K)
+    w = gen(g, E * rows, K)
+    x = synth.activations(g, T, K)
+    ids, rw = synth.moe_routing(g, T, E, topk)
+    ids = ids.astype(np.int32)
+    ids[1, topk - 1] = E + 3  # selects nothing
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(T, rows)
+    S = poisoned_i32(T * topk, rows, K // 32)
+    q.q8k_debug_moe_subblock_sums(qt, to_dev(w), E, rows, K, xq, T, to_dev(ids), to_dev(rw), topk, y, S)
+    got = host(S)
+    oqs, od, obs = oracle.q8k_pack(x)
+    per = w.size // E
+    want = np.full_like(got, -1)  # poisoned entries read as -1
+    for t in range(T):
+        for k in range(topk):
+            e = int(ids[t, k])
+            if 0 <= e < E:
+                want[t * topk + k] = oracle.subblock_sums(ot, w[e * per:(e + 1) * per], rows, K, oqs[t])
+    assert_exact(got, want, f"moe S {fmt}")
+    ok = ids < E
+    wy, A = oracle.moe(ot, w, E, rows, K, oqs, od, obs, np.where(ok, ids, 0), np.where(ok, rw, 0).astype(np.float32),
+                       nthreads=NTH)
+    assert_close(host(y), wy, A, f"moe y of the sums kernel {fmt}")
+
+
+# ================================================================== every column count of every route
+_STAGE_K = 1280    # every batched width 2..8 fits one workgroup's LDS: the staged kernel
+_GLOBAL_K = 65536  # no batched width 2..8 fits: the kernel reading packed columns from global memory
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("ncols", range(1, 9))
+@pytest.mark.parametrize("K", [_STAGE_K, _GLOBAL_K])
+def test_batched_every_width(q, fmt, ncols, K):
+    rows = 33
+    w, wd, qt, ot = fused_weights(q, fmt, 160 + ncols, rows, K)
+    x = acts(161 + ncols, ncols, K)
+    xq = pack_on_device(q, x)
+    y = poisoned_f32(ncols, rows)
+    q.qmatvec_batched(qt, wd, rows, K, xq, ncols, y)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(ot, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(y), want, A, f"batched {fmt} ncols={ncols} K={K}")
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("ncols", range(1, 9))
+def test_fused_every_width(q, fmt, ncols):
+    rows, K = 70, 1024
+    w, wd, qt, ot = fused_weights(q, fmt, 170 + ncols, rows, K)
+    x = acts(171 + ncols, ncols, K)
+    y = poisoned_f32(ncols, rows)
+    q.qmatvec_f32(qt, wd, rows, K, to_dev(x), ncols, y, None)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(ot, w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(y), want, A, f"fused {fmt} ncols={ncols}")
 
 
 def test_prefill_q5k_largest_fields(q):
