@@ -189,6 +189,22 @@ int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64
                         const int32_t* ids, const float* rw, int32_t topk, float* y, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* qmatmul_prefill_moe_noalloc: qmatmul_prefill_moe for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, refusals and result,
+ * without the workspace: the library's own scratch, a static device array of
+ * Q8K_NOALLOC_SCRATCH_BYTES (64 MiB) that each device the library runs on
+ * holds until the process ends, takes its place.  A call whose workspace
+ * (qmatmul_prefill_moe_workspace_bytes) would exceed it is refused with
+ * Q8K_ERR_WORKSPACE.  The call allocates nothing; its first call on a device
+ * asks the runtime for that device's scratch address.  Every call on one
+ * device shares the scratch (it keeps the last call's contents; nothing in it
+ * needs to start at zero): calls that overlap in time on one device race,
+ * stream-ordered calls do not. */
+#define Q8K_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int qmatmul_prefill_moe_noalloc(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq,
+                                int64_t T, const int32_t* ids, const float* rw, int32_t topk, float* y, void* stream);
+
 /* ---------------------------------------------------------- test support --
  * The exact integer sums of the path ("Language models on the device",
  * section 1: the integer dot product does the arithmetic, the sub-block

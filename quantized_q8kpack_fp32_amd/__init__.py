@@ -18,8 +18,8 @@ __all__ = [
     "Q8K_Q4_K", "Q8K_Q5_K", "Q8K_Q6_K_RELAID", "Q8K_Q6_K_GGUF", "Q8K_COLS_MAX", "Q8K_MOE_MAX_TOKENS", "Q8K_MOE_MAX_TOPK", "Q8KError",
     "lib", "LIB_PATH", "q8k_act_bytes", "q8k_act_layout", "q8k_weight_bytes", "q8k_pack", "q8k_bind_q6k",
     "qmatvec", "qmatvec_batched", "qmatvec_f32", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
-    "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe",
-    "q8k_debug_subblock_sums", "q8k_debug_prefill_block_sums", "q8k_debug_moe_subblock_sums",
+    "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe", "qmatmul_prefill_moe_noalloc",
+    "Q8K_NOALLOC_SCRATCH_BYTES", "q8k_debug_subblock_sums", "q8k_debug_prefill_block_sums", "q8k_debug_moe_subblock_sums",
     "q8k_debug_last_launches", "q8k_status_str", "q8k_last_error", "EXPORTED",
 ]
 
@@ -30,6 +30,7 @@ Q8K_Q5_K = 4
 Q8K_COLS_MAX = 8
 Q8K_MOE_MAX_TOKENS = 256
 Q8K_MOE_MAX_TOPK = 64
+Q8K_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq8k.so")
 
@@ -37,7 +38,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq8k.so")
 EXPORTED = (
     "q8k_act_bytes", "q8k_act_layout", "q8k_weight_bytes", "q8k_pack", "q8k_bind_q6k", "qmatvec",
     "qmatvec_batched", "qmatvec_f32", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
-    "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe",
+    "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe", "qmatmul_prefill_moe_noalloc",
     "q8k_debug_subblock_sums", "q8k_debug_prefill_block_sums", "q8k_debug_moe_subblock_sums",
     "q8k_debug_last_launches", "q8k_status_str", "q8k_last_error",
 )
@@ -87,6 +88,8 @@ lib.qmatmul_prefill_moe_workspace_bytes.restype = _SZ
 lib.qmatmul_prefill_moe_workspace_bytes.argtypes = [_INT, _I64, _I64, _I64, _I64, ctypes.c_int32]
 lib.qmatmul_prefill_moe.restype = _INT
 lib.qmatmul_prefill_moe.argtypes = [_INT, _P, _I64, _I64, _I64, _P, _I64, _P, _P, ctypes.c_int32, _P, _P, _SZ, _P]
+lib.qmatmul_prefill_moe_noalloc.restype = _INT
+lib.qmatmul_prefill_moe_noalloc.argtypes = [_INT, _P, _I64, _I64, _I64, _P, _I64, _P, _P, ctypes.c_int32, _P, _P]
 lib.q8k_debug_subblock_sums.restype = _INT
 lib.q8k_debug_subblock_sums.argtypes = [_INT, _P, _I64, _I64, _P, _P, _P, _P]
 lib.q8k_debug_prefill_block_sums.restype = _INT
@@ -200,6 +203,12 @@ def qmatmul_prefill_moe(qtype: int, w, E: int, rows: int, K: int, xq, T: int, id
                         ws_bytes: int = 0, stream=None) -> None:
     _check(lib.qmatmul_prefill_moe(qtype, _ptr(w), E, rows, K, _ptr(xq), T, _ptr(ids), _ptr(rw), topk, _ptr(y),
                                    _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def qmatmul_prefill_moe_noalloc(qtype: int, w, E: int, rows: int, K: int, xq, T: int, ids, rw, topk: int, y,
+                                stream=None) -> None:
+    _check(lib.qmatmul_prefill_moe_noalloc(qtype, _ptr(w), E, rows, K, _ptr(xq), T, _ptr(ids), _ptr(rw), topk,
+                                           _ptr(y), _stream(stream)))
 
 
 def q8k_debug_subblock_sums(qtype: int, w, rows: int, K: int, xq, y, S, stream=None) -> None:

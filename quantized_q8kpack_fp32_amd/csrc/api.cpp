@@ -337,11 +337,29 @@ size_t qmatmul_prefill_moe_workspace_bytes(int qtype, int64_t E, int64_t rows, i
     return (size_t)moe_prefill_ws(E, rows, T, topk).total;
 }
 
+static int prefill_moe_common(const char* fn, int qtype, const void* w, int64_t E, int64_t rows, int64_t K,
+                              const void* xq, int64_t T, const int32_t* ids, const float* rw, int32_t topk, float* y,
+                              void* ws, size_t ws_bytes, bool noalloc, void* stream);
+
 int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq, int64_t T,
                         const int32_t* ids, const float* rw, int32_t topk, float* y, void* ws, size_t ws_bytes,
                         void* stream) {
     begin_call();
-    const char* fn = "qmatmul_prefill_moe";
+    return prefill_moe_common("qmatmul_prefill_moe", qtype, w, E, rows, K, xq, T, ids, rw, topk, y, ws, ws_bytes,
+                              false, stream);
+}
+
+int qmatmul_prefill_moe_noalloc(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq,
+                                int64_t T, const int32_t* ids, const float* rw, int32_t topk, float* y,
+                                void* stream) {
+    begin_call();
+    return prefill_moe_common("qmatmul_prefill_moe_noalloc", qtype, w, E, rows, K, xq, T, ids, rw, topk, y, nullptr,
+                              0, true, stream);
+}
+
+static int prefill_moe_common(const char* fn, int qtype, const void* w, int64_t E, int64_t rows, int64_t K,
+                              const void* xq, int64_t T, const int32_t* ids, const float* rw, int32_t topk, float* y,
+                              void* ws, size_t ws_bytes, bool noalloc, void* stream) {
     Q8K_TRY(check_k(fn, K));
     Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
     if (E < 1 || E > MAX_EXPERTS)
@@ -361,12 +379,25 @@ int qmatmul_prefill_moe(int qtype, const void* w, int64_t E, int64_t rows, int64
     Q8K_TRY(check_ptr(fn, "rw", rw, 4));
     Q8K_TRY(check_ptr(fn, "y", y, 4));
     const size_t need = qmatmul_prefill_moe_workspace_bytes(qtype, E, rows, K, T, topk);
-    if (ws_bytes < need)
-        return fail(Q8K_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
-    if (need > 0) Q8K_TRY(check_ptr(fn, "ws", ws, 16));
+    if (noalloc) {
+        if (need > NOALLOC_SCRATCH_BYTES)
+            return fail(Q8K_ERR_WORKSPACE,
+                        "%s: the call needs %zu bytes of workspace, more than the library's %zu-byte scratch "
+                        "(use qmatmul_prefill_moe with a caller workspace)",
+                        fn, need, NOALLOC_SCRATCH_BYTES);
+    } else {
+        if (ws_bytes < need)
+            return fail(Q8K_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+        if (need > 0) Q8K_TRY(check_ptr(fn, "ws", ws, 16));
+    }
     Q8K_TRY(check_grid(fn, moe_prefill_ws(E, rows, T, topk).max_chunks * ((rows + 63) / 64)));
     Q8K_TRY(check_grid(fn, T * ((rows + 255) / 256)));  // the combine's workgroups, at most
     if (rows == 0 || T == 0) return Q8K_OK;
+    if (noalloc) {
+        const hipError_t e = noalloc_scratch(&ws);
+        if (e != hipSuccess)
+            return fail(Q8K_ERR_LAUNCH, "%s: the library's scratch is not available: %s", fn, hipGetErrorString(e));
+    }
     const int nb = (int)(K / QK);
     const PrefillWeights pw = prefill_weights(qtype, w, E * rows * nb);
     return launched(fn, launch_prefill_moe(pw.fmt, pw.w, pw.prefix, E, rows, nb, acts_of(xq, T, K), T, ids, rw, topk,

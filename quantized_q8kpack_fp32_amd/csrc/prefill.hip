@@ -50,6 +50,8 @@
 #include "q8k_device.h"
 #include "q8k_launch.h"
 
+#include <mutex>
+
 namespace q8k {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -744,6 +746,36 @@ hipError_t launch_prefill_moe(int fmt, const uint8_t* w, const uint16_t* prefix,
         Q8K_LAUNCH(moe_combine_kernel<1>, dim3((unsigned)(T * ((rows + 255) / 256))), dim3(256), 0, s, out, rows, T,
                    ids, rw, topk, E, y);
     return hipGetLastError();
+}
+
+// ------------------------------------------------- allocation-free form ----
+// The MoE prefill's workspace for callers that cannot allocate: a file-scope
+// device array, one copy per device, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: its device
+// address is asked of the runtime once per device (with that device current)
+// and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 // Q4_K runs the register-plane tile (prefill_regw.hip); Q5_K and relaid Q6_K

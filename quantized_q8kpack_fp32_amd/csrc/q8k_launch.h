@@ -100,6 +100,11 @@ inline MoePrefillWs moe_prefill_ws(int64_t E, int64_t rows, int64_t T, int64_t t
     L.total = (L.P == 0 || rows == 0) ? 0 : align256(L.order + 4 * L.P);  // nothing is enqueued then
     return L;
 }
+// Allocation-free MoE prefill: the device address of the library's own
+// scratch array (NOALLOC_SCRATCH_BYTES on every device), found on the first
+// call per device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_prefill_moe(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t E, int64_t rows, int nb,
                               Acts a, int64_t T, const int32_t* ids, const float* rw, int topk, float* y, void* ws,
                               hipStream_t s);
