@@ -164,7 +164,12 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
  * refused with Q8K_ERR_QTYPE: bind it first).  xq: q8_K buffer of M tokens.
  * y: fp32 [M][rows].
  * ws / ws_bytes: caller-owned workspace of at least
- * qmatmul_prefill_workspace_bytes(...) bytes (may be NULL when that is 0). */
+ * qmatmul_prefill_workspace_bytes(...) bytes, 16-byte aligned (may be NULL
+ * when that is 0).  It is non-zero when the problem's 128-token x 64-row tiles
+ * are fewer than the 256 compute units of the device: the reduction is then
+ * split across S <= 8 workgroups (at least 8 blocks of K each; split-K and its
+ * fixup, "Language models on the device", section 2.3) and the workspace holds
+ * their fp32 partials, S * M * rows * 4 bytes, added in a fixed order. */
 size_t qmatmul_prefill_workspace_bytes(int qtype, int64_t rows, int64_t K, int64_t M);
 int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int64_t M, float* y, void* ws,
                     size_t ws_bytes, void* stream);

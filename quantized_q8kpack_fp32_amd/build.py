@@ -108,5 +108,24 @@ def build(verbose: bool = False, out: str = OUT, build_dir: str = BUILD_DIR, def
     return out
 
 
+CALIB_SRC = "calib.hip"
+CALIB_OUT = os.path.join(HERE, "libq8k_calib.so")
+
+
+def build_calib(out: str = CALIB_OUT, build_dir: str = BUILD_DIR) -> str:
+    """The benchmark's streaming-read calibration kernel, a library of its own
+    (csrc/calib.hip; not part of libq8k)."""
+    os.makedirs(build_dir, exist_ok=True)
+    obj, _ = _compile(CALIB_SRC, build_dir)
+    tmp = out + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, obj], capture_output=True,
+                       text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_calib())

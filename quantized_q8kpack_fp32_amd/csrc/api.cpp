@@ -302,10 +302,9 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
 
 size_t qmatmul_prefill_workspace_bytes(int qtype, int64_t rows, int64_t K, int64_t M) {
     (void)qtype;
-    (void)rows;
-    (void)K;
-    (void)M;
-    return 0;
+    if (rows <= 0 || M <= 0 || K <= 0 || K % QK != 0) return 0;
+    const int ks = prefill_ksplit(rows, K / QK, M);
+    return ks > 1 ? (size_t)ks * (size_t)M * (size_t)rows * 4 : 0;
 }
 
 int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int64_t M, float* y, void* ws,
@@ -327,7 +326,7 @@ int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const voi
     const int nb = (int)(K / QK);
     const PrefillWeights pw = prefill_weights(qtype, w, rows * nb);
     return launched(fn, launch_prefill(pw.fmt, pw.w, pw.prefix, rows, nb, acts_of(xq, M, K), M, y,
-                                       (hipStream_t)stream));
+                                       static_cast<float*>(ws), (hipStream_t)stream));
 }
 
 size_t qmatmul_prefill_moe_workspace_bytes(int qtype, int64_t E, int64_t rows, int64_t K, int64_t T, int32_t topk) {

@@ -49,9 +49,9 @@ __device__ __forceinline__ void q4k_load(Q4Chunk<NC, Q5>& L, const uint8_t* __re
                                          int boff, const int8_t* __restrict__ qs, const float* __restrict__ d8,
                                          const int16_t* __restrict__ bs, int64_t K, int nb) {
     const uint8_t* blk = wr + (int64_t)b * kblock<Q5>();
-    L.hdr = *reinterpret_cast<const uint4*>(blk);
-    L.qv = *reinterpret_cast<const uint4*>(blk + (Q5 ? 48 : 16) + 16 * ci);
-    if (Q5) L.qh = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (ci & 1));
+    L.hdr = wload16<!Q5>(blk);
+    L.qv = wload16<!Q5>(blk + (Q5 ? 48 : 16) + 16 * ci);
+    if (Q5) L.qh = wload16<false>(blk + 16 + 16 * (ci & 1));
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
         const int8_t* a = qs + t * K + (int64_t)b * QK + aoff;
@@ -230,9 +230,9 @@ struct Q4Weights {
 template <bool Q5>
 __device__ __forceinline__ void q4k_load_w(Q4Weights<Q5>& W, const uint8_t* __restrict__ wr, int b, int ci) {
     const uint8_t* blk = wr + (int64_t)b * kblock<Q5>();
-    W.hdr = *reinterpret_cast<const uint4*>(blk);
-    W.qv = *reinterpret_cast<const uint4*>(blk + (Q5 ? 48 : 16) + 16 * ci);
-    if (Q5) W.qh = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (ci & 1));
+    W.hdr = wload16<!Q5>(blk);
+    W.qv = wload16<!Q5>(blk + (Q5 ? 48 : 16) + 16 * ci);
+    if (Q5) W.qh = wload16<false>(blk + 16 + 16 * (ci & 1));
 }
 
 // The rows of one wave from activations in LDS (codes sqs [NC][K], sums sbs

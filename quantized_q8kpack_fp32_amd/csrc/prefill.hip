@@ -215,6 +215,25 @@ __device__ __forceinline__ void producer_src(PrefillSrc& S, const uint8_t* __res
     S.d8o = (p >> 1) * nb * 4;
 }
 
+// Split-K: the sources start at block kb0 of every row and token (the strides
+// between rows and tokens are unchanged), so the tile's block loop covers
+// blocks kb0 .. of the problem.
+template <int F>
+__device__ __forceinline__ void producer_src_from_block(PrefillSrc& S, int kb0) {
+    S.w += (int64_t)kb0 * kblock<F>();
+    S.wbytes -= (int64_t)kb0 * kblock<F>();
+    if constexpr (F == PF_Q6) {
+        S.pf += kb0;
+        S.pfbytes -= (int64_t)kb0 * 2;
+    }
+    S.x += (int64_t)kb0 * QK;
+    S.xbytes -= (int64_t)kb0 * QK;
+    S.bs += (int64_t)kb0 * 8;
+    S.bsbytes -= (int64_t)kb0 * 16;
+    S.d8 += kb0;
+    S.d8bytes -= (int64_t)kb0 * 4;
+}
+
 // Mixture-of-experts form: the tile's 128 token rows are the tokens tok[0..127]
 // (gathered from anywhere in the q8_K buffer of T tokens; tok < 0 marks an
 // empty row).  An empty row's offsets point past every record, so its reads
@@ -563,24 +582,59 @@ __device__ __forceinline__ void prefill_tile(PrefillSmem<F>& sm, const PrefillSr
 }
 
 // SUMS (test support): the same kernel also stores every block's exact
-// integer sum I_b to Isum [M][rows][nb].
+// integer sum I_b to Isum [M][rows][nb].  Split-K (ksplit > 1, "Language
+// models on the device", section 2.3): workgroup split ks multiplies blocks
+// [kb0, kb0 + nbk) and stores its partial [M][rows] at y + ks * M * rows, for
+// prefill_fixup_kernel to add.
 template <int F, bool SUMS = false>
 __global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restrict__ w,
                                                           const uint16_t* __restrict__ prefix, int64_t rows, int nb,
                                                           const int8_t* __restrict__ qs, const float* __restrict__ d8,
                                                           const int16_t* __restrict__ bs, int64_t K, int64_t M,
-                                                          float* __restrict__ y, int32_t* __restrict__ Isum) {
+                                                          float* __restrict__ y, int32_t* __restrict__ Isum,
+                                                          int ksplit) {
     __shared__ __attribute__((aligned(16))) PrefillSmem<F> sm;
     const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
-    const int64_t n0 = ((int64_t)blockIdx.x % ntn) * PF_TN;
-    const int64_t m0 = ((int64_t)blockIdx.x / ntn) * PF_TM;
+    const int64_t ntm = (M + PF_TM - 1) / PF_TM;
+    const int64_t tile = (int64_t)blockIdx.x % (ntn * ntm);
+    const int64_t n0 = (tile % ntn) * PF_TN;
+    const int64_t m0 = (tile / ntn) * PF_TM;
+    const int ks = (int)((int64_t)blockIdx.x / (ntn * ntm));
+    const int per = (nb + ksplit - 1) / ksplit;
+    const int kb0 = ks * per;
+    const int nbk = nb - kb0 < per ? nb - kb0 : per;
+    y += (int64_t)ks * M * rows;
     PrefillSrc S;
-    if (threadIdx.x >= 256)
+    if (threadIdx.x >= 256) {
         producer_src<F>(S, w, prefix, rows, nb, qs, d8, bs, K, M, n0, m0, (int)threadIdx.x - 256);
+        producer_src_from_block<F>(S, kb0);
+    }
     PfSums D{};
     if constexpr (SUMS) D = PfSums{Isum + (m0 * rows + n0) * nb, rows, M - m0, rows - n0, nb};
     prefill_tile<F, SUMS>(
-        sm, S, nb, rows, n0, y, [&](int m) { return m0 + m; }, [&](int m) { return m0 + m < M; }, D);
+        sm, S, nbk, rows, n0, y, [&](int m) { return m0 + m; }, [&](int m) { return m0 + m < M; }, D);
+}
+
+// y[i] = sum over the ksplit partials part[s][i], s ascending (a fixed order:
+// the result does not depend on scheduling).  V = 4: 16-byte accesses.
+template <int V>
+__global__ __launch_bounds__(256) void prefill_fixup_kernel(const float* __restrict__ part, int ksplit, int64_t n,
+                                                            float* __restrict__ y) {
+    typedef float fv __attribute__((ext_vector_type(V)));
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
+    if (i >= n) return;
+    fv acc = *reinterpret_cast<const fv*>(part + i);
+    for (int s = 1; s < ksplit; ++s) acc += *reinterpret_cast<const fv*>(part + (int64_t)s * n + i);
+    *reinterpret_cast<fv*>(y + i) = acc;
+}
+
+hipError_t launch_prefill_fixup(const float* part, int ksplit, int64_t n, float* y, hipStream_t s) {
+    if (n % 4 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0)
+        Q8K_LAUNCH(prefill_fixup_kernel<4>, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, part, ksplit, n,
+                   y);
+    else
+        Q8K_LAUNCH(prefill_fixup_kernel<1>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, ksplit, n, y);
+    return hipGetLastError();
 }
 
 // ----------------------------------------------------- mixture of experts ----
@@ -781,15 +835,18 @@ hipError_t noalloc_scratch(void** ptr) {
 // Q4_K runs the register-plane tile (prefill_regw.hip); Q5_K and relaid Q6_K
 // the producer/consumer tile above.
 hipError_t launch_prefill(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a,
-                          int64_t M, float* y, hipStream_t s) {
-    if (fmt == PF_Q4) return launch_prefill_regw_q4k(w, rows, nb, a, M, y, s);
-    const dim3 grid((unsigned)(((rows + PF_TN - 1) / PF_TN) * ((M + PF_TM - 1) / PF_TM)));
+                          int64_t M, float* y, float* part, hipStream_t s) {
+    const int ksplit = prefill_ksplit(rows, nb, M);
+    if (fmt == PF_Q4) return launch_prefill_regw_q4k(w, rows, nb, a, M, y, ksplit, part, s);
+    const dim3 grid((unsigned)(((rows + PF_TN - 1) / PF_TN) * ((M + PF_TM - 1) / PF_TM) * ksplit));
+    float* out = ksplit > 1 ? part : y;
     if (fmt == PF_Q6)
-        Q8K_LAUNCH(prefill_q4k_kernel<PF_Q6>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K, M, y,
-                   nullptr);
+        Q8K_LAUNCH(prefill_q4k_kernel<PF_Q6>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K, M, out,
+                   nullptr, ksplit);
     else
-        Q8K_LAUNCH(prefill_q4k_kernel<PF_Q5>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K, M, y,
-                   nullptr);
+        Q8K_LAUNCH(prefill_q4k_kernel<PF_Q5>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K, M, out,
+                   nullptr, ksplit);
+    if (ksplit > 1) return launch_prefill_fixup(part, ksplit, M * rows, y, s);
     return hipGetLastError();
 }
 
@@ -799,10 +856,10 @@ hipError_t launch_prefill_sums(int fmt, const uint8_t* w, const uint16_t* prefix
     const dim3 grid((unsigned)(((rows + PF_TN - 1) / PF_TN) * ((M + PF_TM - 1) / PF_TM)));
     if (fmt == PF_Q6)
         Q8K_LAUNCH((prefill_q4k_kernel<PF_Q6, true>), grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K,
-                   M, y, I);
+                   M, y, I, 1);
     else
         Q8K_LAUNCH((prefill_q4k_kernel<PF_Q5, true>), grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K,
-                   M, y, I);
+                   M, y, I, 1);
     return hipGetLastError();
 }
 

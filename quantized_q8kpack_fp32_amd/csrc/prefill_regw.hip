@@ -342,6 +342,12 @@ constexpr int RW_RAW_LOADS = 5;  // load_weights() issues five loads
 // in order, count}); the result of pair p goes to row p of y ([P][rows]);
 // workgroups past the chunk count return at once.
 //
+// Split-K (dense tiles, "Language models on the device", section 2.3: when a
+// problem is too small to fill the device, workgroups are added along the
+// reduction and a fixup sums the partials): with ksplit > 1, workgroup split
+// ks multiplies blocks [kb0, kb0 + nbk) of every row and stores its partial
+// [M][rows] at y + ks * M * rows; prefill_fixup_kernel adds the splits.
+//
 // SUMS (test support, dense tiles): the same kernel also stores every block's
 // exact integer sum I_b = 8 P_hi + P_lo to Isum [M][rows][nb].
 template <bool GATHER, bool SUMS = false>
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     const uint8_t* __restrict__ w, int64_t rows, int nb, const int8_t* __restrict__ qs,
     const float* __restrict__ d8, const int16_t* __restrict__ bs, int64_t K, int64_t M, float* __restrict__ y,
     const int32_t* __restrict__ nchunks, const int4* __restrict__ chunks, const int32_t* __restrict__ order,
-    int topk, int32_t* __restrict__ Isum) {
+    int topk, int32_t* __restrict__ Isum, int ksplit) {
     static_assert(!(SUMS && GATHER), "block sums of the dense tile");
     __shared__ __attribute__((aligned(16))) RwCopied sm;
     __shared__ __attribute__((aligned(16))) RwBuilt sb;
@@ -361,8 +367,17 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     // cover every token tile and a set of row tiles, so each weight row is
     // fetched into one L2 (measured: fewer L2 misses and faster than giving
     // each XCD one token tile).
+    // (gathered tiles: workgroup = (chunk, row tile), no split)
     const int64_t ntn = (rows + RW_TN - 1) / RW_TN;
-    const int64_t n0 = ((int64_t)blockIdx.x % ntn) * RW_TN, m0 = ((int64_t)blockIdx.x / ntn) * RW_TM;
+    const int64_t ntm = GATHER ? 1 : (M + RW_TM - 1) / RW_TM;
+    const int64_t tile = GATHER ? (int64_t)blockIdx.x : (int64_t)blockIdx.x % (ntn * ntm);
+    const int64_t n0 = (tile % ntn) * RW_TN, m0 = (tile / ntn) * RW_TM;
+    // this workgroup's blocks [kb0, kb0 + nbk) (all of them without split-K)
+    const int ks = GATHER ? 0 : (int)((int64_t)blockIdx.x / (ntn * ntm));
+    const int per = (nb + ksplit - 1) / ksplit;
+    const int kb0 = ks * per;
+    const int nbk = nb - kb0 < per ? nb - kb0 : per;
+    if constexpr (!GATHER) y += (int64_t)ks * M * rows;
 
     RwSrc S;
     S.nb = nb;
@@ -390,20 +405,22 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         S.bsbytes = span32(M * nb * 16);
         __syncthreads();
     } else {
+        // sources start at block kb0 of the tile's first token / row; the
+        // strides between tokens and rows stay those of whole rows
         live = M - m0;
-        S.w = w + n0 * S.wrow;
-        S.x = qs + m0 * K;
-        S.xbytes = span32((M - m0) * K);
-        S.d8 = d8 + m0 * nb;
-        S.d8bytes = span32((M - m0) * nb * 4);
-        S.bs = bs + m0 * nb * 8;
-        S.bsbytes = span32((M - m0) * nb * 16);
+        S.w = w + n0 * S.wrow + kb0 * Q4K_BLOCK;
+        S.x = qs + m0 * K + (int64_t)kb0 * QK;
+        S.xbytes = span32((M - m0) * K - (int64_t)kb0 * QK);
+        S.d8 = d8 + m0 * nb + kb0;
+        S.d8bytes = span32(((M - m0) * nb - kb0) * 4);
+        S.bs = bs + (m0 * nb + kb0) * 8;
+        S.bsbytes = span32(((M - m0) * nb - kb0) * 16);
     }
-    S.wbytes = span32((rows - n0) * S.wrow);
+    S.wbytes = span32((rows - n0) * S.wrow - (GATHER ? 0 : (int64_t)kb0 * Q4K_BLOCK));
     RwSums D{};
     if constexpr (SUMS) D = RwSums{Isum + (m0 * rows + n0) * nb, rows, live, rows - n0, nb};
 
-    const int steps = (nb + RW_KQ - 1) / RW_KQ;
+    const int steps = (nbk + RW_KQ - 1) / RW_KQ;
     const int nst = 2 * steps;                        // stages
     const bool half2 = live > RW_SM;                  // the tile's second 64 tokens exist
     v16f acc[4];
@@ -436,13 +453,13 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         if (sg + 2 < nst) issue_aux<GATHER>(sm, S, sg + 2, wv, lane);
         build_q4k_planes(PL, R, lane);
         load_weights(R, S, b + RW_KQ, rg, lane);
-        if (b < nb) wave_stage<SUMS>(sm, sb, PL, sg, q, lane, acc, D, rg);
+        if (b < nbk) wave_stage<SUMS>(sm, sb, PL, sg, q, lane, acc, D, rg);
         build_amin(sm, sb, sg + 1, tid);
         stage_barrier<RW_RAW_LOADS>();
         // ---- second 64 tokens
         if (sg + 2 < nst) issue_codes<GATHER>(sm, S, sg + 2, wv, lane);
         if (sg + 3 < nst) issue_aux<GATHER>(sm, S, sg + 3, wv, lane);
-        if (b < nb && half2) wave_stage<SUMS>(sm, sb, PL, sg + 1, q, lane, acc, D, rg);
+        if (b < nbk && half2) wave_stage<SUMS>(sm, sb, PL, sg + 1, q, lane, acc, D, rg);
         if (sg + 2 < nst) build_amin(sm, sb, sg + 2, tid);
         stage_barrier<0>();
     }
@@ -482,10 +499,11 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
 }  // namespace
 
 hipError_t launch_prefill_regw_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
-                                   hipStream_t s) {
-    const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * ((M + RW_TM - 1) / RW_TM)));
-    Q8K_LAUNCH((prefill_regw_q4k_kernel<false>), grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K, M, y,
-               nullptr, nullptr, nullptr, 1, nullptr);
+                                   int ksplit, float* part, hipStream_t s) {
+    const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * ((M + RW_TM - 1) / RW_TM) * ksplit));
+    Q8K_LAUNCH((prefill_regw_q4k_kernel<false>), grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K, M,
+               ksplit > 1 ? part : y, nullptr, nullptr, nullptr, 1, nullptr, ksplit);
+    if (ksplit > 1) return launch_prefill_fixup(part, ksplit, M * rows, y, s);
     return hipGetLastError();
 }
 
@@ -493,7 +511,7 @@ hipError_t launch_prefill_regw_q4k_sums(const uint8_t* w, int64_t rows, int nb, 
                                         int32_t* I, hipStream_t s) {
     const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * ((M + RW_TM - 1) / RW_TM)));
     Q8K_LAUNCH((prefill_regw_q4k_kernel<false, true>), grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K,
-               M, y, nullptr, nullptr, nullptr, 1, I);
+               M, y, nullptr, nullptr, nullptr, 1, I, 1);
     return hipGetLastError();
 }
 
@@ -502,7 +520,7 @@ hipError_t launch_prefill_regw_moe_q4k(const uint8_t* w, int64_t rows, int nb, A
                                        float* out, hipStream_t s) {
     const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * max_chunks));
     Q8K_LAUNCH((prefill_regw_q4k_kernel<true>), grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K, T,
-               out, nchunks, chunks, order, topk, nullptr);
+               out, nchunks, chunks, order, topk, nullptr, 1);
     return hipGetLastError();
 }
 

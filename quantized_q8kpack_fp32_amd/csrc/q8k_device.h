@@ -51,6 +51,22 @@ __device__ __forceinline__ uint2 load8(rsrc_t r, int off) {
 __device__ __forceinline__ uint32_t load4(rsrc_t r, int off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
 __device__ __forceinline__ uint32_t load2(rsrc_t r, int off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
 
+// A 16-byte weight load, non-temporal when NT (the weights of the Q4_K decode
+// mat-vec, read once per launch: a plain streaming read is fastest with the
+// hint on gfx950, and the Q4_K mat-vec measured 6% faster with it; Q5_K,
+// Q6_K and the MoE decode measured slower, because some of their 128-byte
+// lines are touched by more than one load and the hint evicts them between).
+typedef unsigned int v4u_nt __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint4 wload16(const void* p) {
+    if constexpr (NT) {
+        const v4u_nt v = __builtin_nontemporal_load(static_cast<const v4u_nt*>(p));
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    } else {
+        return *static_cast<const uint4*>(p);
+    }
+}
+
 // int8x4 . int8x4 + acc, signed (v_dot4_i32_i8).
 __device__ __forceinline__ int sdot4(int a, int b, int acc) { return __builtin_amdgcn_sdot4(a, b, acc, false); }
 

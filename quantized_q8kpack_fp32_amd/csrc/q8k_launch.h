@@ -64,12 +64,30 @@ hipError_t launch_moe_q5k(const uint8_t* w, int64_t E, int64_t rows, int nb, Act
                           const float* rw, int topk, float* y, hipStream_t s);
 hipError_t launch_moe_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t E, int64_t rows, int nb, Acts a,
                           int64_t T, const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s);
+// Split-K of the prefill ("Language models on the device", section 2.3): a
+// problem whose 128-token x 64-row tiles number fewer than the device's 256
+// compute units gets ksplit workgroups along the reduction, each with at least
+// PREFILL_SPLIT_MIN_BLOCKS blocks of K; their fp32 partials [ksplit][M][rows]
+// live in the caller's workspace and a fixup kernel adds them in split order.
+constexpr int PREFILL_TARGET_WGS = 256;
+constexpr int PREFILL_SPLIT_MAX = 8;
+constexpr int PREFILL_SPLIT_MIN_BLOCKS = 8;
+inline int prefill_ksplit(int64_t rows, int64_t nb, int64_t M) {
+    const int64_t tiles = ((rows + 63) / 64) * ((M + 127) / 128);
+    if (tiles <= 0 || tiles >= PREFILL_TARGET_WGS) return 1;
+    int64_t k = (PREFILL_TARGET_WGS + tiles - 1) / tiles;
+    if (k > PREFILL_SPLIT_MAX) k = PREFILL_SPLIT_MAX;
+    if (k > nb / PREFILL_SPLIT_MIN_BLOCKS) k = nb / PREFILL_SPLIT_MIN_BLOCKS;
+    return k < 1 ? 1 : (int)k;
+}
+// part: the workspace (ksplit * M * rows fp32) when prefill_ksplit(...) > 1.
 hipError_t launch_prefill(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a, int64_t M,
-                          float* y, hipStream_t s);
+                          float* y, float* part, hipStream_t s);
+hipError_t launch_prefill_fixup(const float* part, int ksplit, int64_t n, float* y, hipStream_t s);
 // Q4_K prefill with the weight planes built in the registers of the waves that
 // multiply them (prefill_regw.hip).
-hipError_t launch_prefill_regw_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
-                                   hipStream_t s);
+hipError_t launch_prefill_regw_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y, int ksplit,
+                                   float* part, hipStream_t s);
 // The same tile over the chunks of a mixture-of-experts prefill (T tokens;
 // chunk table and pair order as in the workspace below; out: [P][rows]).
 hipError_t launch_prefill_regw_moe_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t T, int64_t max_chunks,

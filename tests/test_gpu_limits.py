@@ -102,7 +102,8 @@ def test_prefill_largest_k_full_tile(q, fmt):
     q.q8k_pack(x, M, K, xq)
     del x
     y = poisoned_f32(M, rows)
-    q.qmatmul_prefill(qt, wd, rows, K, xq, M, y, None, 0)
+    wsb = q.qmatmul_prefill_workspace_bytes(qt, rows, K, M)
+    q.qmatmul_prefill(qt, wd, rows, K, xq, M, y, poisoned(wsb) if wsb else None, wsb)
     got = host(y)
     for t, xt in xr.items():
         oqs, od, obs = oracle.q8k_pack(xt)
@@ -132,7 +133,8 @@ def test_prefill_largest_k_last_code_bytes(q, fmt):
     q.q8k_pack(x, M, K, xq)
     del x
     y = poisoned_f32(M, rows)
-    q.qmatmul_prefill(qt, wd, rows, K, xq, M, y, None, 0)
+    wsb = q.qmatmul_prefill_workspace_bytes(qt, rows, K, M)
+    q.qmatmul_prefill(qt, wd, rows, K, xq, M, y, poisoned(wsb) if wsb else None, wsb)
     got = host(y)
     oqs, od, obs = oracle.q8k_pack(tail)
     want, A = oracle.matvec(ot, w, rows, K, oqs, od, obs)

@@ -674,6 +674,33 @@ def test_fused_every_width(q, fmt, ncols):
     assert_close(host(y), want, A, f"fused {fmt} ncols={ncols}")
 
 
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("M,rows,K,splits", [(32, 4096, 14336, 4), (128, 4096, 14336, 4), (77, 130, 4096, 2),
+                                             (5, 64, 14336, 7), (1, 70, 4096, 2)])
+def test_prefill_split_k(q, fmt, M, rows, K, splits):
+    """Problems whose tiles do not fill the device split K across workgroups;
+    the fixup adds the partials in split order.  All outputs against the
+    oracle (ragged M and rows; 2, 4 and 7 splits)."""
+    w = _PF_FMT[fmt][2](np.random.default_rng(180 + M), rows, K)
+    x = acts(181 + M, M, K)
+    qt = getattr(q, _PF_FMT[fmt][0])
+    wsb = q.qmatmul_prefill_workspace_bytes(qt, rows, K, M)
+    assert wsb == splits * M * rows * 4, (wsb, splits)
+    got = run_prefill(q, fmt, w, rows, K, x)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(_PF_FMT[fmt][1], w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(got, want, A, f"split-K prefill {fmt} M={M} N={rows} K={K}")
+
+
+def test_prefill_split_k_refuses_short_workspace(q):
+    rows, K, M = 4096, 14336, 32
+    wsb = q.qmatmul_prefill_workspace_bytes(q.Q8K_Q4_K, rows, K, M)
+    assert wsb > 0
+    with pytest.raises(q.Q8KError) as ei:
+        q.qmatmul_prefill(q.Q8K_Q4_K, 1 << 20, rows, K, 1 << 20, M, 1 << 20, 1 << 20, wsb - 4)
+    assert ei.value.name == "Q8K_ERR_WORKSPACE"
+
+
 def test_prefill_q5k_largest_fields(q):
     """Q5_K blocks at the top of every field (scales and mins 63, quants 31)
     against tokens at +-127: the per-block integer sums reach their largest
