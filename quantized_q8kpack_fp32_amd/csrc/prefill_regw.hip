@@ -106,35 +106,33 @@ __device__ __forceinline__ void dma4(rsrc_t r, void* lds_base, int off) {
 
 // Sources of one workgroup: tokens m0.., rows n0...  Offsets stay 32-bit: a
 // tile's rows span at most 64 * (K / 256) * 144 bytes, its tokens 128 * K <=
-// 2^31 bytes.  The byte counts from the tile's start to the end of each
-// buffer are unsigned 32-bit (the largest token span, 2^31, included; the
-// resource's record count is an unsigned 32-bit field), so every resource
-// range below is the count left after the copy's own start offset: one
-// scalar compare and subtraction.
+// 2^31 bytes.  Each buffer's extent from the tile's start is kept as the
+// index of its last byte (int32: a span of 2^31 bytes has last byte 2^31 - 1;
+// an empty span -1), so every resource range below is the count left after
+// the copy's own start offset, with one scalar signed compare.
 struct RwSrc {
     const uint8_t* w;
     const int8_t* x;
     const float* d8;
     const int16_t* bs;
-    uint32_t wbytes, xbytes, d8bytes, bsbytes;
+    int wlast, xlast, d8last, bslast;  // index of the last byte of each source (-1: empty)
     int wrow;  // bytes per weight row
     int nb;
     int K;
     const int* tokoff;  // gathered tiles: LDS offsets of the tile's token rows
 };
-// Byte span as an unsigned 32-bit count (0 if negative, 2^32 - 1 at most).
-__device__ __forceinline__ uint32_t span32(int64_t v) {
-    return v <= 0 ? 0u : v < 0xffffffffLL ? (uint32_t)v : 0xffffffffu;
-}
-// Raw buffer resource over [base + off, base + total): the records left after
-// the start offset `off` (none when off >= total).  The difference is taken in
-// signed 64 bits: an unsigned compare-and-subtract becomes a saturating
-// subtract, which only the vector unit has, and the descriptor must stay in
-// scalar registers for the copies' inline assembly.
-__device__ __forceinline__ rsrc_t rsrc32(const void* base, uint32_t total, uint32_t off) {
-    const int64_t left = (int64_t)total - (int64_t)off;
+// Index of the last byte of a span of v bytes, for spans of at most 2^31
+// bytes (-1 when the span is empty or negative).
+__device__ __forceinline__ int last_of(int64_t v) { return v <= 0 ? -1 : v < 0x80000000LL ? (int)(v - 1) : 0x7fffffff; }
+// Raw buffer resource over [base + off, base + last + 1): the records left
+// after the start offset `off` (none when off > last).  The compare is signed
+// 32-bit (a scalar instruction; an unsigned compare-and-subtract would become
+// a saturating subtract, which only the vector unit has, and the descriptor
+// must stay in scalar registers for the copies' inline assembly).
+__device__ __forceinline__ rsrc_t rsrc32(const void* base, int last, int off) {
+    const uint32_t left = off <= last ? (uint32_t)last - (uint32_t)off + 1u : 0u;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base)) + off, (short)0,
-                                             (int)(uint32_t)(left > 0 ? left : 0), 0x00020000 /* raw, untyped dwords */);
+                                             __builtin_bit_cast(int, left), 0x00020000 /* raw, untyped dwords */);
 }
 
 // The buffer-unit copies of stage sg = 2 s + h (tokens 64 h .. 64 h + 63 of
@@ -149,7 +147,7 @@ __device__ __forceinline__ void issue_codes(RwCopied& sm, const RwSrc& S, int sg
     if constexpr (GATHER) {
         // copy i covers stage tokens 32 half + 4i + tq, each at its own row
         const int bo = (4 * s + q) * QK;
-        const rsrc_t rx = rsrc32(S.x, S.xbytes, (uint32_t)bo);
+        const rsrc_t rx = rsrc32(S.x, S.xlast, bo);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int m = RW_SM * h + 32 * half + 4 * i + tq;
@@ -166,7 +164,7 @@ __device__ __forceinline__ void issue_codes(RwCopied& sm, const RwSrc& S, int sg
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int o = base + 4 * i * S.K;
-        const rsrc_t rx = rsrc32(S.x, S.xbytes, (uint32_t)o);
+        const rsrc_t rx = rsrc32(S.x, S.xlast, o);
         dma16(rx, &sm.codes[sg & 1][q][32 * half + 4 * i][0], vo[i & 3]);
     }
 }
@@ -181,20 +179,20 @@ __device__ __forceinline__ void issue_aux(RwCopied& sm, const RwSrc& S, int sg, 
         const int tok = S.tokoff[t0 + lane];
         if (wv < 4) {
             const int o = (4 * s + q) * 4;
-            dma4(rsrc32(S.d8, S.d8bytes, (uint32_t)o), &sm.d8raw[st][q][0], tok >> 6);
+            dma4(rsrc32(S.d8, S.d8last, o), &sm.d8raw[st][q][0], tok >> 6);
         } else {
             const int o = (4 * s + q) * 16;
-            dma16(rsrc32(S.bs, S.bsbytes, (uint32_t)o), &sm.bs[st][q][0][0], tok >> 4);
+            dma16(rsrc32(S.bs, S.bslast, o), &sm.bs[st][q][0][0], tok >> 4);
         }
         return;
     }
     const int off = lane * S.nb;  // token 64 h + lane, block 4 s + q, in units of one block's record
     if (wv < 4) {
         const int o = (t0 * S.nb + 4 * s + q) * 4;
-        dma4(rsrc32(S.d8, S.d8bytes, (uint32_t)o), &sm.d8raw[st][q][0], off * 4);
+        dma4(rsrc32(S.d8, S.d8last, o), &sm.d8raw[st][q][0], off * 4);
     } else {
         const int o = (t0 * S.nb + 4 * s + q) * 16;
-        dma16(rsrc32(S.bs, S.bsbytes, (uint32_t)o), &sm.bs[st][q][0][0], off * 16);
+        dma16(rsrc32(S.bs, S.bslast, o), &sm.bs[st][q][0][0], off * 16);
     }
 }
 
@@ -202,7 +200,7 @@ __device__ __forceinline__ void load_weights(Q4kRaw& R, const RwSrc& S, int b, i
     // (blocks past the row's end read the next row's bytes or, past the last
     // row, zeros: they are never multiplied)
     const int boff = b * Q4K_BLOCK;
-    const rsrc_t rw = rsrc32(S.w, S.wbytes, (uint32_t)boff);
+    const rsrc_t rw = rsrc32(S.w, S.wlast, boff);
     const int o = (32 * rg + (lane & 31)) * S.wrow;
     R.hdr = load16(rw, o);
     const int oq = o + 16 + 64 * (lane >> 5);
@@ -398,11 +396,11 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         }
         S.w = w + ((int64_t)ch.x * rows + n0) * S.wrow;
         S.x = qs;
-        S.xbytes = span32(M * K);
+        S.xlast = last_of(M * K);
         S.d8 = d8;
-        S.d8bytes = span32(M * nb * 4);
+        S.d8last = last_of(M * nb * 4);
         S.bs = bs;
-        S.bsbytes = span32(M * nb * 16);
+        S.bslast = last_of(M * nb * 16);
         __syncthreads();
     } else {
         // sources start at block kb0 of the tile's first token / row; the
@@ -410,13 +408,13 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         live = M - m0;
         S.w = w + n0 * S.wrow + kb0 * Q4K_BLOCK;
         S.x = qs + m0 * K + (int64_t)kb0 * QK;
-        S.xbytes = span32((M - m0) * K - (int64_t)kb0 * QK);
+        S.xlast = last_of((M - m0) * K - (int64_t)kb0 * QK);
         S.d8 = d8 + m0 * nb + kb0;
-        S.d8bytes = span32(((M - m0) * nb - kb0) * 4);
+        S.d8last = last_of(((M - m0) * nb - kb0) * 4);
         S.bs = bs + (m0 * nb + kb0) * 8;
-        S.bsbytes = span32(((M - m0) * nb - kb0) * 16);
+        S.bslast = last_of(((M - m0) * nb - kb0) * 16);
     }
-    S.wbytes = span32((rows - n0) * S.wrow - (GATHER ? 0 : (int64_t)kb0 * Q4K_BLOCK));
+    S.wlast = last_of((rows - n0) * S.wrow - (GATHER ? 0 : (int64_t)kb0 * Q4K_BLOCK));
     RwSums D{};
     if constexpr (SUMS) D = RwSums{Isum + (m0 * rows + n0) * nb, rows, live, rows - n0, nb};
 

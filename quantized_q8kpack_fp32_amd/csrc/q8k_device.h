@@ -37,8 +37,13 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
 // 32-bit field, so ranges are capped at 2^31 - 1 bytes; callers keep their
 // offsets below that.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// (The clamp compares the two 32-bit halves: the scalar unit has no signed
+// 64-bit compare, and a wave-uniform range should not cost vector
+// instructions.)
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    const int64_t lim = bytes <= 0 ? 0 : bytes < 0x7fffffff ? bytes : 0x7fffffff;
+    const int hi = (int)(bytes >> 32);
+    const uint32_t lo = (uint32_t)bytes;
+    const uint32_t lim = hi < 0 ? 0u : hi > 0 ? 0x7fffffffu : (lo < 0x7fffffffu ? lo : 0x7fffffffu);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)lim,
                                              0x00020000 /* raw, untyped dwords */);
 }
