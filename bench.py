@@ -145,6 +145,13 @@ class StreamCalib:
         self.lib.q8k_calib_stream_workgroups.argtypes = [ctypes.c_int64]
         self.cache = {}
 
+    def sweep(self, nbytes: int) -> dict:
+        """Per-variant times (us per launch) of a streaming read of nbytes."""
+        self.cache.pop(-(-nbytes // 16) * 16, None)
+        self.per_variant = {}
+        self.us(nbytes)
+        return dict(self.per_variant)
+
     def us(self, nbytes: int) -> float:
         """Mean per-launch time of a streaming read of nbytes (graph of >= 64
         back-to-back launches over R rotated copies totalling >= 2x the MALL),
@@ -171,6 +178,8 @@ class StreamCalib:
             g = graph_of(torch, launch, k)
             t = replay_us(torch, g, k, reps=2)
             del g
+            if hasattr(self, "per_variant"):
+                self.per_variant[v] = round(t, 3)
             best = t if best is None else min(best, t)
         t = best
         del bufs, sink
@@ -536,6 +545,8 @@ PROFILE_TARGETS = {
     "prefill_q6k": "qmatmul_prefill on the 4096x14336 relaid Q6_K, 512-token workload",
     "moe_prefill_q6k": "qmatmul_prefill_moe on the 8 x 14336x4096 relaid Q6_K, 512-token top-2 workload",
     "pack": "q8k_pack of 512 x 14336 fp32 activations",
+    "prefill_m32": "qmatmul_prefill (split-K and fixup) on the 4096x14336 Q4_K, 32-token workload",
+    "prefill_m128": "qmatmul_prefill (split-K and fixup) on the 4096x14336 Q4_K, 128-token workload",
     "copy": "a plain 256 MiB device-to-device copy (torch), the counter calibration reference",
 }
 
@@ -566,7 +577,9 @@ def profile_run(q, torch, target, launches):
               "moe_prefill_q5k": lambda: MoEPrefill(q, torch, seed=9, fmt="q5k"),
               "prefill_q6k": lambda: Prefill(q, torch, seed=10, fmt="q6k"),
               "moe_prefill_q6k": lambda: MoEPrefill(q, torch, seed=11, fmt="q6k"),
-              "pack": lambda: Prefill(q, torch)}[target]()
+              "pack": lambda: Prefill(q, torch),
+              "prefill_m32": lambda: Prefill(q, torch, M=32, seed=12),
+              "prefill_m128": lambda: Prefill(q, torch, M=128, seed=13)}[target]()
         wl.step(0)
         torch.cuda.synchronize()
         for i in range(launches):
@@ -590,6 +603,8 @@ def main():
     ap.add_argument("--profile", choices=sorted(PROFILE_TARGETS), default=None,
                     help="run only a few launches of one workload's kernel (for rocprofv3 counter passes)")
     ap.add_argument("--launches", type=int, default=8)
+    ap.add_argument("--stream-sweep", action="store_true",
+                    help="print the streaming-read calibration's per-variant times for the decode workloads' sizes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -606,6 +621,13 @@ def main():
 
     if args.profile:
         profile_run(q, torch, args.profile, args.launches)
+        return
+    if args.stream_sweep:
+        calib = StreamCalib(torch)
+        for n in (9469952, 11567104, 37273600, 107652160, 265229568):
+            t = calib.sweep(n)
+            print(json.dumps({"bytes": n, "R": rotations(-(-n // 16) * 16), "us": t,
+                              "best_TBs": round(n / min(t.values()) / 1e6, 3)}), flush=True)
         return
 
     # ---- headline: 4096x4096 Q4_K decode step, one launch (q8_K pack inside)
