@@ -81,6 +81,9 @@ KERNEL_SOURCES = {
     "batched_q4k_c8": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
     "fused_q5k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
     "fused_q6k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
+    "prefill_f32_q4k": [_CS + "prefill_regw.hip", _CS + "prefill_pack.h", _CS + "q4k_planes.h", _CS + "q8k_device.h",
+                        _CS + "q8k_quant.h"],
+    "prefill_f32_q6k": [_CS + "prefill.hip", _CS + "prefill_pack.h", _CS + "q8k_device.h", _CS + "q8k_quant.h"],
 }
 
 
@@ -403,6 +406,29 @@ class Prefill:
         return close(got, want, A)  # every output
 
 
+class PrefillF32(Prefill):
+    """The same step from fp32 tokens as one call: qmatmul_prefill_f32 packs
+    the tokens inside the GEMM launch (xq receives q8k_pack's bytes)."""
+
+    def __init__(self, q, torch, **kw):
+        super().__init__(q, torch, **kw)
+        self.ws_bytes = q.qmatmul_prefill_f32_workspace_bytes(self.qt, self.rows, self.K, self.M)
+        # sync words zero before the first call; every call leaves them so
+        self.wsp = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=torch.device("cuda"))
+
+    def step(self, i):
+        self.main(i)
+
+    def main(self, i):
+        self.q.qmatmul_prefill_f32(self.qt, self.ws[i % self.R], self.rows, self.K, self.x, self.M, self.xq, self.y,
+                                   self.wsp, self.ws_bytes)
+
+    def parity(self):
+        ok = super().parity()  # one call, every output against the oracle
+        sync = self.wsp[:256].cpu().numpy().view(np.int32)
+        return ok and not sync.any()
+
+
 class MoEPrefill:
     """512 tokens, top-2 of 8 Q4_K (Q5_K, relaid Q6_K) experts of 14336 x 4096: pack + qmatmul_prefill_moe."""
 
@@ -547,6 +573,9 @@ PROFILE_TARGETS = {
     "pack": "q8k_pack of 512 x 14336 fp32 activations",
     "prefill_m32": "qmatmul_prefill (split-K and fixup) on the 4096x14336 Q4_K, 32-token workload",
     "prefill_m128": "qmatmul_prefill (split-K and fixup) on the 4096x14336 Q4_K, 128-token workload",
+    "prefill_f32": "qmatmul_prefill_f32 (q8_K pack inside the launch) on the 4096x14336 Q4_K, 512-token workload",
+    "prefill_f32_q6k": "qmatmul_prefill_f32 (q8_K pack inside the launch) on the 4096x14336 relaid Q6_K, 512-token "
+                       "workload",
     "copy": "a plain 256 MiB device-to-device copy (torch), the counter calibration reference",
 }
 
@@ -579,7 +608,9 @@ def profile_run(q, torch, target, launches):
               "moe_prefill_q6k": lambda: MoEPrefill(q, torch, seed=11, fmt="q6k"),
               "pack": lambda: Prefill(q, torch),
               "prefill_m32": lambda: Prefill(q, torch, M=32, seed=12),
-              "prefill_m128": lambda: Prefill(q, torch, M=128, seed=13)}[target]()
+              "prefill_m128": lambda: Prefill(q, torch, M=128, seed=13),
+              "prefill_f32": lambda: PrefillF32(q, torch),
+              "prefill_f32_q6k": lambda: PrefillF32(q, torch, seed=10, fmt="q6k")}[target]()
         wl.step(0)
         torch.cuda.synchronize()
         for i in range(launches):
@@ -728,6 +759,11 @@ def main():
                 # small token counts: split-K fills the device (the fixup launch is timed with the tile)
                 ("prefill_q4k_4096x14336_m32", "prefill_q4k_m32", lambda: Prefill(q, torch, M=32, seed=12)),
                 ("prefill_q4k_4096x14336_m128", "prefill_q4k_m128", lambda: Prefill(q, torch, M=128, seed=13)),
+                # the step from fp32 tokens in one launch (pack inside); compare its kernel_us with the
+                # two-launch step_ms of the same workload above
+                ("prefill_f32_q4k_4096x14336_m512", "prefill_f32_q4k", lambda: PrefillF32(q, torch)),
+                ("prefill_f32_q6k_4096x14336_m512", "prefill_f32_q6k",
+                 lambda: PrefillF32(q, torch, seed=10, fmt="q6k")),
                 ("moe_prefill_q4k_8x14336x4096_t512_top2", "moe_prefill_q4k", lambda: MoEPrefill(q, torch)),
                 ("moe_prefill_q5k_8x14336x4096_t512_top2", "moe_prefill_q5k",
                  lambda: MoEPrefill(q, torch, seed=9, fmt="q5k")),

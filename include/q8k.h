@@ -30,7 +30,7 @@
  *     allocates and never synchronises.  Its only state: the calling
  *     thread's last-error text and launch record (q8k_debug_last_launches),
  *     and the compute-unit count of each device, asked of the runtime once
- *     (it sizes the MoE decode grid).  Buffers must stay alive until the
+ *     (it sizes the MoE decode grid and bounds qmatmul_prefill_f32).  Buffers must stay alive until the
  *     work enqueued on `stream` has finished.
  *   - `stream` is a hipStream_t (NULL = the default stream).
  *   - Arguments are validated on the host before anything is enqueued.  A
@@ -173,6 +173,34 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
 size_t qmatmul_prefill_workspace_bytes(int qtype, int64_t rows, int64_t K, int64_t M);
 int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int64_t M, float* y, void* ws,
                     size_t ws_bytes, void* stream);
+
+/* qmatmul_prefill_f32: qmatmul_prefill from fp32 tokens, with the q8_K pack
+ * inside the same launch (the fused launches of "Language models on the
+ * device", sections 1 and 3.3).  The workgroups that share a 128-token tile
+ * and a K range first pack that tile's blocks into xq, each an equal share,
+ * with q8k_pack's arithmetic, and wait for one another before multiplying:
+ * xq receives exactly q8k_pack's bytes and y equals q8k_pack followed by
+ * qmatmul_prefill bit for bit.
+ * qtype, w, rows, K, M, y: as qmatmul_prefill.  x: fp32 [M][K], 16-byte
+ * aligned.  xq: a q8_K buffer of M tokens (q8k_act_bytes(M, K) bytes,
+ * 16-byte aligned), written by the call; it must not overlap x, y or ws.
+ * ws / ws_bytes: caller-owned workspace of at least
+ * qmatmul_prefill_f32_workspace_bytes(...) bytes, 16-byte aligned, never NULL
+ * (for M, rows > 0).  It starts with the sync words of the waiting
+ * workgroups, which must be zero before the first call with this workspace;
+ * every call leaves them zero, so stream-ordered calls may share it (calls
+ * that overlap in time may not).  The split-K partials of qmatmul_prefill
+ * follow them.  The int32 at ws[0] is an error word: a workgroup that has
+ * polled for its peers 2^20 times (far longer than any call takes) gives up,
+ * sets it to non-zero and finishes (its results are then not valid); the
+ * library never clears it.
+ * The workgroups of one token tile wait for each other, so they must fit on
+ * the device together: ceil(rows / 64) may not exceed the device's compute
+ * units (256 on MI355X: rows <= 16384), else Q8K_ERR_SHAPE (use q8k_pack +
+ * qmatmul_prefill); this check asks the runtime for the compute-unit count. */
+size_t qmatmul_prefill_f32_workspace_bytes(int qtype, int64_t rows, int64_t K, int64_t M);
+int qmatmul_prefill_f32(int qtype, const void* w, int64_t rows, int64_t K, const float* x, int64_t M, void* xq,
+                        float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* qmatmul_prefill_moe: the prefill of a mixture-of-experts layer ("Language
  * models on the device", section 2.4: each expert's (token, slot) pairs are

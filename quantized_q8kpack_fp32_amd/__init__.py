@@ -18,6 +18,7 @@ __all__ = [
     "Q8K_Q4_K", "Q8K_Q5_K", "Q8K_Q6_K_RELAID", "Q8K_Q6_K_GGUF", "Q8K_COLS_MAX", "Q8K_MOE_MAX_TOKENS", "Q8K_MOE_MAX_TOPK", "Q8KError",
     "lib", "LIB_PATH", "q8k_act_bytes", "q8k_act_layout", "q8k_weight_bytes", "q8k_pack", "q8k_bind_q6k",
     "qmatvec", "qmatvec_batched", "qmatvec_f32", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
+    "qmatmul_prefill_f32_workspace_bytes", "qmatmul_prefill_f32",
     "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe", "qmatmul_prefill_moe_noalloc",
     "Q8K_NOALLOC_SCRATCH_BYTES", "q8k_debug_subblock_sums", "q8k_debug_prefill_block_sums", "q8k_debug_moe_subblock_sums",
     "q8k_debug_last_launches", "q8k_status_str", "q8k_last_error", "EXPORTED",
@@ -38,6 +39,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq8k.so")
 EXPORTED = (
     "q8k_act_bytes", "q8k_act_layout", "q8k_weight_bytes", "q8k_pack", "q8k_bind_q6k", "qmatvec",
     "qmatvec_batched", "qmatvec_f32", "qmatvec_moe", "qmatmul_prefill_workspace_bytes", "qmatmul_prefill",
+    "qmatmul_prefill_f32_workspace_bytes", "qmatmul_prefill_f32",
     "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe", "qmatmul_prefill_moe_noalloc",
     "q8k_debug_subblock_sums", "q8k_debug_prefill_block_sums", "q8k_debug_moe_subblock_sums",
     "q8k_debug_last_launches", "q8k_status_str", "q8k_last_error",
@@ -84,6 +86,10 @@ lib.qmatmul_prefill_workspace_bytes.restype = _SZ
 lib.qmatmul_prefill_workspace_bytes.argtypes = [_INT, _I64, _I64, _I64]
 lib.qmatmul_prefill.restype = _INT
 lib.qmatmul_prefill.argtypes = [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]
+lib.qmatmul_prefill_f32_workspace_bytes.restype = _SZ
+lib.qmatmul_prefill_f32_workspace_bytes.argtypes = [_INT, _I64, _I64, _I64]
+lib.qmatmul_prefill_f32.restype = _INT
+lib.qmatmul_prefill_f32.argtypes = [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P, _SZ, _P]
 lib.qmatmul_prefill_moe_workspace_bytes.restype = _SZ
 lib.qmatmul_prefill_moe_workspace_bytes.argtypes = [_INT, _I64, _I64, _I64, _I64, ctypes.c_int32]
 lib.qmatmul_prefill_moe.restype = _INT
@@ -193,6 +199,16 @@ def qmatmul_prefill(qtype: int, w, rows: int, K: int, xq, M: int, y, ws=None, ws
                     stream=None) -> None:
     _check(lib.qmatmul_prefill(qtype, _ptr(w), rows, K, _ptr(xq), M, _ptr(y), _ptr(ws), ws_bytes,
                                _stream(stream)))
+
+
+def qmatmul_prefill_f32_workspace_bytes(qtype: int, rows: int, K: int, M: int) -> int:
+    return int(lib.qmatmul_prefill_f32_workspace_bytes(qtype, rows, K, M))
+
+
+def qmatmul_prefill_f32(qtype: int, w, rows: int, K: int, x, M: int, xq, y, ws=None, ws_bytes: int = 0,
+                        stream=None) -> None:
+    _check(lib.qmatmul_prefill_f32(qtype, _ptr(w), rows, K, _ptr(x), M, _ptr(xq), _ptr(y), _ptr(ws), ws_bytes,
+                                   _stream(stream)))
 
 
 def qmatmul_prefill_moe_workspace_bytes(qtype: int, E: int, rows: int, K: int, T: int, topk: int) -> int:

@@ -57,8 +57,8 @@ def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> tuple[str, str
 # the product kernel beside its full register file (a spill moves data and
 # changes no result; these kernels are never timed).  Demangled names.
 MAY_SPILL = (
-    "void q8k::(anonymous namespace)::prefill_regw_q4k_kernel<false, true>(",
-    "void q8k::prefill_q4k_kernel<1, true>(",
+    "void q8k::(anonymous namespace)::prefill_regw_q4k_kernel<false, true, false>(",
+    "void q8k::prefill_q4k_kernel<1, true, false>(",
 )
 
 

@@ -329,6 +329,49 @@ int qmatmul_prefill(int qtype, const void* w, int64_t rows, int64_t K, const voi
                                        static_cast<float*>(ws), (hipStream_t)stream));
 }
 
+size_t qmatmul_prefill_f32_workspace_bytes(int qtype, int64_t rows, int64_t K, int64_t M) {
+    (void)qtype;
+    if (rows <= 0 || M <= 0 || K <= 0 || K % QK != 0) return 0;
+    const int ks = prefill_ksplit(rows, K / QK, M);
+    return (size_t)prefill_sync_bytes(M, ks) + (ks > 1 ? (size_t)ks * (size_t)M * (size_t)rows * 4 : 0);
+}
+
+int qmatmul_prefill_f32(int qtype, const void* w, int64_t rows, int64_t K, const float* x, int64_t M, void* xq,
+                        float* y, void* ws, size_t ws_bytes, void* stream) {
+    begin_call();
+    const char* fn = "qmatmul_prefill_f32";
+    Q8K_TRY(check_k(fn, K));
+    Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
+    Q8K_TRY(check_count(fn, "M", M, MAX_TOKENS));
+    Q8K_TRY(check_weight(fn, qtype, w));
+    Q8K_TRY(check_ptr(fn, "x", x, 16));
+    Q8K_TRY(check_ptr(fn, "xq", xq, 16));
+    Q8K_TRY(check_ptr(fn, "y", y, 4));
+    const size_t need = qmatmul_prefill_f32_workspace_bytes(qtype, rows, K, M);
+    if (ws_bytes < need)
+        return fail(Q8K_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+    if (need > 0) Q8K_TRY(check_ptr(fn, "ws", ws, 16));
+    Q8K_TRY(check_grid(fn, ((rows + 31) / 32) * ((M + 63) / 64)));
+    if (rows == 0 || M == 0) return Q8K_OK;
+    // the row tiles of a token tile wait for each other: they must fit on the
+    // device together (one workgroup per compute unit)
+    const int64_t tiles = (rows + 63) / 64, cus = device_cu_count();
+    if (tiles > cus)
+        return fail(Q8K_ERR_SHAPE,
+                    "%s: rows=%lld make %lld row tiles that wait for each other, more than the device's %lld compute "
+                    "units (rows <= %lld; use q8k_pack + qmatmul_prefill)",
+                    fn, (long long)rows, (long long)tiles, (long long)cus, (long long)(64 * cus));
+    const int nb = (int)(K / QK);
+    const int ks = prefill_ksplit(rows, nb, M);
+    const Acts a = acts_of(xq, M, K);
+    PackDst pk{x, const_cast<int8_t*>(a.qs), const_cast<float*>(a.d), const_cast<int16_t*>(a.bs),
+               static_cast<int32_t*>(ws)};
+    float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + prefill_sync_bytes(M, ks));
+    const PrefillWeights pw = prefill_weights(qtype, w, rows * nb);
+    return launched(fn, launch_prefill_f32(pw.fmt, pw.w, pw.prefix, rows, nb, a, M, y, part, pk,
+                                           (hipStream_t)stream));
+}
+
 size_t qmatmul_prefill_moe_workspace_bytes(int qtype, int64_t E, int64_t rows, int64_t K, int64_t T, int32_t topk) {
     if ((qtype != Q8K_Q4_K && qtype != Q8K_Q5_K && qtype != Q8K_Q6_K_RELAID) || E < 1 || rows < 0 || K <= 0 ||
         K % QK != 0 || T < 0 || topk < 1)

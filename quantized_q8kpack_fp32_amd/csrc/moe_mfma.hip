@@ -369,6 +369,8 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
     }
 }
 
+}  // namespace
+
 // Compute units of the current device, asked once per device.
 int64_t device_cu_count() {
     static std::atomic<int> cached[64];
@@ -382,8 +384,6 @@ int64_t device_cu_count() {
     }
     return n;
 }
-
-}  // namespace
 
 bool moe_mfma_q4k_fits(int64_t K) { return mm_tok_bytes(K) <= MM_TOK_BYTES; }
 

@@ -49,6 +49,7 @@
 // A = tokens, B = weight rows, so each consumer lane owns one weight row.
 #include "q8k_device.h"
 #include "q8k_launch.h"
+#include "prefill_pack.h"
 
 #include <mutex>
 
@@ -585,14 +586,15 @@ __device__ __forceinline__ void prefill_tile(PrefillSmem<F>& sm, const PrefillSr
 // integer sum I_b to Isum [M][rows][nb].  Split-K (ksplit > 1, "Language
 // models on the device", section 2.3): workgroup split ks multiplies blocks
 // [kb0, kb0 + nbk) and stores its partial [M][rows] at y + ks * M * rows, for
-// prefill_fixup_kernel to add.
-template <int F, bool SUMS = false>
+// prefill_fixup_kernel to add.  PACK: the tokens arrive as fp32 and the
+// workgroups pack them first (prefill_pack.h).
+template <int F, bool SUMS = false, bool PACK = false>
 __global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restrict__ w,
                                                           const uint16_t* __restrict__ prefix, int64_t rows, int nb,
                                                           const int8_t* __restrict__ qs, const float* __restrict__ d8,
                                                           const int16_t* __restrict__ bs, int64_t K, int64_t M,
                                                           float* __restrict__ y, int32_t* __restrict__ Isum,
-                                                          int ksplit) {
+                                                          int ksplit, PackDst pk) {
     __shared__ __attribute__((aligned(16))) PrefillSmem<F> sm;
     const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
     const int64_t ntm = (M + PF_TM - 1) / PF_TM;
@@ -604,6 +606,8 @@ __global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restr
     const int kb0 = ks * per;
     const int nbk = nb - kb0 < per ? nb - kb0 : per;
     y += (int64_t)ks * M * rows;
+    if constexpr (PACK)
+        pack_group<512>(pk, nb, M, PF_TM, m0, kb0, nbk, tile % ntn, ntn, ks * ntm + tile / ntn, (int)threadIdx.x);
     // Only producers use the sources.  Q6_K: every thread builds them, outside a
     // branch on the thread index, so their wave-uniform parts stay scalar (2%
     // faster); Q5_K measured 4% slower that way and builds them in the
@@ -846,10 +850,28 @@ hipError_t launch_prefill(int fmt, const uint8_t* w, const uint16_t* prefix, int
     float* out = ksplit > 1 ? part : y;
     if (fmt == PF_Q6)
         Q8K_LAUNCH(prefill_q4k_kernel<PF_Q6>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K, M, out,
-                   nullptr, ksplit);
+                   nullptr, ksplit, PackDst{});
     else
         Q8K_LAUNCH(prefill_q4k_kernel<PF_Q5>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K, M, out,
-                   nullptr, ksplit);
+                   nullptr, ksplit, PackDst{});
+    if (ksplit > 1) return launch_prefill_fixup(part, ksplit, M * rows, y, s);
+    return hipGetLastError();
+}
+
+// The same tiles from fp32 tokens: the q8_K pack inside the launch.  `a` is
+// the q8_K buffer the workgroups fill (pk.qs/d/bs are its sections).
+hipError_t launch_prefill_f32(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a,
+                              int64_t M, float* y, float* part, PackDst pk, hipStream_t s) {
+    const int ksplit = prefill_ksplit(rows, nb, M);
+    if (fmt == PF_Q4) return launch_prefill_regw_q4k_f32(w, rows, nb, a, M, y, ksplit, part, pk, s);
+    const dim3 grid((unsigned)(((rows + PF_TN - 1) / PF_TN) * ((M + PF_TM - 1) / PF_TM) * ksplit));
+    float* out = ksplit > 1 ? part : y;
+    if (fmt == PF_Q6)
+        Q8K_LAUNCH((prefill_q4k_kernel<PF_Q6, false, true>), grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d,
+                   a.bs, a.K, M, out, nullptr, ksplit, pk);
+    else
+        Q8K_LAUNCH((prefill_q4k_kernel<PF_Q5, false, true>), grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d,
+                   a.bs, a.K, M, out, nullptr, ksplit, pk);
     if (ksplit > 1) return launch_prefill_fixup(part, ksplit, M * rows, y, s);
     return hipGetLastError();
 }
@@ -860,10 +882,10 @@ hipError_t launch_prefill_sums(int fmt, const uint8_t* w, const uint16_t* prefix
     const dim3 grid((unsigned)(((rows + PF_TN - 1) / PF_TN) * ((M + PF_TM - 1) / PF_TM)));
     if (fmt == PF_Q6)
         Q8K_LAUNCH((prefill_q4k_kernel<PF_Q6, true>), grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K,
-                   M, y, I, 1);
+                   M, y, I, 1, PackDst{});
     else
         Q8K_LAUNCH((prefill_q4k_kernel<PF_Q5, true>), grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K,
-                   M, y, I, 1);
+                   M, y, I, 1, PackDst{});
     return hipGetLastError();
 }
 

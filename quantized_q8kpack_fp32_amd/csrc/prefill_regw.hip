@@ -41,6 +41,7 @@
 // (i % 4) + 4 (i / 8): each lane holds one weight row and 16 tokens.
 #include "q4k_planes.h"
 #include "q8k_launch.h"
+#include "prefill_pack.h"
 
 namespace q8k {
 namespace {
@@ -348,13 +349,14 @@ constexpr int RW_RAW_LOADS = 5;  // load_weights() issues five loads
 //
 // SUMS (test support, dense tiles): the same kernel also stores every block's
 // exact integer sum I_b = 8 P_hi + P_lo to Isum [M][rows][nb].
-template <bool GATHER, bool SUMS = false>
+template <bool GATHER, bool SUMS = false, bool PACK = false>
 __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     const uint8_t* __restrict__ w, int64_t rows, int nb, const int8_t* __restrict__ qs,
     const float* __restrict__ d8, const int16_t* __restrict__ bs, int64_t K, int64_t M, float* __restrict__ y,
     const int32_t* __restrict__ nchunks, const int4* __restrict__ chunks, const int32_t* __restrict__ order,
-    int topk, int32_t* __restrict__ Isum, int ksplit) {
+    int topk, int32_t* __restrict__ Isum, int ksplit, PackDst pk) {
     static_assert(!(SUMS && GATHER), "block sums of the dense tile");
+    static_assert(!(PACK && GATHER), "the pack runs in the dense tile");
     __shared__ __attribute__((aligned(16))) RwCopied sm;
     __shared__ __attribute__((aligned(16))) RwBuilt sb;
     __shared__ RwGather gat;
@@ -428,10 +430,17 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 
     Q4kRaw R;
+    if constexpr (PACK) {
+        // fp32 tokens: the first weights (which do not depend on the tokens)
+        // are loaded first; then this workgroup packs its share of the tile's
+        // blocks and waits for the rest of its group (prefill_pack.h)
+        load_weights(R, S, q, rg, lane);
+        pack_group<RW_THREADS>(pk, nb, M, RW_TM, m0, kb0, nbk, tile % ntn, ntn, ks * ntm + tile / ntn, tid);
+    }
     issue_codes<GATHER>(sm, S, 0, wv, lane);
     issue_aux<GATHER>(sm, S, 0, wv, lane);
     issue_aux<GATHER>(sm, S, 1, wv, lane);
-    load_weights(R, S, q, rg, lane);
+    if constexpr (!PACK) load_weights(R, S, q, rg, lane);
     stage_barrier<0>();
     build_amin(sm, sb, 0, tid);
     stage_barrier<0>();
@@ -500,7 +509,16 @@ hipError_t launch_prefill_regw_q4k(const uint8_t* w, int64_t rows, int nb, Acts 
                                    int ksplit, float* part, hipStream_t s) {
     const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * ((M + RW_TM - 1) / RW_TM) * ksplit));
     Q8K_LAUNCH((prefill_regw_q4k_kernel<false>), grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K, M,
-               ksplit > 1 ? part : y, nullptr, nullptr, nullptr, 1, nullptr, ksplit);
+               ksplit > 1 ? part : y, nullptr, nullptr, nullptr, 1, nullptr, ksplit, PackDst{});
+    if (ksplit > 1) return launch_prefill_fixup(part, ksplit, M * rows, y, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_regw_q4k_f32(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
+                                       int ksplit, float* part, PackDst pk, hipStream_t s) {
+    const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * ((M + RW_TM - 1) / RW_TM) * ksplit));
+    Q8K_LAUNCH((prefill_regw_q4k_kernel<false, false, true>), grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d,
+               a.bs, a.K, M, ksplit > 1 ? part : y, nullptr, nullptr, nullptr, 1, nullptr, ksplit, pk);
     if (ksplit > 1) return launch_prefill_fixup(part, ksplit, M * rows, y, s);
     return hipGetLastError();
 }
@@ -509,7 +527,7 @@ hipError_t launch_prefill_regw_q4k_sums(const uint8_t* w, int64_t rows, int nb, 
                                         int32_t* I, hipStream_t s) {
     const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * ((M + RW_TM - 1) / RW_TM)));
     Q8K_LAUNCH((prefill_regw_q4k_kernel<false, true>), grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K,
-               M, y, nullptr, nullptr, nullptr, 1, I, 1);
+               M, y, nullptr, nullptr, nullptr, 1, I, 1, PackDst{});
     return hipGetLastError();
 }
 
@@ -518,7 +536,7 @@ hipError_t launch_prefill_regw_moe_q4k(const uint8_t* w, int64_t rows, int nb, A
                                        float* out, hipStream_t s) {
     const dim3 grid((unsigned)(((rows + RW_TN - 1) / RW_TN) * max_chunks));
     Q8K_LAUNCH((prefill_regw_q4k_kernel<true>), grid, dim3(RW_THREADS), 0, s, w, rows, nb, a.qs, a.d, a.bs, a.K, T,
-               out, nchunks, chunks, order, topk, nullptr, 1);
+               out, nchunks, chunks, order, topk, nullptr, 1, PackDst{});
     return hipGetLastError();
 }
 

@@ -84,10 +84,34 @@ inline int prefill_ksplit(int64_t rows, int64_t nb, int64_t M) {
 hipError_t launch_prefill(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a, int64_t M,
                           float* y, float* part, hipStream_t s);
 hipError_t launch_prefill_fixup(const float* part, int ksplit, int64_t n, float* y, hipStream_t s);
+// The prefill from fp32 tokens with the q8_K pack inside the launch
+// (prefill_pack.h): the tiles' workgroups pack their group's blocks into the
+// q8_K buffer (qs, d, bs) and meet on sync words in the caller's workspace:
+// word 0 the error word, then two words per group (token tile x K split),
+// zero before the first call.  The split-K partials follow the sync words.
+struct PackDst {
+    const float* x;  // fp32 tokens [M][K]
+    int8_t* qs;      // the q8_K buffer's sections (act_layout(M, K))
+    float* d;
+    int16_t* bs;
+    int32_t* sync;
+};
+constexpr int PACK_SYNC_HEAD = 4;  // words before the first group's
+inline int64_t prefill_groups(int64_t M, int ksplit) { return ((M + 127) / 128) * ksplit; }
+inline int64_t prefill_sync_bytes(int64_t M, int ksplit) {
+    return (4 * (PACK_SYNC_HEAD + 2 * prefill_groups(M, ksplit)) + 255) / 256 * 256;
+}
+// Compute units of the current device (asked once per device): a group of
+// workgroups that wait for each other must fit on the device together.
+int64_t device_cu_count();
+hipError_t launch_prefill_f32(int fmt, const uint8_t* w, const uint16_t* prefix, int64_t rows, int nb, Acts a,
+                              int64_t M, float* y, float* part, PackDst pk, hipStream_t s);
 // Q4_K prefill with the weight planes built in the registers of the waves that
 // multiply them (prefill_regw.hip).
 hipError_t launch_prefill_regw_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y, int ksplit,
                                    float* part, hipStream_t s);
+hipError_t launch_prefill_regw_q4k_f32(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t M, float* y,
+                                       int ksplit, float* part, PackDst pk, hipStream_t s);
 // The same tile over the chunks of a mixture-of-experts prefill (T tokens;
 // chunk table and pair order as in the workspace below; out: [P][rows]).
 hipError_t launch_prefill_regw_moe_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, int64_t T, int64_t max_chunks,

@@ -93,8 +93,8 @@ def short(name: str) -> str:
 # Operations of the binding that launch kernels (everything else is sizing or
 # error text).
 _OPS = ("q8k_pack", "q8k_bind_q6k", "qmatvec", "qmatvec_batched", "qmatvec_f32", "qmatvec_moe", "qmatmul_prefill",
-        "qmatmul_prefill_moe", "q8k_debug_subblock_sums", "q8k_debug_prefill_block_sums",
-        "q8k_debug_moe_subblock_sums")
+        "qmatmul_prefill_f32", "qmatmul_prefill_moe", "qmatmul_prefill_moe_noalloc", "q8k_debug_subblock_sums",
+        "q8k_debug_prefill_block_sums", "q8k_debug_moe_subblock_sums")
 
 
 class _Tracked:

@@ -189,6 +189,33 @@ def test_prefill_moe_arguments(q):
     assert q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q6_K_GGUF, 8, 4, 256, 16, 2) == 0
 
 
+def test_prefill_f32_arguments(q):
+    """The prefill from fp32 tokens: its workspace is the sync words (one
+    256-byte-padded run: an error word, three pad words, two words per token
+    tile and K split) followed by qmatmul_prefill's split-K partials."""
+    f = q.qmatmul_prefill_f32
+    for qt in (q.Q8K_Q4_K, q.Q8K_Q5_K, q.Q8K_Q6_K_RELAID):
+        assert q.qmatmul_prefill_f32_workspace_bytes(qt, 4096, 14336, 512) == 256  # 4 tiles, no split
+        assert q.qmatmul_prefill_f32_workspace_bytes(qt, 4096, 14336, 32) == \
+            256 + q.qmatmul_prefill_workspace_bytes(qt, 4096, 14336, 32) == 256 + 4 * 32 * 4096 * 4
+        assert q.qmatmul_prefill_f32_workspace_bytes(qt, 64, 256, 128 * 60) == 512  # 60 tiles: 4 * (4 + 120) bytes
+        assert q.qmatmul_prefill_f32_workspace_bytes(qt, 0, 256, 4) == 0
+    need = q.qmatmul_prefill_f32_workspace_bytes(q.Q8K_Q4_K, 64, 256, 4)
+    refused(q, "Q8K_ERR_WORKSPACE", f, q.Q8K_Q4_K, A16, 64, 256, A16, 4, A16, A16, A16, need - 1, 0)
+    refused(q, "Q8K_ERR_NULL", f, q.Q8K_Q4_K, A16, 64, 256, A16, 4, A16, A16, None, need, 0)
+    refused(q, "Q8K_ERR_NULL", f, q.Q8K_Q4_K, A16, 64, 256, None, 4, A16, A16, A16, need, 0)
+    refused(q, "Q8K_ERR_ALIGN", f, q.Q8K_Q4_K, A16, 64, 256, A16 + 4, 4, A16, A16, A16, need, 0)
+    refused(q, "Q8K_ERR_ALIGN", f, q.Q8K_Q4_K, A16, 64, 256, A16, 4, A16 + 8, A16, A16, need, 0)
+    refused(q, "Q8K_ERR_SHAPE", f, q.Q8K_Q4_K, A16, 64, 300, A16, 4, A16, A16, A16, need, 0)
+    refused(q, "Q8K_ERR_QTYPE", f, q.Q8K_Q6_K_GGUF, A16, 64, 256, A16, 4, A16, A16, A16, need, 0)
+    # more row tiles than compute units (no device here: the library assumes 256)
+    msg = refused(q, "Q8K_ERR_SHAPE", f, q.Q8K_Q4_K, A16, 64 * 256 + 1, 256, A16, 4, A16, A16, A16, 1 << 20, 0)
+    assert "q8k_pack + qmatmul_prefill" in msg
+    assert q.q8k_debug_last_launches() == []
+    f(q.Q8K_Q4_K, A16, 0, 256, A16, 4, A16, A16, None, 0, 0)  # nothing to do
+    f(q.Q8K_Q4_K, A16, 64, 256, A16, 0, A16, A16, None, 0, 0)
+
+
 def test_empty_inputs_enqueue_nothing(q):
     # zero rows / tokens are valid and return before any launch
     q.qmatvec(q.Q8K_Q4_K, A16, 0, 256, A16, A16, 0)
@@ -223,7 +250,8 @@ def test_census_reads_the_kernel_table(q):
     names = {census.short(n) for n in census.kernel_names(q).values()}
     for k in ("pack_kernel", "bind_q6k_kernel", "matvec_q4k_kernel<1, 2, false, false>",
               "matvec_q6k_kernel<1, false, false>", "matvec_f32_q4k_kernel<1, 2, false>",
-              "moe_mfma_q4k_kernel<false, false>", "prefill_regw_q4k_kernel<false, false>",
-              "prefill_q4k_kernel<2, false>", "moe_group_kernel", "moe_combine_kernel<4>"):
+              "moe_mfma_q4k_kernel<false, false>", "prefill_regw_q4k_kernel<false, false, false>",
+              "prefill_q4k_kernel<2, false, false>", "prefill_regw_q4k_kernel<false, false, true>",
+              "prefill_q4k_kernel<1, false, true>", "moe_group_kernel", "moe_combine_kernel<4>"):
         assert k in names, k
     assert not any(n.startswith("prefill_q4k_kernel<0") for n in names), "the Q4_K prefill runs the register tile"

@@ -34,11 +34,11 @@ def test_only_named_test_kernels_may_spill():
     kernel of the same template still fails the gate."""
     b = _build_module()
     log = LOG.replace("_ZN3q8k10moe_kernelILb0EEEvPKh",
-                      "_ZN3q8k12_GLOBAL__N_123prefill_regw_q4k_kernelILb0ELb1EEEvPKhliPKaPKfPKsllPfPKiPK15HIP_vector_"
+                      "_ZN3q8k12_GLOBAL__N_123prefill_regw_q4k_kernelILb0ELb1ELb0EEEvPKhliPKaPKfPKsllPfPKiPK15HIP_vector_"
                       "typeIiLj4EESC_iPi")
     assert b._check_scratch(log, "prefill_regw.hip") == []
     log = LOG.replace("_ZN3q8k10moe_kernelILb0EEEvPKh",
-                      "_ZN3q8k12_GLOBAL__N_123prefill_regw_q4k_kernelILb0ELb0EEEvPKhliPKaPKfPKsllPfPKiPK15HIP_vector_"
+                      "_ZN3q8k12_GLOBAL__N_123prefill_regw_q4k_kernelILb0ELb0ELb0EEEvPKhliPKaPKfPKsllPfPKiPK15HIP_vector_"
                       "typeIiLj4EESC_iPi")
     assert len(b._check_scratch(log, "prefill_regw.hip")) == 1
 

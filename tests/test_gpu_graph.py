@@ -59,7 +59,14 @@ def test_graph_replays_match_eager(q):
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     wsm_bytes = q.qmatmul_prefill_moe_workspace_bytes(q.Q8K_Q4_K, E, rows, K, T, topk)
     wsm = torch.empty(wsm_bytes, dtype=torch.uint8, device=dev)
-    outs = [xq, xq1, xqT, y4, y6, yb, ym, yp, yp5, yp6, yf4, yf6, xqf, yb5, ypm]
+    # the prefill from fp32 tokens: its sync words start at zero and every
+    # call (each replay) leaves them so
+    xqp = torch.empty(q.q8k_act_bytes(M, K), dtype=torch.uint8, device=dev)
+    ypf = torch.empty(M * rows, dtype=torch.float32, device=dev)
+    ypf6 = torch.empty(M * rows, dtype=torch.float32, device=dev)
+    wsf_bytes = q.qmatmul_prefill_f32_workspace_bytes(q.Q8K_Q4_K, rows, K, M)
+    wsf = torch.zeros(wsf_bytes, dtype=torch.uint8, device=dev)
+    outs = [xq, xq1, xqT, y4, y6, yb, ym, yp, yp5, yp6, yf4, yf6, xqf, yb5, ypm, xqp, ypf, ypf6]
 
     def path():
         q.q8k_pack(x, M, K, xq)
@@ -76,6 +83,8 @@ def test_graph_replays_match_eager(q):
         q.qmatvec_f32(q.Q8K_Q6_K_RELAID, w6, rows, K, x[:1], 1, yf6, xqf)
         q.qmatvec_batched(q.Q8K_Q5_K, w5, rows, K, xqT, T, yb5)
         q.qmatmul_prefill_moe(q.Q8K_Q4_K, w4, E, rows, K, xqT, T, ids, rw, topk, ypm, wsm, wsm_bytes)
+        q.qmatmul_prefill_f32(q.Q8K_Q4_K, w4, rows, K, x, M, xqp, ypf, wsf, wsf_bytes)
+        q.qmatmul_prefill_f32(q.Q8K_Q6_K_RELAID, w6, rows, K, x, M, xqp, ypf6, wsf, wsf_bytes)
 
     path()
     torch.cuda.synchronize()
@@ -85,12 +94,13 @@ def test_graph_replays_match_eager(q):
         them is not written by any kernel), or the whole fp32 output."""
         if o.dtype != torch.uint8:
             return o.view(torch.uint8)
-        tok = {"xq": M, "xq1": 1, "xqT": T, "xqf": 1}[name]
+        tok = {"xq": M, "xq1": 1, "xqT": T, "xqf": 1, "xqp": M}[name]
         total, od, ob = q.q8k_act_layout(tok, K)
         nb = K // 256
         return torch.cat([o[: tok * K], o[od: od + 4 * tok * nb], o[ob: ob + 16 * tok * nb]])
 
-    names = ["xq", "xq1", "xqT", "y4", "y6", "yb", "ym", "yp", "yp5", "yp6", "yf4", "yf6", "xqf", "yb5", "ypm"]
+    names = ["xq", "xq1", "xqT", "y4", "y6", "yb", "ym", "yp", "yp5", "yp6", "yf4", "yf6", "xqf", "yb5", "ypm", "xqp",
+             "ypf", "ypf6"]
     eager = [defined(n, o).clone() for n, o in zip(names, outs)]
 
     graph = torch.cuda.CUDAGraph()
@@ -105,6 +115,7 @@ def test_graph_replays_match_eager(q):
         torch.cuda.synchronize()
         for name, o, e in zip(names, outs, eager):
             assert torch.equal(defined(name, o), e), f"replay {rep}: {name} differs from eager"
+        assert not wsf[:256].any(), f"replay {rep}: sync words not back at zero"
         y_side = torch.empty(rows, dtype=torch.float32, device=dev)
         q.qmatvec(q.Q8K_Q4_K, w4, rows, K, side, y_side)
         torch.cuda.synchronize()

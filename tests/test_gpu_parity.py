@@ -794,6 +794,110 @@ def test_prefill_q5k_without_fifth_bits_matches_q4k(q):
     assert_close(y5, want, A, "q5k prefill without fifth bits")
 
 
+# ================================================================== fused pack + prefill (NEXT row)
+def run_prefill_f32(q, fmt, wd, rows, K, x, ws=None):
+    """qmatmul_prefill_f32 on host fp32 tokens -> (y, q8_K bytes, workspace).
+    A fresh workspace is zeroed (its sync words must start at zero)."""
+    import torch
+
+    M = x.shape[0]
+    qt = getattr(q, _PF_FMT[fmt][0])
+    xq = poisoned(q.q8k_act_bytes(M, K))
+    y = poisoned_f32(M, rows)
+    wsb = q.qmatmul_prefill_f32_workspace_bytes(qt, rows, K, M)
+    if ws is None:
+        ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    q.qmatmul_prefill_f32(qt, wd, rows, K, to_dev(x), M, xq, y, ws, wsb)
+    return y, xq, ws
+
+
+def sync_words(q, fmt, rows, K, M, ws):
+    """The workspace's sync words (error word first) as int32."""
+    qt = getattr(q, _PF_FMT[fmt][0])
+    n = q.qmatmul_prefill_f32_workspace_bytes(qt, rows, K, M) - q.qmatmul_prefill_workspace_bytes(qt, rows, K, M)
+    return host(ws[:n]).view(np.int32)
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("M,rows,K,seed", [(1, 64, 256, 300), (77, 130, 2048, 301), (200, 130, 768, 302),
+                                           (129, 65, 512, 303), (32, 4096, 14336, 304), (5, 64, 14336, 305)])
+def test_prefill_f32(q, fmt, M, rows, K, seed):
+    """The prefill from fp32 tokens, packed inside the launch: every output
+    against the oracle, the q8_K bytes it writes against the oracle's pack,
+    and the sync words back at zero (ragged tiles; split-K at 32 x 4096 x
+    14336 and 5 x 64 x 14336)."""
+    w = _PF_FMT[fmt][2](np.random.default_rng(seed), rows, K)
+    x = acts(seed, M, K)
+    y, xq, ws = run_prefill_f32(q, fmt, pf_weights(q, fmt, w, rows, K), rows, K, x)
+    oqs, od, obs = oracle.q8k_pack(x)
+    qs, d, bs = split_act(q, host(xq), M, K)
+    assert_exact(qs, oqs, "codes")
+    assert_exact(d, od, "scales")
+    assert_exact(bs, obs, "sums")
+    want, A = oracle.matvec(_PF_FMT[fmt][1], w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(y), want, A, f"fused prefill {fmt} M={M} N={rows} K={K}")
+    assert not sync_words(q, fmt, rows, K, M, ws).any()
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
+def test_prefill_f32_down_projection_full(q, fmt):
+    """The 512-token x 4096-row x 14336 prefill from fp32 tokens: all
+    2,097,152 outputs against the oracle, and bit for bit the result of
+    q8k_pack followed by qmatmul_prefill (xq byte for byte q8k_pack's)."""
+    M, rows, K = 512, 4096, 14336
+    w = _PF_FMT[fmt][2](np.random.default_rng(4), rows, K)
+    x = acts(4, M, K)
+    wd = pf_weights(q, fmt, w, rows, K)
+    y, xq, ws = run_prefill_f32(q, fmt, wd, rows, K, x)
+    got = host(y)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(_PF_FMT[fmt][1], w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(got, want, A, f"fused prefill {fmt} 512x4096x14336")
+    assert not sync_words(q, fmt, rows, K, M, ws).any()
+    xq2 = pack_on_device(q, x)
+    y2 = poisoned_f32(M, rows)
+    q.qmatmul_prefill(getattr(q, _PF_FMT[fmt][0]), wd, rows, K, xq2, M, y2, None, 0)
+    assert np.array_equal(got.view(np.uint32), host(y2).view(np.uint32)), "differs from pack + prefill"
+    total, od_, ob_ = q.q8k_act_layout(M, K)
+    a, b = host(xq), host(xq2)
+    for lo, hi in ((0, M * K), (od_, od_ + 4 * M * (K // 256)), (ob_, ob_ + 16 * M * (K // 256))):
+        assert np.array_equal(a[lo:hi], b[lo:hi]), "q8_K bytes differ from q8k_pack's"
+
+
+def test_prefill_f32_calls_share_a_workspace(q):
+    """Stream-ordered calls of different shapes on one workspace: each leaves
+    the sync words at zero for the next, and each result matches the oracle."""
+    import torch
+
+    cases = [(200, 130, 768, 310), (32, 4096, 14336, 311), (1, 64, 256, 312), (200, 130, 768, 313)]
+    wsb = max(q.qmatmul_prefill_f32_workspace_bytes(q.Q8K_Q4_K, r, K, M) for M, r, K, _ in cases)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    runs = []
+    for M, rows, K, seed in cases:  # enqueued back to back, no synchronisation
+        w = q4k(seed, rows, K)
+        x = acts(seed, M, K)
+        y, _, _ = run_prefill_f32(q, "q4k", to_dev(w), rows, K, x, ws)
+        runs.append((w, x, rows, K, y))
+    for w, x, rows, K, y in runs:
+        oqs, od, obs = oracle.q8k_pack(x)
+        want, A = oracle.matvec(oracle.Q4_K, w, rows, K, oqs, od, obs, nthreads=NTH)
+        assert_close(host(y), want, A, f"shared workspace M={x.shape[0]} N={rows} K={K}")
+    assert not host(ws[:256]).view(np.int32).any()
+
+
+def test_prefill_f32_refuses_rows_beyond_the_device(q):
+    """The row tiles of a token tile wait for each other, so more of them than
+    the device has compute units is refused before anything is enqueued."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows, K, M = 64 * cus + 1, 256, 4
+    with pytest.raises(q.Q8KError) as ei:
+        q.qmatmul_prefill_f32(q.Q8K_Q4_K, 1 << 20, rows, K, 1 << 20, M, 1 << 20, 1 << 20, 1 << 20, 1 << 30)
+    assert ei.value.name == "Q8K_ERR_SHAPE"
+    assert q.q8k_debug_last_launches() == []
+
+
 # ================================================================== empty inputs
 def test_empty_calls_leave_outputs_untouched(q):
     y = poisoned_f32(8)
