@@ -864,6 +864,21 @@ def test_prefill_f32_down_projection_full(q, fmt):
         assert np.array_equal(a[lo:hi], b[lo:hi]), "q8_K bytes differ from q8k_pack's"
 
 
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("M,rows,K,seed", [(1000, 4096, 1024, 320), (256, 16384, 256, 321)])
+def test_prefill_f32_more_workgroups_than_compute_units(q, fmt, M, rows, K, seed):
+    """Grids beyond one workgroup per compute unit: 8 token tiles x 64 row
+    tiles (512 workgroups, groups start as earlier ones finish), and row tiles
+    as many as the device's compute units (each group fills the device)."""
+    w = _PF_FMT[fmt][2](np.random.default_rng(seed), rows, K)
+    x = acts(seed, M, K)
+    y, xq, ws = run_prefill_f32(q, fmt, pf_weights(q, fmt, w, rows, K), rows, K, x)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(_PF_FMT[fmt][1], w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(host(y), want, A, f"fused prefill {fmt} M={M} N={rows} K={K}")
+    assert not sync_words(q, fmt, rows, K, M, ws).any()
+
+
 def test_prefill_f32_calls_share_a_workspace(q):
     """Stream-ordered calls of different shapes on one workspace: each leaves
     the sync words at zero for the next, and each result matches the oracle."""
