@@ -196,6 +196,15 @@ def close(got, want, A):
     return bool(np.isfinite(got).all() and (np.abs(got - want) <= TOL_REL * A + TOL_ABS).all())
 
 
+def otime(wl, fn, *a, **k):
+    """Call an oracle function, adding its wall time to wl.oracle_s (the
+    oracle's time for the workload's step, on ncores() threads)."""
+    t0 = time.perf_counter()
+    r = fn(*a, **k)
+    wl.oracle_s = getattr(wl, "oracle_s", 0.0) + time.perf_counter() - t0
+    return r
+
+
 def rotations(nbytes: int, minimum: int = 2) -> int:
     return max(minimum, -(-2 * MALL_BYTES // max(nbytes, 1)))
 
@@ -261,8 +270,8 @@ class Decode:
 
         self.step(0)
         got = self.y.cpu().numpy()
-        qs, d, bs = oracle.q8k_pack(self.x_host)
-        want, A = oracle.matvec(_oracle_qtype(oracle, self.fmt), self.w_host, self.rows, self.K, qs, d, bs,
+        qs, d, bs = otime(self, oracle.q8k_pack, self.x_host)
+        want, A = otime(self, oracle.matvec, _oracle_qtype(oracle, self.fmt), self.w_host, self.rows, self.K, qs, d, bs,
                                 nthreads=ncores())
         return close(got, want[0], A[0])
 
@@ -294,8 +303,8 @@ class Batched(Decode):
 
         self.step(0)
         got = self.y.cpu().numpy().reshape(self.ncols, self.rows)
-        qs, d, bs = oracle.q8k_pack(self.x_host)
-        want, A = oracle.matvec(_oracle_qtype(oracle, self.fmt), self.w_host, self.rows, self.K, qs, d, bs,
+        qs, d, bs = otime(self, oracle.q8k_pack, self.x_host)
+        want, A = otime(self, oracle.matvec, _oracle_qtype(oracle, self.fmt), self.w_host, self.rows, self.K, qs, d, bs,
                                 nthreads=ncores())
         return close(got, want, A)
 
@@ -342,8 +351,8 @@ class MoE:
 
         self.step(0)
         got = self.y.cpu().numpy().reshape(self.T, self.rows)
-        qs, d, bs = oracle.q8k_pack(self.x_host)
-        want, A = oracle.moe(_oracle_qtype(oracle, self.fmt), self.w_host, self.E, self.rows, self.K, qs, d, bs,
+        qs, d, bs = otime(self, oracle.q8k_pack, self.x_host)
+        want, A = otime(self, oracle.moe, _oracle_qtype(oracle, self.fmt), self.w_host, self.E, self.rows, self.K, qs, d, bs,
                              self.ids_host, self.rw_host, nthreads=ncores())
         return close(got, want, A)
 
@@ -400,8 +409,8 @@ class Prefill:
 
         self.step(0)
         got = self.y.cpu().numpy().reshape(self.M, self.rows)
-        qs, d, bs = oracle.q8k_pack(self.x_host)
-        want, A = oracle.matvec(_oracle_qtype(oracle, self.fmt), self.w_host, self.rows, self.K, qs, d, bs,
+        qs, d, bs = otime(self, oracle.q8k_pack, self.x_host)
+        want, A = otime(self, oracle.matvec, _oracle_qtype(oracle, self.fmt), self.w_host, self.rows, self.K, qs, d, bs,
                                 nthreads=ncores())
         return close(got, want, A)  # every output
 
@@ -472,8 +481,8 @@ class MoEPrefill:
 
         self.step(0)
         got = self.y.cpu().numpy().reshape(self.T, self.rows)
-        qs, d, bs = oracle.q8k_pack(self.x_host)
-        want, A = oracle.moe(_oracle_qtype(oracle, self.fmt), self.w_host, self.E, self.rows, self.K, qs, d, bs,
+        qs, d, bs = otime(self, oracle.q8k_pack, self.x_host)
+        want, A = otime(self, oracle.moe, _oracle_qtype(oracle, self.fmt), self.w_host, self.E, self.rows, self.K, qs, d, bs,
                              self.ids_host, self.rw_host, nthreads=ncores())
         return close(got, want, A)
 
@@ -482,8 +491,19 @@ def ncores() -> int:
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
+TIMING_ROUNDS = 5
+
+
+def rounds_summary(r):
+    """Median, min and spread ((max - min) / median) of per-round times."""
+    m = float(np.median(r))
+    return {"rounds": len(r), "median": round(m, 3), "min": round(min(r), 3),
+            "spread": round((max(r) - min(r)) / m, 4)}
+
+
 def run_timed(torch, wl, steps, warmup):
-    """-> (seconds per step over exactly `steps` timed steps, dominant-kernel us per launch)."""
+    """-> (seconds per step over exactly `steps` timed steps, dominant-kernel us
+    per launch (the median of TIMING_ROUNDS replays), the per-round times)."""
     for i in range(warmup):
         wl.step(i)
     torch.cuda.synchronize()
@@ -497,12 +517,26 @@ def run_timed(torch, wl, steps, warmup):
     del g
     n = wl.R * max(1, -(-64 // wl.R))  # whole rotations, at least 64 launches
     gk = graph_of(torch, wl.main, n)
-    us = replay_us(torch, gk, n, reps=2)
+    rounds = [replay_us(torch, gk, n) for _ in range(TIMING_ROUNDS)]
     del gk
-    return (t1 - t0) / steps, us
+    return (t1 - t0) / steps, float(np.median(rounds)), rounds
 
 
 # ---------------------------------------------------------------- CPU baseline
+def gpu_env(torch) -> dict:
+    """The device and software the figures were measured on."""
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "rocm": rocm, "hip_runtime": torch.version.hip,
+            "torch": torch.__version__}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -655,7 +689,7 @@ def main():
         return
     if args.stream_sweep:
         calib = StreamCalib(torch)
-        for n in (9469952, 11567104, 37273600, 107652160, 265229568):
+        for n in (9469952, 11567104, 37273600, 107652160, 265229568, 1 << 30):
             t = calib.sweep(n)
             print(json.dumps({"bytes": n, "R": rotations(-(-n // 16) * 16), "us": t,
                               "best_TBs": round(n / min(t.values()) / 1e6, 3)}), flush=True)
@@ -665,7 +699,7 @@ def main():
     log("headline: decode_q4k_4096x4096")
     hd = Decode(q, torch, "q4k", 4096, 4096, seed=1, fused=True)
     parity = hd.parity()
-    sec, mv_us = run_timed(torch, hd, args.steps, args.warmup)
+    sec, mv_us, mv_rounds = run_timed(torch, hd, args.steps, args.warmup)
     value = hd.step_bytes / sec / 1e9
     achieved = hd.mv_bytes / (mv_us * 1e-6) / 1e9
     tr = traffic_record("fused_q4k")
@@ -689,9 +723,11 @@ def main():
                    "step": "qmatvec_f32 (q8_K pack inside the launch)", "step_bytes": hd.step_bytes,
                    "timing": "hip graph replay",
                    "parity": "pass" if parity else "FAIL"},
+        "env": gpu_env(torch),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
                      "kernel": HEADLINE_KERNEL, "launch_us": round(mv_us, 3),
+                     "launch_us_rounds": rounds_summary(mv_rounds),
                      "algorithmic_bytes_per_launch": hd.mv_bytes,
                      "stream_read": {"us": round(st_us, 3), "GB/s": round(hd.mv_bytes / (st_us * 1e-6) / 1e9, 2),
                                      "frac": round(st_us / mv_us, 4),
@@ -706,15 +742,25 @@ def main():
         wl = {}
         steps = max(20, min(args.steps, 100))
 
+        def oracle_fields(w, s):
+            """The oracle's time for the same step (all ncores() threads, from the
+            parity check) and the GPU step's speed-up over it."""
+            o = getattr(w, "oracle_s", None)
+            if o is None:
+                return {}
+            return {"oracle_ms": round(o * 1e3, 3), "oracle_threads": ncores(),
+                    "gpu_speedup_vs_oracle": round(o / s, 1)}
+
         def decode_entry(name, d, kernel=None):
             p = d.parity()
-            s, us = run_timed(torch, d, steps, 5)
+            s, us, r = run_timed(torch, d, steps, 5)
             gbs = d.mv_bytes / (us * 1e-6) / 1e9
             sus = calib.us(d.mv_bytes)
-            wl[name] = {"parity": "pass" if p else "FAIL", "kernel_us": round(us, 3), "GB/s": round(gbs, 1),
+            wl[name] = {"parity": "pass" if p else "FAIL", "kernel_us": round(us, 3),
+                        "kernel_us_rounds": rounds_summary(r), "GB/s": round(gbs, 1),
                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "stream_read_us": round(sus, 3),
                         "frac_stream_read": round(sus / us, 4), "step_ms": round(s * 1e3, 4),
-                        "bytes_per_launch": d.mv_bytes, "weight_copies_rotated": d.R}
+                        "bytes_per_launch": d.mv_bytes, "weight_copies_rotated": d.R, **oracle_fields(d, s)}
             if kernel:
                 wl[name]["traffic"] = traffic_record(kernel)
 
@@ -772,12 +818,13 @@ def main():
             log(f"workload: {name}")
             p = make()
             ok = p.parity()
-            s, us = run_timed(torch, p, max(10, steps // 4), 3)
+            s, us, r = run_timed(torch, p, max(10, steps // 4), 3)
             tops = p.ops / (us * 1e-6) / 1e12
             wl[name] = {
-                "parity": "pass" if ok else "FAIL", "kernel_us": round(us, 2), "TOPS": round(tops, 1),
-                "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "step_ms": round(s * 1e3, 4),
-                "ops_per_launch": p.ops, "weight_copies_rotated": p.R, "traffic": traffic_record(key)}
+                "parity": "pass" if ok else "FAIL", "kernel_us": round(us, 2), "kernel_us_rounds": rounds_summary(r),
+                "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+                "step_ms": round(s * 1e3, 4), "ops_per_launch": p.ops, "weight_copies_rotated": p.R,
+                "traffic": traffic_record(key), **oracle_fields(p, s)}
             del p
             torch.cuda.empty_cache()
         p = Prefill(q, torch)
