@@ -586,6 +586,73 @@ def cpu_baseline(budget_s: float):
             "cpu_model": cpu_model(), "one_thread": out["one_thread"], "all_cores": allc}
 
 
+def cpu_configs():
+    """The oracle on the other configurations, on this host, with one thread
+    and with all usable cores: the 32000x4096 Q6_K and the 8-expert MoE decode
+    steps (pack + product, medians of 3 runs each), and the 512-token prefill
+    (one all-core run over the full output; one thread on 16 of its 512 token
+    rows, scaled by 32).  Same shapes, seeds and input recipes as the
+    workloads; the oracle's time does not depend on the values."""
+    import oracle
+    import synth
+
+    oracle.build()
+    nth = ncores()
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)
+
+    out = {}
+    g = np.random.default_rng(2)
+    rows, K = 32000, 4096
+    w = synth.q6k_weights(g, rows, K)
+    x = synth.activations(g, 1, K)
+
+    def q6(n):
+        qs, d, bs = oracle.q8k_pack(x)
+        oracle.matvec(oracle.Q6_K, w, rows, K, qs, d, bs, nthreads=n)
+
+    t1, ta = timed(lambda: q6(1), 3), timed(lambda: q6(nth), 3)
+    out["decode_q6k_32000x4096"] = {"one_thread_ms": round(t1[1] * 1e3, 3), "all_cores_ms": round(ta[1] * 1e3, 3),
+                                     "threads": nth, "runs": "median of 3"}
+    del w
+    g = np.random.default_rng(3)
+    E, rows, K, T, topk = 8, 14336, 4096, 16, 2
+    w = synth.q4k_weights(g, E * rows, K)
+    x = synth.activations(g, T, K)
+    ids, rw = synth.moe_routing(g, T, E, topk)
+
+    def moe(n):
+        qs, d, bs = oracle.q8k_pack(x)
+        oracle.moe(oracle.Q4_K, w, E, rows, K, qs, d, bs, ids, rw, nthreads=n)
+
+    t1, ta = timed(lambda: moe(1), 3), timed(lambda: moe(nth), 3)
+    out["moe_q4k_8x14336x4096_t16_top2"] = {"one_thread_ms": round(t1[1] * 1e3, 3),
+                                             "all_cores_ms": round(ta[1] * 1e3, 3), "threads": nth,
+                                             "runs": "median of 3"}
+    del w
+    g = np.random.default_rng(4)
+    rows, K, M = 4096, 14336, 512
+    w = synth.q4k_weights(g, rows, K)
+    x = synth.activations(g, M, K)
+
+    def pf(xx, n):
+        qs, d, bs = oracle.q8k_pack(xx)
+        oracle.matvec(oracle.Q4_K, w, rows, K, qs, d, bs, nthreads=n)
+
+    ta = timed(lambda: pf(x, nth), 1)
+    t1 = timed(lambda: pf(x[:16], 1), 1)
+    out["prefill_q4k_4096x14336_m512"] = {"one_thread_ms": round(t1[0] * 32 * 1e3, 1),
+                                           "all_cores_ms": round(ta[0] * 1e3, 1), "threads": nth,
+                                           "runs": "one run each; one thread on 16 of the 512 token rows, x 32"}
+    return out
+
+
 # ---------------------------------------------------------------- profiling
 PROFILE_TARGETS = {
     "decode_q4k": "qmatvec on the 4096x4096 Q4_K decode workload",
@@ -843,6 +910,9 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        if not args.only_headline:
+            log("cpu baseline, other configurations")
+            out["cpu_baseline"]["configs"] = cpu_configs()
 
     print(json.dumps(out), flush=True)
 
