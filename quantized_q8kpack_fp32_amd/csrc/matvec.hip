@@ -288,6 +288,69 @@ __device__ __forceinline__ void q4k_first_weights(Q4Weights<Q5> (&W)[U], const u
     }
 }
 
+// RW rows of one wave from the activations in LDS: each trip reads the
+// columns' operands once and multiplies them into every row's accumulators.
+// Each row's arithmetic (and its order) is that of q4k_row_from_lds, so the
+// results are the same bits.  W[r] holds row r's weights of the first trip.
+template <int NC, int U, bool Q5, int RW>
+__device__ __forceinline__ void q4k_rows_from_lds(Q4Weights<Q5> (&W)[RW][U], const uint8_t* const (&wr)[RW], int nb,
+                                                  const int8_t* sqs, const int16_t* sbs, const float* sd, int64_t K,
+                                                  int64_t rows, const int64_t (&row)[RW], float* __restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const int ci = lane & 7, c = ci >> 1, half = ci & 1;
+    const int aoff = 64 * c + 16 * half, boff = 2 * c;
+    float acc[RW][NC];
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int t = 0; t < NC; ++t) acc[r][t] = 0.0f;
+    for (int b0 = lane >> 3; b0 - (lane >> 3) < nb; b0 += 8 * U) {
+        Q4Chunk<NC, Q5> L[RW][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int b = b0 + 8 * u;
+            const int bc = b < nb ? b : nb - 1;
+#pragma unroll
+            for (int t = 0; t < NC; ++t) {
+                const int8_t* a = sqs + t * K + bc * QK + aoff;
+                L[0][u].alo[t] = *reinterpret_cast<const int4*>(a);
+                L[0][u].ahi[t] = *reinterpret_cast<const int4*>(a + 32);
+                L[0][u].bs[t] = *reinterpret_cast<const uint32_t*>(sbs + (t * nb + bc) * 8 + boff);
+                L[0][u].d8[t] = sd[t * nb + bc];
+            }
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                if (r > 0) {
+#pragma unroll
+                    for (int t = 0; t < NC; ++t) {
+                        L[r][u].alo[t] = L[0][u].alo[t];
+                        L[r][u].ahi[t] = L[0][u].ahi[t];
+                        L[r][u].bs[t] = L[0][u].bs[t];
+                        L[r][u].d8[t] = L[0][u].d8[t];
+                    }
+                }
+                L[r][u].hdr = W[r][u].hdr;
+                L[r][u].qv = W[r][u].qv;
+                L[r][u].qh = W[r][u].qh;
+                // the next trip's weights
+                const int bn = b + 8 * U;
+                if (b0 - (lane >> 3) + 8 * U < nb) q4k_load_w(W[r][u], wr[r], bn < nb ? bn : nb - 1, ci);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+            for (int u = 0; u < U; ++u) q4k_accum(L[r][u], c, half, b0 + 8 * u < nb, acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int t = 0; t < NC; ++t) {
+            const float v = wave_sum_dpp(acc[r][t]);
+            if (lane == 0 && row[r] < rows) y[(int64_t)t * rows + row[r]] = v;
+        }
+}
+
 template <int NC, int U, bool Q5>
 __global__ __launch_bounds__(64 * fused_waves<NC>()) void matvec_f32_q4k_kernel(const uint8_t* __restrict__ w,
                                                                                  int64_t rows, int nb,
@@ -314,6 +377,13 @@ __global__ __launch_bounds__(64 * fused_waves<NC>()) void matvec_f32_q4k_kernel(
 // them there instead of each through the vector cache.  The first copy loads
 // are issued before the weights (loads complete in issue order).
 constexpr int STAGE_REGS = 4;  // 16-byte copy units per thread held across the weight loads
+// Rows per wave of the staged kernel: each wave multiplies the columns' LDS
+// operands into mv_rows_per_wave() rows, so the workgroup's one staging and
+// every operand read serve that many rows.  Two rows raise the registers per
+// wave; measured at 4096x4096 they pay for Q4_K at 3-4 columns and Q5_K from 3
+// (4-5% faster) and cost elsewhere (6-7% slower at 2 and 8 Q4_K columns).
+template <int NC, bool Q5>
+constexpr int mv_rows_per_wave() { return NC >= 3 && (Q5 || NC <= 4) ? 2 : 1; }
 template <int NC, int U, bool Q5>
 __global__ __launch_bounds__(64 * mv_waves<NC>()) void matvec_staged_q4k_kernel(
     const uint8_t* __restrict__ w, int64_t rows, int nb, const int8_t* __restrict__ qs, const float* __restrict__ d8,
@@ -322,9 +392,17 @@ __global__ __launch_bounds__(64 * mv_waves<NC>()) void matvec_staged_q4k_kernel(
     int8_t* sqs = reinterpret_cast<int8_t*>(lds);
     int16_t* sbs = reinterpret_cast<int16_t*>(lds + (int64_t)NC * K);
     float* sd = reinterpret_cast<float*>(lds + (int64_t)NC * K + 16 * NC * nb);
+    constexpr int MV_RW = mv_rows_per_wave<NC, Q5>();
     const int T = 64 * mv_waves<NC>();
-    const int64_t row = (int64_t)blockIdx.x * mv_waves<NC>() + (threadIdx.x >> 6);
-    const uint8_t* wr = w + (row < rows ? row : rows - 1) * (int64_t)nb * kblock<Q5>();
+    // wave v takes rows first + v + r * waves (r < MV_RW) of the workgroup's run
+    const int64_t first = (int64_t)blockIdx.x * mv_waves<NC>() * MV_RW;
+    int64_t row[MV_RW];
+    const uint8_t* wr[MV_RW];
+#pragma unroll
+    for (int r = 0; r < MV_RW; ++r) {
+        row[r] = first + (threadIdx.x >> 6) + (int64_t)r * mv_waves<NC>();
+        wr[r] = w + (row[r] < rows ? row[r] : rows - 1) * (int64_t)nb * kblock<Q5>();
+    }
     // codes and sums as one run of 16-byte units: NC*K/16 of codes, then NC*nb of sums
     const int ncode = (int)(NC * K / 16), nunit = ncode + NC * nb;
     auto src = [&](int u) -> uint4 {
@@ -341,8 +419,9 @@ __global__ __launch_bounds__(64 * mv_waves<NC>()) void matvec_staged_q4k_kernel(
     }
     float dv = 0.0f;
     if ((int)threadIdx.x < NC * nb) dv = d8[threadIdx.x];
-    Q4Weights<Q5> W[U];
-    q4k_first_weights<NC, U, Q5>(W, wr, nb);
+    Q4Weights<Q5> W[MV_RW][U];
+#pragma unroll
+    for (int r = 0; r < MV_RW; ++r) q4k_first_weights<NC, U, Q5>(W[r], wr[r], nb);
 #pragma unroll
     for (int i = 0; i < STAGE_REGS; ++i) {
         const int u = (int)threadIdx.x + i * T;
@@ -352,8 +431,8 @@ __global__ __launch_bounds__(64 * mv_waves<NC>()) void matvec_staged_q4k_kernel(
     if ((int)threadIdx.x < NC * nb) sd[threadIdx.x] = dv;
     for (int i = (int)threadIdx.x + T; i < NC * nb; i += T) sd[i] = d8[i];
     __syncthreads();
-    if (row >= rows) return;  // uniform per wave, after the barrier
-    q4k_row_from_lds<NC, U, Q5>(W, wr, nb, sqs, sbs, sd, K, rows, row, y);
+    if (row[0] >= rows) return;  // uniform per wave, after the barrier
+    q4k_rows_from_lds<NC, U, Q5, MV_RW>(W, wr, nb, sqs, sbs, sd, K, rows, row, y);
 }
 
 // ---------------------------------------------------------------- Q6_K ----
@@ -540,7 +619,9 @@ static void go_q4k(const uint8_t* w, int64_t rows, int nb, Acts a, float* y, hip
     constexpr int U = NC <= Q8K_MV_U2_MAXNC ? 2 : 1;
     constexpr int WV = mv_waves<NC>();
     if (NC >= Q8K_MV_STAGED_MINNC && fused_lds_bytes(NC, a.K) <= FUSED_LDS_MAX) {
-        Q8K_LAUNCH((matvec_staged_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + WV - 1) / WV)), dim3(64 * WV),
+        constexpr int RW = mv_rows_per_wave<NC, Q5>();
+        Q8K_LAUNCH((matvec_staged_q4k_kernel<NC, U, Q5>), dim3((unsigned)((rows + WV * RW - 1) / (WV * RW))),
+                   dim3(64 * WV),
                    fused_lds_bytes(NC, a.K), s, w, rows, nb, a.qs, a.d, a.bs, a.K, y);
         return;
     }
