@@ -269,6 +269,13 @@ int q8k_debug_moe_subblock_sums(int qtype, const void* w, int64_t E, int64_t row
                                 int64_t T, const int32_t* ids, const float* rw, int32_t topk, float* y, int32_t* S,
                                 void* stream);
 
+/* q8k_debug_wave_sums: the wave reduction every mat-vec ends with, on
+ * closed-form inputs ("One kernel, any device" prints the sum of 0..255,
+ * 32640, as the check of its reduce helpers).  One workgroup of 256 threads,
+ * thread t holding t: out[w] = the sum over wave w's 64 lanes (4096 w + 2016)
+ * and out[4] = the four wave sums added (32640).  out: fp32 [5]. */
+int q8k_debug_wave_sums(float* out, void* stream);
+
 /* q8k_debug_last_launches: the kernels the calling thread's last operation
  * (any call above that takes a stream) enqueued, as host kernel handles in
  * launch order: the first min(count, max) go to handles.  Returns the count.

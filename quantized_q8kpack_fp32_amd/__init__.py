@@ -21,7 +21,7 @@ __all__ = [
     "qmatmul_prefill_f32_workspace_bytes", "qmatmul_prefill_f32",
     "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe", "qmatmul_prefill_moe_noalloc",
     "Q8K_NOALLOC_SCRATCH_BYTES", "q8k_debug_subblock_sums", "q8k_debug_prefill_block_sums", "q8k_debug_moe_subblock_sums",
-    "q8k_debug_last_launches", "q8k_status_str", "q8k_last_error", "EXPORTED",
+    "q8k_debug_wave_sums", "q8k_debug_last_launches", "q8k_status_str", "q8k_last_error", "EXPORTED",
 ]
 
 Q8K_Q4_K = 1
@@ -42,7 +42,7 @@ EXPORTED = (
     "qmatmul_prefill_f32_workspace_bytes", "qmatmul_prefill_f32",
     "qmatmul_prefill_moe_workspace_bytes", "qmatmul_prefill_moe", "qmatmul_prefill_moe_noalloc",
     "q8k_debug_subblock_sums", "q8k_debug_prefill_block_sums", "q8k_debug_moe_subblock_sums",
-    "q8k_debug_last_launches", "q8k_status_str", "q8k_last_error",
+    "q8k_debug_wave_sums", "q8k_debug_last_launches", "q8k_status_str", "q8k_last_error",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -102,6 +102,8 @@ lib.q8k_debug_prefill_block_sums.restype = _INT
 lib.q8k_debug_prefill_block_sums.argtypes = [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P]
 lib.q8k_debug_moe_subblock_sums.restype = _INT
 lib.q8k_debug_moe_subblock_sums.argtypes = [_INT, _P, _I64, _I64, _I64, _P, _I64, _P, _P, ctypes.c_int32, _P, _P, _P]
+lib.q8k_debug_wave_sums.restype = _INT
+lib.q8k_debug_wave_sums.argtypes = [_P, _P]
 lib.q8k_debug_last_launches.restype = _INT
 lib.q8k_debug_last_launches.argtypes = [ctypes.POINTER(_P), _INT]
 lib.q8k_status_str.restype = ctypes.c_char_p
@@ -240,6 +242,10 @@ def q8k_debug_moe_subblock_sums(qtype: int, w, E: int, rows: int, K: int, xq, T:
                                 stream=None) -> None:
     _check(lib.q8k_debug_moe_subblock_sums(qtype, _ptr(w), E, rows, K, _ptr(xq), T, _ptr(ids), _ptr(rw), topk,
                                            _ptr(y), _ptr(S), _stream(stream)))
+
+
+def q8k_debug_wave_sums(out, stream=None) -> None:
+    _check(lib.q8k_debug_wave_sums(_ptr(out), _stream(stream)))
 
 
 def q8k_debug_last_launches() -> list:

@@ -514,6 +514,12 @@ int q8k_debug_moe_subblock_sums(int qtype, const void* w, int64_t E, int64_t row
                                              acts_of(xq, T, K), T, ids, rw, topk, y, S, (hipStream_t)stream));
 }
 
+int q8k_debug_wave_sums(float* out, void* stream) {
+    begin_call();
+    Q8K_TRY(check_ptr("q8k_debug_wave_sums", "out", out, 4));
+    return launched("q8k_debug_wave_sums", launch_wave_sums(out, (hipStream_t)stream));
+}
+
 int q8k_debug_last_launches(const void** handles, int max) {
     const int n = g_nlaunched < LAUNCH_RECORD_MAX ? g_nlaunched : LAUNCH_RECORD_MAX;
     for (int i = 0; i < n && i < max; ++i) handles[i] = g_launched[i];

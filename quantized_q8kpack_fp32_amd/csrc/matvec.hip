@@ -604,6 +604,27 @@ __global__ __launch_bounds__(256) void matvec_q6k_kernel(const uint16_t* __restr
     }
 }
 
+// Test support: the wave reduction on closed-form inputs.  Thread t of one
+// 256-thread workgroup holds t; out[w] = wave w's wave_sum_dpp (sum over its
+// 64 lanes: 4096 w + 2016) and out[4] = the four wave sums added in order
+// (sum of 0..255 = 32640), the reduction checks that the pages print.
+__global__ __launch_bounds__(256) void wave_sums_kernel(float* __restrict__ out) {
+    __shared__ float part[4];
+    const int w = threadIdx.x >> 6;
+    const float s = wave_sum_dpp((float)threadIdx.x);
+    if ((threadIdx.x & 63) == 0) {
+        out[w] = s;
+        part[w] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) out[4] = (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+hipError_t launch_wave_sums(float* out, hipStream_t s) {
+    Q8K_LAUNCH(wave_sums_kernel, dim3(1), dim3(256), 0, s, out);
+    return hipGetLastError();
+}
+
 // ----------------------------------------------------------- launchers ----
 // Q4_K: two 8-block groups per loop trip for up to Q8K_MV_U2_MAXNC columns
 // (a 4096-wide row in one trip); one group per trip for more columns, where

@@ -166,6 +166,8 @@ hipError_t launch_prefill_regw_q4k_sums(const uint8_t* w, int64_t rows, int nb, 
 // qmatvec_moe's matrix-core kernel (Q4_K, Q5_K): y [T][rows] and the sub-block
 // sums S [T * topk][rows][nb][8] of every (token, slot) pair that selects an
 // expert in [0, E) (other pairs' entries are not written).
+// The wave reduction on closed-form inputs: out [5] (four wave sums, total).
+hipError_t launch_wave_sums(float* out, hipStream_t s);
 hipError_t launch_moe_mfma_sums(bool q5, const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
                                 const int32_t* ids, const float* rw, int topk, float* y, int32_t* S, hipStream_t s);
 

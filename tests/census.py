@@ -94,7 +94,7 @@ def short(name: str) -> str:
 # error text).
 _OPS = ("q8k_pack", "q8k_bind_q6k", "qmatvec", "qmatvec_batched", "qmatvec_f32", "qmatvec_moe", "qmatmul_prefill",
         "qmatmul_prefill_f32", "qmatmul_prefill_moe", "qmatmul_prefill_moe_noalloc", "q8k_debug_subblock_sums",
-        "q8k_debug_prefill_block_sums", "q8k_debug_moe_subblock_sums")
+        "q8k_debug_prefill_block_sums", "q8k_debug_moe_subblock_sums", "q8k_debug_wave_sums")
 
 
 class _Tracked:

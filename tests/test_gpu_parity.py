@@ -91,6 +91,17 @@ def test_pack_special_blocks_bit_exact(q, K):
     assert_exact(bs, obs, "sums")
 
 
+# ================================================================== a9 wave reduction
+def test_wave_reduction_closed_form(q):
+    """The wave reduction every mat-vec ends with, on the closed form the pages
+    print for their reduce helpers: thread t of 256 holds t, each wave's sum is
+    4096 w + 2016 and the four add to 32640 (exact in fp32).  A dropped or
+    doubled lane, or a wrong DPP row step, changes a sum."""
+    out = poisoned_f32(5)
+    q.q8k_debug_wave_sums(out)
+    assert_exact(host(out), np.array([2016, 6112, 10208, 14304, 32640], np.float32), "wave sums")
+
+
 # ================================================================== a3 Q4_K decode
 @pytest.mark.parametrize("rows,K,seed", [(256, 1024, 0), (4096, 4096, 1), (37, 256, 5), (13, 768, 6),
                                          (70, 1280, 7), (9, 14336, 8)])
