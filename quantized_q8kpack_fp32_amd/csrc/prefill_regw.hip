@@ -470,34 +470,44 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         if (sg + 2 < nst) build_amin(sm, sb, sg + 2, tid);
         stage_barrier<0>();
     }
-    // quarters 1..3 hand their sums to quarter 0 (fixed order q = 0, 1, 2, 3).
-    // The lane index is read afresh (mbcnt) so that nothing lane-dependent
-    // stays live across the loop for this epilogue.
+    // The quarters meet in LDS: every wave stores its partial sums there, then
+    // wave (q, rg) adds tile t = q of row group rg over the quarters in the
+    // fixed order 0, 1, 2, 3 and stores it (register r of lane (j, g) in tile
+    // t: token 32 t + 8 (r / 4) + 4 g + r % 4, row 32 rg + j; partials move as
+    // float4 of registers 4 r4 .. 4 r4 + 3, so the 64 lanes of an access touch
+    // 1 KB of consecutive LDS).  The lane index is read afresh (mbcnt) so that
+    // nothing lane-dependent stays live across the loop for this epilogue.
     const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    float* red = reinterpret_cast<float*>(&sm.codes[0][0][0][0]);
-    if (q > 0) {
+    float4* red = reinterpret_cast<float4*>(&sm.codes[0][0][0][0]);  // [q][rg][t][r4][lane], 128 KB
+    static_assert(sizeof(sm.codes) == RW_KQ * 2 * 4 * 4 * 64 * sizeof(float4), "partials fill the code buffers");
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) red[((((q - 1) * 2 + rg) * 4 + t) * 16 + r) * 64 + ln] = acc[t][r];
-    }
+        for (int r4 = 0; r4 < 4; ++r4)
+            red[(((q * 2 + rg) * 4 + t) * 4 + r4) * 64 + ln] =
+                make_float4(acc[t][4 * r4], acc[t][4 * r4 + 1], acc[t][4 * r4 + 2], acc[t][4 * r4 + 3]);
     __syncthreads();
-    if (q == 0) {
-        const int64_t n = n0 + 32 * rg + (ln & 31);
+    const int64_t n = n0 + 32 * rg + (ln & 31);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+    for (int r4 = 0; r4 < 4; ++r4) {
+        float4 v = red[((rg * 4 + q) * 4 + r4) * 64 + ln];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int mt = 32 * t + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);  // tile row
-                float v = acc[t][r];
+        for (int qq = 1; qq < RW_KQ; ++qq) {
+            const float4 u = red[(((qq * 2 + rg) * 4 + q) * 4 + r4) * 64 + ln];
+            v.x += u.x;
+            v.y += u.y;
+            v.z += u.z;
+            v.w += u.w;
+        }
+        const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int qq = 1; qq < RW_KQ; ++qq) v += red[((((qq - 1) * 2 + rg) * 4 + t) * 16 + r) * 64 + ln];
-                if (mt < live && n < rows) {
-                    if constexpr (GATHER)
-                        y[(int64_t)gat.pair[mt] * rows + n] = v;
-                    else
-                        y[(m0 + mt) * rows + n] = v;
-                }
+        for (int e = 0; e < 4; ++e) {
+            const int mt = 32 * q + 8 * r4 + 4 * (ln >> 5) + e;  // tile row
+            if (mt < live && n < rows) {
+                if constexpr (GATHER)
+                    y[(int64_t)gat.pair[mt] * rows + n] = vv[e];
+                else
+                    y[(m0 + mt) * rows + n] = vv[e];
             }
         }
     }
