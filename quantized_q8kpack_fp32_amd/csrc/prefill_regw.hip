@@ -439,7 +439,7 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     }
     issue_codes<GATHER>(sm, S, 0, wv, lane);
     issue_aux<GATHER>(sm, S, 0, wv, lane);
-    issue_aux<GATHER>(sm, S, 1, wv, lane);
+    if (half2) issue_aux<GATHER>(sm, S, 1, wv, lane);
     if constexpr (!PACK) load_weights(R, S, q, rg, lane);
     stage_barrier<0>();
     build_amin(sm, sb, 0, tid);
@@ -456,16 +456,16 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         asm volatile("" ::"v"(__builtin_bit_cast(v4i, R.hdr)), "v"(__builtin_bit_cast(v4i, R.q[0])),
                      "v"(__builtin_bit_cast(v4i, R.q[1])), "v"(__builtin_bit_cast(v4i, R.q[2])),
                      "v"(__builtin_bit_cast(v4i, R.q[3])));
-        issue_codes<GATHER>(sm, S, sg + 1, wv, lane);
+        if (half2) issue_codes<GATHER>(sm, S, sg + 1, wv, lane);
         if (sg + 2 < nst) issue_aux<GATHER>(sm, S, sg + 2, wv, lane);
         build_q4k_planes(PL, R, lane);
         load_weights(R, S, b + RW_KQ, rg, lane);
         if (b < nbk) wave_stage<SUMS>(sm, sb, PL, sg, q, lane, acc, D, rg);
-        build_amin(sm, sb, sg + 1, tid);
+        if (half2) build_amin(sm, sb, sg + 1, tid);
         stage_barrier<RW_RAW_LOADS>();
         // ---- second 64 tokens
         if (sg + 2 < nst) issue_codes<GATHER>(sm, S, sg + 2, wv, lane);
-        if (sg + 3 < nst) issue_aux<GATHER>(sm, S, sg + 3, wv, lane);
+        if (half2 && sg + 3 < nst) issue_aux<GATHER>(sm, S, sg + 3, wv, lane);
         if (b < nbk && half2) wave_stage<SUMS>(sm, sb, PL, sg + 1, q, lane, acc, D, rg);
         if (sg + 2 < nst) build_amin(sm, sb, sg + 2, tid);
         stage_barrier<0>();
