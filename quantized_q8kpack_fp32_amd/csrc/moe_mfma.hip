@@ -160,7 +160,9 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
     MmWave<Q5>& L = sm.wave[wv];
     const MmLane<F::NL> ml = mm_lane<Q5>(lane, wrow);  // rows past `live` read zeros
     const int64_t KS = K + 16, cpt = K / 16;  // staged code row stride; 16-byte chunks of codes per token
-    const int64_t tsl = MM_TOK_BYTES / mm_tok_bytes(K);  // >= 1 (checked by the launcher)
+    // (32-bit divisions: the slab bounds K, so these fit, and 64-bit ones cost
+    // about a hundred instructions each)
+    const int tsl = MM_TOK_BYTES / (int)mm_tok_bytes(K);  // >= 1 (checked by the launcher)
     const int64_t ts = MM_SLOT / topk < tsl ? MM_SLOT / topk : tsl;  // tokens per slab
     int8_t* const tokc = sm.tok;
     int8_t* const tokb = sm.tok + ts * KS;
@@ -171,8 +173,9 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
         // ---- stage the slab's packed tokens
         {
             const int64_t nt = t1 - t0;
-            for (int64_t c = threadIdx.x; c < nt * cpt; c += 64 * MM_WAVES) {
-                const int64_t t = c / cpt, o = c - t * cpt;
+            const int ncp = (int)(nt * cpt), cp = (int)cpt;
+            for (int c = threadIdx.x; c < ncp; c += 64 * MM_WAVES) {
+                const int t = c / cp, o = c - t * cp;
                 *reinterpret_cast<v4i*>(tokc + t * KS + 16 * o) =
                     *reinterpret_cast<const v4i*>(qs + (t0 + t) * K + 16 * o);
             }

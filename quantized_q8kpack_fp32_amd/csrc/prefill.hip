@@ -596,18 +596,22 @@ __global__ __launch_bounds__(512) void prefill_q4k_kernel(const uint8_t* __restr
                                                           float* __restrict__ y, int32_t* __restrict__ Isum,
                                                           int ksplit, PackDst pk) {
     __shared__ __attribute__((aligned(16))) PrefillSmem<F> sm;
-    const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
-    const int64_t ntm = (M + PF_TM - 1) / PF_TM;
-    const int64_t tile = (int64_t)blockIdx.x % (ntn * ntm);
-    const int64_t n0 = (tile % ntn) * PF_TN;
-    const int64_t m0 = (tile / ntn) * PF_TM;
-    const int ks = (int)((int64_t)blockIdx.x / (ntn * ntm));
+    // (tile counts are below 2^31, as the grid is: 32-bit divisions, which
+    // cost far fewer scalar instructions ahead of the first load)
+    const uint32_t ntn = (uint32_t)((rows + PF_TN - 1) / PF_TN);
+    const uint32_t ntm = (uint32_t)((M + PF_TM - 1) / PF_TM);
+    const uint32_t ks32 = blockIdx.x / (ntn * ntm);
+    const uint32_t tile = blockIdx.x - ks32 * (ntn * ntm);
+    const uint32_t tm = tile / ntn, tn = tile - tm * ntn;
+    const int64_t n0 = (int64_t)tn * PF_TN;
+    const int64_t m0 = (int64_t)tm * PF_TM;
+    const int ks = (int)ks32;
     const int per = (nb + ksplit - 1) / ksplit;
     const int kb0 = ks * per;
     const int nbk = nb - kb0 < per ? nb - kb0 : per;
     y += (int64_t)ks * M * rows;
     if constexpr (PACK)
-        pack_group<512>(pk, nb, M, PF_TM, m0, kb0, nbk, tile % ntn, ntn, ks * ntm + tile / ntn, (int)threadIdx.x);
+        pack_group<512>(pk, nb, M, PF_TM, m0, kb0, nbk, tn, ntn, (int64_t)ks * ntm + tm, (int)threadIdx.x);
     // Only producers use the sources.  Q6_K: every thread builds them, outside a
     // branch on the thread index, so their wave-uniform parts stay scalar (2%
     // faster); Q5_K measured 4% slower that way and builds them in the
@@ -737,10 +741,10 @@ __global__ __launch_bounds__(512) void prefill_moe_q4k_kernel(const uint8_t* __r
     __shared__ __attribute__((aligned(16))) PrefillSmem<F> sm;
     __shared__ int tok[PF_TM];   // token of each tile row, -1 past the chunk's end
     __shared__ int pair[PF_TM];  // pair index of each tile row
-    const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
-    const int64_t c = (int64_t)blockIdx.x / ntn;
-    if (c >= nchunks[0]) return;  // uniform: the grid covers the most chunks P pairs can make
-    const int64_t n0 = ((int64_t)blockIdx.x % ntn) * PF_TN;
+    const uint32_t ntn = (uint32_t)((rows + PF_TN - 1) / PF_TN);
+    const uint32_t c = blockIdx.x / ntn;
+    if ((int64_t)c >= nchunks[0]) return;  // uniform: the grid covers the most chunks P pairs can make
+    const int64_t n0 = (int64_t)(blockIdx.x - c * ntn) * PF_TN;
     const int4 ch = chunks[c];
     const int count = ch.z;
     for (int i = threadIdx.x; i < PF_TM; i += 512) {
@@ -769,9 +773,10 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
                                                           const float* __restrict__ rw, int topk, int64_t E,
                                                           float* __restrict__ y) {
     typedef float fv __attribute__((ext_vector_type(V)));
-    const int64_t nrb = (rows + 256 * V - 1) / (256 * V);
-    const int64_t t = (int64_t)blockIdx.x / nrb;
-    const int64_t r = ((int64_t)blockIdx.x % nrb * 256 + threadIdx.x) * V;
+    const uint32_t nrb = (uint32_t)((rows + 256 * V - 1) / (256 * V));  // the grid is below 2^31
+    const uint32_t tt = blockIdx.x / nrb;
+    const int64_t t = tt;
+    const int64_t r = ((int64_t)(blockIdx.x - tt * nrb) * 256 + threadIdx.x) * V;
     if (r >= rows) return;
     fv s = {};
     for (int k = 0; k < topk; ++k) {

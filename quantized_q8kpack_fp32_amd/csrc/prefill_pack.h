@@ -39,20 +39,23 @@ __device__ __forceinline__ void pack_share(const PackDst& P, int nb, int64_t m0,
                                            int64_t member, int64_t members, int tid) {
     constexpr int ROWS = THREADS / 16;  // blocks per round
     constexpr int U = 4;                // rounds in flight
-    const int64_t total = live * nbk;
-    const int64_t per = (total + members - 1) / members;
-    const int64_t i0 = member * per;
-    const int64_t i1 = i0 + per < total ? i0 + per : total;
+    // block indices inside the group stay below 2^31 (at most a token tile
+    // times the blocks of a row), so they are divided in 32 bits
+    const int total = (int)live * nbk;
+    const int per = (total + (int)members - 1) / (int)members;
+    const int i0 = (int)member * per;
+    const int i1 = i0 + per < total ? i0 + per : total;
     const int r = tid & 15;
-    for (int64_t ib = i0 + (tid >> 4); ib < i1; ib += (int64_t)U * ROWS) {
+    for (int ib = i0 + (tid >> 4); ib < i1; ib += U * ROWS) {
         float4 v[U][4];
         int64_t blk[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t i = ib + (int64_t)u * ROWS;  // the same for the 16 lanes of a row
+            const int i = ib + u * ROWS;  // the same for the 16 lanes of a row
             blk[u] = -1;
             if (i < i1) {
-                blk[u] = (m0 + i / nbk) * nb + kb0 + i % nbk;
+                const int tok = i / nbk;
+                blk[u] = (m0 + tok) * nb + kb0 + (i - tok * nbk);
                 const float4* src = reinterpret_cast<const float4*>(P.x + blk[u] * QK + 16 * r);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[u][e] = src[e];

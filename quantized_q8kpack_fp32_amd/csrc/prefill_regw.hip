@@ -368,12 +368,18 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     // fetched into one L2 (measured: fewer L2 misses and faster than giving
     // each XCD one token tile).
     // (gathered tiles: workgroup = (chunk, row tile), no split)
-    const int64_t ntn = (rows + RW_TN - 1) / RW_TN;
-    const int64_t ntm = GATHER ? 1 : (M + RW_TM - 1) / RW_TM;
-    const int64_t tile = GATHER ? (int64_t)blockIdx.x : (int64_t)blockIdx.x % (ntn * ntm);
-    const int64_t n0 = (tile % ntn) * RW_TN, m0 = (tile / ntn) * RW_TM;
+    // The tile counts are below 2^31 (the grid is), so the workgroup index is
+    // split with 32-bit divisions: 64-bit ones cost a few hundred scalar
+    // instructions ahead of the first load.
+    const uint32_t ntn = (uint32_t)((rows + RW_TN - 1) / RW_TN);
+    const uint32_t ntm = GATHER ? 1u : (uint32_t)((M + RW_TM - 1) / RW_TM);
+    const uint32_t bid = blockIdx.x;
+    const uint32_t ks32 = GATHER ? 0u : bid / (ntn * ntm);
+    const uint32_t tile = bid - ks32 * (ntn * ntm);
+    const uint32_t tm = tile / ntn, tn = tile - tm * ntn;  // token tile (gathered: chunk), row tile
+    const int64_t n0 = (int64_t)tn * RW_TN, m0 = GATHER ? 0 : (int64_t)tm * RW_TM;
     // this workgroup's blocks [kb0, kb0 + nbk) (all of them without split-K)
-    const int ks = GATHER ? 0 : (int)((int64_t)blockIdx.x / (ntn * ntm));
+    const int ks = (int)ks32;
     const int per = (nb + ksplit - 1) / ksplit;
     const int kb0 = ks * per;
     const int nbk = nb - kb0 < per ? nb - kb0 : per;
@@ -386,7 +392,7 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     S.tokoff = gat.tokoff;
     int64_t live;  // tokens of the tile
     if constexpr (GATHER) {
-        const int64_t c = (int64_t)blockIdx.x / ntn;
+        const int64_t c = tm;
         if (c >= *nchunks) return;  // the whole workgroup
         const int4 ch = chunks[c];
         live = ch.z;
@@ -435,7 +441,7 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         // are loaded first; then this workgroup packs its share of the tile's
         // blocks and waits for the rest of its group (prefill_pack.h)
         load_weights(R, S, q, rg, lane);
-        pack_group<RW_THREADS>(pk, nb, M, RW_TM, m0, kb0, nbk, tile % ntn, ntn, ks * ntm + tile / ntn, tid);
+        pack_group<RW_THREADS>(pk, nb, M, RW_TM, m0, kb0, nbk, tn, ntn, (int64_t)ks * ntm + tm, tid);
     }
     issue_codes<GATHER>(sm, S, 0, wv, lane);
     issue_aux<GATHER>(sm, S, 0, wv, lane);
