@@ -391,24 +391,32 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     S.wrow = nb * Q4K_BLOCK;
     S.tokoff = gat.tokoff;
     int64_t live;  // tokens of the tile
+    Q4kRaw R;
     if constexpr (GATHER) {
         const int64_t c = tm;
         if (c >= *nchunks) return;  // the whole workgroup
         const int4 ch = chunks[c];
         live = ch.z;
-        // rows past the chunk's count repeat its first pair (never stored)
-        for (int m = tid; m < RW_TM; m += RW_THREADS) {
-            const int p = order[ch.y + (m < ch.z ? m : 0)];
-            gat.pair[m] = p;
-            gat.tokoff[m] = (int)((int64_t)(p / topk) * K);
-        }
         S.w = w + ((int64_t)ch.x * rows + n0) * S.wrow;
+        S.wlast = last_of((rows - n0) * S.wrow);
         S.x = qs;
         S.xlast = last_of(M * K);
         S.d8 = d8;
         S.d8last = last_of(M * nb * 4);
         S.bs = bs;
         S.bslast = last_of(M * nb * 16);
+        // The tile's pair indices, then its first weights: the weights (from
+        // HBM) stay in flight while the indices land and the token offsets go
+        // to LDS (loads complete in issue order, so the indices are issued
+        // first).  Rows past the chunk's count repeat its first pair (never
+        // stored).
+        static_assert(RW_TM <= RW_THREADS, "one pair index per thread");
+        const int p = tid < RW_TM ? order[ch.y + (tid < ch.z ? tid : 0)] : 0;
+        load_weights(R, S, q, rg, lane);
+        if (tid < RW_TM) {
+            gat.pair[tid] = p;
+            gat.tokoff[tid] = (int)((int64_t)(p / topk) * K);
+        }
         __syncthreads();
     } else {
         // sources start at block kb0 of the tile's first token / row; the
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
         S.bs = bs + (m0 * nb + kb0) * 8;
         S.bslast = last_of(((M - m0) * nb - kb0) * 16);
     }
-    S.wlast = last_of((rows - n0) * S.wrow - (GATHER ? 0 : (int64_t)kb0 * Q4K_BLOCK));
+    if constexpr (!GATHER) S.wlast = last_of((rows - n0) * S.wrow - (int64_t)kb0 * Q4K_BLOCK);
     RwSums D{};
     if constexpr (SUMS) D = RwSums{Isum + (m0 * rows + n0) * nb, rows, live, rows - n0, nb};
 
@@ -435,7 +443,6 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 
-    Q4kRaw R;
     if constexpr (PACK) {
         // fp32 tokens: the first weights (which do not depend on the tokens)
         // are loaded first; then this workgroup packs its share of the tile's
@@ -446,7 +453,7 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     issue_codes<GATHER>(sm, S, 0, wv, lane);
     issue_aux<GATHER>(sm, S, 0, wv, lane);
     if (half2) issue_aux<GATHER>(sm, S, 1, wv, lane);
-    if constexpr (!PACK) load_weights(R, S, q, rg, lane);
+    if constexpr (!PACK && !GATHER) load_weights(R, S, q, rg, lane);
     stage_barrier<0>();
     build_amin(sm, sb, 0, tid);
     stage_barrier<0>();
