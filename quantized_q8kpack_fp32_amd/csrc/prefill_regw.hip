@@ -500,27 +500,44 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
             red[(((q * 2 + rg) * 4 + t) * 4 + r4) * 64 + ln] =
                 make_float4(acc[t][4 * r4], acc[t][4 * r4 + 1], acc[t][4 * r4 + 2], acc[t][4 * r4 + 3]);
     __syncthreads();
-    const int64_t n = n0 + 32 * rg + (ln & 31);
+    // The sums go back to LDS as [token][row] (the partials are read: one
+    // barrier) and leave as 16-byte stores, four rows of one token per lane.
+    float4 v[4];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-        float4 v = red[((rg * 4 + q) * 4 + r4) * 64 + ln];
+        v[r4] = red[((rg * 4 + q) * 4 + r4) * 64 + ln];
 #pragma unroll
         for (int qq = 1; qq < RW_KQ; ++qq) {
             const float4 u = red[(((qq * 2 + rg) * 4 + q) * 4 + r4) * 64 + ln];
-            v.x += u.x;
-            v.y += u.y;
-            v.z += u.z;
-            v.w += u.w;
+            v[r4].x += u.x;
+            v[r4].y += u.y;
+            v[r4].z += u.z;
+            v[r4].w += u.w;
         }
-        const float vv[4] = {v.x, v.y, v.z, v.w};
+    }
+    __syncthreads();
+    float* out = reinterpret_cast<float*>(&sm.codes[0][0][0][0]);  // [RW_TM][RW_TN]
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int mt = 32 * q + 8 * r4 + 4 * (ln >> 5) + e;  // tile row
-            if (mt < live && n < rows) {
-                if constexpr (GATHER)
-                    y[(int64_t)gat.pair[mt] * rows + n] = vv[e];
-                else
-                    y[(m0 + mt) * rows + n] = vv[e];
+    for (int r4 = 0; r4 < 4; ++r4) {
+        const float vv[4] = {v[r4].x, v[r4].y, v[r4].z, v[r4].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            out[(32 * q + 8 * r4 + 4 * (ln >> 5) + e) * RW_TN + 32 * rg + (ln & 31)] = vv[e];
+    }
+    __syncthreads();
+    // lane l of wave wv: rows 4 (l & 15) .. +3 of tokens 16 wv + 4 k + (l >> 4)
+    const int64_t n = n0 + 4 * (ln & 15);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int mt = 16 * wv + 4 * k + (ln >> 4);  // tile row
+        const float4 o = *reinterpret_cast<const float4*>(&out[mt * RW_TN + 4 * (ln & 15)]);
+        if (mt < live && n < rows) {
+            float* dst = GATHER ? y + (int64_t)gat.pair[mt] * rows + n : y + (m0 + mt) * rows + n;
+            if (n + 4 <= rows && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                *reinterpret_cast<float4*>(dst) = o;
+            } else {
+                const float oo[4] = {o.x, o.y, o.z, o.w};
+                for (int e = 0; e < 4 && n + e < rows; ++e) dst[e] = oo[e];
             }
         }
     }
