@@ -485,7 +485,7 @@ __global__ __launch_bounds__(RW_THREADS) void prefill_regw_q4k_kernel(
     }
     // The quarters meet in LDS: every wave stores its partial sums there, then
     // wave (q, rg) adds tile t = q of row group rg over the quarters in the
-    // fixed order 0, 1, 2, 3 and stores it (register r of lane (j, g) in tile
+    // fixed order 0, 1, 2, 3 (register r of lane (j, g) in tile
     // t: token 32 t + 8 (r / 4) + 4 g + r % 4, row 32 rg + j; partials move as
     // float4 of registers 4 r4 .. 4 r4 + 3, so the 64 lanes of an access touch
     // 1 KB of consecutive LDS).  The lane index is read afresh (mbcnt) so that
