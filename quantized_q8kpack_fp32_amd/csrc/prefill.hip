@@ -570,13 +570,36 @@ __device__ __forceinline__ void prefill_tile(PrefillSmem<F>& sm, const PrefillSr
             consumer_block<F, SUMS>(sm.buf[b & 1], lane, rg, tg0, accf, accj, D, b);
             lds_barrier();
         }
-        const int64_t n = n0 + 32 * rg + (lane & 31);
+        // the results to LDS as [token][row] (the buffers are free after the
+        // last block's barrier)
+        float* out = reinterpret_cast<float*>(&sm.buf[0]);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = tg0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (ok(m) && n < rows) y[orow(m) * rows + n] = F == PF_Q6 ? accf[i][r] : accf[i][r] - accj[i][r];
+                out[m * PF_TN + 32 * rg + (lane & 31)] = F == PF_Q6 ? accf[i][r] : accf[i][r] - accj[i][r];
+            }
+        }
+    }
+    // Every wave stores: lane l of wave wv takes rows 4 (l & 15) .. +3 of
+    // tokens 16 wv + 4 k + (l >> 4), one 16-byte store each (4-byte stores
+    // for a ragged or unaligned row end).
+    lds_barrier();
+    static_assert(sizeof(PrefillBuf<F>) >= PF_TM * PF_TN * sizeof(float), "the results fit one buffer");
+    const float* out = reinterpret_cast<const float*>(&sm.buf[0]);
+    const int64_t n = n0 + 4 * (lane & 15);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int m = 16 * wv + 4 * k + (lane >> 4);
+        const float4 o = *reinterpret_cast<const float4*>(&out[m * PF_TN + 4 * (lane & 15)]);
+        if (ok(m) && n < rows) {
+            float* dst = y + orow(m) * rows + n;
+            if (n + 4 <= rows && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                *reinterpret_cast<float4*>(dst) = o;
+            } else {
+                const float oo[4] = {o.x, o.y, o.z, o.w};
+                for (int e = 0; e < 4 && n + e < rows; ++e) dst[e] = oo[e];
             }
         }
     }
