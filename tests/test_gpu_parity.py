@@ -566,6 +566,29 @@ def run_prefill(q, fmt, w, rows, K, x):
 
 
 @pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
+def test_prefill_output_four_byte_aligned(q, fmt):
+    """y one float past a 16-byte boundary, with enough tiles that K is not
+    split (the tiles store y themselves): their 16-byte result stores fall
+    back to 4-byte stores.  Every output against the oracle (the last token
+    tile ragged, 44 tokens), and the floats on either side of y keep their
+    poison."""
+    M, rows, K = 300, 5508, 256  # 3 x 87 = 261 tiles: no split
+    w = _PF_FMT[fmt][2](np.random.default_rng(96), rows, K)
+    x = acts(96, M, K)
+    qt = getattr(q, _PF_FMT[fmt][0])
+    assert q.qmatmul_prefill_workspace_bytes(qt, rows, K, M) == 0
+    buf = poisoned_f32(M * rows + 2)
+    y = buf[1:1 + M * rows]
+    assert y.data_ptr() % 16 == 4
+    q.qmatmul_prefill(qt, pf_weights(q, fmt, w, rows, K), rows, K, pack_on_device(q, x), M, y, None, 0)
+    b = host(buf)
+    oqs, od, obs = oracle.q8k_pack(x)
+    want, A = oracle.matvec(_PF_FMT[fmt][1], w, rows, K, oqs, od, obs, nthreads=NTH)
+    assert_close(b[1:1 + M * rows].reshape(M, rows), want, A, f"prefill {fmt} into a 4-byte aligned y")
+    assert b[:1].view(np.uint32)[0] == 0xFFFFFFFF and b[-1:].view(np.uint32)[0] == 0xFFFFFFFF
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,rows,K,seed", [(1, 64, 256, 41), (17, 100, 512, 42), (64, 64, 256, 43),
                                            (127, 256, 1024, 44), (200, 130, 768, 45), (65, 4096, 256, 46)])
 def test_prefill_full(q, fmt, M, rows, K, seed):
