@@ -54,8 +54,7 @@ __global__ __launch_bounds__(CAL_THREADS) void stream_read_kernel(const uint4* _
 }
 
 constexpr int CAL_VARIANTS = 6;
-constexpr int CAL_U[CAL_VARIANTS] = {1, 2, 4, 8, 2, 4};
-constexpr bool CAL_NT[CAL_VARIANTS] = {false, false, false, false, true, true};
+constexpr int CAL_U[CAL_VARIANTS] = {1, 2, 4, 8, 2, 4};  // loads per lane; variants 4 and 5 non-temporal
 constexpr int64_t CAL_GRID_CAP = 8192;
 
 int64_t workgroups(int64_t bytes, int variant) {

@@ -791,7 +791,7 @@ __global__ __launch_bounds__(512) void prefill_moe_q4k_kernel(const uint8_t* __r
 // a multiple of 4 and y 16-byte aligned: 16-byte loads and stores); the
 // token's ids and router weights are the same for all its threads.
 template <int V>
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ out, int64_t rows, int64_t T,
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ out, int64_t rows,
                                                           const int32_t* __restrict__ ids,
                                                           const float* __restrict__ rw, int topk, int64_t E,
                                                           float* __restrict__ y) {
@@ -821,20 +821,22 @@ hipError_t launch_prefill_moe(int fmt, const uint8_t* w, const uint16_t* prefix,
     Q8K_LAUNCH(moe_group_kernel, dim3(1), dim3(1024), 0, s, ids, L.P, (int)E, nchunks, chunks, order);
     const int64_t ntn = (rows + PF_TN - 1) / PF_TN;
     const dim3 grid((unsigned)(L.max_chunks * ntn));
-    if (fmt == PF_Q4)
-        launch_prefill_regw_moe_q4k(w, rows, nb, a, T, L.max_chunks, nchunks, chunks, order, topk, out, s);
-    else if (fmt == PF_Q6)
+    if (fmt == PF_Q4) {
+        const hipError_t e = launch_prefill_regw_moe_q4k(w, rows, nb, a, T, L.max_chunks, nchunks, chunks, order,
+                                                         topk, out, s);
+        if (e != hipSuccess) return e;
+    } else if (fmt == PF_Q6)
         Q8K_LAUNCH(prefill_moe_q4k_kernel<PF_Q6>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K, T,
                    nchunks, chunks, order, topk, out);
     else if (fmt == PF_Q5)
         Q8K_LAUNCH(prefill_moe_q4k_kernel<PF_Q5>, grid, dim3(512), 0, s, w, prefix, rows, nb, a.qs, a.d, a.bs, a.K, T,
                    nchunks, chunks, order, topk, out);
     if (rows % 4 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0)
-        Q8K_LAUNCH(moe_combine_kernel<4>, dim3((unsigned)(T * ((rows + 1023) / 1024))), dim3(256), 0, s, out, rows, T,
+        Q8K_LAUNCH(moe_combine_kernel<4>, dim3((unsigned)(T * ((rows + 1023) / 1024))), dim3(256), 0, s, out, rows,
                    ids, rw, topk, E, y);
     else
-        Q8K_LAUNCH(moe_combine_kernel<1>, dim3((unsigned)(T * ((rows + 255) / 256))), dim3(256), 0, s, out, rows, T,
-                   ids, rw, topk, E, y);
+        Q8K_LAUNCH(moe_combine_kernel<1>, dim3((unsigned)(T * ((rows + 255) / 256))), dim3(256), 0, s, out, rows, ids,
+                   rw, topk, E, y);
     return hipGetLastError();
 }
 
