@@ -20,7 +20,7 @@ the five interleaved rounds / medians of its section 4.2):
   * the dominant kernel's per-launch duration comes from HIP events on the
     stream it runs on, bracketing a replayed graph of back-to-back launches
     of that kernel alone (rotating weight copies);
-  * a workload's numbers are reported together with its parity verdict
+  * a workload's numbers are reported together with its parity result
     against the CPU oracle, computed in the same run.
 
 The CPU baseline is the oracle as it stands (plain C, not tuned), timed on
@@ -740,8 +740,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
-              "multi-GPU sharding is described in the design notes but not built", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (--gpus {args.gpus} requested); "
+              "sharding across GPUs is described in the design notes but not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch
