@@ -30,7 +30,11 @@
 // reads, so the only vector-memory loads in flight during the block walk are
 // the weight blocks, and each wave keeps the next one in flight while it
 // multiplies the current one (vector loads complete in issue order, so token
-// loads interleaved with them would be waited for with every block).  An expert nobody
+// loads interleaved with them would be waited for with every block).  The
+// slab, the ids and the router weights reach LDS through buffer-unit copies,
+// and each walk's first block is fetched into the cache ahead of the walk
+// (during the staging, and across the previous tile's barrier and slot sums),
+// so no walk starts on a cold memory latency.  An expert nobody
 // chose is never read; an id outside [0, E) matches no expert and its slot is
 // skipped.
 #include "q4k_planes.h"  // vector types, bf16 split
@@ -77,6 +81,8 @@ template <bool Q5>
 struct MmSmem {
     MmWave<Q5> wave[MM_WAVES];
     float slot[MM_SLOT * MM_ROWS];  // dot of (pair, row), pair-major
+    int32_t sid[MM_SLOT];           // the slab's expert ids and router weights, by pair
+    float srw[MM_SLOT];
     // slab tokens: codes [ts][K + 16], then sums [ts][K / 32] int16, then scales [ts][K / 256] fp32
     int8_t tok[MM_TOK_BYTES];
 };
@@ -137,6 +143,36 @@ __device__ __forceinline__ void mm_wait_w(MmW<6>& W) {
                  : "n"(N));
 }
 
+// Buffer-unit copies straight into LDS: 16 (4) bytes per lane land at
+// base + 16 (4) * lane (M0 holds the LDS base, with one wait state between
+// writing M0 and the copy).  No register receives the data, so a copy may stay
+// in flight across barriers and loops; a vmcnt wait covers it.  A partial copy
+// runs on the lowest lanes only.  mm_issue_tile copies a block into the wave's
+// tile in the register loads' lane map (the last copy's upper half-wave would
+// repeat the lower one past the tile, so it runs on lanes 0-31).
+typedef __attribute__((address_space(3))) void mm_lds_void;
+__device__ __forceinline__ void mm_dma16(rsrc_t r, void* lds_base, int off) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"((uint32_t)(uintptr_t)(mm_lds_void*)lds_base), "v"(off), "s"(r)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void mm_dma4(rsrc_t r, void* lds_base, int off) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"((uint32_t)(uintptr_t)(mm_lds_void*)lds_base), "v"(off), "s"(r)
+                 : "memory", "m0");
+}
+template <bool Q5>
+__device__ __forceinline__ void mm_issue_tile(uint8_t* tile, rsrc_t wr, const MmLane<MmFmt<Q5>::NL>& m, int lane,
+                                              int b) {
+    using F = MmFmt<Q5>;
+    const int boff = b * F::BLK;
+#pragma unroll
+    for (int x = 0; x < F::NL - 1; ++x) mm_dma16(wr, tile + 1024 * x, m.go[x] + boff);
+    if (lane < 32) mm_dma16(wr, tile + 1024 * (F::NL - 1), m.go[F::NL - 1] + boff);
+}
+
 // The wave hands data between its own lanes through LDS.  The hardware runs
 // one wave's LDS instructions in order, but the compiler reasons per thread:
 // the memory clobbers keep a lane's reads behind the other lanes' writes and
@@ -167,33 +203,68 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
     int8_t* const tokc = sm.tok;
     int8_t* const tokb = sm.tok + ts * KS;
     float* const tokd = reinterpret_cast<float*>(sm.tok + ts * KS + ts * cpt);
+    // expert e's rows of a tile (rows past the tile's live rows read zeros)
+    auto tile_rsrc = [&](int64_t tile, int64_t e) {
+        const int64_t r0 = tile * rt;
+        const int64_t live = rows - r0 < rt ? rows - r0 : rt;
+        return make_rsrc(w + (e * rows + r0) * wrow, live * wrow);
+    };
+    // Each wave's first walk of a tile (expert wv) finds its first block in the
+    // cache: the block is copied into the wave's tile ahead (at the start of a
+    // slab, before the staging; at the end of the previous tile's walks, across
+    // the barrier and the slot sums).  The walk then loads it again into
+    // registers, a cache hit, and overwrites the tile only after waiting for its
+    // own load, which is younger than the copy.
     for (int64_t t0 = 0; t0 < T; t0 += ts) {
         const int64_t t1 = t0 + ts < T ? t0 + ts : T;
         const int64_t pb = t0 * topk, pe = t1 * topk;
-        // ---- stage the slab's packed tokens
+        // ---- stage the slab's packed tokens, ids and router weights with
+        // buffer-unit copies (waves take copies w, w + MM_WAVES, ...); then the
+        // first block of this wave's first walk, and a wait for everything but
+        // that block: the staging never waits for the weight fetch.
         {
-            const int64_t nt = t1 - t0;
-            const int ncp = (int)(nt * cpt), cp = (int)cpt;
-            for (int c = threadIdx.x; c < ncp; c += 64 * MM_WAVES) {
-                const int t = c / cp, o = c - t * cp;
-                *reinterpret_cast<v4i*>(tokc + t * KS + 16 * o) =
-                    *reinterpret_cast<const v4i*>(qs + (t0 + t) * K + 16 * o);
+            const int nt = (int)(t1 - t0), cp = (int)cpt, nbt = nt * nb, np = (int)(pe - pb);
+            const int ipt = (cp + 63) >> 6;  // copies per token (64 chunks of 16 bytes each)
+            const rsrc_t rq = make_rsrc(qs + t0 * K, (int64_t)nt * K);
+            for (int g = wv; g < nt * ipt; g += MM_WAVES) {
+                const int t = g / ipt, i = g - t * ipt, c = 64 * i + lane;
+                if (c < cp) mm_dma16(rq, tokc + t * KS + 1024 * i, t * (int)K + 16 * c);
             }
             // sums: one 16-byte chunk per block; scales: one fp32 per block
-            for (int64_t c = threadIdx.x; c < nt * nb; c += 64 * MM_WAVES) {
-                *reinterpret_cast<v4i*>(tokb + 16 * c) = *reinterpret_cast<const v4i*>(bs + (t0 * nb + c) * 8);
-                tokd[c] = d8[t0 * nb + c];
+            const rsrc_t rb = make_rsrc(bs + t0 * nb * 8, (int64_t)nbt * 16);
+            const rsrc_t rd = make_rsrc(d8 + t0 * nb, (int64_t)nbt * 4);
+            for (int g = wv; g < (nbt + 63) >> 6; g += MM_WAVES) {
+                const int c = 64 * g + lane;
+                if (c < nbt) {
+                    mm_dma16(rb, tokb + 1024 * g, 16 * c);
+                    mm_dma4(rd, tokd + 64 * g, 4 * c);
+                }
             }
+            const rsrc_t ri = make_rsrc(ids + pb, (int64_t)np * 4);
+            const rsrc_t rr = make_rsrc(rw + pb, (int64_t)np * 4);
+            for (int g = wv; g < (np + 63) >> 6; g += MM_WAVES) {
+                const int c = 64 * g + lane;
+                if (c < np) {
+                    mm_dma4(ri, sm.sid + 64 * g, 4 * c);
+                    mm_dma4(rr, sm.srw + 64 * g, 4 * c);
+                }
+            }
+        }
+        if (wv < E) {
+            mm_issue_tile<Q5>(L.tile, tile_rsrc(blockIdx.x, wv), ml, lane, 0);  // grid <= ntiles
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(F::NL) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         __syncthreads();
         for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
             const int64_t r0 = tile * rt;
             const int64_t live = rows - r0 < rt ? rows - r0 : rt;  // rows of this tile
             for (int64_t e = wv; e < E; e += MM_WAVES) {
-                const rsrc_t wr = make_rsrc(w + (e * rows + r0) * wrow, live * wrow);
+                const rsrc_t wr = tile_rsrc(tile, e);
                 for (int64_t p0 = pb; p0 < pe; p0 += 64) {
                     const int64_t p = p0 + lane;
-                    const bool hit = p < pe && ids[p] == (int32_t)e;
+                    const bool hit = p < pe && sm.sid[p - pb] == (int32_t)e;
                     const uint64_t mask = __ballot(hit);
                     if (mask == 0) continue;
                     const int count = __popcll(mask);
@@ -352,6 +423,13 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
                     }
                 }
             }
+            // the next tile's first block for this wave's first expert, fetched
+            // while the workgroup meets and adds its slots (this wave's reads of
+            // the tile are done: every step ends with an LDS wait)
+            if (wv < E && tile + gridDim.x < ntiles) {
+                wave_lds_fence();
+                mm_issue_tile<Q5>(L.tile, tile_rsrc(tile + gridDim.x, wv), ml, lane, 0);
+            }
             __syncthreads();
             // ---- each token's slots, added in slot order
             for (int idx = threadIdx.x; idx < (int)(t1 - t0) * MM_ROWS; idx += 64 * MM_WAVES) {
@@ -361,8 +439,8 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
                     float s = 0.0f;
                     for (int k = 0; k < topk; ++k) {
                         const int64_t pp = t * topk + k;
-                        const int32_t id = ids[pp];
-                        if (id >= 0 && id < E) s += rw[pp] * sm.slot[(pp - pb) * MM_ROWS + r];
+                        const int32_t id = sm.sid[pp - pb];
+                        if (id >= 0 && id < E) s += sm.srw[pp - pb] * sm.slot[(pp - pb) * MM_ROWS + r];
                     }
                     y[t * rows + r0 + r] = s;
                 }
@@ -370,6 +448,9 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
             __syncthreads();
         }
     }
+    // a copy ahead for a walk that did not come (an expert nobody chose)
+    // lands before the wave ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace
