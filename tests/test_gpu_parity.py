@@ -438,6 +438,9 @@ def moe_case(q, fmt, E, rows, K, T, topk, seed, ids=None):
     ("q5k", 1, 29, 256, 3, 1, 43),         # one expert, one slot, fewer rows than a tile
     ("q5k", 2, 40, 88064, 3, 2, 40),       # one packed token per LDS stage: a slab per token
     ("q5k", 2, 40, 131072, 3, 2, 41),      # a packed token beyond the LDS stage: one lane per row
+    # more row tiles than compute units (two per workgroup) and two slabs of tokens (32, then 8)
+    ("q4k", 4, 8200, 256, 40, 4, 44),
+    ("q5k", 4, 8200, 256, 40, 4, 45),
 ])
 def test_moe(q, fmt, E, rows, K, T, topk, seed):
     got, w, ot, oqs, od, obs, ids, rw = moe_case(q, fmt, E, rows, K, T, topk, seed)
