@@ -4,7 +4,8 @@ Every source is compiled for gfx950 only, with packed FP32 instructions
 disabled, and the kernel resource report of each translation unit is checked:
 a kernel that uses scratch (spills) fails the build, since a spilling kernel is
 not a tuned kernel (the build gate idea of "One kernel, any device", section
-2.2).  Usage: ``python quantized_q8kpack_fp32_amd/build.py`` (or via
+2.2).  Sources that load registers with inline assembly also have their device
+assembly checked (ASM_LOAD_CHECKED).  Usage: ``python quantized_q8kpack_fp32_amd/build.py`` (or via
 ``__graft_entry__.build()``).
 """
 from __future__ import annotations
@@ -87,11 +88,101 @@ def _check_scratch(log: str, src: str) -> list[str]:
             if not dem.get(n, n).startswith(MAY_SPILL)]
 
 
+# Sources that load registers with inline-assembly buffer loads and wait for them
+# with an explicit count (the mixture-of-experts decode's weight walk).  The
+# compiler takes such a register as written when the load is issued, so nothing
+# keeps it from copying or reusing the register while the load is still in
+# flight; the build reads the device assembly and refuses it unless (1) no
+# other instruction writes a register that such a load writes, and (2) the LDS
+# stores that follow each explicit wait store exactly such registers.
+ASM_LOAD_CHECKED = ("moe_mfma.hip",)
+_FUNC = re.compile(r"^(_Z\S+):")
+_VRANGE = re.compile(r"^v\[(\d+):(\d+)\]$|^v(\d+)$")
+
+
+def _vregs(tok: str) -> set[int]:
+    m = _VRANGE.match(tok.rstrip(","))
+    if not m:
+        return set()
+    if m.group(3) is not None:
+        return {int(m.group(3))}
+    return set(range(int(m.group(1)), int(m.group(2)) + 1))
+
+
+def _check_asm_loads(asm: str, src: str) -> list[str]:
+    """Problems with inline-assembly register loads in device assembly (see ASM_LOAD_CHECKED)."""
+    problems = []
+    func, lines = None, []
+    funcs = []
+    for line in asm.splitlines():
+        m = _FUNC.match(line)
+        if m:
+            func, lines = m.group(1), []
+            funcs.append((func, lines))
+        elif func is not None:
+            lines.append(line.strip())
+    for name, body in funcs:
+        loaded, stored, other = set(), [], {}
+        in_asm = after_wait = False
+        for t in body:
+            if t.startswith(";;#ASMSTART"):
+                in_asm = True
+                continue
+            if t.startswith(";;#ASMEND"):
+                in_asm = False
+                continue
+            if not t or t.startswith((";", ".")):
+                continue
+            op = t.split()[0]
+            if in_asm:
+                if op.startswith("buffer_load") and not t.endswith(" lds"):
+                    loaded |= _vregs(t.split()[1])
+                elif op == "s_waitcnt" and "vmcnt" in t:
+                    after_wait = True
+                continue
+            if op.startswith("ds_write") and after_wait:
+                stored.append((t, _vregs(t.split()[2])))
+                continue
+            if op.startswith("s_waitcnt"):
+                continue
+            after_wait = False
+            if op.startswith(("s_", "ds_write", "buffer_store", "global_store", "buffer_load")) or " " not in t:
+                continue
+            for r in _vregs(t.split()[1]):
+                other.setdefault(r, t)
+        if not loaded:
+            continue
+        dem = _demangle([name]).get(name, name)
+        clobbered = sorted(r for r in other if r in loaded)
+        if clobbered:
+            problems.append(f"{src}: {dem}: v{clobbered[0]} is written by '{other[clobbered[0]]}' "
+                            f"besides an inline-assembly load")
+        for t, regs in stored:
+            if regs and not regs <= loaded:
+                problems.append(f"{src}: {dem}: '{t}' after an explicit wait stores registers no "
+                                f"inline-assembly load wrote")
+                break
+    return problems
+
+
+def _device_asm(src: str, build_dir: str, defines=()) -> str:
+    out = os.path.join(build_dir, os.path.splitext(src)[0] + ".s")
+    cmd = [HIPCC, *[f for f in FLAGS if f != "-Rpass-analysis=kernel-resource-usage"], *SOURCE_FLAGS.get(src, []),
+           *[f"-D{d}" for d in defines], "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    with open(out) as f:
+        return f.read()
+
+
 def build(verbose: bool = False, out: str = OUT, build_dir: str = BUILD_DIR, defines=()) -> str:
     """Compile and link; `defines` override compile-time tile parameters."""
     os.makedirs(build_dir, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(ASM_LOAD_CHECKED))) as ex:
+        asms = [ex.submit(_device_asm, s, build_dir, defines) for s in ASM_LOAD_CHECKED]
         results = list(ex.map(lambda s: _compile(s, build_dir, defines), SOURCES))
+        asm_texts = [a.result() for a in asms]
     problems = []
     for src, (_, log) in zip(SOURCES, results):
         problems += _check_scratch(log, src)
@@ -99,6 +190,10 @@ def build(verbose: bool = False, out: str = OUT, build_dir: str = BUILD_DIR, def
             sys.stderr.write(log)
     if problems:
         raise RuntimeError("kernels using scratch (spills):\n  " + "\n  ".join(problems))
+    for src, asm in zip(ASM_LOAD_CHECKED, asm_texts):
+        problems += _check_asm_loads(asm, src)
+    if problems:
+        raise RuntimeError("inline-assembly loads not kept in place:\n  " + "\n  ".join(problems))
     tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
     r = subprocess.run(cmd, capture_output=True, text=True)
