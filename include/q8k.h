@@ -29,9 +29,11 @@
  *   - Buffers are device pointers owned by the caller; the library never
  *     allocates and never synchronises.  Its only state: the calling
  *     thread's last-error text and launch record (q8k_debug_last_launches),
- *     and the compute-unit count of each device, asked of the runtime once
- *     (it sizes the MoE decode grid and bounds qmatmul_prefill_f32).  Buffers must stay alive until the
- *     work enqueued on `stream` has finished.
+ *     the compute-unit count of each device, asked of the runtime once (it
+ *     sizes the MoE decode grid and bounds qmatmul_prefill_f32), and the
+ *     static device scratch of qmatmul_prefill_moe_noalloc with its address
+ *     on each device (below).  Buffers must stay alive until the work
+ *     enqueued on `stream` has finished.
  *   - `stream` is a hipStream_t (NULL = the default stream).
  *   - Arguments are validated on the host before anything is enqueued.  A
  *     refusal returns a non-zero q8k_status, enqueues nothing, leaves every
