@@ -415,6 +415,21 @@ class Prefill:
         return close(got, want, A)  # every output
 
 
+def pack_parity(q, torch, p) -> bool:
+    """The packed buffer the replays left in p.xq against the oracle's q8k_pack of
+    the same tokens: codes, scales and sub-block sums, byte for byte."""
+    import oracle
+
+    torch.cuda.synchronize()
+    buf = p.xq.cpu().numpy()
+    _, od, ob = q.q8k_act_layout(p.M, p.K)
+    nb = p.K // 256
+    qs, d, bs = oracle.q8k_pack(p.x_host)
+    return (buf[: p.M * p.K].view(np.int8).tobytes() == qs.tobytes()
+            and buf[od: od + 4 * p.M * nb].tobytes() == d.tobytes()
+            and buf[ob: ob + 16 * p.M * nb].tobytes() == bs.tobytes())
+
+
 class PrefillF32(Prefill):
     """The same step from fp32 tokens as one call: qmatmul_prefill_f32 packs
     the tokens inside the GEMM launch (xq receives q8k_pack's bytes)."""
@@ -900,7 +915,8 @@ def main():
         pus = replay_us(torch, gp, 32, reps=2)
         del gp
         sus = calib.us(p.pack_bytes)
-        wl["pack_512x14336"] = {"kernel_us": round(pus, 2), "GB/s": round(p.pack_bytes / (pus * 1e-6) / 1e9, 1),
+        wl["pack_512x14336"] = {"parity": "pass" if pack_parity(q, torch, p) else "FAIL",
+                                "kernel_us": round(pus, 2), "GB/s": round(p.pack_bytes / (pus * 1e-6) / 1e9, 1),
                                 "frac_hbm": round(p.pack_bytes / (pus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                                 "stream_read_us": round(sus, 3), "frac_stream_read": round(sus / pus, 4),
                                 "bytes_per_launch": p.pack_bytes, "traffic": traffic_record("pack")}
