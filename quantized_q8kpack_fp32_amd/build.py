@@ -5,7 +5,8 @@ disabled, and the kernel resource report of each translation unit is checked:
 a kernel that uses scratch (spills) fails the build, since a spilling kernel is
 not a tuned kernel (the build gate idea of "One kernel, any device", section
 2.2).  Sources that load registers with inline assembly also have their device
-assembly checked (ASM_LOAD_CHECKED).  Usage: ``python quantized_q8kpack_fp32_amd/build.py`` (or via
+assembly checked (ASM_LOAD_CHECKED): registers loaded by inline assembly stay
+in place, and M0, which the LDS copies set, is used by nothing else.  Usage: ``python quantized_q8kpack_fp32_amd/build.py`` (or via
 ``__graft_entry__.build()``).
 """
 from __future__ import annotations
@@ -88,14 +89,19 @@ def _check_scratch(log: str, src: str) -> list[str]:
             if not dem.get(n, n).startswith(MAY_SPILL)]
 
 
-# Sources that load registers with inline-assembly buffer loads and wait for them
-# with an explicit count (the mixture-of-experts decode's weight walk).  The
-# compiler takes such a register as written when the load is issued, so nothing
-# keeps it from copying or reusing the register while the load is still in
-# flight; the build reads the device assembly and refuses it unless (1) no
-# other instruction writes a register that such a load writes, and (2) the LDS
-# stores that follow each explicit wait store exactly such registers.
-ASM_LOAD_CHECKED = ("moe_mfma.hip",)
+# Sources whose inline assembly the compiler cannot see into, checked in their
+# device assembly:
+# - register loads by inline-assembly buffer loads, waited for with an explicit
+#   count (the mixture-of-experts decode's weight walk): the compiler takes such
+#   a register as written when the load is issued, so nothing keeps it from
+#   copying or reusing the register while the load is still in flight.  The
+#   build refuses the source unless (1) no other instruction writes a register
+#   that such a load writes, and (2) the LDS stores that follow each explicit
+#   wait store exactly such registers;
+# - buffer-unit copies into LDS, which set M0 inside the assembly: M0 is a
+#   reserved register, so the compiler does not restore it after the copies,
+#   and the build refuses the source if the compiler itself uses M0 anywhere.
+ASM_LOAD_CHECKED = ("moe_mfma.hip", "prefill_regw.hip")
 _FUNC = re.compile(r"^(_Z\S+):")
 _VRANGE = re.compile(r"^v\[(\d+):(\d+)\]$|^v(\d+)$")
 
@@ -165,6 +171,20 @@ def _check_asm_loads(asm: str, src: str) -> list[str]:
     return problems
 
 
+def _check_m0(asm: str, src: str) -> list[str]:
+    """Compiler instructions (outside inline assembly) that use M0."""
+    in_asm, found = False, []
+    for line in asm.splitlines():
+        t = line.strip()
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+        elif t.startswith(";;#ASMEND"):
+            in_asm = False
+        elif not in_asm and t and not t.startswith((";", ".")) and re.search(r"\bm0\b", t):
+            found.append(f"{src}: the compiler uses M0 ('{t}'), which the inline-assembly LDS copies overwrite")
+    return found[:3]
+
+
 def _device_asm(src: str, build_dir: str, defines=()) -> str:
     out = os.path.join(build_dir, os.path.splitext(src)[0] + ".s")
     cmd = [HIPCC, *[f for f in FLAGS if f != "-Rpass-analysis=kernel-resource-usage"], *SOURCE_FLAGS.get(src, []),
@@ -191,9 +211,9 @@ def build(verbose: bool = False, out: str = OUT, build_dir: str = BUILD_DIR, def
     if problems:
         raise RuntimeError("kernels using scratch (spills):\n  " + "\n  ".join(problems))
     for src, asm in zip(ASM_LOAD_CHECKED, asm_texts):
-        problems += _check_asm_loads(asm, src)
+        problems += _check_asm_loads(asm, src) + _check_m0(asm, src)
     if problems:
-        raise RuntimeError("inline-assembly loads not kept in place:\n  " + "\n  ".join(problems))
+        raise RuntimeError("inline assembly not safe in the compiled code:\n  " + "\n  ".join(problems))
     tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
     r = subprocess.run(cmd, capture_output=True, text=True)

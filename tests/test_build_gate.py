@@ -105,3 +105,14 @@ def test_lds_copies_and_other_functions_are_not_loads():
     assert b._check_asm_loads(asm, "moe_mfma.hip") == []
     other = "_ZN3q8k5otherEv:\n\tv_mov_b32_e32 v110, 0\n\ts_endpgm\n"
     assert b._check_asm_loads(ASM_GOOD + other, "moe_mfma.hip") == []
+
+
+def test_compiler_use_of_m0_is_refused():
+    """M0 set inside inline assembly (the LDS copies) is fine; an M0 use the
+    compiler emitted itself is named."""
+    b = _build_module()
+    ok = "_ZN3q8k4copyEv:\n\t;;#ASMSTART\n\ts_mov_b32 m0, s4\n\ts_nop 0\n\tbuffer_load_dword v1, s[0:3], 0 offen lds\n\t;;#ASMEND\n\ts_endpgm\n"
+    assert b._check_m0(ok, "prefill_regw.hip") == []
+    bad = ok.replace("\ts_endpgm\n", "\ts_mov_b32 m0, -1\n\tds_read_b32 v2, v3\n\ts_endpgm\n")
+    problems = b._check_m0(bad, "prefill_regw.hip")
+    assert len(problems) == 1 and "s_mov_b32 m0, -1" in problems[0]
