@@ -211,8 +211,8 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
     };
     // Each wave's first walk of a tile (expert wv) finds its first block in the
     // cache: the block is copied into the wave's tile ahead (at the start of a
-    // slab, before the staging; at the end of the previous tile's walks, across
-    // the barrier and the slot sums).  The walk then loads it again into
+    // slab, right behind the staging copies; at the end of the previous tile's
+    // walks, across the barrier and the slot sums).  The walk then loads it again into
     // registers, a cache hit, and overwrites the tile only after waiting for its
     // own load, which is younger than the copy.
     for (int64_t t0 = 0; t0 < T; t0 += ts) {
@@ -226,27 +226,27 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
             const int nt = (int)(t1 - t0), cp = (int)cpt, nbt = nt * nb, np = (int)(pe - pb);
             const int ipt = (cp + 63) >> 6;  // copies per token (64 chunks of 16 bytes each)
             const rsrc_t rq = make_rsrc(qs + t0 * K, (int64_t)nt * K);
-            for (int g = wv; g < nt * ipt; g += MM_WAVES) {
-                const int t = g / ipt, i = g - t * ipt, c = 64 * i + lane;
-                if (c < cp) mm_dma16(rq, tokc + t * KS + 1024 * i, t * (int)K + 16 * c);
+            for (int n = wv; n < nt * ipt; n += MM_WAVES) {
+                const int t = n / ipt, j = n - t * ipt, c = 64 * j + lane;
+                if (c < cp) mm_dma16(rq, tokc + t * KS + 1024 * j, t * (int)K + 16 * c);
             }
             // sums: one 16-byte chunk per block; scales: one fp32 per block
             const rsrc_t rb = make_rsrc(bs + t0 * nb * 8, (int64_t)nbt * 16);
             const rsrc_t rd = make_rsrc(d8 + t0 * nb, (int64_t)nbt * 4);
-            for (int g = wv; g < (nbt + 63) >> 6; g += MM_WAVES) {
-                const int c = 64 * g + lane;
+            for (int n = wv; n < (nbt + 63) >> 6; n += MM_WAVES) {
+                const int c = 64 * n + lane;
                 if (c < nbt) {
-                    mm_dma16(rb, tokb + 1024 * g, 16 * c);
-                    mm_dma4(rd, tokd + 64 * g, 4 * c);
+                    mm_dma16(rb, tokb + 1024 * n, 16 * c);
+                    mm_dma4(rd, tokd + 64 * n, 4 * c);
                 }
             }
             const rsrc_t ri = make_rsrc(ids + pb, (int64_t)np * 4);
             const rsrc_t rr = make_rsrc(rw + pb, (int64_t)np * 4);
-            for (int g = wv; g < (np + 63) >> 6; g += MM_WAVES) {
-                const int c = 64 * g + lane;
+            for (int n = wv; n < (np + 63) >> 6; n += MM_WAVES) {
+                const int c = 64 * n + lane;
                 if (c < np) {
-                    mm_dma4(ri, sm.sid + 64 * g, 4 * c);
-                    mm_dma4(rr, sm.srw + 64 * g, 4 * c);
+                    mm_dma4(ri, sm.sid + 64 * n, 4 * c);
+                    mm_dma4(rr, sm.srw + 64 * n, 4 * c);
                 }
             }
         }
