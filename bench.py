@@ -67,6 +67,7 @@ KERNEL_SOURCES = {
     "moe": [_CS + "moe_mfma.hip", _CS + "q4k_planes.h", _CS + "q8k_device.h"],
     "matvec_q5k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
     "moe_q5k": [_CS + "moe_mfma.hip", _CS + "q4k_planes.h", _CS + "q8k_device.h"],
+    "moe_q6k": [_CS + "moe.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
     "prefill_q4k": [_CS + "prefill_regw.hip", _CS + "q4k_planes.h", _CS + "q8k_device.h"],
     "moe_prefill_q4k": [_CS + "prefill_regw.hip", _CS + "q4k_planes.h", _CS + "prefill.hip", _CS + "q8k_device.h"],
     "prefill_q5k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
@@ -317,11 +318,11 @@ class MoE:
 
         self.q, self.torch, self.E, self.rows, self.K, self.T, self.topk = q, torch, E, rows, K, T, topk
         self.fmt = fmt
-        self.qt = q.Q8K_Q4_K if fmt == "q4k" else q.Q8K_Q5_K
+        self.qt, gen = _prefill_format(q, synth, fmt)  # Q4_K, Q5_K or relaid Q6_K
         g = np.random.default_rng(seed)
         dev = torch.device("cuda")
-        self.w_host = (synth.q4k_weights if fmt == "q4k" else synth.q5k_weights)(g, E * rows, K)
-        w0 = torch.from_numpy(self.w_host).to(dev)
+        self.w_host = gen(g, E * rows, K)
+        w0 = _device_weight(q, torch, fmt, self.w_host, E * rows, K)
         self.R = rotations(w0.numel())
         self.ws = [w0] + [w0.clone() for _ in range(self.R - 1)]
         self.x_host = synth.activations(g, T, K)
@@ -680,6 +681,7 @@ PROFILE_TARGETS = {
     "fused_q5k": "qmatvec_f32 (pack inside the launch) on the 4096x4096 Q5_K decode workload",
     "fused_q6k": "qmatvec_f32 (pack inside the launch) on the 32000x4096 relaid Q6_K workload",
     "moe_q5k": "qmatvec_moe on the 8 x 14336x4096 Q5_K, 16-token top-2 workload",
+    "moe_q6k": "qmatvec_moe on the 8 x 14336x4096 relaid Q6_K, 16-token top-2 workload",
     "prefill": "qmatmul_prefill on the 4096x14336 Q4_K, 512-token workload",
     "moe_prefill": "qmatmul_prefill_moe on the 8 x 14336x4096 Q4_K, 512-token top-2 workload",
     "prefill_q5k": "qmatmul_prefill on the 4096x14336 Q5_K, 512-token workload",
@@ -716,6 +718,7 @@ def profile_run(q, torch, target, launches):
               "fused_q5k": lambda: Decode(q, torch, "q5k", 4096, 4096, seed=5, fused=True),
               "fused_q6k": lambda: Decode(q, torch, "q6k", 32000, 4096, seed=2, fused=True),
               "moe_q5k": lambda: MoE(q, torch, seed=6, fmt="q5k"),
+              "moe_q6k": lambda: MoE(q, torch, seed=14, fmt="q6k"),
               "prefill": lambda: Prefill(q, torch),
               "moe_prefill": lambda: MoEPrefill(q, torch),
               "prefill_q5k": lambda: Prefill(q, torch, seed=8, fmt="q5k"),
@@ -878,6 +881,13 @@ def main():
         m = MoE(q, torch, seed=6, fmt="q5k")
         decode_entry("moe_q5k_8x14336x4096_t16_top2", m, "moe_q5k")
         wl["moe_q5k_8x14336x4096_t16_top2"]["experts_hit"] = m.experts_hit
+        del m
+        torch.cuda.empty_cache()
+        # relaid Q6_K experts at the same layer shape (the per-chunk kernel)
+        log("workload: moe_q6k_8x14336x4096_t16_top2")
+        m = MoE(q, torch, seed=14, fmt="q6k")
+        decode_entry("moe_q6k_8x14336x4096_t16_top2", m, "moe_q6k")
+        wl["moe_q6k_8x14336x4096_t16_top2"]["experts_hit"] = m.experts_hit
         del m
         torch.cuda.empty_cache()
         for name, key, make in (

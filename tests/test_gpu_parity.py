@@ -431,6 +431,7 @@ def moe_case(q, fmt, E, rows, K, T, topk, seed, ids=None):
     ("q4k", 2, 40, 88064, 3, 2, 38),       # one packed token per LDS stage: a slab per token
     ("q4k", 2, 40, 131072, 3, 2, 39),      # a packed token beyond the LDS stage: one lane per row
     ("q6k", 8, 300, 1024, 16, 2, 34),
+    ("q6k", 8, 14336, 4096, 16, 2, 46),    # the MoE decode layer shape in relaid Q6_K
     ("q5k", 8, 14336, 4096, 16, 2, 35),    # the MoE decode layer shape in Q5_K
     ("q5k", 4, 100, 512, 5, 3, 36),
     ("q5k", 16, 64, 256, 200, 4, 37),
