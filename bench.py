@@ -67,7 +67,7 @@ KERNEL_SOURCES = {
     "moe": [_CS + "moe_mfma.hip", _CS + "q4k_planes.h", _CS + "q8k_device.h"],
     "matvec_q5k": [_CS + "matvec.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
     "moe_q5k": [_CS + "moe_mfma.hip", _CS + "q4k_planes.h", _CS + "q8k_device.h"],
-    "moe_q6k": [_CS + "moe.hip", _CS + "kquant.h", _CS + "q8k_device.h"],
+    "moe_q6k": [_CS + "moe_mfma.hip", _CS + "q4k_planes.h", _CS + "q8k_device.h"],
     "prefill_q4k": [_CS + "prefill_regw.hip", _CS + "q4k_planes.h", _CS + "q8k_device.h"],
     "moe_prefill_q4k": [_CS + "prefill_regw.hip", _CS + "q4k_planes.h", _CS + "prefill.hip", _CS + "q8k_device.h"],
     "prefill_q5k": [_CS + "prefill.hip", _CS + "q8k_device.h"],
@@ -883,7 +883,7 @@ def main():
         wl["moe_q5k_8x14336x4096_t16_top2"]["experts_hit"] = m.experts_hit
         del m
         torch.cuda.empty_cache()
-        # relaid Q6_K experts at the same layer shape (the per-chunk kernel)
+        # relaid Q6_K experts at the same layer shape
         log("workload: moe_q6k_8x14336x4096_t16_top2")
         m = MoE(q, torch, seed=14, fmt="q6k")
         decode_entry("moe_q6k_8x14336x4096_t16_top2", m, "moe_q6k")

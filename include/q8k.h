@@ -262,11 +262,12 @@ int q8k_debug_subblock_sums(int qtype, const void* w, int64_t rows, int64_t K, c
 int q8k_debug_prefill_block_sums(int qtype, const void* w, int64_t rows, int64_t K, const void* xq, int64_t M,
                                  float* y, int32_t* I, void* stream);
 
-/* q8k_debug_moe_subblock_sums: qmatvec_moe's matrix-core kernel (Q8K_Q4_K or
- *   Q8K_Q5_K; K small enough that a packed token fits its shared-memory
- *   stage, else Q8K_ERR_SHAPE).  y: fp32 [T][rows]; S: int32 sub-block sums
- *   [T * topk][rows][K/32] of pair (t, k) against expert ids[t][k]; entries
- *   of pairs whose id is outside [0, E) are not written. */
+/* q8k_debug_moe_subblock_sums: qmatvec_moe's matrix-core kernels (Q8K_Q4_K,
+ *   Q8K_Q5_K or Q8K_Q6_K_RELAID; K small enough that a packed token fits the
+ *   kernel's shared-memory stage, else Q8K_ERR_SHAPE).  y: fp32 [T][rows]; S:
+ *   int32 sub-block sums of pair (t, k) against expert ids[t][k],
+ *   [T * topk][rows][K/32] (Q4_K, Q5_K) or [T * topk][rows][K/16] (Q6_K);
+ *   entries of pairs whose id is outside [0, E) are not written. */
 int q8k_debug_moe_subblock_sums(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, const void* xq,
                                 int64_t T, const int32_t* ids, const float* rw, int32_t topk, float* y, int32_t* S,
                                 void* stream);

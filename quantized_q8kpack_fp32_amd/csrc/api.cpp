@@ -294,8 +294,13 @@ int qmatvec_moe(int qtype, const void* w, int64_t E, int64_t rows, int64_t K, co
             e = launch_moe_q5k(static_cast<const uint8_t*>(w), E, rows, nb, a, T, ids, rw, topk, y,
                                (hipStream_t)stream);
     } else {
+        // relaid Q6_K: the matrix-core kernel while a packed token fits its
+        // stage (K up to about 84k), the per-chunk kernel beyond
         const Q6View v = q6_view(w, E * rows * nb);
-        e = launch_moe_q6k(v.prefix, v.bodies, E, rows, nb, a, T, ids, rw, topk, y, (hipStream_t)stream);
+        if (moe_mfma_q6k_fits(K))
+            e = launch_moe_mfma_q6k(v.prefix, v.bodies, E, rows, nb, a, T, ids, rw, topk, y, (hipStream_t)stream);
+        else
+            e = launch_moe_q6k(v.prefix, v.bodies, E, rows, nb, a, T, ids, rw, topk, y, (hipStream_t)stream);
     }
     return launched(fn, e);
 }
@@ -489,9 +494,10 @@ int q8k_debug_moe_subblock_sums(int qtype, const void* w, int64_t E, int64_t row
     const char* fn = "q8k_debug_moe_subblock_sums";
     Q8K_TRY(check_k(fn, K));
     Q8K_TRY(check_count(fn, "rows", rows, MAX_ROWS));
-    if (qtype != Q8K_Q4_K && qtype != Q8K_Q5_K)
-        return fail(Q8K_ERR_QTYPE, "%s: qtype=%d: the matrix-core MoE kernel serves Q8K_Q4_K and Q8K_Q5_K", fn, qtype);
-    if (!moe_mfma_q4k_fits(K))
+    if (qtype != Q8K_Q4_K && qtype != Q8K_Q5_K && qtype != Q8K_Q6_K_RELAID)
+        return fail(Q8K_ERR_QTYPE,
+                    "%s: qtype=%d: the matrix-core MoE kernels serve Q8K_Q4_K, Q8K_Q5_K and Q8K_Q6_K_RELAID", fn, qtype);
+    if (qtype == Q8K_Q6_K_RELAID ? !moe_mfma_q6k_fits(K) : !moe_mfma_q4k_fits(K))
         return fail(Q8K_ERR_SHAPE, "%s: K=%lld: a packed token exceeds the matrix-core MoE kernel's LDS stage", fn,
                     (long long)K);
     if (E < 1 || E > MAX_EXPERTS)
@@ -510,6 +516,11 @@ int q8k_debug_moe_subblock_sums(int qtype, const void* w, int64_t E, int64_t row
     Q8K_TRY(check_ptr(fn, "y", y, 4));
     Q8K_TRY(check_ptr(fn, "S", S, 4));
     if (rows == 0 || T == 0) return Q8K_OK;
+    if (qtype == Q8K_Q6_K_RELAID) {
+        const Q6View v = q6_view(w, E * rows * (K / QK));
+        return launched(fn, launch_moe_mfma6_sums(v.prefix, v.bodies, E, rows, (int)(K / QK), acts_of(xq, T, K), T, ids,
+                                                  rw, topk, y, S, (hipStream_t)stream));
+    }
     return launched(fn, launch_moe_mfma_sums(qtype == Q8K_Q5_K, static_cast<const uint8_t*>(w), E, rows, (int)(K / QK),
                                              acts_of(xq, T, K), T, ids, rw, topk, y, S, (hipStream_t)stream));
 }

@@ -453,6 +453,283 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+
+// ================================================================ relaid Q6_K
+// The same walk over relaid Q6_K experts (fp16 d per (row, block) in the
+// prefix; bodies ql[128] | qh[64] | int8 scales[16]).  A Q6_K sub-block is 16
+// values with its own signed 8-bit scale, so each takes one 32x32x16 int8
+// MFMA: lane (i, g) supplies values 16s + 8g .. +7 of sub-block s, the pairs'
+// q8_K codes as A and the rows' 6-bit values q (0..63, before the -32 offset)
+// as B.  A second MFMA of the same codes against -32 in every byte adds
+// -32 times each pair's code sum, so the accumulator holds S_s = sum (q - 32) x
+// exactly; the scales then fold in int32, I = sum_s sc_s * S_s, and
+// acc += (d8 * float(I)) * d.
+// Value v = 128h + 32t + l of a block has its low four bits in
+// ql[64h + 32(t&1) + l] (nibble t >> 1) and its high two in qh[32h + l] (bits
+// 2t, 2t + 1); sub-block s = v / 16.
+constexpr int M6_CH = Q6K_BODY / 16;  // 13 chunks of a body
+constexpr int M6_NL = 7;              // ceil(32 * 13 / 64) loads per lane and block
+static_assert(32 * M6_CH - 64 * (M6_NL - 1) == 32, "the last load takes the last 32 chunks");
+constexpr int M6_TOK_BYTES = 86016;   // LDS stage of the slab's packed tokens
+
+// LDS bytes of one staged token: codes padded by 16 bytes, block scales (no
+// sub-block sums: Q6_K has no min term).
+__host__ __device__ constexpr int64_t m6_tok_bytes(int64_t K) { return (K + 16) + K / 64; }
+
+struct Mm6Wave {
+    int plist[64];
+    float d8[32];
+    uint32_t dd[2][64];  // by block parity: lane l's dword of the prefix run holding row l % 32's d
+    __attribute__((aligned(16))) uint8_t tile[MM_ROWS * Q6K_BODY];  // block b of the tile's rows, [row][body]
+};
+struct Mm6Smem {
+    Mm6Wave wave[MM_WAVES];
+    float slot[MM_SLOT * MM_ROWS];
+    int32_t sid[MM_SLOT];
+    float srw[MM_SLOT];
+    int8_t tok[M6_TOK_BYTES];  // codes [ts][K + 16], then scales [ts][K / 256] fp32
+};
+static_assert(sizeof(Mm6Smem) <= 160 * 1024, "LDS of one workgroup");
+
+// One block of the tile's rows: the body chunks in the sector-contiguous lane
+// map (chunk c = 64x + l of the 416, row c / 13) into registers, and the rows'
+// d by a buffer-unit copy into LDS (lane l: the aligned dword of the prefix run
+// that holds row l % 32's d).  The wait names every register it covers.
+struct M6W {
+    v4i c[M6_NL];
+};
+__device__ __forceinline__ MmLane<M6_NL> m6_lane(int lane, int64_t brow) {
+    MmLane<M6_NL> m;
+#pragma unroll
+    for (int x = 0; x < M6_NL; ++x) {
+        const int c = x < M6_NL - 1 ? 64 * x + lane : 64 * (M6_NL - 1) + (lane & 31);
+        m.go[x] = (c / M6_CH) * (int)brow + 16 * (c % M6_CH);
+        m.lo[x] = 16 * c;
+    }
+    return m;
+}
+__device__ __forceinline__ void m6_issue(M6W& W, rsrc_t wr, rsrc_t pr, const MmLane<M6_NL>& m, uint32_t (&dd)[2][64],
+                                         int drow, int b) {
+    const int boff = b * Q6K_BODY;
+#pragma unroll
+    for (int x = 0; x < M6_NL; ++x) W.c[x] = mm_vload16(wr, m.go[x] + boff);
+    mm_dma4(pr, &dd[b & 1][0], ((drow + b) * 2) & ~3);
+}
+template <int N>
+__device__ __forceinline__ void m6_wait(M6W& W) {
+    asm volatile("s_waitcnt vmcnt(%7)"
+                 : "+v"(W.c[0]), "+v"(W.c[1]), "+v"(W.c[2]), "+v"(W.c[3]), "+v"(W.c[4]), "+v"(W.c[5]), "+v"(W.c[6])
+                 : "n"(N));
+}
+constexpr int M6_LOADS = M6_NL + 1;  // loads per block
+
+// SUMS (test support): also store each pair's exact sub-block sums, Sout
+// [T * topk][rows][nb][16], as its matrix cores produce them.
+template <bool SUMS = false>
+__global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q6k_kernel(
+    const uint16_t* __restrict__ prefix, const uint8_t* __restrict__ bodies, int64_t E, int64_t rows, int nb,
+    const int8_t* __restrict__ qs, const float* __restrict__ d8, int64_t K, int64_t T,
+    const int32_t* __restrict__ ids, const float* __restrict__ rw, int topk, float* __restrict__ y, int rt,
+    int64_t ntiles, int32_t* __restrict__ Sout) {
+    __shared__ __attribute__((aligned(16))) Mm6Smem sm;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: expert and rsrc are scalar
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 31, g = lane >> 5;
+    const int64_t brow = (int64_t)nb * Q6K_BODY;  // body bytes per row
+    Mm6Wave& L = sm.wave[wv];
+    const MmLane<M6_NL> ml = m6_lane(lane, brow);  // rows past `live` read zeros
+    const int drow = i * nb;                       // index of row i's d of block 0 in the tile's prefix run
+    const int64_t KS = K + 16, cpt = K / 16;
+    const int tsl = M6_TOK_BYTES / (int)m6_tok_bytes(K);  // >= 1 (checked by the launcher)
+    const int64_t ts = MM_SLOT / topk < tsl ? MM_SLOT / topk : tsl;  // tokens per slab
+    int8_t* const tokc = sm.tok;
+    float* const tokd = reinterpret_cast<float*>(sm.tok + ts * KS);
+    // expert e's rows of a tile: bodies and the prefix run of their d
+    auto tile_rsrc = [&](int64_t tile, int64_t e) {
+        const int64_t r0 = tile * rt;
+        const int64_t live = rows - r0 < rt ? rows - r0 : rt;
+        return make_rsrc(bodies + (e * rows + r0) * brow, live * brow);
+    };
+    // (2 bytes past the run: a dword copy may end there; they are the next
+    // row's entries or the prefix array's padding to 256 bytes)
+    auto tile_prsrc = [&](int64_t tile, int64_t e) {
+        const int64_t r0 = tile * rt;
+        const int64_t live = rows - r0 < rt ? rows - r0 : rt;
+        return make_rsrc(prefix + (e * rows + r0) * nb, live * nb * 2 + 2);
+    };
+    for (int64_t t0 = 0; t0 < T; t0 += ts) {
+        const int64_t t1 = t0 + ts < T ? t0 + ts : T;
+        const int64_t pb = t0 * topk, pe = t1 * topk;
+        // ---- stage the slab's codes, block scales, ids and router weights
+        // with buffer-unit copies; then the first body block of this wave's
+        // first walk, and a wait for everything but that block
+        {
+            const int nt = (int)(t1 - t0), cp = (int)cpt, nbt = nt * nb, np = (int)(pe - pb);
+            const int ipt = (cp + 63) >> 6;
+            const rsrc_t rq = make_rsrc(qs + t0 * K, (int64_t)nt * K);
+            for (int n = wv; n < nt * ipt; n += MM_WAVES) {
+                const int t = n / ipt, j = n - t * ipt, c = 64 * j + lane;
+                if (c < cp) mm_dma16(rq, tokc + t * KS + 1024 * j, t * (int)K + 16 * c);
+            }
+            const rsrc_t rd = make_rsrc(d8 + t0 * nb, (int64_t)nbt * 4);
+            for (int n = wv; n < (nbt + 63) >> 6; n += MM_WAVES)
+                if (64 * n + lane < nbt) mm_dma4(rd, tokd + 64 * n, 4 * (64 * n + lane));
+            const rsrc_t ri = make_rsrc(ids + pb, (int64_t)np * 4);
+            const rsrc_t rr = make_rsrc(rw + pb, (int64_t)np * 4);
+            for (int n = wv; n < (np + 63) >> 6; n += MM_WAVES) {
+                const int c = 64 * n + lane;
+                if (c < np) {
+                    mm_dma4(ri, sm.sid + 64 * n, 4 * c);
+                    mm_dma4(rr, sm.srw + 64 * n, 4 * c);
+                }
+            }
+        }
+        if (wv < E) {
+            // block 0 of the first walk into the wave's tile (a cache fill, as
+            // in the Q4_K walk; the last copy on lanes 0-31)
+            const rsrc_t wr0 = tile_rsrc(blockIdx.x, wv);  // grid <= ntiles
+#pragma unroll
+            for (int x = 0; x < M6_NL - 1; ++x) mm_dma16(wr0, L.tile + 1024 * x, ml.go[x]);
+            if (lane < 32) mm_dma16(wr0, L.tile + 1024 * (M6_NL - 1), ml.go[M6_NL - 1]);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(M6_NL) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+        for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+            const int64_t r0 = tile * rt;
+            const int64_t live = rows - r0 < rt ? rows - r0 : rt;
+            for (int64_t e = wv; e < E; e += MM_WAVES) {
+                const rsrc_t wr = tile_rsrc(tile, e);
+                const rsrc_t pr = tile_prsrc(tile, e);
+                for (int64_t p0 = pb; p0 < pe; p0 += 64) {
+                    const int64_t p = p0 + lane;
+                    const bool hit = p < pe && sm.sid[p - pb] == (int32_t)e;
+                    const uint64_t mask = __ballot(hit);
+                    if (mask == 0) continue;
+                    const int count = __popcll(mask);
+                    wave_lds_fence();
+                    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                    if (hit) L.plist[rank] = (int)p;
+                    wave_lds_fence();
+                    for (int k0 = 0; k0 < count; k0 += MM_GROUP) {
+                        const int n = count - k0 < MM_GROUP ? count - k0 : MM_GROUP;
+                        const int pi = L.plist[k0 + (i < n ? i : 0)];
+                        const int tl = (int)(pi / topk - t0);
+                        // the pair's codes and scales as 32-bit offsets into the stage
+                        // (under 2^17 bytes), so every address stays an LDS address
+                        const int xoff = tl * (int)KS;
+                        const float* d8row = tokd + tl * nb;
+                        // The block walk, as for Q4_K: block b's registers are
+                        // multiplied while block b + 1's are in flight (M0 / M1 by
+                        // parity); the last step reloads the last block and the
+                        // walk ends by draining it.
+                        v16f acc = {};
+                        M6W M0, M1;
+                        auto step = [&](int b, M6W& Wc, M6W& Wfree) __attribute__((always_inline)) {
+                            m6_issue(Wfree, wr, pr, ml, L.dd, drow, b + 1 < nb ? b + 1 : nb - 1);
+                            if (b < 0) return;
+                            m6_wait<M6_LOADS>(Wc);
+                            wave_lds_fence();
+#pragma unroll
+                            for (int x = 0; x < M6_NL; ++x)
+                                *reinterpret_cast<v4i*>(L.tile + ml.lo[x]) = Wc.c[x];
+                            if (g == 0) L.d8[i] = d8row[b];
+                            wave_lds_fence();
+                            const uint8_t* tr = L.tile + i * Q6K_BODY;
+                            // this lane's ql pieces (h, t & 1, s & 1) and qh pieces
+                            // (h, s & 1): 8 bytes each at value offset 16 (s & 1) + 8g
+                            uint2 lq[8], hq[4];
+#pragma unroll
+                            for (int k = 0; k < 8; ++k)
+                                lq[k] = *reinterpret_cast<const uint2*>(tr + 64 * (k >> 2) + 32 * ((k >> 1) & 1) +
+                                                                         16 * (k & 1) + 8 * g);
+#pragma unroll
+                            for (int k = 0; k < 4; ++k)
+                                hq[k] = *reinterpret_cast<const uint2*>(tr + 128 + 32 * (k >> 1) + 16 * (k & 1) + 8 * g);
+                            const uint4 scv = *reinterpret_cast<const uint4*>(tr + 192);
+                            const uint32_t scw[4] = {scv.x, scv.y, scv.z, scv.w};
+                            int I[4] = {0, 0, 0, 0};
+                            const long m32 = (long)0xE0E0E0E0E0E0E0E0uLL;  // eight int8 -32
+                            const v16i zero = {};
+#pragma unroll
+                            for (int sb = 0; sb < 16; ++sb) {
+                                const int h = sb >> 3, t = (sb >> 1) & 3, c = sb & 1;
+                                const uint2 l2 = lq[4 * h + 2 * (t & 1) + c], h2 = hq[2 * h + c];
+                                const uint32_t bx = ((l2.x >> (4 * (t >> 1))) & 0x0F0F0F0Fu) |
+                                                    (((h2.x >> (2 * t)) & 0x03030303u) << 4);
+                                const uint32_t by = ((l2.y >> (4 * (t >> 1))) & 0x0F0F0F0Fu) |
+                                                    (((h2.y >> (2 * t)) & 0x03030303u) << 4);
+                                const long B = (long)((uint64_t)bx | ((uint64_t)by << 32));
+                                const long A = *reinterpret_cast<const long*>(&sm.tok[xoff + b * QK + 16 * sb + 8 * g]);
+                                v16i S = __builtin_amdgcn_mfma_i32_32x32x16_i8(A, B, zero, 0, 0, 0);
+                                S = __builtin_amdgcn_mfma_i32_32x32x16_i8(A, m32, S, 0, 0, 0);
+                                const int sc = (int)(int8_t)((scw[sb >> 2] >> (8 * (sb & 3))) & 0xffu);
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const int Ss = S[r];
+                                    if constexpr (SUMS) {
+                                        // register r < 4 of lane (i, g): pair 4g + r of the group, row i
+                                        if (4 * g + r < n && i < live)
+                                            Sout[((int64_t)L.plist[k0 + 4 * g + r] * rows + r0 + i) * (nb * 16) +
+                                                 16 * b + sb] = Ss;
+                                    }
+                                    I[r] += __mul24(sc, Ss);  // |Ss| <= 65024, |sc| <= 128
+                                }
+                            }
+                            // acc += (d8 * float(I)) * d: register r < 4 of lane (i, g)
+                            // holds pair 4g + r
+                            const float4 dv = *reinterpret_cast<const float4*>(&L.d8[4 * g]);
+                            const float d8a[4] = {dv.x, dv.y, dv.z, dv.w};
+                            const uint32_t dw = L.dd[b & 1][i];
+                            const float dd = half_bits_to_float(((drow + b) & 1 ? dw >> 16 : dw) & 0xffffu);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[r] = fmaf((float)I[r] * d8a[r], dd, acc[r]);
+                            wave_lds_fence();
+                        };
+                        for (int b = -1; b < nb; b += 2) {
+                            step(b, M1, M0);
+                            if (b + 1 == nb) break;
+                            step(b + 1, M0, M1);
+                        }
+                        m6_wait<0>(M0);
+                        m6_wait<0>(M1);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int prr = 8 * (r >> 2) + 4 * g + (r & 3);
+                            if (prr < n) sm.slot[(L.plist[k0 + prr] - (int)pb) * MM_ROWS + i] = acc[r];
+                        }
+                    }
+                }
+            }
+            if (wv < E && tile + gridDim.x < ntiles) {
+                wave_lds_fence();
+                const rsrc_t wn = tile_rsrc(tile + gridDim.x, wv);
+#pragma unroll
+                for (int x = 0; x < M6_NL - 1; ++x) mm_dma16(wn, L.tile + 1024 * x, ml.go[x]);
+                if (lane < 32) mm_dma16(wn, L.tile + 1024 * (M6_NL - 1), ml.go[M6_NL - 1]);
+            }
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < (int)(t1 - t0) * MM_ROWS; idx += 64 * MM_WAVES) {
+                const int64_t t = t0 + idx / MM_ROWS;
+                const int r = idx % MM_ROWS;
+                if (r < live) {
+                    float s = 0.0f;
+                    for (int k = 0; k < topk; ++k) {
+                        const int64_t pp = t * topk + k;
+                        const int32_t id = sm.sid[pp - pb];
+                        if (id >= 0 && id < E) s += sm.srw[pp - pb] * sm.slot[(pp - pb) * MM_ROWS + r];
+                    }
+                    y[t * rows + r0 + r] = s;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 }  // namespace
 
 // Compute units of the current device, asked once per device.
@@ -488,6 +765,35 @@ hipError_t launch_moe_mfma(const uint8_t* w, int64_t E, int64_t rows, int nb, Ac
     Q8K_LAUNCH((moe_mfma_q4k_kernel<Q5, SUMS>), dim3(grid), dim3(64 * MM_WAVES), 0, s, w, E, rows, nb, a.qs, a.d, a.bs,
                a.K, T, ids, rw, topk, y, (int)rt, ntiles, Sout);
     return hipGetLastError();
+}
+
+bool moe_mfma_q6k_fits(int64_t K) { return m6_tok_bytes(K) <= M6_TOK_BYTES; }
+
+template <bool SUMS = false>
+hipError_t launch_moe_mfma6(const uint16_t* prefix, const uint8_t* bodies, int64_t E, int64_t rows, int nb, Acts a,
+                            int64_t T, const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s,
+                            int32_t* Sout = nullptr) {
+    if (!moe_mfma_q6k_fits(a.K)) return hipErrorInvalidValue;
+    // the grid and row tiles of the Q4_K kernel
+    const int64_t cus = device_cu_count();
+    const int64_t rounds = ((rows + MM_ROWS - 1) / MM_ROWS + cus - 1) / cus;
+    int64_t rt = (rows + rounds * cus - 1) / (rounds * cus);
+    rt = rt < 16 ? 16 : rt > MM_ROWS ? MM_ROWS : rt;
+    const int64_t ntiles = (rows + rt - 1) / rt;
+    const unsigned grid = (unsigned)(ntiles < cus ? ntiles : cus);
+    Q8K_LAUNCH((moe_mfma_q6k_kernel<SUMS>), dim3(grid), dim3(64 * MM_WAVES), 0, s, prefix, bodies, E, rows, nb, a.qs,
+               a.d, a.K, T, ids, rw, topk, y, (int)rt, ntiles, Sout);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_mfma_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t E, int64_t rows, int nb, Acts a,
+                               int64_t T, const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s) {
+    return launch_moe_mfma6(prefix, bodies, E, rows, nb, a, T, ids, rw, topk, y, s);
+}
+hipError_t launch_moe_mfma6_sums(const uint16_t* prefix, const uint8_t* bodies, int64_t E, int64_t rows, int nb,
+                                 Acts a, int64_t T, const int32_t* ids, const float* rw, int topk, float* y,
+                                 int32_t* S, hipStream_t s) {
+    return launch_moe_mfma6<true>(prefix, bodies, E, rows, nb, a, T, ids, rw, topk, y, s, S);
 }
 
 hipError_t launch_moe_mfma_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,

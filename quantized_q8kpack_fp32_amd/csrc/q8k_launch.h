@@ -56,6 +56,14 @@ hipError_t launch_moe_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Act
 // Q4_K mixture-of-experts decode on the int8 matrix cores (moe_mfma.hip); it
 // stages a token's packed row in LDS, so it serves K with moe_mfma_q4k_fits(K).
 bool moe_mfma_q4k_fits(int64_t K);
+// relaid Q6_K on the matrix cores (32x32x16 per 16-value sub-block); K with
+// moe_mfma_q6k_fits(K), launch_moe_q6k beyond
+bool moe_mfma_q6k_fits(int64_t K);
+hipError_t launch_moe_mfma_q6k(const uint16_t* prefix, const uint8_t* bodies, int64_t E, int64_t rows, int nb, Acts a,
+                               int64_t T, const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s);
+hipError_t launch_moe_mfma6_sums(const uint16_t* prefix, const uint8_t* bodies, int64_t E, int64_t rows, int nb,
+                                 Acts a, int64_t T, const int32_t* ids, const float* rw, int topk, float* y,
+                                 int32_t* S, hipStream_t s);
 hipError_t launch_moe_mfma_q4k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,
                                const int32_t* ids, const float* rw, int topk, float* y, hipStream_t s);
 hipError_t launch_moe_mfma_q5k(const uint8_t* w, int64_t E, int64_t rows, int nb, Acts a, int64_t T,

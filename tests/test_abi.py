@@ -237,7 +237,7 @@ def test_refused_call_records_no_launch(q):
     """A refusal enqueues nothing: the launch record of the call is empty."""
     refused(q, "Q8K_ERR_SHAPE", q.qmatvec, q.Q8K_Q4_K, A16, 4, 1000, A16, A16, 0)
     assert q.q8k_debug_last_launches() == []
-    refused(q, "Q8K_ERR_QTYPE", q.q8k_debug_moe_subblock_sums, q.Q8K_Q6_K_RELAID, A16, 2, 4, 256, A16, 1, A16, A16, 1,
+    refused(q, "Q8K_ERR_QTYPE", q.q8k_debug_moe_subblock_sums, q.Q8K_Q6_K_GGUF, A16, 2, 4, 256, A16, 1, A16, A16, 1,
             A16, A16, 0)
     assert q.q8k_debug_last_launches() == []
 

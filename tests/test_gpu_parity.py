@@ -432,6 +432,8 @@ def moe_case(q, fmt, E, rows, K, T, topk, seed, ids=None):
     ("q4k", 2, 40, 131072, 3, 2, 39),      # a packed token beyond the LDS stage: one lane per row
     ("q6k", 8, 300, 1024, 16, 2, 34),
     ("q6k", 8, 14336, 4096, 16, 2, 46),    # the MoE decode layer shape in relaid Q6_K
+    ("q6k", 2, 40, 83968, 3, 2, 47),       # Q6_K: one packed token per LDS stage, a slab per token
+    ("q6k", 2, 40, 88064, 3, 2, 48),       # Q6_K: a packed token beyond the stage: the per-chunk kernel
     ("q5k", 8, 14336, 4096, 16, 2, 35),    # the MoE decode layer shape in Q5_K
     ("q5k", 4, 100, 512, 5, 3, 36),
     ("q5k", 16, 64, 256, 200, 4, 37),
@@ -645,6 +647,7 @@ def test_prefill_block_sums_bit_exact(q, fmt, M, rows, K, seed):
 @pytest.mark.parametrize("fmt,E,rows,K,T,topk,seed", [
     ("q4k", 4, 100, 512, 5, 3, 150), ("q4k", 8, 300, 1024, 16, 2, 151), ("q4k", 2, 40, 256, 20, 2, 152),
     ("q5k", 4, 100, 512, 5, 3, 153), ("q5k", 8, 300, 1024, 16, 2, 154),
+    ("q6k", 4, 100, 512, 5, 3, 155), ("q6k", 8, 300, 1024, 16, 2, 156), ("q6k", 2, 40, 256, 20, 2, 157),
 ])
 def test_moe_subblock_sums_bit_exact(q, fmt, E, rows, K, T, topk, seed):
     """qmatvec_moe's matrix-core kernel with its sums flag: each (token, slot)
@@ -652,8 +655,9 @@ def test_moe_subblock_sums_bit_exact(q, fmt, E, rows, K, T, topk, seed):
     bit (more than 8 pairs per expert in the 20-token case: several groups);
     an out-of-range id's entries stay unwritten."""
     g = np.random.default_rng(seed)
-    gen, qt, ot = (synth.q4k_weights, q.Q8K_Q4_K, oracle.Q4_K) if fmt == "q4k" else \
-        (synth.q5k_weights, q.Q8K_Q5_K, oracle.Q5_K)
+    gen, qt, ot = {"q4k": (synth.q4k_weights, q.Q8K_Q4_K, oracle.Q4_K),
+                   "q5k": (synth.q5k_weights, q.Q8K_Q5_K, oracle.Q5_K),
+                   "q6k": (synth.q6k_weights, q.Q8K_Q6_K_RELAID, oracle.Q6_K)}[fmt]
     w = gen(g, E * rows, K)
     x = synth.activations(g, T, K)
     ids, rw = synth.moe_routing(g, T, E, topk)
@@ -661,8 +665,9 @@ def test_moe_subblock_sums_bit_exact(q, fmt, E, rows, K, T, topk, seed):
     ids[1, topk - 1] = E + 3  # selects nothing
     xq = pack_on_device(q, x)
     y = poisoned_f32(T, rows)
-    S = poisoned_i32(T * topk, rows, K // 32)
-    q.q8k_debug_moe_subblock_sums(qt, to_dev(w), E, rows, K, xq, T, to_dev(ids), to_dev(rw), topk, y, S)
+    S = poisoned_i32(T * topk, rows, K // (16 if fmt == "q6k" else 32))  # Q6_K: 16-value sub-blocks
+    q.q8k_debug_moe_subblock_sums(qt, pf_weights(q, fmt, w, E * rows, K), E, rows, K, xq, T, to_dev(ids), to_dev(rw),
+                                  topk, y, S)
     got = host(S)
     oqs, od, obs = oracle.q8k_pack(x)
     per = w.size // E
