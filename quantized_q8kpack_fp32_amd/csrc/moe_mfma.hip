@@ -653,8 +653,9 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q6k_kernel(
                             int I[4] = {0, 0, 0, 0};
                             const long m32 = (long)0xE0E0E0E0E0E0E0E0uLL;  // eight int8 -32
                             const v16i zero = {};
-#pragma unroll
-                            for (int sb = 0; sb < 16; ++sb) {
+                            // sub-block sb's two MFMAs; sub-block sb + 1's are issued
+                            // before sb's fold
+                            auto sums = [&](int sb) {
                                 const int h = sb >> 3, t = (sb >> 1) & 3, c = sb & 1;
                                 const uint2 l2 = lq[4 * h + 2 * (t & 1) + c], h2 = hq[2 * h + c];
                                 const uint32_t bx = ((l2.x >> (4 * (t >> 1))) & 0x0F0F0F0Fu) |
@@ -663,8 +664,10 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q6k_kernel(
                                                     (((h2.y >> (2 * t)) & 0x03030303u) << 4);
                                 const long B = (long)((uint64_t)bx | ((uint64_t)by << 32));
                                 const long A = *reinterpret_cast<const long*>(&sm.tok[xoff + b * QK + 16 * sb + 8 * g]);
-                                v16i S = __builtin_amdgcn_mfma_i32_32x32x16_i8(A, B, zero, 0, 0, 0);
-                                S = __builtin_amdgcn_mfma_i32_32x32x16_i8(A, m32, S, 0, 0, 0);
+                                const v16i S = __builtin_amdgcn_mfma_i32_32x32x16_i8(A, B, zero, 0, 0, 0);
+                                return __builtin_amdgcn_mfma_i32_32x32x16_i8(A, m32, S, 0, 0, 0);
+                            };
+                            auto fold = [&](int sb, const v16i& S) {
                                 const int sc = (int)(int8_t)((scw[sb >> 2] >> (8 * (sb & 3))) & 0xffu);
 #pragma unroll
                                 for (int r = 0; r < 4; ++r) {
@@ -677,6 +680,16 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q6k_kernel(
                                     }
                                     I[r] += __mul24(sc, Ss);  // |Ss| <= 65024, |sc| <= 128
                                 }
+                            };
+                            v16i S0 = sums(0), S1;
+#pragma unroll
+                            for (int sb = 0; sb < 16; sb += 2) {
+                                S1 = sums(sb + 1);
+                                fold(sb, S0);
+                                __builtin_amdgcn_sched_barrier(0);
+                                if (sb + 2 < 16) S0 = sums(sb + 2);
+                                fold(sb + 1, S1);
+                                __builtin_amdgcn_sched_barrier(0);
                             }
                             // acc += (d8 * float(I)) * d: register r < 4 of lane (i, g)
                             // holds pair 4g + r
