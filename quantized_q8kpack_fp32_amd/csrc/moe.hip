@@ -1,5 +1,7 @@
 // Mixture-of-experts decode: expert-indexed mat-vec with the weighted sum of
-// each token's selected experts fused in.
+// each token's selected experts fused in.  These kernels serve K beyond the
+// LDS token stage of the matrix-core kernels (moe_mfma.hip), which take every
+// format below it.
 //
 // "Language models on the device: the cajeta-llm kernels", section 2.4: for a
 // decode, every token's selected experts are visited in one launch and the

@@ -1,4 +1,5 @@
-// Mixture-of-experts decode for Q4_K on the int8 matrix cores.
+// Mixture-of-experts decode on the int8 matrix cores: Q4_K and Q5_K here,
+// relaid Q6_K further below.
 //
 // "Language models on the device: the cajeta-llm kernels", section 2.4: for a
 // decode, every token's selected experts are visited in one launch and each
