@@ -434,6 +434,9 @@ def moe_case(q, fmt, E, rows, K, T, topk, seed, ids=None):
     ("q6k", 8, 14336, 4096, 16, 2, 46),    # the MoE decode layer shape in relaid Q6_K
     ("q6k", 2, 40, 83968, 3, 2, 47),       # Q6_K: one packed token per LDS stage, a slab per token
     ("q6k", 2, 40, 88064, 3, 2, 48),       # Q6_K: a packed token beyond the stage: the per-chunk kernel
+    ("q6k", 1, 29, 256, 3, 1, 49),         # Q6_K: one expert, one slot, fewer rows than a tile
+    ("q6k", 64, 40, 512, 5, 64, 50),       # Q6_K: topk at its limit, two tokens per slab
+    ("q6k", 4, 8200, 256, 40, 4, 51),      # Q6_K: two row tiles per workgroup, two token slabs
     ("q5k", 8, 14336, 4096, 16, 2, 35),    # the MoE decode layer shape in Q5_K
     ("q5k", 4, 100, 512, 5, 3, 36),
     ("q5k", 16, 64, 256, 200, 4, 37),
@@ -451,17 +454,18 @@ def test_moe(q, fmt, E, rows, K, T, topk, seed):
     assert_close(got, want, A, f"moe {fmt} E={E} rows={rows} T={T}")
 
 
-def test_moe_crowded_expert_and_bad_ids(q):
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_moe_crowded_expert_and_bad_ids(q, fmt):
     """20 tokens all choose experts 0 and 1 (more pairs than one group holds);
     an id outside [0, E) selects nothing."""
     E, rows, K, T, topk = 4, 50, 512, 20, 2
     ids = np.tile(np.array([[0, 1]], np.int32), (T, 1))
     ids[3, 1] = 7      # out of range: dropped
     ids[5, 0] = -1     # out of range: dropped
-    got, w, ot, oqs, od, obs, ids, rw = moe_case(q, "q4k", E, rows, K, T, topk, 77, ids=ids)
+    got, w, ot, oqs, od, obs, ids, rw = moe_case(q, fmt, E, rows, K, T, topk, 77, ids=ids)
     ok = (ids >= 0) & (ids < E)
     want, A = oracle.moe(ot, w, E, rows, K, oqs, od, obs, np.where(ok, ids, 0), np.where(ok, rw, 0).astype(np.float32))
-    assert_close(got, want, A, "moe crowded")
+    assert_close(got, want, A, f"moe crowded {fmt}")
 
 
 # ================================================================== MoE prefill (NEXT row)
