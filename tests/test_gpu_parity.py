@@ -173,6 +173,9 @@ def test_q5k_subblock_sums_bit_exact(q, rows, K, seed):
     assert_exact(host(S), oracle.subblock_sums(oracle.Q5_K, w, rows, K, oqs[0]), "S")
     want, A = oracle.matvec(oracle.Q5_K, w, rows, K, oqs, od, obs, nthreads=NTH)
     assert_close(host(y), want[0], A[0], "y of the sums kernel")
+    y1 = poisoned_f32(rows)
+    q.qmatvec(q.Q8K_Q5_K, to_dev(w), rows, K, xq, y1)
+    assert np.array_equal(host(y1).view(np.uint32), host(y).view(np.uint32))
 
 
 @pytest.mark.parametrize("rows,K,seed", [(256, 1024, 50), (4096, 4096, 51), (37, 256, 52), (13, 768, 53),
@@ -657,7 +660,8 @@ def test_moe_subblock_sums_bit_exact(q, fmt, E, rows, K, T, topk, seed):
     """qmatvec_moe's matrix-core kernel with its sums flag: each (token, slot)
     pair's sub-block sums S_j against its expert equal the oracle's bit for
     bit (more than 8 pairs per expert in the 20-token case: several groups);
-    an out-of-range id's entries stay unwritten."""
+    an out-of-range id's entries stay unwritten; its y equals qmatvec_moe's
+    bit for bit."""
     g = np.random.default_rng(seed)
     gen, qt, ot = {"q4k": (synth.q4k_weights, q.Q8K_Q4_K, oracle.Q4_K),
                    "q5k": (synth.q5k_weights, q.Q8K_Q5_K, oracle.Q5_K),
@@ -670,8 +674,8 @@ def test_moe_subblock_sums_bit_exact(q, fmt, E, rows, K, T, topk, seed):
     xq = pack_on_device(q, x)
     y = poisoned_f32(T, rows)
     S = poisoned_i32(T * topk, rows, K // (16 if fmt == "q6k" else 32))  # Q6_K: 16-value sub-blocks
-    q.q8k_debug_moe_subblock_sums(qt, pf_weights(q, fmt, w, E * rows, K), E, rows, K, xq, T, to_dev(ids), to_dev(rw),
-                                  topk, y, S)
+    wd = pf_weights(q, fmt, w, E * rows, K)
+    q.q8k_debug_moe_subblock_sums(qt, wd, E, rows, K, xq, T, to_dev(ids), to_dev(rw), topk, y, S)
     got = host(S)
     oqs, od, obs = oracle.q8k_pack(x)
     per = w.size // E
@@ -686,6 +690,9 @@ def test_moe_subblock_sums_bit_exact(q, fmt, E, rows, K, T, topk, seed):
     wy, A = oracle.moe(ot, w, E, rows, K, oqs, od, obs, np.where(ok, ids, 0), np.where(ok, rw, 0).astype(np.float32),
                        nthreads=NTH)
     assert_close(host(y), wy, A, f"moe y of the sums kernel {fmt}")
+    y1 = poisoned_f32(T, rows)
+    q.qmatvec_moe(qt, wd, E, rows, K, xq, T, to_dev(ids), to_dev(rw), topk, y1)
+    assert np.array_equal(host(y1).view(np.uint32), host(y).view(np.uint32)), f"moe y {fmt}: sums flag changed y"
 
 
 # ================================================================== every column count of every route
