@@ -294,6 +294,15 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
                         auto step = [&](int b, MmW<F::NL>& Wc, MmW<F::NL>& Wfree) __attribute__((always_inline)) {
                             mm_issue_w<Q5>(Wfree, wr, ml, b + 1 < nb ? b + 1 : nb - 1);
                             if (b < 0) return;
+                            // the pairs' side of block b (staged codes, sums and scale) is
+                            // read before the wait for the weights, so its LDS latency hides
+                            // behind the memory wait and the MFMAs wait on no LDS read
+                            v4i av[8];
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)
+                                av[j] = *reinterpret_cast<const v4i*>(xrow + b * QK + 32 * j + 16 * g);
+                            const uint2 bsv = *reinterpret_cast<const uint2*>(bsrow + 16 * b);
+                            const float a8 = d8row[b];
                             mm_wait_w<F::NL>(Wc);
                             // block b through the tile into this wave's lane map
                             wave_lds_fence();
@@ -303,8 +312,6 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
                             wave_lds_fence();
                             const uint8_t* tr = L.tile + i * F::BLK;
                             const uint4 hdr = *reinterpret_cast<const uint4*>(tr);
-                            const uint2 bsv = *reinterpret_cast<const uint2*>(bsrow + 16 * b);
-                            const float a8 = d8row[b];
                             // the row's min-term operands for sub-blocks 4g..4g+3 (-dmin *
                             // m_j, high and low bf16 parts, repeated in both fragment
                             // halves) and d
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q4k_kernel(
                                 const uint32_t sc03 = hy & 0x3F3F3F3Fu;
                                 const uint32_t sc47 = (hw & 0x0F0F0F0Fu) | ((hy >> 2) & 0x30303030u);
                                 auto sums = [&](int j) {
-                                    const v4i aj = *reinterpret_cast<const v4i*>(xrow + b * QK + 32 * j + 16 * g);
+                                    const v4i aj = av[j];
                                     v4i bj;
 #pragma unroll
                                     for (int x = 0; x < 4; ++x) {
@@ -631,12 +638,19 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q6k_kernel(
                         auto step = [&](int b, M6W& Wc, M6W& Wfree) __attribute__((always_inline)) {
                             m6_issue(Wfree, wr, pr, ml, L.dd, drow, b + 1 < nb ? b + 1 : nb - 1);
                             if (b < 0) return;
+                            // the pairs' codes and scale of block b, read before the wait
+                            // for the weights (as in the Q4_K walk)
+                            long av[16];
+#pragma unroll
+                            for (int sb = 0; sb < 16; ++sb)
+                                av[sb] = *reinterpret_cast<const long*>(&sm.tok[xoff + b * QK + 16 * sb + 8 * g]);
+                            const float a8 = d8row[b];
                             m6_wait<M6_LOADS>(Wc);
                             wave_lds_fence();
 #pragma unroll
                             for (int x = 0; x < M6_NL; ++x)
                                 *reinterpret_cast<v4i*>(L.tile + ml.lo[x]) = Wc.c[x];
-                            if (g == 0) L.d8[i] = d8row[b];
+                            if (g == 0) L.d8[i] = a8;
                             wave_lds_fence();
                             const uint8_t* tr = L.tile + i * Q6K_BODY;
                             // this lane's ql pieces (h, t & 1, s & 1) and qh pieces
@@ -664,7 +678,7 @@ __global__ __launch_bounds__(64 * MM_WAVES) void moe_mfma_q6k_kernel(
                                 const uint32_t by = ((l2.y >> (4 * (t >> 1))) & 0x0F0F0F0Fu) |
                                                     (((h2.y >> (2 * t)) & 0x03030303u) << 4);
                                 const long B = (long)((uint64_t)bx | ((uint64_t)by << 32));
-                                const long A = *reinterpret_cast<const long*>(&sm.tok[xoff + b * QK + 16 * sb + 8 * g]);
+                                const long A = av[sb];
                                 const v16i S = __builtin_amdgcn_mfma_i32_32x32x16_i8(A, B, zero, 0, 0, 0);
                                 return __builtin_amdgcn_mfma_i32_32x32x16_i8(A, m32, S, 0, 0, 0);
                             };
